@@ -1,0 +1,304 @@
+"""Pins for the CPU oracle: it is checked against the pages' figures, a
+hand-worked example, closed forms, invariants and brute force, never against
+itself or the GPU library.  CPU only."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import nq_oracle as O
+from tests.conftest import GOLDEN
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand_pm1(g, shape):
+    return np.where(g.random(shape) < 0.5, -1, 1).astype(np.int64)
+
+
+def _layer_from_pm1(U, V, s1, s2):
+    """Pack +-1 integer matrices with the oracle's packer."""
+    d_out, r = U.shape
+    d_in = V.shape[0]
+    return O.LRB(O.pack_ref(U.astype(np.float32)), O.pack_ref(V.T.astype(np.float32)),
+                 s1, s2, d_out, d_in, r)
+
+
+def _py_pack(M):
+    """Independent packer: plain Python integers, one bit at a time."""
+    n_out, n_red = len(M), len(M[0])
+    nw = (n_red + 31) // 32
+    out = [[0] * n_out for _ in range(nw)]
+    for o in range(n_out):
+        for e in range(n_red):
+            if M[o][e] < 0:
+                out[e // 32][o] |= 1 << (e % 32)
+    return np.array(out, dtype=np.uint64).astype(np.uint32)
+
+
+# --------------------------------------------------------------------------
+# hand-worked example
+# --------------------------------------------------------------------------
+
+
+def test_hand_example():
+    ex = _load("hand_example.json")
+    U = np.array(ex["U"], dtype=np.float32)
+    V = np.array(ex["V"], dtype=np.float32)
+    assert np.array_equal(O.pack_ref(U), np.array(ex["u_words"], dtype=np.uint32))
+    assert np.array_equal(O.pack_ref(V.T), np.array(ex["vt_words"], dtype=np.uint32))
+    L = O.LRB(ex["u_words"], ex["vt_words"], ex["s1"], ex["s2"], ex["d_out"], ex["d_in"], ex["r"])
+    assert np.array_equal(O.sign_product_ref(L), np.array(ex["UVt"], dtype=np.float64))
+    assert np.array_equal(O.reconstruct_ref(L), np.array(ex["W"]))
+    assert np.array_equal(O.reconstruct_expected_f32(L), np.array(ex["W"], dtype=np.float32))
+    x = np.array(ex["x"], dtype=np.float32)
+    assert np.array_equal(O.linear_ref(L, x), np.array(ex["y"]))
+    assert np.array_equal(O.linear_factored_ref(L, x), np.array(ex["y"]))
+
+
+# --------------------------------------------------------------------------
+# packing layout: special cases, brute force, round trip
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("n_out,n_red", [(1, 1), (3, 31), (5, 32), (7, 33), (64, 100), (2, 257)])
+def test_single_negative_sets_one_bit(n_out, n_red):
+    g = np.random.default_rng(n_out * 1000 + n_red)
+    for _ in range(5):
+        o, e = int(g.integers(n_out)), int(g.integers(n_red))
+        M = np.ones((n_out, n_red), dtype=np.float32)
+        M[o, e] = -0.5
+        W = O.pack_ref(M)
+        assert W.shape == (O.n_words(n_red), n_out)
+        expect = np.zeros_like(W)
+        expect[e // 32, o] = np.uint32(1) << np.uint32(e % 32)
+        assert np.array_equal(W, expect)
+
+
+def test_all_positive_and_all_negative():
+    M = np.abs(np.random.default_rng(1).standard_normal((9, 70))).astype(np.float32)
+    assert not O.pack_ref(M).any()
+    W = O.pack_ref(-M - 1)
+    # full words are all ones, the last word holds 70-64 = 6 ones and zero padding
+    assert np.all(W[0] == 0xFFFFFFFF) and np.all(W[1] == 0xFFFFFFFF)
+    assert np.all(W[2] == 0x3F)
+
+
+def test_sign_tie_breaks():
+    vals = np.array([[0.0, -0.0, np.nan, -np.inf, np.inf, -1e-45, 1e-45, -np.nan]], dtype=np.float32)
+    W = O.pack_ref(vals)
+    # only -inf (bit 3) and the negative denormal (bit 5) encode -1
+    assert int(W[0, 0]) == (1 << 3) | (1 << 5)
+
+
+@pytest.mark.parametrize("n_out,n_red", [(1, 1), (4, 31), (6, 64), (3, 95), (33, 129)])
+def test_pack_matches_bitwise_brute_force(n_out, n_red):
+    M = np.random.default_rng(7 + n_red).standard_normal((n_out, n_red)).astype(np.float32)
+    assert np.array_equal(O.pack_ref(M), _py_pack(M.tolist()))
+
+
+def test_round_trip():
+    g = np.random.default_rng(3)
+    for n_out, n_red in [(1, 1), (10, 31), (17, 200), (64, 64)]:
+        M = g.standard_normal((n_out, n_red)).astype(np.float32)
+        S = O.unpack_ref(O.pack_ref(M), n_red)
+        assert np.array_equal(S, np.where(M < 0, -1.0, 1.0))
+
+
+def test_unpack_ignores_padding():
+    W = np.full((2, 3), 0xFFFFFFFF, dtype=np.uint32)  # padding bits set on purpose
+    S = O.unpack_ref(W, 40, n_out=2)
+    assert S.shape == (2, 40) and np.all(S == -1.0)
+
+
+# --------------------------------------------------------------------------
+# storage formula against the pages
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("d_out,d_in,r", [(256, 256, 64), (4096, 4096, 2048), (11008, 4096, 2368),
+                                          (96, 64, 32)])
+def test_packed_sizes_match_storage_formula(d_out, d_in, r):
+    # pack only shapes, not values: the buffers' bit counts + fp32 scales
+    u_bits = O.n_words(r) * d_out * 32
+    v_bits = O.n_words(d_in) * r * 32
+    assert u_bits + v_bits + 32 * (d_out + d_in) == O.storage_bits_ref(d_out, d_in, r)
+
+
+def test_small_pack_buffer_bits_equal_formula():
+    U = np.random.default_rng(0).standard_normal((96, 32)).astype(np.float32)
+    V = np.random.default_rng(1).standard_normal((64, 32)).astype(np.float32)
+    bits = O.pack_ref(U).size * 32 + O.pack_ref(V.T).size * 32
+    assert bits + 32 * (96 + 64) == O.storage_bits_ref(96, 64, 32)
+
+
+def test_bits_per_weight_values():
+    assert O.bits_per_weight_ref(256, 256, 64) == pytest.approx(0.75)
+    assert O.bits_per_weight_ref(4096, 4096, 2048) == pytest.approx(1.015625)
+    # the 7B MLP set at r = 2368: about the 0.8 bit/parameter the video quotes
+    claims = _load("storage_claims.json")
+    b = O.bits_per_weight_ref(11008, 4096, 2368)
+    assert abs(b - claims["effective_bits_per_parameter"]["value"]) < 0.01
+
+
+def test_70b_storage_matches_pages():
+    """0.55-bit 70B linears + fp16 embeddings/head ~ 5.75 GB, ~24x (pages)."""
+    claims = _load("storage_claims.json")
+    layer = synth.llama2_70b_layer(0.55)
+    lin_bits = 80 * sum(O.storage_bits_ref(s.d_out, s.d_in, s.r) for s in layer)
+    embed_bits = 2 * 32000 * 8192 * 16  # Llama-2 vocabulary, fp16 embedding + lm_head
+    total_gb = (lin_bits + embed_bits) / 8 / 1e9
+    assert abs(total_gb - claims["compressed_70b_gb"]["value"]) < 0.03
+    ratio = claims["fp16_70b_gb"]["value"] / total_gb
+    assert abs(ratio - claims["compression_ratio_70b"]["value"]) < 0.6
+    assert total_gb < claims["fits_consumer_gpu_gb"]["value"]
+
+
+def test_rank_rule_values():
+    assert [s.r for s in synth.llama2_70b_layer(1.0)] == [4096, 896, 896, 4096, 6336, 6336, 6336]
+    assert [s.r for s in synth.llama2_70b_layer(0.55)] == [2240, 448, 448, 2240, 3456, 3456, 3456]
+
+
+# --------------------------------------------------------------------------
+# closed forms and invariants
+# --------------------------------------------------------------------------
+
+
+def test_rank1_all_ones_closed_form():
+    g = np.random.default_rng(11)
+    d_out, d_in = 7, 13
+    s1 = synth.scales_halfnormal("t/s1", d_out)
+    s2 = synth.scales_halfnormal("t/s2", d_in)
+    L = _layer_from_pm1(np.ones((d_out, 1), np.int64), np.ones((d_in, 1), np.int64), s1, s2)
+    W = O.reconstruct_ref(L)
+    assert np.array_equal(W, np.outer(s1.astype(np.float64), s2.astype(np.float64)))
+    x = g.standard_normal((3, d_in)).astype(np.float32)
+    y = O.linear_ref(L, x)
+    expect = s1.astype(np.float64)[None, :] * (x.astype(np.float64) @ s2.astype(np.float64))[:, None]
+    np.testing.assert_allclose(y, expect, rtol=1e-14, atol=0)
+
+
+def test_joint_flip_and_permutation_invariance():
+    g = np.random.default_rng(5)
+    d_out, d_in, r = 9, 40, 6
+    U, V = _rand_pm1(g, (d_out, r)), _rand_pm1(g, (d_in, r))
+    s1 = synth.scales_halfnormal("f/s1", d_out)
+    s2 = synth.scales_halfnormal("f/s2", d_in)
+    base = O.reconstruct_ref(_layer_from_pm1(U, V, s1, s2))
+    for k in range(r):
+        U2, V2 = U.copy(), V.copy()
+        U2[:, k] *= -1
+        V2[:, k] *= -1
+        assert np.array_equal(O.reconstruct_ref(_layer_from_pm1(U2, V2, s1, s2)), base)
+        # flipping only U's column k subtracts twice that rank-1 term
+        M1 = O.sign_product_ref(_layer_from_pm1(U2, V, s1, s2))
+        M0 = O.sign_product_ref(_layer_from_pm1(U, V, s1, s2))
+        assert np.array_equal(M1, M0 - 2 * np.outer(U[:, k], V[:, k]))
+    perm = g.permutation(r)
+    assert np.array_equal(O.reconstruct_ref(_layer_from_pm1(U[:, perm], V[:, perm], s1, s2)), base)
+
+
+def test_popcount_identity():
+    """(U V^T)[i,j] = r - 2 popcount(u_i xor v_j) with rows packed along r."""
+    g = np.random.default_rng(9)
+    d_out, d_in, r = 6, 11, 45
+    U, V = _rand_pm1(g, (d_out, r)), _rand_pm1(g, (d_in, r))
+    M = O.sign_product_ref(_layer_from_pm1(U, V, np.ones(d_out, np.float32), np.ones(d_in, np.float32)))
+
+    def row_int(v):
+        return sum(1 << k for k in range(r) if v[k] < 0)
+
+    for i in range(d_out):
+        for j in range(d_in):
+            m = r - 2 * bin(row_int(U[i]) ^ row_int(V[j])).count("1")
+            assert M[i, j] == m
+    assert np.all(np.abs(M) <= r) and np.all((M - r) % 2 == 0)
+
+
+@pytest.mark.parametrize("d_out,d_in,r,T", [(1, 1, 1, 1), (3, 5, 2, 3), (5, 33, 31, 1), (33, 3, 33, 3),
+                                            (5, 33, 33, 1)])
+def test_brute_force_exact_fractions(d_out, d_in, r, T):
+    g = np.random.default_rng(d_out * 100 + d_in * 10 + r)
+    U, V = _rand_pm1(g, (d_out, r)), _rand_pm1(g, (d_in, r))
+    s1 = synth.scales_lognormal(f"bf/s1/{d_out}", d_out)
+    s2 = synth.scales_halfnormal(f"bf/s2/{d_in}", d_in)
+    x = synth.round_bf16(g.standard_normal((T, d_in)).astype(np.float32))
+    y = O.linear_ref(_layer_from_pm1(U, V, s1, s2), x)
+    yf = O.linear_factored_ref(_layer_from_pm1(U, V, s1, s2), x)
+    exact = np.zeros((T, d_out))
+    for t in range(T):
+        for i in range(d_out):
+            acc = Fraction(0)
+            for j in range(d_in):
+                m = sum(int(U[i, k]) * int(V[j, k]) for k in range(r))
+                acc += Fraction(float(s1[i])) * m * Fraction(float(s2[j])) * Fraction(float(x[t, j]))
+            exact[t, i] = float(acc)
+    assert O.rel_err(y, exact) <= 1e-12
+    assert O.rel_err(yf, exact) <= 1e-12
+
+
+def test_factored_equals_reconstructed():
+    g = np.random.default_rng(21)
+    d_out, d_in, r, T = 48, 80, 40, 4
+    L = _layer_from_pm1(_rand_pm1(g, (d_out, r)), _rand_pm1(g, (d_in, r)),
+                        synth.scales_halfnormal("fe/s1", d_out), synth.scales_halfnormal("fe/s2", d_in))
+    x = g.standard_normal((T, d_in)).astype(np.float32)
+    assert O.rel_err(O.linear_factored_ref(L, x), O.linear_ref(L, x)) <= 1e-12
+
+
+def test_linearity():
+    g = np.random.default_rng(22)
+    d_out, d_in, r = 20, 30, 8
+    U, V = _rand_pm1(g, (d_out, r)), _rand_pm1(g, (d_in, r))
+    s1 = synth.scales_halfnormal("li/s1", d_out)
+    s2 = synth.scales_halfnormal("li/s2", d_in)
+    L = _layer_from_pm1(U, V, s1, s2)
+    # small integers keep the combination exact in the oracle's fp32 input
+    x1 = g.integers(-50, 50, (2, d_in)).astype(np.float32)
+    x2 = g.integers(-50, 50, (2, d_in)).astype(np.float32)
+    y = O.linear_ref(L, x1 * 2 + x2 * 0.5)
+    np.testing.assert_allclose(y, 2 * O.linear_ref(L, x1) + 0.5 * O.linear_ref(L, x2), rtol=1e-12, atol=1e-14)
+    y1 = O.linear_ref(_layer_from_pm1(U, V, s1 * np.float32(4), s2), x1)
+    np.testing.assert_allclose(y1, 4 * O.linear_ref(L, x1), rtol=1e-14, atol=0)
+    y2 = O.linear_ref(_layer_from_pm1(U, V, s1, s2 * np.float32(0.5)), x1)
+    np.testing.assert_allclose(y2, 0.5 * O.linear_ref(L, x1), rtol=1e-14, atol=0)
+
+
+def test_reconstruct_f32_rounding_emulation():
+    """fl32(fl32(s1*m)*s2) checked with exact float64 products + one rounding each."""
+    g = np.random.default_rng(4)
+    d_out, d_in, r = 12, 37, 33
+    U, V = _rand_pm1(g, (d_out, r)), _rand_pm1(g, (d_in, r))
+    s1 = synth.scales_lognormal("rf/s1", d_out)
+    s2 = synth.scales_lognormal("rf/s2", d_in)
+    W = O.reconstruct_expected_f32(_layer_from_pm1(U, V, s1, s2))
+    for i in range(d_out):
+        for j in range(d_in):
+            m = int(np.dot(U[i], V[j]))
+            a = float(np.float32(float(s1[i]) * m))      # product exact in float64, one rounding
+            w = np.float32(a * float(s2[j]))             # 24x24-bit product exact in float64
+            assert W[i, j] == w and np.signbit(W[i, j]) == np.signbit(w)
+
+
+@pytest.mark.parametrize("chunk", [48, 64, 4096])
+def test_sampled_rows_match_full(chunk):
+    g = np.random.default_rng(8)
+    d_out, d_in, r, T = 40, 150, 70, 3
+    L = _layer_from_pm1(_rand_pm1(g, (d_out, r)), _rand_pm1(g, (d_in, r)),
+                        synth.scales_halfnormal("sr/s1", d_out), synth.scales_halfnormal("sr/s2", d_in))
+    x = g.standard_normal((T, d_in)).astype(np.float32)
+    rows = np.array([0, 7, 39, 12])
+    full = O.linear_ref(L, x)
+    np.testing.assert_allclose(O.sampled_linear_ref(L, x, rows, chunk=chunk), full[:, rows], rtol=1e-12, atol=1e-15)
+
+
+def test_rel_err():
+    a = np.array([3.0, 4.0])
+    assert O.rel_err(a, a) == 0.0
+    assert O.rel_err(a * 1.001, a) == pytest.approx(1e-3)
