@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the NanoQuant low-rank binary (LRB) linear on one MI355X.
+
+Workload (one "step"): one decode token (T=1) through every linear of a
+Llama-2-70B-shaped stack -- 80 layers x {q, k, v, o, gate, up, down} = 560 LRB
+linears at ~1.0 bit/weight (r = d_out*d_in/(d_out+d_in) rounded down to a
+multiple of 64), each y = s1 (.) U (V^T (s2 (.) x)) on its own bf16 input.
+Sign words are drawn directly with SplitMix64 on the device; scales and inputs
+come from the seeded host generators (module synth).  The same run also times
+the 0.55-bit stack (decode) and a T=2048 prefill pass over the ~1.0-bit stack.
+
+Prints ONE JSON line.  value = decode tokens/s of the ~1.0-bit stack.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(shapes, T: int, x_bytes: int = 2) -> int:
+    """Packed signs + fp32 scales + x + fp32 y, per pass over `shapes`."""
+    tot = 0
+    for s in shapes:
+        tot += (s.r * s.d_in + 7) // 8 + (s.r * s.d_out + 7) // 8
+        tot += 4 * (s.d_in + s.d_out) + T * s.d_in * x_bytes + T * s.d_out * 4
+    return tot
+
+
+def algorithmic_flops(shapes, T: int) -> int:
+    return sum(2 * T * s.r * (s.d_in + s.d_out) for s in shapes)
+
+
+class Stack:
+    """All 560 linears of the 70B-shaped stack, resident in HBM."""
+
+    def __init__(self, cfg, n_layers: int, device: str):
+        import torch
+
+        import sub_bit_weight_amd as nq
+        import synth
+        self.cfg, self.n_layers = cfg, n_layers
+        self.shapes = []
+        self.layers = []
+        for l in range(n_layers):
+            for s in cfg.layers:
+                inp = synth.lrb_inputs(cfg, s, l)
+                nwu, nwv = nq.n_words(s.r), nq.n_words(s.d_in)
+                u = nq.fill_random_words(nwu * s.d_out, inp["u_seed"], device).view(nwu, s.d_out)
+                v = nq.fill_random_words(nwv * s.r, inp["v_seed"], device).view(nwv, s.r)
+                self.layers.append(nq.Lrb(s.d_out, s.d_in, s.r, u, v,
+                                          torch.from_numpy(inp["s1"]).to(device),
+                                          torch.from_numpy(inp["s2"]).to(device)))
+                self.shapes.append(s)
+        torch.cuda.synchronize()
+
+
+def time_decode(stack, T: int, steps: int, warmup: int, device: str):
+    import torch
+
+    import sub_bit_weight_amd as nq
+    import synth
+    xs_by_din = {d: torch.from_numpy(synth.x_for(stack.cfg, d, T)).to(device).to(torch.bfloat16)
+                 for d in sorted({s.d_in for s in stack.shapes})}
+    xs = [xs_by_din[s.d_in] for s in stack.shapes]
+    ys = [torch.empty((T, s.d_out), dtype=torch.float32, device=device) for s in stack.shapes]
+    seq = nq.Seq(stack.layers, xs, ys)
+    for _ in range(warmup):
+        seq.run()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        seq.run()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    return ms, seq, xs, ys
+
+
+def parity_sample(stack, xs, ys, idx: int, n_rows: int = 16) -> float:
+    """Oracle check of one linear of the stack on sampled output rows."""
+    import numpy as np
+
+    import synth
+    from oracle import nq_oracle as O
+    s = stack.shapes[idx]
+    l = idx // len(stack.cfg.layers)
+    inp = synth.lrb_inputs(stack.cfg, s, l)
+    nwu, nwv = (s.r + 31) // 32, (s.d_in + 31) // 32
+    ref = O.LRB(synth.random_words(inp["u_seed"], np.arange(nwu * s.d_out, dtype=np.uint64)).reshape(nwu, s.d_out),
+                synth.random_words(inp["v_seed"], np.arange(nwv * s.r, dtype=np.uint64)).reshape(nwv, s.r),
+                inp["s1"], inp["s2"], s.d_out, s.d_in, s.r)
+    rows = np.sort(synth.rng(f"bench/rows/{idx}").choice(s.d_out, n_rows, replace=False))
+    x = xs[idx].float().cpu().numpy()
+    y = ys[idx].cpu().numpy()
+    return O.rel_err(y[:, rows], O.sampled_linear_ref(ref, x, rows))
+
+
+def time_prefill(stack, T: int, device: str, warmup_layers: int = 1):
+    import torch
+
+    import sub_bit_weight_amd as nq
+    import synth
+    per = len(stack.cfg.layers)
+    xs_by_din = {d: torch.from_numpy(synth.x_for(stack.cfg, d, T)).to(device).to(torch.bfloat16)
+                 for d in sorted({s.d_in for s in stack.shapes})}
+    ys = [torch.empty((T, s.d_out), dtype=torch.float32, device=device) for s in stack.shapes[:per]]
+    ws = torch.empty(max(nq.lrb_workspace_bytes(L, T) for L in stack.layers[:per]), dtype=torch.uint8,
+                     device=device)
+    for i in range(warmup_layers * per):
+        nq.lrb_linear(stack.layers[i], xs_by_din[stack.shapes[i].d_in], ys[i % per], ws)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i, L in enumerate(stack.layers):
+        nq.lrb_linear(L, xs_by_din[stack.shapes[i].d_in], ys[i % per], ws)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
+def cpu_baseline(cfg, budget_s: float = 20.0) -> dict:
+    """The oracle (reconstruct in fp64, then multiply) on the host cores, on a
+    bounded sample of the decode step: the k, v and q matrices of layer 0,
+    then extrapolated to the 560-linear step by reconstruction flops."""
+    import numpy as np
+
+    import synth
+    from oracle import nq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                      default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    sample = [s for s in cfg.layers if s.name in ("k", "v", "q")]
+    done_flops, elapsed = 0, 0.0
+    for s in sample:
+        inp = synth.lrb_inputs(cfg, s, 0)
+        nwu, nwv = (s.r + 31) // 32, (s.d_in + 31) // 32
+        ref = O.LRB(synth.random_words(inp["u_seed"], np.arange(nwu * s.d_out, dtype=np.uint64)).reshape(nwu, s.d_out),
+                    synth.random_words(inp["v_seed"], np.arange(nwv * s.r, dtype=np.uint64)).reshape(nwv, s.r),
+                    inp["s1"], inp["s2"], s.d_out, s.d_in, s.r)
+        x = synth.x_for(cfg, s.d_in, 1)
+        t = time.perf_counter()
+        O.linear_ref(ref, x)
+        elapsed += time.perf_counter() - t
+        done_flops += 2 * s.d_out * s.d_in * s.r + 2 * s.d_out * s.d_in
+        if elapsed > budget_s:
+            break
+    step_flops = 80 * sum(2 * s.d_out * s.d_in * s.r + 2 * s.d_out * s.d_in for s in cfg.layers)
+    step_s = elapsed * step_flops / done_flops
+    return {"value": 1.0 / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"oracle linear_ref (fp64 reconstruct-then-multiply) on layer-0 {'/'.join(s.name for s in sample)} "
+                       f"({elapsed:.1f} s), extrapolated by reconstruction flops to the 560-linear T=1 step "
+                       f"({step_s:.0f} s/token)")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=80, help="decoder layers in the stack (80 = Llama-2-70B)")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-055", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (see the design notes "
+              "for how the layer would shard). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+
+    cfg = synth.CONFIGS["70b_stack"]
+    log(f"[bench] building 70B stack (~1.0 bit), {args.layers} layers")
+    stack = Stack(cfg, args.layers, device)
+    T = 1
+    log("[bench] decode T=1")
+    ms, seq, xs, ys = time_decode(stack, T, args.steps, args.warmup, device)
+    bytes_step = algorithmic_bytes(stack.shapes, T)
+    gbs = bytes_step / (ms * 1e-3) / 1e9
+    log(f"[bench] decode {ms:.3f} ms/step, {gbs:.0f} GB/s")
+    err = parity_sample(stack, xs, ys, idx=len(cfg.layers) - 1)
+    log(f"[bench] parity (layer 0 down, 16 rows) rel err {err:.2e}")
+    del seq
+
+    extra = {}
+    if not args.no_prefill:
+        Tp = 2048
+        log("[bench] prefill T=2048")
+        pms = time_prefill(stack, Tp, device)
+        flops = algorithmic_flops(stack.shapes, Tp)
+        extra["prefill"] = {"T": Tp, "ms_per_pass": pms, "tflops": flops / (pms * 1e-3) / 1e12,
+                            "frac_of_bf16_peak": flops / (pms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                            "tokens_per_s": Tp / (pms * 1e-3), "algorithmic_flop": flops}
+        log(f"[bench] prefill {pms:.1f} ms/pass, {extra['prefill']['tflops']:.0f} TFLOP/s")
+    del stack
+    torch.cuda.empty_cache()
+
+    if not args.no_055:
+        cfg55 = synth.CONFIGS["70b_stack_055"]
+        log("[bench] decode T=1, 0.55-bit stack")
+        st55 = Stack(cfg55, args.layers, device)
+        ms55, seq55, _, _ = time_decode(st55, 1, args.steps, args.warmup, device)
+        b55 = algorithmic_bytes(st55.shapes, 1)
+        extra["decode_055bit"] = {"ms_per_step": ms55, "tokens_per_s": 1000.0 / ms55,
+                                  "hbm_gbs": b55 / (ms55 * 1e-3) / 1e9, "algorithmic_bytes": b55}
+        del seq55, st55
+        torch.cuda.empty_cache()
+
+    out = {
+        "metric": "decode tokens/s + HBM GB/s (T=1), prefill TFLOP/s (T=2048), 70B-shaped LRB layers",
+        "value": T * 1000.0 / ms,
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": f"Llama-2-70B-shaped LRB linear stack, {args.layers} layers x 7 linears, "
+                               f"~1.0 bit/weight, T=1 decode, bf16 x, fp32 y",
+                   "global_batch": T, "layers": args.layers, "parallelism": "single-gpu"},
+        "hbm_gbs": gbs,
+        "algorithmic_bytes_per_step": bytes_step,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "parity_rel_err": err,
+    }
+    out.update(extra)
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,186 @@
+/*
+ * nq.h -- C ABI of libnq, the MI355X (gfx950) library for NanoQuant's
+ * low-rank binary (LRB) linear layer.
+ *
+ * The layer (research.samsung.com blog "NanoQuant: Efficient Sub-1-Bit
+ * Quantization of Large Language Models", section 2 "Problem Formulation and
+ * Background", subsection "Low-Rank Binary Factorization", the factorization
+ * equation) approximates a weight matrix W (d_out x d_in) by
+ *
+ *     W[i,j] = s1[i] * (sum_k U[i,k] * V[j,k]) * s2[j],
+ *
+ * with U in {-1,+1}^(d_out x r), V in {-1,+1}^(d_in x r) and real scale vectors
+ * s1 (d_out) and s2 (d_in).  The library evaluates y = W x for T tokens in the
+ * factored order y = s1 (.) U (V^T (s2 (.) x)) without forming W.
+ *
+ * Conventions shared by every call:
+ *  - Every pointer argument except `const nq_lrb*`, `nq_seq*` and the arrays of
+ *    nq_seq_create is DEVICE memory of the current HIP device.  The caller
+ *    allocates and frees all device buffers; libnq keeps no device allocation.
+ *  - Every call that launches work enqueues it on `stream` (a hipStream_t
+ *    passed as void*; NULL is the default stream) and returns without waiting.
+ *    Device faults surface at the caller's next synchronisation.
+ *  - Arguments are validated on the host before any HIP call.  A failed check
+ *    returns a non-zero status, launches nothing, and sets a thread-local
+ *    message readable with nq_last_error().  No C++ exception crosses the ABI.
+ *  - Buffers passed to one call must not overlap unless stated.
+ *  - Calls are re-entrant; different streams may be used concurrently.
+ *
+ * Sign-word layout (the "packed integer format"; the pages say only that the
+ * frozen binary factors are packed into integer formats, section 3 "Phase 3:
+ * Scale-Only Model Reconstruction"):
+ *  A stage with n_out outputs and a reduction of length n_red is stored as
+ *  words[w][o], w < ceil(n_red/32), o < n_out, with row stride ld >= n_out
+ *  (in 32-bit words).  Bit b of words[w][o] is 1 exactly when the sign of
+ *  element (o, 32w+b) is -1.  Bits for 32w+b >= n_red are 0.
+ *    U   is stored with outputs i < d_out and reduction k < r    (words along r),
+ *    V^T is stored with outputs k < r     and reduction j < d_in (words along d_in).
+ *  With dimensions that are multiples of 32 and ld = n_out the two buffers hold
+ *  exactly r(d_out+d_in) bits, the storage the pages give for the signs
+ *  (section 2, the sentence after the factorization equation).
+ */
+#ifndef NQ_H
+#define NQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NQ_OK = 0,
+  NQ_ERR_ARG = 1,         /* invalid argument (null pointer, bad size, bad stride) */
+  NQ_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. a shape limit)        */
+  NQ_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required           */
+  NQ_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed           */
+} nq_status;
+
+typedef enum { NQ_F32 = 0, NQ_BF16 = 1 } nq_dtype;
+
+/* One packed LRB matrix.  A host struct, read only during a call. */
+typedef struct {
+  int64_t d_out, d_in, r;   /* all >= 1 */
+  const uint32_t* u_bits;   /* [ceil(r/32)][ldu] words, ldu >= d_out   */
+  int64_t ldu;
+  const uint32_t* vt_bits;  /* [ceil(d_in/32)][ldv] words, ldv >= r    */
+  int64_t ldv;
+  const float* s1;          /* [d_out] fp32 */
+  const float* s2;          /* [d_in]  fp32 */
+} nq_lrb;
+
+/*
+ * nq_pack_signs -- pack the signs of a real matrix into sign words.
+ * The binary factors are sign(U) and sign(V) of real latent factors (section 3
+ * "Step 3: Factorized Component Refinement"); once frozen they are packed into
+ * integer formats (section 3 "Phase 3").
+ *   dst[w*ld + o] bit b = (src[o*stride_out + (32w+b)*stride_red] < 0.0f)
+ * for o < n_out, 32w+b < n_red; padding bits are 0; dst columns n_out..ld-1 are
+ * not written.  sign() reads -1 only for values < 0 under IEEE comparison:
+ * +0, -0 and NaN pack as +1.
+ *   U latent [d_out][r]:  n_out=d_out, n_red=r,    stride_out=r, stride_red=1
+ *   V latent [d_in][r]:   n_out=r,     n_red=d_in, stride_out=1, stride_red=r
+ * Errors: NQ_ERR_ARG for null pointers, n_out or n_red < 1, strides < 1,
+ * ld < n_out.
+ */
+nq_status nq_pack_signs(const float* src, int64_t n_out, int64_t n_red,
+                        int64_t stride_out, int64_t stride_red,
+                        uint32_t* dst, int64_t ld, void* stream);
+
+/*
+ * nq_unpack_signs -- inverse of nq_pack_signs for checking the layout.
+ *   dst[o*n_red + e] = bit(words[e/32][o], e%32) ? -1.0f : +1.0f
+ * dst is [n_out][n_red] fp32, row-major.  Padding bits are ignored.
+ * Errors: NQ_ERR_ARG as for nq_pack_signs.
+ */
+nq_status nq_unpack_signs(const uint32_t* bits, int64_t n_out, int64_t n_red, int64_t ld,
+                          float* dst, void* stream);
+
+/*
+ * nq_lrb_workspace_bytes -- device workspace nq_lrb_linear needs for T tokens
+ * (the rank-r intermediate t and split-reduction partial sums).  Returns 0 if
+ * the arguments are invalid (see nq_lrb_linear).
+ */
+size_t nq_lrb_workspace_bytes(const nq_lrb* L, int64_t T);
+
+/*
+ * nq_lrb_linear -- y = s1 (.) U (V^T (s2 (.) x)) for T tokens.
+ * The pages run binary GEMV kernels for token-by-token decoding and binary GEMM
+ * kernels for batches (section 4 "Results", subsection "Inference Performance").
+ *   x: [T][d_in] row-major, fp32 or bf16 (x_dtype);  y: [T][d_out] fp32.
+ *   workspace: at least nq_lrb_workspace_bytes(L, T) bytes, 256-byte aligned.
+ * Regimes: T <= 8 runs the decode kernels (fp32 arithmetic throughout);
+ * T > 8 runs the matrix-core kernels (bf16 operands, fp32 accumulation, one
+ * operand of the cheaper stage split into two bf16 terms).
+ * y is fully overwritten.  Summation order is fixed: results are run-to-run
+ * deterministic, but not bitwise equal across regimes.
+ * Errors: NQ_ERR_ARG for null pointers, dims < 1, ldu < d_out, ldv < r, T < 1,
+ * an unknown dtype or a misaligned pointer (x, y: 4 bytes; bits, scales: 4
+ * bytes); NQ_ERR_WORKSPACE when workspace_bytes is too small;
+ * NQ_ERR_HIP when a launch fails.
+ */
+nq_status nq_lrb_linear(const nq_lrb* L, const void* x, nq_dtype x_dtype, int64_t T,
+                        float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nq_reconstruct -- the dense W for checking (the factorization equation):
+ *   w[i*d_in + j] = fl32( fl32(s1[i] * m) * s2[j] ),  m = sum_k U[i,k] V[j,k]
+ * with m an exact integer and both products rounded to nearest even, so the
+ * result is unique bit for bit.  w is [d_out][d_in] fp32.
+ * Errors: NQ_ERR_ARG as for nq_lrb_linear; NQ_ERR_UNSUPPORTED for r > 65536.
+ */
+nq_status nq_reconstruct(const nq_lrb* L, float* w, void* stream);
+
+/*
+ * nq_storage_bits -- storage of one LRB matrix in bits: r(d_out+d_in) signs
+ * plus (d_out+d_in) fp32 scales (section 2, the sentence after the
+ * factorization equation).  Returns 0 for non-positive arguments.  Host only.
+ */
+uint64_t nq_storage_bits(int64_t d_out, int64_t d_in, int64_t r);
+
+/*
+ * Sequences of independent LRB linears (e.g. every linear of a decoder stack)
+ * run as one device-side schedule.  Running the sequence is equivalent to
+ * calling nq_lrb_linear on each entry in order, except that consecutive entries
+ * may overlap (each entry's inputs must not depend on another entry's output).
+ *
+ * nq_seq_create: host-only planning.  `layers`, `xs`, `ys` are host arrays of
+ *   n entries (the nq_lrb structs are copied; xs[i], ys[i] are device
+ *   pointers).  All entries share T and x_dtype.  The decode regime (T <= 8)
+ *   runs as one persistent kernel; T > 8 runs the per-entry kernels.
+ *   Errors: as for nq_lrb_linear, per entry.
+ * nq_seq_workspace_bytes: device workspace the plan needs.
+ * nq_seq_run: runs the whole sequence on `stream`.  The workspace must stay
+ *   the same buffer across runs of one plan (the first run uploads the
+ *   schedule into it) and must not be shared by plans running concurrently.
+ * nq_seq_destroy: frees the host plan.
+ */
+typedef struct nq_seq nq_seq;
+nq_status nq_seq_create(const nq_lrb* layers, const void* const* xs, float* const* ys, int64_t n,
+                        nq_dtype x_dtype, int64_t T, nq_seq** out);
+size_t nq_seq_workspace_bytes(const nq_seq* s);
+nq_status nq_seq_run(nq_seq* s, void* workspace, size_t workspace_bytes, void* stream);
+void nq_seq_destroy(nq_seq* s);
+
+/*
+ * nq_fill_random_words -- synthetic sign words for large benchmark matrices:
+ *   dst[i] = low 32 bits of SplitMix64(seed, i), i < n, where SplitMix64(seed,
+ *   i) is output number i+1 of the SplitMix64 stream started at `seed`
+ *   (Steele, Lea, Flood 2014).  Uniform words give iid +-1 signs.  This is an
+ *   input generator, not part of the layer.  Errors: NQ_ERR_ARG for a null
+ *   dst or n < 0.
+ */
+nq_status nq_fill_random_words(uint32_t* dst, int64_t n, uint64_t seed, void* stream);
+
+/* Thread-local message for the last non-OK status of this thread ("" if none). */
+const char* nq_last_error(void);
+
+/* Library version string. */
+const char* nq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NQ_H */

@@ -1,0 +1,270 @@
+"""Python binding of libnq (NanoQuant low-rank binary linear layer on MI355X).
+
+Argument marshalling only: every computation runs in the HIP kernels of
+libnq.so.  torch provides device memory and the current HIP stream.  There is
+no fallback: if libnq.so is missing or fails to load, every call raises.
+
+Names follow the C ABI in include/nq.h:
+  pack_signs, unpack_signs, lrb_linear, lrb_workspace_bytes, reconstruct,
+  storage_bits, fill_random_words, Seq (nq_seq_*), last_error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnq.so")
+
+NQ_OK, NQ_ERR_ARG, NQ_ERR_UNSUPPORTED, NQ_ERR_WORKSPACE, NQ_ERR_HIP = range(5)
+NQ_F32, NQ_BF16 = 0, 1
+STATUS_NAMES = {0: "NQ_OK", 1: "NQ_ERR_ARG", 2: "NQ_ERR_UNSUPPORTED", 3: "NQ_ERR_WORKSPACE", 4: "NQ_ERR_HIP"}
+
+EXPORTED = [
+    "nq_pack_signs", "nq_unpack_signs", "nq_lrb_workspace_bytes", "nq_lrb_linear", "nq_reconstruct",
+    "nq_storage_bits", "nq_seq_create", "nq_seq_workspace_bytes", "nq_seq_run", "nq_seq_destroy",
+    "nq_fill_random_words", "nq_last_error", "nq_version",
+]
+
+
+class NqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class nq_lrb(ctypes.Structure):
+    _fields_ = [
+        ("d_out", ctypes.c_int64), ("d_in", ctypes.c_int64), ("r", ctypes.c_int64),
+        ("u_bits", ctypes.c_void_p), ("ldu", ctypes.c_int64),
+        ("vt_bits", ctypes.c_void_p), ("ldv", ctypes.c_int64),
+        ("s1", ctypes.c_void_p), ("s2", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libnq.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sub_bit_weight_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp, u64, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_size_t
+    st = ctypes.c_int
+    P = ctypes.POINTER
+    L.nq_pack_signs.argtypes = [vp, i64, i64, i64, i64, vp, i64, vp]
+    L.nq_pack_signs.restype = st
+    L.nq_unpack_signs.argtypes = [vp, i64, i64, i64, vp, vp]
+    L.nq_unpack_signs.restype = st
+    L.nq_lrb_workspace_bytes.argtypes = [P(nq_lrb), i64]
+    L.nq_lrb_workspace_bytes.restype = sz
+    L.nq_lrb_linear.argtypes = [P(nq_lrb), vp, ctypes.c_int, i64, vp, vp, sz, vp]
+    L.nq_lrb_linear.restype = st
+    L.nq_reconstruct.argtypes = [P(nq_lrb), vp, vp]
+    L.nq_reconstruct.restype = st
+    L.nq_storage_bits.argtypes = [i64, i64, i64]
+    L.nq_storage_bits.restype = u64
+    L.nq_seq_create.argtypes = [P(nq_lrb), P(vp), P(vp), i64, ctypes.c_int, i64, P(vp)]
+    L.nq_seq_create.restype = st
+    L.nq_seq_workspace_bytes.argtypes = [vp]
+    L.nq_seq_workspace_bytes.restype = sz
+    L.nq_seq_run.argtypes = [vp, vp, sz, vp]
+    L.nq_seq_run.restype = st
+    L.nq_seq_destroy.argtypes = [vp]
+    L.nq_seq_destroy.restype = None
+    L.nq_fill_random_words.argtypes = [vp, i64, u64, vp]
+    L.nq_fill_random_words.restype = st
+    L.nq_last_error.argtypes = []
+    L.nq_last_error.restype = ctypes.c_char_p
+    L.nq_version.argtypes = []
+    L.nq_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().nq_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != NQ_OK:
+        raise NqError(status, last_error())
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def n_words(n: int) -> int:
+    return (int(n) + 31) // 32
+
+
+# ---------------------------------------------------------------- packing
+
+
+def pack_signs(src: torch.Tensor, n_out: int, n_red: int, stride_out: int, stride_red: int,
+               out: torch.Tensor | None = None, ld: int | None = None, stream=None) -> torch.Tensor:
+    """Sign words [ceil(n_red/32)][ld] (int32 storage of uint32 words)."""
+    _dev(src, "src")
+    if src.dtype != torch.float32:
+        raise ValueError("src must be float32")
+    ld = n_out if ld is None else ld
+    if out is None:
+        out = torch.zeros((n_words(n_red), ld), dtype=torch.int32, device=src.device)
+    _check(lib().nq_pack_signs(_ptr(src), n_out, n_red, stride_out, stride_red, _ptr(out), ld, _stream(stream)))
+    return out
+
+
+def pack_u(U_latent: torch.Tensor, ld: int | None = None) -> torch.Tensor:
+    """U latent [d_out][r] -> U words [ceil(r/32)][ld]."""
+    d_out, r = U_latent.shape
+    return pack_signs(U_latent, d_out, r, r, 1, ld=ld)
+
+
+def pack_v(V_latent: torch.Tensor, ld: int | None = None) -> torch.Tensor:
+    """V latent [d_in][r] -> V^T words [ceil(d_in/32)][ld]."""
+    d_in, r = V_latent.shape
+    return pack_signs(V_latent, r, d_in, 1, r, ld=ld)
+
+
+def unpack_signs(bits: torch.Tensor, n_out: int, n_red: int, ld: int | None = None,
+                 stream=None) -> torch.Tensor:
+    _dev(bits, "bits")
+    ld = bits.shape[1] if ld is None else ld
+    out = torch.empty((n_out, n_red), dtype=torch.float32, device=bits.device)
+    _check(lib().nq_unpack_signs(_ptr(bits), n_out, n_red, ld, _ptr(out), _stream(stream)))
+    return out
+
+
+def fill_random_words(n: int, seed: int, device="cuda", out: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Synthetic sign words: low 32 bits of SplitMix64(seed, i) (an input generator)."""
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=device)
+    _check(lib().nq_fill_random_words(_ptr(out), n, seed & 0xFFFFFFFFFFFFFFFF, _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------- layer
+
+
+@dataclass
+class Lrb:
+    """One packed LRB matrix on the device (the tensors are kept alive here)."""
+    d_out: int
+    d_in: int
+    r: int
+    u_bits: torch.Tensor   # [ceil(r/32)][ldu] int32
+    vt_bits: torch.Tensor  # [ceil(d_in/32)][ldv] int32
+    s1: torch.Tensor       # [d_out] float32
+    s2: torch.Tensor       # [d_in] float32
+
+    def struct(self) -> nq_lrb:
+        for name in ("u_bits", "vt_bits", "s1", "s2"):
+            _dev(getattr(self, name), name)
+        return nq_lrb(self.d_out, self.d_in, self.r,
+                      self.u_bits.data_ptr(), self.u_bits.shape[1],
+                      self.vt_bits.data_ptr(), self.vt_bits.shape[1],
+                      self.s1.data_ptr(), self.s2.data_ptr())
+
+
+def _x_dtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return NQ_F32
+    if x.dtype == torch.bfloat16:
+        return NQ_BF16
+    raise ValueError(f"x dtype {x.dtype} not supported (float32 or bfloat16)")
+
+
+def lrb_workspace_bytes(layer: Lrb, T: int) -> int:
+    s = layer.struct()
+    return int(lib().nq_lrb_workspace_bytes(ctypes.byref(s), T))
+
+
+def lrb_linear(layer: Lrb, x: torch.Tensor, y: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = s1 (.) U (V^T (s2 (.) x)); x [T][d_in] fp32/bf16 -> y [T][d_out] fp32."""
+    _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != layer.d_in:
+        raise ValueError(f"x must be [T][{layer.d_in}], got {tuple(x.shape)}")
+    T = x.shape[0]
+    s = layer.struct()
+    if y is None:
+        y = torch.empty((T, layer.d_out), dtype=torch.float32, device=x.device)
+    need = int(lib().nq_lrb_workspace_bytes(ctypes.byref(s), T))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().nq_lrb_linear(ctypes.byref(s), _ptr(x), _x_dtype(x), T, _ptr(y), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y
+
+
+def reconstruct(layer: Lrb, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    s = layer.struct()
+    if out is None:
+        out = torch.empty((layer.d_out, layer.d_in), dtype=torch.float32, device=layer.s1.device)
+    _check(lib().nq_reconstruct(ctypes.byref(s), _ptr(out), _stream(stream)))
+    return out
+
+
+def storage_bits(d_out: int, d_in: int, r: int) -> int:
+    return int(lib().nq_storage_bits(d_out, d_in, r))
+
+
+class Seq:
+    """A planned sequence of independent LRB linears (nq_seq_*)."""
+
+    def __init__(self, layers: list[Lrb], xs: list[torch.Tensor], ys: list[torch.Tensor]):
+        if not (len(layers) == len(xs) == len(ys)) or not layers:
+            raise ValueError("layers, xs, ys must be non-empty lists of equal length")
+        T = xs[0].shape[0]
+        xd = _x_dtype(xs[0])
+        for x, y, L in zip(xs, ys, layers):
+            _dev(x, "x")
+            _dev(y, "y")
+            if x.shape != (T, L.d_in) or _x_dtype(x) != xd or y.shape != (T, L.d_out) or y.dtype != torch.float32:
+                raise ValueError("inconsistent x/y shapes or dtypes in sequence")
+        n = len(layers)
+        self._keep = (layers, xs, ys)
+        self._structs = (nq_lrb * n)(*[L.struct() for L in layers])
+        self._xs = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+        self._ys = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+        h = ctypes.c_void_p()
+        _check(lib().nq_seq_create(self._structs, self._xs, self._ys, n, xd, T, ctypes.byref(h)))
+        self._h = h
+        self.workspace_bytes = int(lib().nq_seq_workspace_bytes(h))
+        self.workspace = torch.empty(max(self.workspace_bytes, 1), dtype=torch.uint8, device=xs[0].device)
+
+    def run(self, stream=None) -> None:
+        _check(lib().nq_seq_run(self._h, _ptr(self.workspace), self.workspace.numel(), _stream(stream)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib().nq_seq_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,213 @@
+// C ABI of libnq: argument validation, status codes and dispatch.
+// Every check runs on the host before any HIP call; no exception crosses the ABI.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "nq_internal.h"
+
+namespace nq {
+
+namespace {
+thread_local char g_err[512] = "";
+}
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+nq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return NQ_OK;
+  set_error("%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  return NQ_ERR_HIP;
+}
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+nq_status check_words(const char* who, const void* p, int64_t n_out, int64_t n_red, int64_t ld) {
+  if (!p) return set_error("%s: null pointer", who), NQ_ERR_ARG;
+  if (n_out < 1 || n_red < 1) return set_error("%s: n_out=%lld n_red=%lld must be >= 1", who, (long long)n_out, (long long)n_red), NQ_ERR_ARG;
+  if (ld < n_out) return set_error("%s: ld=%lld < n_out=%lld", who, (long long)ld, (long long)n_out), NQ_ERR_ARG;
+  if (!aligned(p, 4)) return set_error("%s: pointer not 4-byte aligned", who), NQ_ERR_ARG;
+  return NQ_OK;
+}
+
+nq_status check_lrb(const char* who, const nq_lrb* L) {
+  if (!L) return set_error("%s: null layer", who), NQ_ERR_ARG;
+  if (L->d_out < 1 || L->d_in < 1 || L->r < 1)
+    return set_error("%s: d_out=%lld d_in=%lld r=%lld must be >= 1", who, (long long)L->d_out,
+                     (long long)L->d_in, (long long)L->r), NQ_ERR_ARG;
+  if (L->r > (int64_t(1) << 24))
+    return set_error("%s: r=%lld exceeds 2^24", who, (long long)L->r), NQ_ERR_UNSUPPORTED;
+  if (L->d_out > (int64_t(1) << 31) || L->d_in > (int64_t(1) << 31))
+    return set_error("%s: dimension exceeds 2^31", who), NQ_ERR_UNSUPPORTED;
+  nq_status st;
+  if ((st = check_words(who, L->u_bits, L->d_out, L->r, L->ldu)) != NQ_OK) return st;
+  if ((st = check_words(who, L->vt_bits, L->r, L->d_in, L->ldv)) != NQ_OK) return st;
+  if (!L->s1 || !L->s2) return set_error("%s: null scale vector", who), NQ_ERR_ARG;
+  if (!aligned(L->s1, 4) || !aligned(L->s2, 4)) return set_error("%s: scale vector not 4-byte aligned", who), NQ_ERR_ARG;
+  return NQ_OK;
+}
+
+nq_status check_io(const char* who, const nq_lrb* L, const void* x, nq_dtype xd, int64_t T, const float* y) {
+  if (T < 1) return set_error("%s: T=%lld must be >= 1", who, (long long)T), NQ_ERR_ARG;
+  if (T > (int64_t(1) << 24)) return set_error("%s: T=%lld too large", who, (long long)T), NQ_ERR_UNSUPPORTED;
+  if (xd != NQ_F32 && xd != NQ_BF16) return set_error("%s: unknown x dtype %d", who, (int)xd), NQ_ERR_ARG;
+  if (!x || !y) return set_error("%s: null x or y", who), NQ_ERR_ARG;
+  if (!aligned(x, xd == NQ_F32 ? 4 : 2) || !aligned(y, 4))
+    return set_error("%s: x or y misaligned", who), NQ_ERR_ARG;
+  (void)L;
+  return NQ_OK;
+}
+
+constexpr int64_t kDecodeMaxT = 8;
+
+size_t linear_workspace(const nq_lrb& L, int64_t T) {
+  return T <= kDecodeMaxT ? decode_workspace_bytes(L, T) : prefill_workspace_bytes(L, T);
+}
+
+hipError_t launch_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
+                         hipStream_t s) {
+  return T <= kDecodeMaxT ? launch_decode(L, x, xd, T, y, ws, s) : launch_prefill(L, x, xd, T, y, ws, s);
+}
+
+}  // namespace
+}  // namespace nq
+
+struct nq_seq {
+  std::vector<nq_lrb> layers;
+  std::vector<const void*> xs;
+  std::vector<float*> ys;
+  nq_dtype xd;
+  int64_t T;
+  size_t ws_bytes;
+};
+
+using namespace nq;
+
+extern "C" {
+
+const char* nq_last_error(void) { return g_err; }
+
+const char* nq_version(void) { return "libnq 0.1 (gfx950)"; }
+
+uint64_t nq_storage_bits(int64_t d_out, int64_t d_in, int64_t r) {
+  if (d_out < 1 || d_in < 1 || r < 1) return 0;
+  return (uint64_t)r * (uint64_t)(d_out + d_in) + 32ull * (uint64_t)(d_out + d_in);
+}
+
+nq_status nq_pack_signs(const float* src, int64_t n_out, int64_t n_red, int64_t stride_out,
+                        int64_t stride_red, uint32_t* dst, int64_t ld, void* stream) {
+  clear_error();
+  if (!src) return set_error("nq_pack_signs: null src"), NQ_ERR_ARG;
+  if (stride_out < 1 || stride_red < 1) return set_error("nq_pack_signs: strides must be >= 1"), NQ_ERR_ARG;
+  if (!aligned(src, 4)) return set_error("nq_pack_signs: src not 4-byte aligned"), NQ_ERR_ARG;
+  nq_status st = check_words("nq_pack_signs", dst, n_out, n_red, ld);
+  if (st != NQ_OK) return st;
+  return hip_status(launch_pack(src, n_out, n_red, stride_out, stride_red, dst, ld, (hipStream_t)stream),
+                    "nq_pack_signs launch");
+}
+
+nq_status nq_unpack_signs(const uint32_t* bits, int64_t n_out, int64_t n_red, int64_t ld, float* dst,
+                          void* stream) {
+  clear_error();
+  nq_status st = check_words("nq_unpack_signs", bits, n_out, n_red, ld);
+  if (st != NQ_OK) return st;
+  if (!dst) return set_error("nq_unpack_signs: null dst"), NQ_ERR_ARG;
+  if (!aligned(dst, 4)) return set_error("nq_unpack_signs: dst not 4-byte aligned"), NQ_ERR_ARG;
+  return hip_status(launch_unpack(bits, n_out, n_red, ld, dst, (hipStream_t)stream), "nq_unpack_signs launch");
+}
+
+size_t nq_lrb_workspace_bytes(const nq_lrb* L, int64_t T) {
+  if (check_lrb("nq_lrb_workspace_bytes", L) != NQ_OK || T < 1 || T > (int64_t(1) << 24)) return 0;
+  return linear_workspace(*L, T);
+}
+
+nq_status nq_lrb_linear(const nq_lrb* L, const void* x, nq_dtype x_dtype, int64_t T, float* y,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  nq_status st = check_lrb("nq_lrb_linear", L);
+  if (st != NQ_OK) return st;
+  if ((st = check_io("nq_lrb_linear", L, x, x_dtype, T, y)) != NQ_OK) return st;
+  const size_t need = linear_workspace(*L, T);
+  if (!workspace || workspace_bytes < need)
+    return set_error("nq_lrb_linear: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0, need),
+           NQ_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return set_error("nq_lrb_linear: workspace not 256-byte aligned"), NQ_ERR_ARG;
+  return hip_status(launch_linear(*L, x, x_dtype, T, y, workspace, (hipStream_t)stream), "nq_lrb_linear launch");
+}
+
+nq_status nq_reconstruct(const nq_lrb* L, float* w, void* stream) {
+  clear_error();
+  nq_status st = check_lrb("nq_reconstruct", L);
+  if (st != NQ_OK) return st;
+  if (!w) return set_error("nq_reconstruct: null w"), NQ_ERR_ARG;
+  if (!aligned(w, 4)) return set_error("nq_reconstruct: w not 4-byte aligned"), NQ_ERR_ARG;
+  return hip_status(launch_reconstruct(*L, w, (hipStream_t)stream), "nq_reconstruct launch");
+}
+
+nq_status nq_fill_random_words(uint32_t* dst, int64_t n, uint64_t seed, void* stream) {
+  clear_error();
+  if (!dst || n < 0) return set_error("nq_fill_random_words: null dst or n < 0"), NQ_ERR_ARG;
+  if (!aligned(dst, 4)) return set_error("nq_fill_random_words: dst not 4-byte aligned"), NQ_ERR_ARG;
+  return hip_status(launch_fill_words(dst, n, seed, (hipStream_t)stream), "nq_fill_random_words launch");
+}
+
+nq_status nq_seq_create(const nq_lrb* layers, const void* const* xs, float* const* ys, int64_t n,
+                        nq_dtype x_dtype, int64_t T, nq_seq** out) {
+  clear_error();
+  if (!out) return set_error("nq_seq_create: null out"), NQ_ERR_ARG;
+  *out = nullptr;
+  if (!layers || !xs || !ys || n < 1) return set_error("nq_seq_create: empty or null arrays"), NQ_ERR_ARG;
+  nq_seq* s = new (std::nothrow) nq_seq;
+  if (!s) return set_error("nq_seq_create: out of host memory"), NQ_ERR_ARG;
+  s->xd = x_dtype;
+  s->T = T;
+  s->ws_bytes = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    char who[64];
+    snprintf(who, sizeof(who), "nq_seq_create[%lld]", (long long)i);
+    nq_status st = check_lrb(who, &layers[i]);
+    if (st == NQ_OK) st = check_io(who, &layers[i], xs[i], x_dtype, T, ys[i]);
+    if (st != NQ_OK) {
+      delete s;
+      return st;
+    }
+    s->layers.push_back(layers[i]);
+    s->xs.push_back(xs[i]);
+    s->ys.push_back(ys[i]);
+    s->ws_bytes = std::max<size_t>(s->ws_bytes, linear_workspace(layers[i], T));
+  }
+  *out = s;
+  return NQ_OK;
+}
+
+size_t nq_seq_workspace_bytes(const nq_seq* s) { return s ? s->ws_bytes : 0; }
+
+nq_status nq_seq_run(nq_seq* s, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (!s) return set_error("nq_seq_run: null plan"), NQ_ERR_ARG;
+  if (!workspace || workspace_bytes < s->ws_bytes)
+    return set_error("nq_seq_run: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0, s->ws_bytes),
+           NQ_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return set_error("nq_seq_run: workspace not 256-byte aligned"), NQ_ERR_ARG;
+  for (size_t i = 0; i < s->layers.size(); ++i) {
+    hipError_t e = launch_linear(s->layers[i], s->xs[i], s->xd, s->T, s->ys[i], workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "nq_seq_run launch");
+  }
+  return NQ_OK;
+}
+
+void nq_seq_destroy(nq_seq* s) { delete s; }
+
+}  // extern "C"

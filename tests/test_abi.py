@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+nq = pytest.importorskip("sub_bit_weight_amd")
+
+HEADER = os.path.join(ROOT, "include", "nq.h")
+
+# Device pointers are never dereferenced by these tests: every call below fails
+# host-side validation first.  A non-null, aligned dummy stands in for a buffer.
+DUMMY = 0x100000
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_builds_and_loads():
+    assert os.path.exists(nq.LIB_PATH), "run `python -m sub_bit_weight_amd.build` first"
+    L = nq.lib()
+    assert b"gfx950" in L.nq_version()
+
+
+def test_exports_every_declared_symbol():
+    L = nq.lib()
+    names = _declared()
+    assert "nq_lrb_linear" in names and "nq_pack_signs" in names and "nq_reconstruct" in names
+    for name in names:
+        assert hasattr(L, name), name
+    assert sorted(nq.EXPORTED) == names
+
+
+def test_storage_bits_formula():
+    L = nq.lib()
+    assert L.nq_storage_bits(256, 256, 64) == 64 * 512 + 32 * 512
+    assert L.nq_storage_bits(8192, 28672, 6336) == 6336 * (8192 + 28672) + 32 * (8192 + 28672)
+    assert L.nq_storage_bits(0, 5, 5) == 0
+
+
+def _layer(**kw):
+    d = dict(d_out=64, d_in=64, r=32, u_bits=DUMMY, ldu=64, vt_bits=DUMMY, ldv=32, s1=DUMMY, s2=DUMMY)
+    d.update(kw)
+    return nq.nq_lrb(**d)
+
+
+def _linear(layer, x=DUMMY, dtype=nq.NQ_BF16, T=1, y=DUMMY, ws=DUMMY, wsb=1 << 40):
+    return nq.lib().nq_lrb_linear(ctypes.byref(layer), x, dtype, T, y, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_out=0), nq.NQ_ERR_ARG),
+    (dict(r=-1), nq.NQ_ERR_ARG),
+    (dict(ldu=63), nq.NQ_ERR_ARG),
+    (dict(ldv=31), nq.NQ_ERR_ARG),
+    (dict(u_bits=None), nq.NQ_ERR_ARG),
+    (dict(vt_bits=DUMMY + 2), nq.NQ_ERR_ARG),
+    (dict(s2=None), nq.NQ_ERR_ARG),
+    (dict(r=(1 << 24) + 1, ldv=(1 << 24) + 1), nq.NQ_ERR_UNSUPPORTED),
+])
+def test_linear_rejects_bad_layer(kw, status):
+    assert _linear(_layer(**kw)) == status
+    assert nq.last_error() != ""
+
+
+def test_linear_rejects_bad_io():
+    L = _layer()
+    assert _linear(L, T=0) == nq.NQ_ERR_ARG
+    assert _linear(L, dtype=7) == nq.NQ_ERR_ARG
+    assert _linear(L, x=None) == nq.NQ_ERR_ARG
+    assert _linear(L, y=DUMMY + 2) == nq.NQ_ERR_ARG
+    assert _linear(L, ws=None) == nq.NQ_ERR_WORKSPACE
+    assert _linear(L, wsb=16) == nq.NQ_ERR_WORKSPACE
+    assert "workspace" in nq.last_error()
+    assert _linear(L, ws=DUMMY + 4) == nq.NQ_ERR_ARG  # not 256-byte aligned
+
+
+def test_workspace_query():
+    L = _layer()
+    lib = nq.lib()
+    assert lib.nq_lrb_workspace_bytes(ctypes.byref(L), 1) > 0
+    assert lib.nq_lrb_workspace_bytes(ctypes.byref(L), 2048) >= 2048 * 32 * 4
+    assert lib.nq_lrb_workspace_bytes(ctypes.byref(_layer(d_out=0)), 1) == 0
+    assert lib.nq_lrb_workspace_bytes(ctypes.byref(L), 0) == 0
+
+
+def test_pack_and_unpack_reject_bad_args():
+    lib = nq.lib()
+    assert lib.nq_pack_signs(None, 4, 4, 4, 1, DUMMY, 4, None) == nq.NQ_ERR_ARG
+    assert lib.nq_pack_signs(DUMMY, 4, 4, 0, 1, DUMMY, 4, None) == nq.NQ_ERR_ARG
+    assert lib.nq_pack_signs(DUMMY, 4, 4, 4, 1, DUMMY, 3, None) == nq.NQ_ERR_ARG
+    assert lib.nq_pack_signs(DUMMY, 0, 4, 4, 1, DUMMY, 4, None) == nq.NQ_ERR_ARG
+    assert lib.nq_unpack_signs(DUMMY, 4, 4, 3, DUMMY, None) == nq.NQ_ERR_ARG
+    assert lib.nq_unpack_signs(DUMMY, 4, 4, 4, None, None) == nq.NQ_ERR_ARG
+    assert lib.nq_fill_random_words(None, 4, 1, None) == nq.NQ_ERR_ARG
+    assert lib.nq_fill_random_words(DUMMY, -1, 1, None) == nq.NQ_ERR_ARG
+
+
+def test_reconstruct_rejects_bad_args():
+    lib = nq.lib()
+    assert lib.nq_reconstruct(ctypes.byref(_layer()), None, None) == nq.NQ_ERR_ARG
+    assert lib.nq_reconstruct(ctypes.byref(_layer(ldu=1)), DUMMY, None) == nq.NQ_ERR_ARG
+
+
+def test_seq_rejects_bad_entries():
+    lib = nq.lib()
+    layers = (nq.nq_lrb * 2)(_layer(), _layer(d_in=0))
+    xs = (ctypes.c_void_p * 2)(DUMMY, DUMMY)
+    ys = (ctypes.c_void_p * 2)(DUMMY, DUMMY)
+    h = ctypes.c_void_p()
+    assert lib.nq_seq_create(layers, xs, ys, 2, nq.NQ_BF16, 1, ctypes.byref(h)) == nq.NQ_ERR_ARG
+    assert "[1]" in nq.last_error()
+    assert lib.nq_seq_create(layers, xs, ys, 0, nq.NQ_BF16, 1, ctypes.byref(h)) == nq.NQ_ERR_ARG
+    ok = (nq.nq_lrb * 1)(_layer())
+    assert lib.nq_seq_create(ok, xs, ys, 1, nq.NQ_BF16, 1, ctypes.byref(h)) == nq.NQ_OK
+    assert lib.nq_seq_workspace_bytes(h) > 0
+    assert lib.nq_seq_run(h, None, 0, None) == nq.NQ_ERR_WORKSPACE
+    lib.nq_seq_destroy(h)

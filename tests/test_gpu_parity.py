@@ -1,0 +1,197 @@
+"""GPU parity: libnq (through its C ABI) against the CPU oracle on the same
+seeded inputs.  Packing, the pack/unpack round trip, the word layout and the
+dense reconstruction are bit-exact; nq_lrb_linear is within the normwise
+relative-error bar (2e-3 for bf16 activations in the matrix-core regime,
+1e-5 for fp32 arithmetic)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import nq_oracle as O
+from tests import gpu_cases as G
+
+pytestmark = pytest.mark.gpu
+
+nq = pytest.importorskip("sub_bit_weight_amd")
+
+TINY = [  # (d_out, d_in, r): odd sizes, single elements, ragged words
+    (1, 1, 1), (3, 5, 2), (33, 47, 5), (7, 1, 1), (1, 40, 33), (65, 129, 31), (100, 37, 64),
+]
+
+
+# ---------------------------------------------------------------- generator
+
+
+@pytest.mark.parametrize("n,seed", [(1, 0), (1000, 1234567), ((1 << 20) + 13, 0xDEADBEEFCAFEF00D)])
+def test_fill_words_matches_host_splitmix(n, seed):
+    got = G.words_to_host(nq.fill_random_words(n, seed, G.DEV))
+    assert np.array_equal(got, synth.random_words(seed, np.arange(n, dtype=np.uint64)))
+
+
+# ---------------------------------------------------------------- packing
+
+
+@pytest.mark.parametrize("n_out,n_red,ld_pad", [(1, 1, 0), (5, 31, 3), (64, 64, 0), (33, 100, 1),
+                                                (256, 256, 0), (300, 1000, 5), (4096, 2048, 0)])
+def test_pack_bit_exact(n_out, n_red, ld_pad):
+    M = synth.normal_f32(f"pack/{n_out}/{n_red}", (n_out, n_red))
+    ref = O.pack_ref(M)
+    dev = torch.from_numpy(M).to(G.DEV)
+    words = nq.pack_signs(dev, n_out, n_red, n_red, 1, ld=n_out + ld_pad)
+    got = G.words_to_host(words)
+    assert np.array_equal(got[:, :n_out], ref)
+    assert not got[:, n_out:].any()  # columns past n_out untouched (zero-initialised)
+    # the transposed source (V latent: stride_out = 1, stride_red = n_out)
+    Mt = np.ascontiguousarray(M.T)
+    words_t = nq.pack_signs(torch.from_numpy(Mt).to(G.DEV), n_out, n_red, 1, n_out)
+    assert np.array_equal(G.words_to_host(words_t), ref)
+
+
+def test_pack_special_values():
+    vals = np.array([[0.0, -0.0, np.nan, -np.inf, np.inf, -1e-45, 1e-45, -1.0, 3.0] * 4], dtype=np.float32)
+    words = nq.pack_signs(torch.from_numpy(vals).to(G.DEV), 1, vals.shape[1], vals.shape[1], 1)
+    assert np.array_equal(G.words_to_host(words), O.pack_ref(vals))
+
+
+@pytest.mark.parametrize("n_out,n_red", [(1, 1), (17, 45), (64, 96), (130, 257)])
+def test_unpack_round_trip(n_out, n_red):
+    M = synth.normal_f32(f"rt/{n_out}/{n_red}", (n_out, n_red))
+    words = nq.pack_signs(torch.from_numpy(M).to(G.DEV), n_out, n_red, n_red, 1)
+    S = nq.unpack_signs(words, n_out, n_red).cpu().numpy()
+    assert np.array_equal(S, np.where(M < 0, -1.0, 1.0).astype(np.float32))
+    assert np.array_equal(S.astype(np.float64), O.unpack_ref(G.words_to_host(words), n_red))
+
+
+# ---------------------------------------------------------------- reconstruct
+
+
+@pytest.mark.parametrize("shape", TINY + [(256, 256, 64), (96, 64, 1100)])
+def test_reconstruct_bit_exact(shape):
+    d_out, d_in, r = shape
+    cfg = G.tiny_config(f"rec/{d_out}/{d_in}/{r}", scale_kind="lognormal")
+    dev, ref, _ = G.latent_layer(cfg, synth.LayerShape("w", d_out, d_in, r), ld_pad=(3 if d_out > 50 else 0))
+    W = nq.reconstruct(dev).cpu().numpy()
+    expect = O.reconstruct_expected_f32(ref)
+    assert np.array_equal(W.view(np.uint32), expect.view(np.uint32))
+
+
+# ---------------------------------------------------------------- linear
+
+
+def _linear_err(dev, ref, x_np, x_dtype, factored=False):
+    y = nq.lrb_linear(dev, G.to_device_x(x_np, x_dtype)).cpu().numpy()
+    y_ref = O.linear_factored_ref(ref, x_np) if factored else O.linear_ref(ref, x_np)
+    assert np.all(np.isfinite(y))
+    return O.rel_err(y, y_ref)
+
+
+def test_config_single_lrb_fp32():
+    cfg = synth.CONFIGS["single"]
+    dev, ref, _ = G.latent_layer(cfg, cfg.layers[0])
+    x = synth.x_for(cfg, 256, 1)
+    err = _linear_err(dev, ref, x, "f32")
+    print(f"single 256x256 r64 T1 fp32: rel err {err:.3e}")
+    assert err <= 1e-5
+
+
+def test_config_7b_attention():
+    cfg = synth.CONFIGS["7b_attn"]
+    dev, ref, _ = G.latent_layer(cfg, cfg.layers[0])
+    x = synth.x_for(cfg, 4096, 1)
+    err = _linear_err(dev, ref, x, "bf16")
+    print(f"7b attn 4096x4096 r2048 T1: rel err {err:.3e}")
+    assert err <= 2e-3
+    assert err <= 1e-5  # decode arithmetic is fp32 throughout
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_config_7b_mlp(T):
+    cfg = synth.CONFIGS["7b_mlp"]
+    for shape in cfg.layers:
+        dev, ref, _ = G.latent_layer(cfg, shape)
+        x = synth.x_for(cfg, shape.d_in, T)
+        err = _linear_err(dev, ref, x, "bf16", factored=True)
+        print(f"7b mlp {shape.name} {shape.d_out}x{shape.d_in} r{shape.r} T{T}: rel err {err:.3e}")
+        assert err <= 1e-5
+
+
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 63, 64, 65, 130])
+def test_linear_token_sweep(T, x_dtype):
+    shape = synth.LayerShape("sweep", 160, 200, 70)
+    cfg = G.tiny_config(f"sweep/{x_dtype}", x_dtype=x_dtype)
+    dev, ref, _ = G.latent_layer(cfg, shape, ld_pad=2)
+    x = synth.activations(f"sweep/x/{T}/{x_dtype}", T, shape.d_in, x_dtype)
+    err = _linear_err(dev, ref, x, x_dtype)
+    assert err <= G.tol_for(T, x_dtype), err
+
+
+@pytest.mark.parametrize("T", [1, 3, 9, 40])
+@pytest.mark.parametrize("shape", TINY)
+def test_linear_tiny_shapes(shape, T):
+    d_out, d_in, r = shape
+    cfg = G.tiny_config(f"tiny/{d_out}/{d_in}/{r}")
+    dev, ref, _ = G.latent_layer(cfg, synth.LayerShape("w", d_out, d_in, r))
+    x = synth.activations(f"tiny/x/{shape}/{T}", T, d_in, "bf16")
+    err = _linear_err(dev, ref, x, "bf16")
+    assert err <= G.tol_for(T, "bf16"), err
+
+
+def test_linear_deterministic():
+    shape = synth.LayerShape("det", 1024, 768, 256)
+    dev, _, _ = G.latent_layer(G.tiny_config("det"), shape)
+    for T in (1, 4, 100):
+        x = G.to_device_x(synth.activations(f"det/x/{T}", T, shape.d_in, "bf16"), "bf16")
+        y1 = nq.lrb_linear(dev, x).cpu()
+        y2 = nq.lrb_linear(dev, x).cpu()
+        assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_sequence_matches_single_calls():
+    cfg = G.tiny_config("seq")
+    shapes = [synth.LayerShape("a", 300, 200, 64), synth.LayerShape("b", 96, 300, 40),
+              synth.LayerShape("c", 200, 96, 33)]
+    layers = [G.latent_layer(cfg, s, i)[0] for i, s in enumerate(shapes)]
+    for T in (1, 8, 33):
+        xs = [G.to_device_x(synth.activations(f"seq/x/{T}/{i}", T, s.d_in, "bf16"), "bf16")
+              for i, s in enumerate(shapes)]
+        ys = [torch.full((T, s.d_out), float("nan"), device=G.DEV) for s in shapes]
+        seq = nq.Seq(layers, xs, ys)
+        seq.run()
+        seq.run()  # a second run reuses the uploaded schedule
+        for L, x, y in zip(layers, xs, ys):
+            assert torch.equal(y.view(torch.int32), nq.lrb_linear(L, x).view(torch.int32))
+        seq.close()
+
+
+# ---------------------------------------------------------------- 70B shapes (sampled rows)
+
+
+def _sampled_err(dev, ref, x_np, rows):
+    y = nq.lrb_linear(dev, G.to_device_x(x_np, "bf16")).cpu().numpy()
+    assert np.all(np.isfinite(y))
+    return O.rel_err(y[:, rows], O.sampled_linear_ref(ref, x_np, rows))
+
+
+@pytest.mark.parametrize("name", ["k", "down"])
+def test_70b_decode_sampled_rows(name):
+    cfg = synth.CONFIGS["70b_stack"]
+    shape = next(s for s in cfg.layers if s.name == name)
+    dev, ref = G.splitmix_layer(cfg, shape, layer_idx=0)
+    rows = np.sort(synth.rng(f"rows/{name}").choice(shape.d_out, 64, replace=False))
+    x = synth.x_for(cfg, shape.d_in, 1)
+    err = _sampled_err(dev, ref, x, rows)
+    print(f"70b {name} T1 sampled 64 rows: rel err {err:.3e}")
+    assert err <= 1e-5
+
+
+def test_70b_prefill_sampled_rows():
+    cfg = synth.CONFIGS["70b_prefill"]
+    shape = next(s for s in cfg.layers if s.name == "q")
+    dev, ref = G.splitmix_layer(cfg, shape, layer_idx=0)
+    rows = np.sort(synth.rng("rows/prefill/q").choice(shape.d_out, 64, replace=False))
+    x = synth.x_for(cfg, shape.d_in, 2048)
+    err = _sampled_err(dev, ref, x, rows)
+    print(f"70b q T2048 sampled 64 rows: rel err {err:.3e}")
+    assert err <= 2e-3
