@@ -245,6 +245,7 @@ class Seq:
             if x.shape != (T, L.d_in) or _x_dtype(x) != xd or y.shape != (T, L.d_out) or y.dtype != torch.float32:
                 raise ValueError("inconsistent x/y shapes or dtypes in sequence")
         n = len(layers)
+        self.T = T
         self._keep = (layers, xs, ys)
         self._structs = (nq_lrb * n)(*[L.struct() for L in layers])
         self._xs = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
@@ -257,6 +258,14 @@ class Seq:
 
     def run(self, stream=None) -> None:
         _check(lib().nq_seq_run(self._h, _ptr(self.workspace), self.workspace.numel(), _stream(stream)))
+
+    def device_error(self) -> int:
+        """The device error word (first 4 bytes of the workspace) after the last
+        run: 0, or non-zero if a dependency wait gave up (synchronises)."""
+        torch.cuda.synchronize()
+        if self.T > 8:  # the matrix-core regime runs per-entry kernels without waits
+            return 0
+        return int(self.workspace[:4].view(torch.int32).item())
 
     def close(self) -> None:
         if getattr(self, "_h", None):

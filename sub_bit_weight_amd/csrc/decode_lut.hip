@@ -1,0 +1,571 @@
+// Decode regime (T <= 8), table-lookup kernels.
+//
+// The layer is evaluated in factored form, stage 1 t = V^T (s2 (.) x) and
+// stage 2 y = s1 (.) (U t) (research.samsung.com NanoQuant blog, section 2,
+// subsection "Low-Rank Binary Factorization", the factorization equation; the
+// GEMV regime for token-by-token decoding is section 4, "Inference
+// Performance").  Both stages have the form
+//     out[t][o] = sum_e sign(o,e) * v[t][e],   sign from words[e/32][o] bit e%32.
+//
+// Design (gfx950):
+//  * One output row per lane: a wave reads one word row of 64 consecutive
+//    outputs (256 contiguous bytes) and every lane needs the same elements of v.
+//  * Per group of 4 reduction elements the workgroup builds, in LDS, the 16
+//    signed sums  L[g][n] = sum_b (bit b of n ? -v[4g+b] : +v[4g+b])  (the sign
+//    is applied by flipping the float sign bit).  A 4-bit nibble of a sign word
+//    then selects one entry: one LDS read and one fp32 add per 4 weights.  All
+//    lanes of a wave read the same group, so the 16 candidate entries sit in 16
+//    different banks and equal nibbles broadcast: the reads are conflict-free.
+//  * The reduction is split into chunks of at most kcmax(T) elements; each
+//    (row block, chunk) is one tile.  Partial sums go to the workspace; the last
+//    tile of a row block to finish (arrival counter) adds them in chunk order,
+//    so results are deterministic, then applies s1 for stage 2.
+//  * A persistent kernel runs a whole sequence of linears from one launch: tiles
+//    are taken in schedule order from an atomic counter, and a stage-2 tile
+//    first waits until its linear's stage-1 row blocks are all final.  Waits
+//    only target earlier tiles, which are already running, so the queue always
+//    drains; each wait also has a spin limit that records an error and exits.
+#include "nq_internal.h"
+
+namespace nq {
+
+namespace {
+
+constexpr int kRows = 256;           // rows (outputs) per tile = threads per workgroup
+constexpr int kLutFloats = 8192;     // 32 KiB of tables per workgroup
+constexpr unsigned kSpinLimit = 1u << 21;  // ~1 s of polling, then give up and flag
+
+// Table geometry for T tokens.  Entries are token-innermost: the TT tokens of
+// one (group, nibble) entry are adjacent, so one ds_read_b32/b64/b128 fetches
+// them together; T > 4 uses NQ = 2 such arrays.  The reduction is walked in
+// chunks of GMAX groups (4*GMAX elements, 32 KiB of tables), each chunk in NB
+// batches of B sign words; D batches of words are kept in flight per lane.
+template <int T>
+struct Geo {
+  static constexpr int TT = T == 1 ? 1 : (T == 2 ? 2 : 4);
+  static constexpr int NQ = (T + TT - 1) / TT;
+  static constexpr int QF = kLutFloats / NQ;                 // floats per array
+  static constexpr int GMAX = QF / (16 * TT);                // groups per chunk
+  static constexpr int CW = GMAX / 8;                        // words per chunk
+  static constexpr int B = CW >= 32 ? 8 : (CW >= 16 ? 4 : 2);  // words per batch
+  static constexpr int NB = CW / B;                          // batches per chunk
+  static constexpr int D = 4;                                // batches in flight
+  static constexpr int SHIFT = TT == 1 ? 2 : (TT == 2 ? 3 : 4);  // log2 of the entry size in bytes
+  static constexpr int GPT = (GMAX + kRows - 1) / kRows;     // table groups built per thread
+  static_assert(NB % D == 0, "batches per chunk must be a multiple of the ring depth");
+};
+
+__device__ inline float bf16_bits(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Loads through pointers held in a descriptor: tell the compiler they are
+// global memory (plain global_load, not flat).
+template <typename V>
+__device__ inline V gload(const V* p) {
+  typedef const __attribute__((address_space(1))) V* gptr;
+  return *(gptr)(p);
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
+// outstanding global load, which would drain the sign words kept in flight.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// (selected byte BYTE of w) & mask, one VALU op (SDWA byte select).
+template <int BYTE>
+__device__ inline uint32_t and_byte(uint32_t mask, uint32_t w) {
+  uint32_t r;
+  if constexpr (BYTE == 0)
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(r) : "v"(mask), "v"(w));
+  if constexpr (BYTE == 1)
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(r) : "v"(mask), "v"(w));
+  if constexpr (BYTE == 2)
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(r) : "v"(mask), "v"(w));
+  if constexpr (BYTE == 3)
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(r) : "v"(mask), "v"(w));
+  return r;
+}
+
+// The raw activations and column scales one thread needs for its table groups
+// of one chunk (GPT groups x 4 elements).  They are kept raw until the tables
+// are built, so the loads stay in flight while the previous chunk is processed.
+template <int T>
+struct TableInputs {
+  uint32_t x[Geo<T>::GPT][T][4];  // bf16 or fp32 bit patterns
+  float cs[Geo<T>::GPT][4];
+};
+
+template <int T>
+__device__ inline void load_inputs(const StageDesc& S, int64_t c0, int64_t cend, TableInputs<T>& in) {
+  using G = Geo<T>;
+#pragma unroll
+  for (int i = 0; i < G::GPT; ++i) {
+    const int g = threadIdx.x + i * kRows;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t j = c0 + 4 * g + b;
+      const bool ok = g < G::GMAX && j < cend;
+      const int64_t jc = ok ? j : 0;  // in-bounds index; the value is dropped when !ok
+      in.cs[i][b] = S.colscale ? gload(S.colscale + jc) : 1.0f;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int64_t idx = (int64_t)t * S.n_red + jc;
+        in.x[i][t][b] = S.x_bf16 ? (uint32_t)gload(static_cast<const uint16_t*>(S.xin) + idx)
+                                 : gload(static_cast<const uint32_t*>(S.xin) + idx);
+      }
+    }
+  }
+}
+
+// Write the 16 signed sums of each of this thread's groups:
+//   L[g][n] = sum_b (bit b of n ? -z[4g+b] : +z[4g+b])
+// (negation flips the float sign bit).
+template <int T>
+__device__ inline void build_tables(const TableInputs<T>& in, int64_t c0, int64_t cend, int x_bf16, float* lut) {
+  using G = Geo<T>;
+#pragma unroll
+  for (int i = 0; i < G::GPT; ++i) {
+    const int g = threadIdx.x + i * kRows;
+    if (g >= G::GMAX) break;
+#pragma unroll
+    for (int q = 0; q < G::NQ; ++q) {
+      float ent[16][G::TT];
+#pragma unroll
+      for (int tt = 0; tt < G::TT; ++tt) {
+        const int t = q * G::TT + tt;
+        float z[4] = {0.f, 0.f, 0.f, 0.f};
+        if (t < T) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t raw = in.x[i][t < T ? t : 0][b];
+            const float v = x_bf16 ? bf16_bits(raw) : __uint_as_float(raw);
+            z[b] = (c0 + 4 * g + b < cend) ? v * in.cs[i][b] : 0.0f;
+          }
+        }
+        const float p01[4] = {z[0] + z[1], -z[0] + z[1], z[0] - z[1], -z[0] - z[1]};
+        const float p23[4] = {z[2] + z[3], -z[2] + z[3], z[2] - z[3], -z[2] - z[3]};
+#pragma unroll
+        for (int n = 0; n < 16; ++n) ent[n][tt] = p01[n & 3] + p23[n >> 2];
+      }
+      float4* dst = reinterpret_cast<float4*>(lut + q * G::QF + g * 16 * G::TT);
+      const float* src = &ent[0][0];
+#pragma unroll
+      for (int k = 0; k < 4 * G::TT; ++k)
+        dst[k] = make_float4(src[4 * k], src[4 * k + 1], src[4 * k + 2], src[4 * k + 3]);
+    }
+  }
+}
+
+// Table reads for one sign word: the 8 nibbles of word WI (compile-time index
+// within the chunk, so table offsets are immediates) select 8 entries of T
+// floats each.
+template <int T, int WI>
+__device__ inline void read_entries(uint32_t w, const float* lut, float (&e)[8][Geo<T>::NQ * Geo<T>::TT]) {
+  using G = Geo<T>;
+  const uint32_t mask = 15u << G::SHIFT;
+  const char* base = reinterpret_cast<const char*>(lut);
+  const uint32_t lo = w << G::SHIFT;        // bytes -> nibbles 0,2,4,6 times the entry size
+  const uint32_t hi = w >> (4 - G::SHIFT);  // bytes -> nibbles 1,3,5,7 times the entry size
+  uint32_t a[8];
+  a[0] = and_byte<0>(mask, lo);
+  a[1] = and_byte<0>(mask, hi);
+  a[2] = and_byte<1>(mask, lo);
+  a[3] = and_byte<1>(mask, hi);
+  a[4] = and_byte<2>(mask, lo);
+  a[5] = and_byte<2>(mask, hi);
+  a[6] = and_byte<3>(mask, lo);
+  a[7] = and_byte<3>(mask, hi);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    constexpr int kEntryBytes = 4 * G::TT;
+    const int group = WI * 8 + k;
+#pragma unroll
+    for (int q = 0; q < G::NQ; ++q) {
+      const char* p = base + (q * G::QF * 4) + group * 16 * kEntryBytes + a[k];
+      if constexpr (G::TT == 1) {
+        e[k][q] = *reinterpret_cast<const float*>(p);
+      } else if constexpr (G::TT == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(p);
+        e[k][2 * q] = v.x;
+        e[k][2 * q + 1] = v.y;
+      } else {
+        const float4 v = *reinterpret_cast<const float4*>(p);
+        e[k][4 * q] = v.x;
+        e[k][4 * q + 1] = v.y;
+        e[k][4 * q + 2] = v.z;
+        e[k][4 * q + 3] = v.w;
+      }
+    }
+  }
+}
+
+// acc holds two partial sums per token (even / odd nibbles): shorter add chains.
+template <int T>
+__device__ inline void add_entries(const float (&e)[8][Geo<T>::NQ * Geo<T>::TT], float* acc) {
+  using G = Geo<T>;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int t = 0; t < G::NQ * G::TT; ++t)
+      if (t < T) acc[(k & 1) * G::NQ * G::TT + t] += e[k][t];
+}
+
+// One chunk, software-pipelined: while the entries of word WI are added, the
+// reads for word WI+1 are in flight.  Sign words come from a ring of D batches
+// of B words: when the last word of batch b has been read, its ring slot is
+// refilled with the words D batches ahead (possibly in the next chunk).  Words
+// past the end of a tile's reduction span only select table entries of groups
+// past the span, which are all zero, so loads need no masking: the word index
+// is clamped (uniformly) to stay inside the matrix.
+template <int T, int WI>
+__device__ inline void chunk_words(const uint32_t* wp, int64_t ld, int64_t wnext, int64_t wlast,
+                                   uint32_t (&ring)[Geo<T>::D][Geo<T>::B], const float* lut, float* acc,
+                                   float (&cur)[8][Geo<T>::NQ * Geo<T>::TT]) {
+  using G = Geo<T>;
+  if constexpr (WI < G::CW) {
+    constexpr int b = WI / G::B, j = WI % G::B;
+    float nxt[8][G::NQ * G::TT];
+    if constexpr (WI + 1 < G::CW) {
+      constexpr int b1 = (WI + 1) / G::B, j1 = (WI + 1) % G::B;
+      read_entries<T, WI + 1>(ring[b1 % G::D][j1], lut, nxt);
+    }
+    if constexpr (j == G::B - 1) {
+#pragma unroll
+      for (int jj = 0; jj < G::B; ++jj) {
+        const int64_t w = imin(wnext + (int64_t)b * G::B + jj, wlast);
+        ring[b % G::D][jj] = gload(wp + w * ld);
+      }
+    }
+    add_entries<T>(cur, acc);
+    __builtin_amdgcn_sched_barrier(0);  // one word per scheduling region: bounded registers
+    if constexpr (WI + 1 < G::CW) chunk_words<T, WI + 1>(wp, ld, wnext, wlast, ring, lut, acc, nxt);
+  }
+}
+
+// One tile: row block rb (one row per lane) over reduction span ks of stage S.
+template <int T>
+__device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag, int* err) {
+  using G = Geo<T>;
+  const int tid = threadIdx.x;
+  const int rb = local % S.nrb;
+  const int ks = local / S.nrb;
+  const int64_t span0 = (int64_t)ks * S.kc;                 // this tile's reduction span
+  const int64_t span1 = imin(span0 + S.kc, S.n_red);
+  const int64_t o = (int64_t)rb * kRows + tid;
+  const bool valid = o < S.n_rows;
+  const int64_t w0 = span0 / kWordBits;
+  const int64_t wlast = cdiv(S.n_red, kWordBits) - 1;  // last word row of the matrix
+  // lanes past the last row read row n_rows-1 and store nothing
+  const uint32_t* wp = S.bits + (valid ? o : S.n_rows - 1);
+  const int nchunks = (int)cdiv(span1 - span0, 4 * G::GMAX);
+
+  if (S.wait_ctr) {
+    if (tid == 0) {
+      // poll with relaxed loads (an acquire per poll would invalidate caches
+      // that streaming workgroups are using), then acquire once
+      unsigned spins = 0;
+      while (__hip_atomic_load(S.wait_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < S.wait_target) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > kSpinLimit) {
+          atomicOr(err, 1);
+          break;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+  }
+
+  // fill the ring with the first D batches (independent of the tables)
+  uint32_t ring[G::D][G::B];
+#pragma unroll
+  for (int d = 0; d < G::D; ++d)
+#pragma unroll
+    for (int j = 0; j < G::B; ++j) ring[d][j] = gload(wp + imin(w0 + d * G::B + j, wlast) * S.ld);
+
+  TableInputs<T> in;
+  load_inputs<T>(S, span0, span1, in);
+
+  float acc[2 * G::NQ * G::TT];  // [even/odd nibbles][token]
+#pragma unroll
+  for (int t = 0; t < 2 * G::NQ * G::TT; ++t) acc[t] = 0.0f;
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int64_t c0 = span0 + (int64_t)c * 4 * G::GMAX;
+    lds_barrier();  // everyone is done with the previous chunk's tables
+    build_tables<T>(in, c0, span1, S.x_bf16, lut);
+    if (c + 1 < nchunks) load_inputs<T>(S, c0 + 4 * G::GMAX, span1, in);  // next chunk's inputs
+    lds_barrier();
+    const int64_t wnext = c0 / kWordBits + (int64_t)G::D * G::B;  // first word not yet in the ring
+    float first[8][G::NQ * G::TT];
+    read_entries<T, 0>(ring[0][0], lut, first);
+    chunk_words<T, 0>(wp, S.ld, wnext, wlast, ring, lut, acc, first);
+  }
+#pragma unroll
+  for (int t = 0; t < G::NQ * G::TT; ++t) acc[t] += acc[G::NQ * G::TT + t];
+
+  if (S.nks == 1) {
+    if (valid) {
+      const float sc = S.rowscale ? S.rowscale[o] : 1.0f;
+#pragma unroll
+      for (int t = 0; t < T; ++t) S.out[(int64_t)t * S.n_rows + o] = sc * acc[t];
+    }
+  } else {
+    if (valid) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) S.part[((int64_t)ks * T + t) * S.n_rows + o] = acc[t];
+    }
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // publish this workgroup's partial sums
+      *s_flag = (atomicAdd(&S.rb_count[rb], 1) == S.nks - 1);
+      if (*s_flag) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see the other spans' sums
+    }
+    __syncthreads();
+    if (!*s_flag) {
+      __syncthreads();  // s_flag is reused by the next tile
+      return;
+    }
+    if (valid) {
+      const float sc = S.rowscale ? S.rowscale[o] : 1.0f;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        float sum = 0.0f;
+        for (int c = 0; c < S.nks; ++c) sum += S.part[((int64_t)c * T + t) * S.n_rows + o];
+        S.out[(int64_t)t * S.n_rows + o] = sc * sum;
+      }
+    }
+    if (tid == 0) S.rb_count[rb] = 0;  // all arrivals happened: ready for the next run
+  }
+  if (S.signal) {
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // publish the final row block
+      atomicAdd(S.signal, 1);
+    }
+  }
+  __syncthreads();
+}
+
+template <int T>
+__global__ __launch_bounds__(kRows) void lut_stage_kernel(StageDesc S, int* err) {
+  __shared__ __attribute__((aligned(16))) float lut[kLutFloats];
+  __shared__ int s_flag;
+  lut_tile<T>(S, blockIdx.x, lut, &s_flag, err);
+}
+
+template <int T>
+__global__ __launch_bounds__(kRows) void lut_persistent_kernel(const StageDesc* __restrict__ segs, int nseg,
+                                                               int ntiles, int* next_tile, int* err) {
+  __shared__ __attribute__((aligned(16))) float lut[kLutFloats];
+  __shared__ int s_flag;
+  __shared__ int s_tile;
+  if (threadIdx.x == 0) s_tile = atomicAdd(next_tile, 1);
+  __syncthreads();
+  int tile = s_tile;
+  int seg = 0;
+  while (tile < ntiles) {
+    int nxt = 0;
+    if (threadIdx.x == 0) nxt = atomicAdd(next_tile, 1);  // prefetch the next tile id
+    while (seg + 1 < nseg && tile >= segs[seg + 1].tile0) ++seg;
+    const StageDesc S = segs[seg];
+    lut_tile<T>(S, tile - S.tile0, lut, &s_flag, err);
+    if (threadIdx.x == 0) s_tile = nxt;
+    __syncthreads();
+    tile = s_tile;
+    __syncthreads();
+  }
+}
+
+__global__ void zero_ints_kernel(int* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+}  // namespace
+
+// Reduction spans per row block: `kspan_max` bounds a span (0 = whole reduction).
+StagePlan lut_stage_plan(int64_t n_rows, int64_t n_red, int64_t T, int64_t kspan_max) {
+  StagePlan p;
+  p.n_rows = n_rows;
+  p.n_red = n_red;
+  p.nrb = (int)cdiv(n_rows, kRows);
+  const int64_t span = kspan_max > 0 ? imin(kspan_max, n_red) : n_red;
+  p.nks = (int)cdiv(n_red, span);
+  p.kc = (int)round_up(cdiv(n_red, p.nks), kWordBits);
+  p.nks = (int)cdiv(n_red, p.kc);
+  (void)T;
+  return p;
+}
+
+// Single calls split the reduction until the two stages have enough tiles to
+// fill the GPU; sequences keep whole reductions (no partial sums).
+int64_t lut_single_span(int64_t n_rows, int64_t n_red) {
+  const int64_t nrb = cdiv(n_rows, kRows);
+  const int64_t want = cdiv(512, nrb);
+  const int64_t span = round_up(cdiv(n_red, want), 1024);
+  return span;
+}
+
+hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = imin(cdiv(n, 256), 1024);
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_lut_stage(const StageDesc& S, int64_t T, int* err, hipStream_t s) {
+  const unsigned grid = (unsigned)(S.nrb * S.nks);
+  switch (T) {
+#define NQ_CASE(TT) \
+  case TT: hipLaunchKernelGGL(lut_stage_kernel<TT>, dim3(grid), dim3(kRows), 0, s, S, err); break;
+    NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
+#undef NQ_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int lut_persistent_grid(int64_t T) {
+  int dev = 0, cus = 256, per = 1;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
+  }
+  hipError_t e = hipErrorInvalidValue;
+  switch (T) {
+#define NQ_CASE(TT) \
+  case TT: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, lut_persistent_kernel<TT>, kRows, 0); break;
+    NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
+#undef NQ_CASE
+  }
+  if (e != hipSuccess || per < 1) per = 1;
+  return cus * per;
+}
+
+hipError_t launch_lut_persistent(const StageDesc* segs, int nseg, int ntiles, int* next_tile, int* err,
+                                 int64_t T, int grid, hipStream_t s) {
+  switch (T) {
+#define NQ_CASE(TT)                                                                                     \
+  case TT:                                                                                              \
+    hipLaunchKernelGGL(lut_persistent_kernel<TT>, dim3(grid), dim3(kRows), 0, s, segs, nseg, ntiles, \
+                       next_tile, err);                                                                 \
+    break;
+    NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
+#undef NQ_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ layouts
+
+namespace {
+
+void plans(const nq_lrb& L, int64_t T, bool split, StagePlan* p1, StagePlan* p2) {
+  *p1 = lut_stage_plan(L.r, L.d_in, T, split ? lut_single_span(L.r, L.d_in) : 0);
+  *p2 = lut_stage_plan(L.d_out, L.r, T, split ? lut_single_span(L.d_out, L.r) : 0);
+}
+
+size_t part_bytes(const StagePlan& p, int64_t T) {
+  return p.nks > 1 ? (size_t)p.nks * T * p.n_rows * sizeof(float) : 0;
+}
+
+}  // namespace
+
+// Per-linear device buffers: [part1][t][part2].
+size_t lut_linear_bytes(const nq_lrb& L, int64_t T, bool split) {
+  StagePlan p1, p2;
+  plans(L, T, split, &p1, &p2);
+  size_t off = align_up(part_bytes(p1, T));
+  off = align_up(off + (size_t)T * L.r * sizeof(float));
+  return align_up(off + part_bytes(p2, T));
+}
+
+// Per-linear counters: [stage-1 row blocks][stage-2 row blocks][t-ready].
+int lut_linear_counters(const nq_lrb& L, int64_t T, bool split) {
+  StagePlan p1, p2;
+  plans(L, T, split, &p1, &p2);
+  return p1.nrb + p2.nrb + 1;
+}
+
+void lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, bool split,
+                     char* ws_linear, int* ctr_base, StageDesc* s1, StageDesc* s2) {
+  StagePlan p1, p2;
+  plans(L, T, split, &p1, &p2);
+  size_t off = 0;
+  float* part1 = reinterpret_cast<float*>(ws_linear + off);
+  off = align_up(off + part_bytes(p1, T));
+  float* tbuf = reinterpret_cast<float*>(ws_linear + off);
+  off = align_up(off + (size_t)T * L.r * sizeof(float));
+  float* part2 = reinterpret_cast<float*>(ws_linear + off);
+
+  StageDesc a{};
+  a.bits = L.vt_bits;
+  a.ld = L.ldv;
+  a.xin = x;
+  a.colscale = L.s2;
+  a.rowscale = nullptr;
+  a.out = tbuf;
+  a.part = part1;
+  a.rb_count = ctr_base;
+  a.signal = ctr_base + p1.nrb + p2.nrb;
+  a.wait_ctr = nullptr;
+  a.wait_target = 0;
+  a.n_rows = (int)L.r;
+  a.n_red = (int)L.d_in;
+  a.kc = p1.kc;
+  a.nks = p1.nks;
+  a.nrb = p1.nrb;
+  a.x_bf16 = xd == NQ_BF16;
+  a.tile0 = 0;
+  StageDesc b = a;
+  b.bits = L.u_bits;
+  b.ld = L.ldu;
+  b.xin = tbuf;
+  b.colscale = nullptr;
+  b.rowscale = L.s1;
+  b.out = y;
+  b.part = part2;
+  b.rb_count = ctr_base + p1.nrb;
+  b.signal = nullptr;
+  b.wait_ctr = a.signal;
+  b.wait_target = p1.nrb;
+  b.n_rows = (int)L.d_out;
+  b.n_red = (int)L.r;
+  b.kc = p2.kc;
+  b.nks = p2.nks;
+  b.nrb = p2.nrb;
+  b.x_bf16 = 0;
+  *s1 = a;
+  *s2 = b;
+}
+
+size_t lut_workspace_bytes(const nq_lrb& L, int64_t T) {
+  return align_up((size_t)(1 + lut_linear_counters(L, T, true)) * sizeof(int)) + lut_linear_bytes(L, T, true);
+}
+
+hipError_t launch_lut_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
+                             hipStream_t s) {
+  char* base = static_cast<char*>(ws);
+  int* err = reinterpret_cast<int*>(base);
+  int* ctr = err + 1;
+  const int nctr = lut_linear_counters(L, T, true);
+  char* lin = base + align_up((size_t)(1 + nctr) * sizeof(int));
+  StageDesc a, b;
+  lut_stage_descs(L, x, xd, T, y, true, lin, ctr, &a, &b);
+  a.signal = nullptr;  // stream order separates the two launches
+  b.wait_ctr = nullptr;
+  hipError_t e;
+  if ((e = launch_zero_ints(err, 1 + nctr, s)) != hipSuccess) return e;
+  if ((e = launch_lut_stage(a, T, err, s)) != hipSuccess) return e;
+  return launch_lut_stage(b, T, err, s);
+}
+
+}  // namespace nq

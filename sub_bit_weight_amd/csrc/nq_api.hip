@@ -2,6 +2,8 @@
 // Every check runs on the host before any HIP call; no exception crosses the ABI.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <new>
@@ -72,13 +74,22 @@ nq_status check_io(const char* who, const nq_lrb* L, const void* x, nq_dtype xd,
 
 constexpr int64_t kDecodeMaxT = 8;
 
+// NQ_DECODE_VARIANT=xor selects the per-weight sign-XOR decode kernels (kept
+// for comparison); the default is the table-lookup kernels.
+bool decode_xor() {
+  const char* e = getenv("NQ_DECODE_VARIANT");
+  return e && strcmp(e, "xor") == 0;
+}
+
 size_t linear_workspace(const nq_lrb& L, int64_t T) {
-  return T <= kDecodeMaxT ? decode_workspace_bytes(L, T) : prefill_workspace_bytes(L, T);
+  if (T > kDecodeMaxT) return prefill_workspace_bytes(L, T);
+  return decode_xor() ? decode_workspace_bytes(L, T) : lut_workspace_bytes(L, T);
 }
 
 hipError_t launch_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
                          hipStream_t s) {
-  return T <= kDecodeMaxT ? launch_decode(L, x, xd, T, y, ws, s) : launch_prefill(L, x, xd, T, y, ws, s);
+  if (T > kDecodeMaxT) return launch_prefill(L, x, xd, T, y, ws, s);
+  return decode_xor() ? launch_decode(L, x, xd, T, y, ws, s) : launch_lut_linear(L, x, xd, T, y, ws, s);
 }
 
 }  // namespace
@@ -91,7 +102,82 @@ struct nq_seq {
   nq_dtype xd;
   int64_t T;
   size_t ws_bytes;
+  // persistent decode schedule (T <= 8)
+  bool persistent = false;
+  int grid = 0, ntiles = 0;
+  int64_t n_ints = 0;                 // [error flag][next tile][per-linear counters]
+  std::vector<int64_t> ctr_off;       // per linear, in ints from the start of the workspace
+  std::vector<size_t> buf_off;        // per linear, in bytes
+  std::vector<std::pair<int, int>> order;  // (linear, stage) in schedule order
+  size_t off_sched = 0;
+  std::vector<nq::StageDesc> segs;    // host copy of the uploaded schedule
+  void* uploaded_for = nullptr;
 };
+
+namespace {
+
+// Stage 2 of linear i is scheduled after stage 1 of linear i+lag, so that its
+// inputs are usually final by the time a workgroup takes its first tile and
+// enough independent tiles are ready to keep every workgroup streaming.
+int seq_lag() {
+  const char* e = getenv("NQ_SEQ_LAG");
+  const int v = e ? atoi(e) : 14;
+  return v < 0 ? 0 : v;
+}
+
+void plan_persistent(nq_seq* s) {
+  using namespace nq;
+  const int64_t n = (int64_t)s->layers.size();
+  s->persistent = true;
+  int64_t ints = 2;
+  size_t bufs = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    s->ctr_off.push_back(ints);
+    ints += lut_linear_counters(s->layers[i], s->T, false);
+    s->buf_off.push_back(bufs);
+    bufs = align_up(bufs + lut_linear_bytes(s->layers[i], s->T, false));
+  }
+  s->n_ints = ints;
+  const int lag = seq_lag();
+  for (int64_t i = 0; i < n; ++i) {
+    s->order.push_back({(int)i, 1});
+    if (i >= lag) s->order.push_back({(int)(i - lag), 2});
+  }
+  for (int64_t i = std::max<int64_t>(0, n - lag); i < n; ++i) s->order.push_back({(int)i, 2});
+  s->off_sched = align_up((size_t)ints * sizeof(int));
+  const size_t off_bufs = align_up(s->off_sched + s->order.size() * sizeof(StageDesc));
+  for (auto& b : s->buf_off) b += off_bufs;
+  s->ws_bytes = off_bufs + bufs;
+  s->grid = 0;
+}
+
+nq_status build_and_upload(nq_seq* s, void* ws, hipStream_t stream) {
+  using namespace nq;
+  char* base = static_cast<char*>(ws);
+  int* ints = reinterpret_cast<int*>(base);
+  std::vector<StageDesc> st1(s->layers.size()), st2(s->layers.size());
+  for (size_t i = 0; i < s->layers.size(); ++i)
+    lut_stage_descs(s->layers[i], s->xs[i], s->xd, s->T, s->ys[i], false, base + s->buf_off[i], ints + s->ctr_off[i],
+                    &st1[i], &st2[i]);
+  s->segs.clear();
+  int tile = 0;
+  for (auto& o : s->order) {
+    StageDesc d = o.second == 1 ? st1[o.first] : st2[o.first];
+    d.tile0 = tile;
+    tile += d.nrb * d.nks;
+    s->segs.push_back(d);
+  }
+  s->ntiles = tile;
+  if (s->grid == 0) s->grid = lut_persistent_grid(s->T);
+  hipError_t e = hipMemcpyAsync(base + s->off_sched, s->segs.data(), s->segs.size() * sizeof(StageDesc),
+                                hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e, "nq_seq_run schedule upload");
+  s->uploaded_for = ws;
+  return NQ_OK;
+}
+
+}  // namespace
 
 using namespace nq;
 
@@ -188,6 +274,7 @@ nq_status nq_seq_create(const nq_lrb* layers, const void* const* xs, float* cons
     s->ys.push_back(ys[i]);
     s->ws_bytes = std::max<size_t>(s->ws_bytes, linear_workspace(layers[i], T));
   }
+  if (T <= kDecodeMaxT && !decode_xor()) plan_persistent(s);
   *out = s;
   return NQ_OK;
 }
@@ -201,6 +288,19 @@ nq_status nq_seq_run(nq_seq* s, void* workspace, size_t workspace_bytes, void* s
     return set_error("nq_seq_run: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0, s->ws_bytes),
            NQ_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return set_error("nq_seq_run: workspace not 256-byte aligned"), NQ_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (s->persistent) {
+    if (s->uploaded_for != workspace) {
+      nq_status r = build_and_upload(s, workspace, st);
+      if (r != NQ_OK) return r;
+    }
+    int* ints = static_cast<int*>(workspace);
+    hipError_t e = launch_zero_ints(ints, s->n_ints, st);
+    if (e == hipSuccess)
+      e = launch_lut_persistent(reinterpret_cast<const StageDesc*>(static_cast<char*>(workspace) + s->off_sched),
+                                (int)s->segs.size(), s->ntiles, ints + 1, ints, s->T, s->grid, st);
+    return hip_status(e, "nq_seq_run launch");
+  }
   for (size_t i = 0; i < s->layers.size(); ++i) {
     hipError_t e = launch_linear(s->layers[i], s->xs[i], s->xd, s->T, s->ys[i], workspace, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "nq_seq_run launch");

@@ -42,6 +42,44 @@ size_t decode_workspace_bytes(const nq_lrb& L, int64_t T);
 hipError_t launch_decode(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y,
                          void* ws, hipStream_t s);
 
+// Decode regime, table-lookup kernels.  One stage of one linear:
+//   out[t][o] = rowscale[o] * sum_e sign(o,e) * xin[t][e] * colscale[e]
+struct StageDesc {
+  const uint32_t* bits;   // words[e/32][o], row stride ld
+  int64_t ld;
+  const void* xin;        // [T][n_red], fp32 or bf16 (x_bf16)
+  const float* colscale;  // [n_red] or null
+  const float* rowscale;  // [n_rows] or null
+  float* out;             // [T][n_rows]
+  float* part;            // [nks][T][n_rows] partial sums (nks > 1)
+  int* rb_count;          // [nrb] arrival counters (nks > 1)
+  int* signal;            // incremented once per final row block (or null)
+  const int* wait_ctr;    // wait for *wait_ctr >= wait_target before reading xin (or null)
+  int wait_target;
+  int n_rows, n_red;
+  int kc, nks, nrb;       // reduction span per tile (elements), spans, row blocks
+  int x_bf16;
+  int tile0;              // first tile of this stage in a persistent schedule
+};
+struct StagePlan {
+  int64_t n_rows, n_red;
+  int kc, nks, nrb;
+};
+StagePlan lut_stage_plan(int64_t n_rows, int64_t n_red, int64_t T, int64_t kspan_max);
+int64_t lut_single_span(int64_t n_rows, int64_t n_red);
+size_t lut_workspace_bytes(const nq_lrb& L, int64_t T);
+// split = true: single-call plan (reduction split over workgroups); false: sequence plan
+size_t lut_linear_bytes(const nq_lrb& L, int64_t T, bool split);
+int lut_linear_counters(const nq_lrb& L, int64_t T, bool split);
+void lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, bool split,
+                     char* ws_linear, int* ctr_base, StageDesc* s1, StageDesc* s2);
+hipError_t launch_lut_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
+                             hipStream_t s);
+hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t s);
+int lut_persistent_grid(int64_t T);
+hipError_t launch_lut_persistent(const StageDesc* segs, int nseg, int ntiles, int* next_tile, int* err,
+                                 int64_t T, int grid, hipStream_t s);
+
 // Matrix-core regime (T > 8).
 size_t prefill_workspace_bytes(const nq_lrb& L, int64_t T);
 hipError_t launch_prefill(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y,

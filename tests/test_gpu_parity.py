@@ -148,6 +148,16 @@ def test_linear_deterministic():
         assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
+@pytest.mark.parametrize("T", [1, 2, 5, 8])
+def test_decode_xor_variant(T, monkeypatch):
+    """The per-weight sign-XOR decode kernels (kept for comparison) also match the oracle."""
+    monkeypatch.setenv("NQ_DECODE_VARIANT", "xor")
+    shape = synth.LayerShape("xor", 300, 200, 70)
+    dev, ref, _ = G.latent_layer(G.tiny_config("xor"), shape, ld_pad=1)
+    x = synth.activations(f"xor/x/{T}", T, shape.d_in, "bf16")
+    assert _linear_err(dev, ref, x, "bf16") <= 1e-5
+
+
 def test_sequence_matches_single_calls():
     cfg = G.tiny_config("seq")
     shapes = [synth.LayerShape("a", 300, 200, 64), synth.LayerShape("b", 96, 300, 40),
@@ -160,9 +170,30 @@ def test_sequence_matches_single_calls():
         seq = nq.Seq(layers, xs, ys)
         seq.run()
         seq.run()  # a second run reuses the uploaded schedule
+        assert seq.device_error() == 0
         for L, x, y in zip(layers, xs, ys):
             assert torch.equal(y.view(torch.int32), nq.lrb_linear(L, x).view(torch.int32))
         seq.close()
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_sequence_many_linears_parity(T):
+    """A persistent schedule over many linears of mixed shapes (ragged row blocks,
+    several reduction chunks) matches the oracle on every entry."""
+    cfg = G.tiny_config(f"seqmany/{T}")
+    shapes = [synth.LayerShape(f"m{i}", d_out, d_in, r) for i, (d_out, d_in, r) in enumerate(
+        [(1000, 3000, 300), (64, 5000, 1100), (700, 33, 9), (257, 2500, 2100), (3, 3, 3), (1500, 700, 640)])]
+    built = [G.latent_layer(cfg, s, i) for i, s in enumerate(shapes)]
+    xs_np = [synth.activations(f"seqmany/x/{T}/{i}", T, s.d_in, "bf16") for i, s in enumerate(shapes)]
+    xs = [G.to_device_x(x, "bf16") for x in xs_np]
+    ys = [torch.full((T, s.d_out), float("nan"), device=G.DEV) for s in shapes]
+    seq = nq.Seq([b[0] for b in built], xs, ys)
+    for _ in range(3):
+        seq.run()
+    assert seq.device_error() == 0
+    for (dev, ref, _), x, y in zip(built, xs_np, ys):
+        assert O.rel_err(y.cpu().numpy(), O.linear_ref(ref, x)) <= 1e-5
+    seq.close()
 
 
 # ---------------------------------------------------------------- 70B shapes (sampled rows)
