@@ -121,7 +121,7 @@ namespace {
 // enough independent tiles are ready to keep every workgroup streaming.
 int seq_lag() {
   const char* e = getenv("NQ_SEQ_LAG");
-  const int v = e ? atoi(e) : 14;
+  const int v = e ? atoi(e) : 64;
   return v < 0 ? 0 : v;
 }
 

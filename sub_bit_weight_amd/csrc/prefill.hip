@@ -1,161 +1,312 @@
 // Matrix-core regime (T > 8): the two stages of y = s1 (.) U (V^T (s2 (.) x))
 // as binary GEMMs (research.samsung.com NanoQuant blog, section 4, subsection
-// "Inference Performance": binary GEMM kernels for batch processing).
+// "Inference Performance": binary GEMM kernels for batch processing; the
+// stages follow the factorization equation of section 2).
 //
-// C[m][n] = sum_k A[m][k] * S[k][n] with A the activations of the stage
-// (stage 1: x*s2, stage 2: t) and S = +-1 from the sign words of the stage.
-// +-1 is exact in bf16, so the only rounding of the product is the conversion
-// of A to bf16.  A is written as a sum of NT bf16 terms (hi, lo, ...), each
-// multiplied on the matrix cores with fp32 accumulation
-// (v_mfma_f32_16x16x32_bf16).  NT = 1 rounds A once, NT = 2 keeps ~16
-// significant bits, NT = 3 keeps fp32's 24.
+// Each stage is C[m][n] = sum_k A[m][k] * S[k][n] with A the stage's
+// activations (stage 1: x (.) s2, stage 2: t) and S = +-1 from the stage's
+// sign words, words[k/32][n] bit k%32.
+//
+// Numerics.  +-1 is exact in fp16 and fp32 accumulation is used throughout, so
+// the only rounding of a product is the conversion of A to fp16.  Each token
+// row of A is first scaled by an exact power of two 2^e (chosen from the row's
+// largest magnitude so that it lands in [2^13, 2^14)); the fp16 rounding then
+// has relative error <= 2^-11 for every element above 2^-28 of the row maximum,
+// independent of the data's range.  The epilogue multiplies by 2^-e (exact).
+// For fp32 activations A is kept as two fp16 terms (hi + lo), ~22 bits.
+//
+// Kernels per stage: a prep kernel (row maxima, exponents, fp16 terms) and the
+// GEMM.  GEMM tiles are 256 (tokens) x 128 (outputs) x 64 (reduction) per
+// workgroup of 4 waves, each wave 128 x 64 as 4 x 2 v_mfma_f32_32x32x16_f16
+// tiles.  A goes through double-buffered LDS; the +-1 operand is built in
+// registers straight from the sign words: a 32x32x16 MFMA lane needs 8 signs
+// of one column, and with the reduction order below two signs 16 bits apart
+// become one fp16 pair with a shift and a v_and_or_b32:
+//   pair q (0..15) of each 32-element block holds elements (q, q+16);
+//   the prep kernel writes A in that interleaved order.
 #include "nq_internal.h"
 
 namespace nq {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int kBM = 256, kBN = 128, kBK = 64;
 constexpr int kThreads = 256;
-constexpr int kTileM = 64;
-constexpr int kTileN = 64;
+constexpr int kLdsRow = kBK + 8;  // fp16 per LDS row (16 bytes of padding: conflict-free b128 reads)
+constexpr int kPrepThreads = 256;
 
 enum ASrc { kAF32Scaled = 0, kABF16Scaled = 1, kAF32 = 2 };
 
 template <int SRC>
-__device__ inline float load_a(const void* __restrict__ a, const float* __restrict__ cs, int64_t M,
-                               int64_t K, int64_t m, int64_t k) {
-  if (m >= M || k >= K) return 0.0f;
+__device__ inline float act(const void* a, const float* cs, int64_t m, int64_t K, int64_t k) {
   const int64_t g = m * K + k;
   if (SRC == kAF32Scaled) return static_cast<const float*>(a)[g] * cs[k];
-  if (SRC == kABF16Scaled)
-    return __uint_as_float((uint32_t) static_cast<const uint16_t*>(a)[g] << 16) * cs[k];
+  if (SRC == kABF16Scaled) return __uint_as_float((uint32_t) static_cast<const uint16_t*>(a)[g] << 16) * cs[k];
   return static_cast<const float*>(a)[g];
 }
 
-// +-1 bf16 operand for 8 consecutive reduction elements starting at bit `b0`
-// of `word`: bf16 1.0 = 0x3F80, the sign bit (bit 15) set for a stored 1.
-__device__ inline bf16x8 signs_to_bf16(uint32_t word, int b0) {
-  const uint32_t s = word >> b0;
+// One workgroup per token row m:
+//   e[m] = 14 - exponent(max_k |a[m][k]|)  (0 for an all-zero row)
+//   out[term][m][2p], out[term][m][2p+1] = fp16 terms of a[m][k]*2^e for the
+//   element pair p (block p/16, elements q and q+16 with q = p%16); zero past K.
+template <int SRC>
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restrict__ a,
+                                                            const float* __restrict__ cs, int64_t M,
+                                                            int64_t K, int64_t Kpad, int nt,
+                                                            _Float16* __restrict__ out, int* __restrict__ e_out) {
+  __shared__ float red[kPrepThreads / 64];
+  const int64_t m = blockIdx.x;
+  const int tid = threadIdx.x;
+  float mx = 0.0f;
+  for (int64_t k = tid; k < K; k += kPrepThreads) mx = fmaxf(mx, fabsf(act<SRC>(a, cs, m, K, k)));
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (tid % 64 == 0) red[tid / 64] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int e = 0;
+  if (mx > 0.0f && isfinite(mx)) {
+    int ex;
+    frexpf(mx, &ex);  // mx = f * 2^ex, f in [0.5, 1)
+    e = 14 - ex;      // mx * 2^e in [2^13, 2^14)
+  }
+  if (tid == 0) e_out[m] = e;
+  const int64_t npairs = Kpad / 2;
+  uint32_t* hi = reinterpret_cast<uint32_t*>(out + m * Kpad);
+  uint32_t* lo = reinterpret_cast<uint32_t*>(out + (M + m) * Kpad);
+  for (int64_t p = tid; p < npairs; p += kPrepThreads) {
+    const int64_t k0 = (p / 16) * 32 + (p % 16);
+    const int64_t k1 = k0 + 16;
+    const float v0 = k0 < K ? ldexpf(act<SRC>(a, cs, m, K, k0), e) : 0.0f;
+    const float v1 = k1 < K ? ldexpf(act<SRC>(a, cs, m, K, k1), e) : 0.0f;
+    const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+    hi[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    if (nt == 2) {
+      const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
+      lo[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+  }
+}
+
+// +-1 fp16 operand of a 32x32x16 MFMA lane: 8 signs of one column, the pairs
+// (b+d, b+d+16) for d = 0..3 of sign word w; fp16 1.0 = 0x3C00, sign bit 15.
+__device__ inline f16x8 signs_f16(uint32_t w, int b) {
   u32x4 v;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t lo = (s >> (2 * d)) & 1u, hi = (s >> (2 * d + 1)) & 1u;
-    v[d] = 0x3F803F80u | (lo << 15) | (hi << 31);
-  }
-  return __builtin_bit_cast(bf16x8, v);
+  for (int d = 0; d < 4; ++d) v[d] = ((w << (15 - b - d)) & 0x80008000u) | 0x3C003C00u;
+  return __builtin_bit_cast(f16x8, v);
 }
 
-// One workgroup = 4 waves = a 64x64 tile of C; a wave owns a 32x32 quarter
-// as 2x2 MFMA tiles of 16x16.  Lane l of a 16x16x32 MFMA holds A row l%16 and
-// B column l%16 for the 8 reduction elements of group l/16; A and B use the
-// same element order, so the pairing of reduction indices is consistent.
-template <int NT, int SRC>
-__global__ __launch_bounds__(kThreads) void sign_gemm_kernel(const void* __restrict__ a,
-                                                             const float* __restrict__ colscale,
-                                                             const uint32_t* __restrict__ bits,
-                                                             int64_t ld, int64_t M, int64_t N, int64_t K,
-                                                             const float* __restrict__ rowscale,
-                                                             float* __restrict__ out) {
-  const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
-  const int64_t m_base = (int64_t)blockIdx.y * kTileM + (wave / 2) * 32;
-  const int64_t n_base = (int64_t)blockIdx.x * kTileN + (wave % 2) * 32;
-  const int r16 = lane % 16, grp = lane / 16;
+template <int NT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const _Float16* __restrict__ A, const int* __restrict__ erow,
+                                                           const uint32_t* __restrict__ bits, int64_t ldb,
+                                                           int64_t M, int64_t N, int64_t K, int64_t Kpad,
+                                                           int tiles_m, int tiles_n, const float* __restrict__ colscale,
+                                                           float* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 lds[];  // [2][NT][kBM][kLdsRow]
+  const int tid = threadIdx.x;
+  const int lane = tid % 64, wave = tid / 64;
+  const int wm = wave / 2, wn = wave % 2;
+  const int l32 = lane % 32, h = lane / 32;
 
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a
+  // contiguous range of tiles (N fastest) so concurrent tiles share A rows in L2.
+  const int ntiles = tiles_m * tiles_n;
+  const int per_xcd = (ntiles + 7) / 8;
+  const int t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (t >= ntiles) return;
+  const int64_t m0 = (int64_t)(t / tiles_n) * kBM;
+  const int64_t n0 = (int64_t)(t % tiles_n) * kBN;
+  const int64_t nwords = cdiv(K, kWordBits);
+  const int nk = (int)(Kpad / kBK);
 
-  for (int64_t k0 = 0; k0 < K; k0 += 32) {
-    bf16x8 bfrag[2];
+  // global -> LDS copy of A: thread covers 16 bytes of 8 rows (row tid/8 + 32 i)
+  const int crow = tid / 8, cchunk = tid % 8;
+  u32x4 areg[NT][8];
+  auto load_a = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n_base + j * 16 + r16;
-      const uint32_t word = (n < N) ? bits[(k0 / 32) * ld + n] : 0u;
-      bfrag[j] = signs_to_bf16(word, 8 * grp);
+    for (int term = 0; term < NT; ++term)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t m = m0 + crow + 32 * i;
+        const u32x4* src = reinterpret_cast<const u32x4*>(A + ((int64_t)term * M + (m < M ? m : 0)) * Kpad +
+                                                          (int64_t)kt * kBK + cchunk * 8);
+        const u32x4 v = *src;
+        areg[term][i] = m < M ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int term = 0; term < NT; ++term)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(lds + (((int64_t)buf * NT + term) * kBM + crow + 32 * i) * kLdsRow + cchunk * 8) =
+            areg[term][i];
+  };
+  // sign words of this wave's 2 column blocks for one 64-deep step
+  uint32_t bw[2][2], bwn[2][2];
+  auto load_b = [&](int kt, uint32_t (&dst)[2][2]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int64_t n = n0 + wn * 64 + nb * 32 + l32;
+        const int64_t kw = (int64_t)kt * 2 + q;
+        dst[nb][q] = (n < N && kw < nwords) ? bits[kw * ldb + n] : 0u;
+      }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  load_a(0);
+  load_b(0, bw);
+  store_a(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) {
+      load_a(kt + 1);
+      load_b(kt + 1, bwn);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t m = m_base + i * 16 + r16;
-      float v[8];
+    for (int s = 0; s < 4; ++s) {  // 16-deep MFMA steps within the 64-deep tile
+      const int q = s / 2, b = 8 * (s % 2) + 4 * h;
+      f16x8 bf[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = load_a<SRC>(a, colscale, M, K, m, k0 + 8 * grp + e);
+      for (int nb = 0; nb < 2; ++nb) bf[nb] = signs_f16(bw[nb][q], b);
 #pragma unroll
       for (int term = 0; term < NT; ++term) {
-        bf16x8 af;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const __bf16 h = static_cast<__bf16>(v[e]);
-          af[e] = h;
-          v[e] = v[e] - static_cast<float>(h);  // exact residual
+        for (int mb = 0; mb < 4; ++mb) {
+          const _Float16* p = lds + (((int64_t)buf * NT + term) * kBM + wm * 128 + mb * 32 + l32) * kLdsRow +
+                              q * 32 + (2 * (s % 2) + h) * 8;
+          const f16x8 af = *reinterpret_cast<const f16x8*>(p);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[nb], acc[mb][nb], 0, 0, 0);
         }
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfrag[j], acc[i][j], 0, 0, 0);
       }
     }
+    if (kt + 1 < nk) {
+      store_a(buf ^ 1);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) bw[nb][q] = bwn[nb][q];
+    }
+    __syncthreads();
   }
 
-  // C/D layout of a 16x16 MFMA: lane l, register q -> row 4*(l/16)+q, column l%16.
+  // 32x32 MFMA result layout: lane l, register 4a+c -> row 8a + 4(l/32) + c, column l%32.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n_base + j * 16 + r16;
-      if (n >= N) continue;
-      const float sc = rowscale ? rowscale[n] : 1.0f;
+    for (int nb = 0; nb < 2; ++nb) {
+      const int64_t n = n0 + wn * 64 + nb * 32 + l32;
+      const float sc = (n < N && colscale) ? colscale[n] : 1.0f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t m = m_base + i * 16 + 4 * grp + q;
-        if (m < M) out[m * N + n] = sc * acc[i][j][q];
-      }
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t m = m0 + wm * 128 + mb * 32 + 8 * a + 4 * h + c;
+          if (m < M && n < N) out[m * N + n] = sc * ldexpf(acc[mb][nb][4 * a + c], -erow[m]);
+        }
     }
 }
+
+size_t gemm_lds_bytes(int nt) { return (size_t)2 * nt * kBM * kLdsRow * sizeof(_Float16); }
 
 template <int SRC>
-hipError_t launch_gemm(int nt, const void* a, const float* cs, const uint32_t* bits, int64_t ld, int64_t M,
-                       int64_t N, int64_t K, const float* rs, float* out, hipStream_t s) {
-  dim3 grid((unsigned)cdiv(N, kTileN), (unsigned)cdiv(M, kTileM));
-  switch (nt) {
-    case 1: hipLaunchKernelGGL((sign_gemm_kernel<1, SRC>), grid, dim3(kThreads), 0, s, a, cs, bits, ld, M, N, K, rs, out); break;
-    case 2: hipLaunchKernelGGL((sign_gemm_kernel<2, SRC>), grid, dim3(kThreads), 0, s, a, cs, bits, ld, M, N, K, rs, out); break;
-    case 3: hipLaunchKernelGGL((sign_gemm_kernel<3, SRC>), grid, dim3(kThreads), 0, s, a, cs, bits, ld, M, N, K, rs, out); break;
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int64_t Kpad, int nt, _Float16* out,
+                       int* e, hipStream_t s) {
+  hipLaunchKernelGGL(prep_kernel<SRC>, dim3((unsigned)M), dim3(kPrepThreads), 0, s, a, cs, M, K, Kpad, nt, out, e);
   return hipGetLastError();
 }
+
+hipError_t launch_gemm(int nt, const _Float16* A, const int* e, const uint32_t* bits, int64_t ldb, int64_t M,
+                       int64_t N, int64_t K, int64_t Kpad, const float* colscale, float* out, hipStream_t s) {
+  const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
+  const unsigned grid = (unsigned)(8 * ((tiles_m * tiles_n + 7) / 8));
+  if (nt == 1)
+    hipLaunchKernelGGL(gemm_kernel<1>, dim3(grid), dim3(kThreads), gemm_lds_bytes(1), s, A, e, bits, ldb, M, N, K,
+                       Kpad, tiles_m, tiles_n, colscale, out);
+  else
+    hipLaunchKernelGGL(gemm_kernel<2>, dim3(grid), dim3(kThreads), gemm_lds_bytes(2), s, A, e, bits, ldb, M, N, K,
+                       Kpad, tiles_m, tiles_n, colscale, out);
+  return hipGetLastError();
+}
+
+struct PrefillLayout {
+  int nt;
+  int64_t kpad1, kpad2;
+  size_t off_z, off_e1, off_t, off_t16, off_e2, total;
+};
+
+PrefillLayout prefill_layout(const nq_lrb& L, int64_t T, nq_dtype xd) {
+  PrefillLayout d;
+  d.nt = xd == NQ_F32 ? 2 : 1;
+  d.kpad1 = round_up(L.d_in, kBK);
+  d.kpad2 = round_up(L.r, kBK);
+  size_t off = 0;
+  d.off_z = off;
+  off = align_up(off + (size_t)d.nt * T * d.kpad1 * sizeof(_Float16));
+  d.off_e1 = off;
+  off = align_up(off + (size_t)T * sizeof(int));
+  d.off_t = off;
+  off = align_up(off + (size_t)T * L.r * sizeof(float));
+  d.off_t16 = off;
+  off = align_up(off + (size_t)d.nt * T * d.kpad2 * sizeof(_Float16));
+  d.off_e2 = off;
+  off = align_up(off + (size_t)T * sizeof(int));
+  d.total = off;
+  return d;
+}
+
+bool lds_configured = false;
 
 }  // namespace
 
 size_t prefill_workspace_bytes(const nq_lrb& L, int64_t T) {
-  return align_up((size_t)T * L.r * sizeof(float));
+  // sized for the larger (fp32 activation) plan so one size serves both dtypes
+  return prefill_layout(L, T, NQ_F32).total;
 }
 
 hipError_t launch_prefill(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
                           hipStream_t s) {
-  float* t = static_cast<float*>(ws);
-  // bf16 x: split the cheaper stage's activations into two bf16 terms, round
-  // the other stage's once.  fp32 x: three terms on both stages.
-  int nt1, nt2;
-  if (xd == NQ_F32) {
-    nt1 = nt2 = 3;
-  } else if (L.d_in <= L.d_out) {
-    nt1 = 2, nt2 = 1;
-  } else {
-    nt1 = 1, nt2 = 2;
+  if (!lds_configured) {
+    hipError_t e1 = hipFuncSetAttribute((const void*)gemm_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        (int)gemm_lds_bytes(1));
+    hipError_t e2 = hipFuncSetAttribute((const void*)gemm_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        (int)gemm_lds_bytes(2));
+    if (e1 != hipSuccess) return e1;
+    if (e2 != hipSuccess) return e2;
+    lds_configured = true;
   }
+  const PrefillLayout d = prefill_layout(L, T, xd);
+  char* base = static_cast<char*>(ws);
+  _Float16* z = reinterpret_cast<_Float16*>(base + d.off_z);
+  int* e1 = reinterpret_cast<int*>(base + d.off_e1);
+  float* t = reinterpret_cast<float*>(base + d.off_t);
+  _Float16* t16 = reinterpret_cast<_Float16*>(base + d.off_t16);
+  int* e2 = reinterpret_cast<int*>(base + d.off_e2);
   hipError_t e;
   if (xd == NQ_BF16)
-    e = launch_gemm<kABF16Scaled>(nt1, x, L.s2, L.vt_bits, L.ldv, T, L.r, L.d_in, nullptr, t, s);
+    e = launch_prep<kABF16Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, z, e1, s);
   else
-    e = launch_gemm<kAF32Scaled>(nt1, x, L.s2, L.vt_bits, L.ldv, T, L.r, L.d_in, nullptr, t, s);
+    e = launch_prep<kAF32Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, z, e1, s);
   if (e != hipSuccess) return e;
-  return launch_gemm<kAF32>(nt2, t, nullptr, L.u_bits, L.ldu, T, L.d_out, L.r, L.s1, y, s);
+  if ((e = launch_gemm(d.nt, z, e1, L.vt_bits, L.ldv, T, L.r, L.d_in, d.kpad1, nullptr, t, s)) != hipSuccess) return e;
+  if ((e = launch_prep<kAF32>(t, nullptr, T, L.r, d.kpad2, d.nt, t16, e2, s)) != hipSuccess) return e;
+  return launch_gemm(d.nt, t16, e2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, L.s1, y, s);
 }
 
 }  // namespace nq
