@@ -17,9 +17,10 @@
 //
 // Kernels per stage: a prep kernel (row maxima, exponents, fp16 terms) and the
 // GEMM.  GEMM tiles are 256 (tokens) x 128 (outputs) x 64 (reduction) per
-// workgroup of 4 waves, each wave 128 x 64 as 4 x 2 v_mfma_f32_32x32x16_f16
-// tiles.  A goes through double-buffered LDS; the +-1 operand is built in
-// registers straight from the sign words: a 32x32x16 MFMA lane needs 8 signs
+// workgroup of 8 waves (two per SIMD), each wave 64 x 64 as 2 x 2
+// v_mfma_f32_32x32x16_f16 tiles.  A streams into a ring of LDS stages with direct global->LDS loads
+// issued several 64-deep steps ahead; the +-1 operand is built in registers
+// straight from the sign words: a 32x32x16 MFMA lane needs 8 signs
 // of one column, and with the reduction order below two signs 16 bits apart
 // become one fp16 pair with a shift and a v_and_or_b32:
 //   pair q (0..15) of each 32-element block holds elements (q, q+16);
@@ -34,8 +35,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256, kBN = 128, kBK = 64;
-constexpr int kThreads = 256;
-constexpr int kLdsRow = kBK + 8;  // fp16 per LDS row (16 bytes of padding: conflict-free b128 reads)
+constexpr int kWaves = 8;                 // 4 (tokens) x 2 (outputs); each wave owns 64 x 64
+constexpr int kThreads = 64 * kWaves;
 constexpr int kPrepThreads = 256;
 
 enum ASrc { kAF32Scaled = 0, kABF16Scaled = 1, kAF32 = 2 };
@@ -99,16 +100,40 @@ __device__ inline f16x8 signs_f16(uint32_t w, int b) {
   return __builtin_bit_cast(f16x8, v);
 }
 
+// s_waitcnt that waits until at most n vector-memory operations of this wave
+// are outstanding (lgkmcnt and expcnt left alone).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int NT>
+struct Pipe {
+  static constexpr int S = NT == 1 ? 4 : 2;                       // LDS stages
+  static constexpr int A_BYTES = NT * kBM * kBK * 2;              // A tile(s) of one stage
+  static constexpr int B_BYTES = kWaves * 2 * 64 * 4;             // per wave: 2 word rows x 64 columns
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int ROWS_PER_WAVE = kBM / kWaves;              // A rows each wave moves
+  static constexpr int DMA_PER_WAVE = NT * ROWS_PER_WAVE / 8;     // 8 rows (1 KiB) per 16-byte DMA
+  static constexpr int PER_STAGE = DMA_PER_WAVE + 2;              // + 2 sign-word DMA instructions
+};
+
+// A stage holds NT tiles of kBM rows x kBK fp16 (128 bytes per row) written by
+// direct global->LDS loads: one instruction moves 64 lanes x 16 bytes = 8 rows.
+// The 16-byte chunk c of row r is stored at chunk c ^ (r & 7), which makes the
+// 32-row fragment reads below conflict-free.
 template <int NT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const _Float16* __restrict__ A, const int* __restrict__ erow,
                                                            const uint32_t* __restrict__ bits, int64_t ldb,
                                                            int64_t M, int64_t N, int64_t K, int64_t Kpad,
                                                            int tiles_m, int tiles_n, const float* __restrict__ colscale,
                                                            float* __restrict__ out) {
-  extern __shared__ __attribute__((aligned(16))) _Float16 lds[];  // [2][NT][kBM][kLdsRow]
+  using P = Pipe<NT>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];  // [S][NT][kBM][128 bytes]
   const int tid = threadIdx.x;
   const int lane = tid % 64, wave = tid / 64;
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / 2, wn = wave % 2;  // wave tile: rows 64*wm .., columns 64*wn ..
   const int l32 = lane % 32, h = lane / 32;
 
   // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a
@@ -122,93 +147,102 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const _Float16* __res
   const int64_t nwords = cdiv(K, kWordBits);
   const int nk = (int)(Kpad / kBK);
 
-  // global -> LDS copy of A: thread covers 16 bytes of 8 rows (row tid/8 + 32 i)
-  const int crow = tid / 8, cchunk = tid % 8;
-  u32x4 areg[NT][8];
-  auto load_a = [&](int kt) {
+  // this lane's DMA source rows: wave w fills rows ROWS_PER_WAVE*w .., 8 per instruction
+  const int drow = lane / 8, dchunk = lane % 8;
+  // Every global read is a direct global->LDS load, so no register waits on a
+  // global load and the explicit vmcnt waits below are the only ones.  A stage
+  // is exactly PER_STAGE such instructions per wave.  Sign words past the last
+  // word row or column are clamped: they only ever meet zero-padded A columns
+  // or produce outputs that are not stored.
+  auto issue = [&](int kt, int st) {
+    char* stage = lds + (int64_t)st * P::STAGE_BYTES;
 #pragma unroll
     for (int term = 0; term < NT; ++term)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t m = m0 + crow + 32 * i;
-        const u32x4* src = reinterpret_cast<const u32x4*>(A + ((int64_t)term * M + (m < M ? m : 0)) * Kpad +
-                                                          (int64_t)kt * kBK + cchunk * 8);
-        const u32x4 v = *src;
-        areg[term][i] = m < M ? v : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < P::ROWS_PER_WAVE / 8; ++j) {
+        const int r = wave * P::ROWS_PER_WAVE + j * 8 + drow;
+        const int64_t m = m0 + r < M ? m0 + r : M - 1;  // rows past M load row M-1 (never stored)
+        const int c = dchunk ^ (r & 7);
+        const _Float16* src = A + ((int64_t)term * M + m) * Kpad + (int64_t)kt * kBK + c * 8;
+        char* dst = stage + ((int64_t)term * kBM + wave * P::ROWS_PER_WAVE + j * 8) * 128;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
       }
-  };
-  auto store_a = [&](int buf) {
+    const int64_t n = imin(n0 + wn * 64 + lane, N - 1);
 #pragma unroll
-    for (int term = 0; term < NT; ++term)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(lds + (((int64_t)buf * NT + term) * kBM + crow + 32 * i) * kLdsRow + cchunk * 8) =
-            areg[term][i];
-  };
-  // sign words of this wave's 2 column blocks for one 64-deep step
-  uint32_t bw[2][2], bwn[2][2];
-  auto load_b = [&](int kt, uint32_t (&dst)[2][2]) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int64_t n = n0 + wn * 64 + nb * 32 + l32;
-        const int64_t kw = (int64_t)kt * 2 + q;
-        dst[nb][q] = (n < N && kw < nwords) ? bits[kw * ldb + n] : 0u;
-      }
+    for (int q = 0; q < 2; ++q) {
+      const int64_t kw = imin((int64_t)kt * 2 + q, nwords - 1);
+      char* dst = stage + P::A_BYTES + (wave * 2 + q) * 64 * 4;
+      __builtin_amdgcn_global_load_lds(bits + kw * ldb + n, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+    }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  load_a(0);
-  load_b(0, bw);
-  store_a(0);
-  __syncthreads();
+#pragma unroll
+  for (int kt = 0; kt < P::S - 1; ++kt)
+    if (kt < nk) issue(kt, kt);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      load_a(kt + 1);
-      load_b(kt + 1, bwn);
-    }
+  // the ring index is kept compile-time (kt = kt0 + st, st < S) so the sign
+  // words stay in registers
+  for (int kt0 = 0; kt0 < nk; kt0 += P::S) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {  // 16-deep MFMA steps within the 64-deep tile
-      const int q = s / 2, b = 8 * (s % 2) + 4 * h;
-      f16x8 bf[2];
+    for (int st = 0; st < P::S; ++st) {
+      const int kt = kt0 + st;
+      if (kt >= nk) break;
+      // wait for stage kt: later stages (up to S-2 of them) may stay in flight
+      const int ahead = nk - 1 - kt;
+      if (ahead >= P::S - 2) {
+        wait_vmcnt<(P::S - 2) * P::PER_STAGE>();
+      } else if (P::S > 3 && ahead == 1) {
+        wait_vmcnt<P::PER_STAGE>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __syncthreads();  // every wave's DMA for stage kt landed; stage kt-1 fully consumed
+      if (kt + P::S - 1 < nk) issue(kt + P::S - 1, (st + P::S - 1) % P::S);
+
+      // 16-deep MFMA steps within the 64-deep tile; the A fragments of step
+      // s+1 are read from LDS while the MFMAs of step s run
+      const char* stage = lds + (int64_t)st * P::STAGE_BYTES;
+      const uint32_t* bws = reinterpret_cast<const uint32_t*>(stage + P::A_BYTES) + wave * 2 * 64;
+      f16x8 af[2][NT][2];
+      auto read_a = [&](int s, f16x8 (&dst)[NT][2]) {
+        const int chunk = (4 * (s / 2) + 2 * (s % 2) + h) ^ (l32 & 7);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) bf[nb] = signs_f16(bw[nb][q], b);
+        for (int term = 0; term < NT; ++term)
 #pragma unroll
-      for (int term = 0; term < NT; ++term) {
+          for (int mb = 0; mb < 2; ++mb)
+            dst[term][mb] = *reinterpret_cast<const f16x8*>(
+                stage + ((int64_t)term * kBM + wm * 64 + mb * 32 + l32) * 128 + chunk * 16);
+      };
+      read_a(0, af[0]);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const _Float16* p = lds + (((int64_t)buf * NT + term) * kBM + wm * 128 + mb * 32 + l32) * kLdsRow +
-                              q * 32 + (2 * (s % 2) + h) * 8;
-          const f16x8 af = *reinterpret_cast<const f16x8*>(p);
+      for (int s = 0; s < 4; ++s) {
+        if (s + 1 < 4) read_a(s + 1, af[(s + 1) & 1]);
+        const int q = s / 2, b = 8 * (s % 2) + 4 * h;
+        f16x8 bf[2];
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[nb], acc[mb][nb], 0, 0, 0);
-        }
+        for (int nb = 0; nb < 2; ++nb) bf[nb] = signs_f16(bws[q * 64 + nb * 32 + l32], b);
+#pragma unroll
+        for (int term = 0; term < NT; ++term)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][term][mb], bf[nb], acc[mb][nb], 0, 0, 0);
       }
     }
-    if (kt + 1 < nk) {
-      store_a(buf ^ 1);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) bw[nb][q] = bwn[nb][q];
-    }
-    __syncthreads();
   }
 
   // 32x32 MFMA result layout: lane l, register 4a+c -> row 8a + 4(l/32) + c, column l%32.
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int64_t n = n0 + wn * 64 + nb * 32 + l32;
@@ -217,13 +251,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const _Float16* __res
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int64_t m = m0 + wm * 128 + mb * 32 + 8 * a + 4 * h + c;
+          const int64_t m = m0 + wm * 64 + mb * 32 + 8 * a + 4 * h + c;
           if (m < M && n < N) out[m * N + n] = sc * ldexpf(acc[mb][nb][4 * a + c], -erow[m]);
         }
     }
 }
 
-size_t gemm_lds_bytes(int nt) { return (size_t)2 * nt * kBM * kLdsRow * sizeof(_Float16); }
+size_t gemm_lds_bytes(int nt) {
+  return nt == 1 ? (size_t)Pipe<1>::S * Pipe<1>::STAGE_BYTES : (size_t)Pipe<2>::S * Pipe<2>::STAGE_BYTES;
+}
 
 template <int SRC>
 hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int64_t Kpad, int nt, _Float16* out,
