@@ -23,7 +23,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16/bf16 matrix cores, TFLOP/s
+DECODE_SRC = os.path.join(ROOT, "sub_bit_weight_amd", "csrc", "decode_lut.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_lut_persistent_70b_stack_hbm_traffic.md")
 
 
 def log(msg: str) -> None:
@@ -65,6 +67,26 @@ class Stack:
                                           torch.from_numpy(inp["s2"]).to(device)))
                 self.shapes.append(s)
         torch.cuda.synchronize()
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated against a copy of known size), or None
+    when the decode kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines() if ":" in line and line.startswith("- "))
+    fields = {k[2:].strip(): v.strip() for k, v in fields.items()}
+    src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if fields.get("decode_lut.hip sha256") != src_hash:
+        return None
+    try:
+        return float(fields["hbm bytes per launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def time_decode(stack, T: int, steps: int, warmup: int, device: str):
@@ -178,6 +200,8 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-055", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -191,6 +215,17 @@ def main() -> int:
     device = "cuda:0"
     torch.cuda.set_device(0)
 
+    if args.copy_calibration:
+        a = torch.ones(1 << 28, dtype=torch.int32, device=device)  # 1 GiB
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read_per_copy": a.numel() * 4,
+                                               "bytes_written_per_copy": a.numel() * 4, "copies": 5}}))
+        return 0
+
     cfg = synth.CONFIGS["70b_stack"]
     log(f"[bench] building 70B stack (~1.0 bit), {args.layers} layers")
     stack = Stack(cfg, args.layers, device)
@@ -199,7 +234,7 @@ def main() -> int:
     ms, seq, xs, ys = time_decode(stack, T, args.steps, args.warmup, device)
     bytes_step = algorithmic_bytes(stack.shapes, T)
     gbs = bytes_step / (ms * 1e-3) / 1e9
-    log(f"[bench] decode {ms:.3f} ms/step, {gbs:.0f} GB/s")
+    log(f"[bench] decode {ms:.3f} ms/step, {gbs:.0f} GB/s (one persistent-kernel launch per step)")
     err = parity_sample(stack, xs, ys, idx=len(cfg.layers) - 1)
     log(f"[bench] parity (layer 0 down, 16 rows) rel err {err:.2e}")
     del seq
@@ -211,8 +246,10 @@ def main() -> int:
         pms = time_prefill(stack, Tp, device)
         flops = algorithmic_flops(stack.shapes, Tp)
         extra["prefill"] = {"T": Tp, "ms_per_pass": pms, "tflops": flops / (pms * 1e-3) / 1e12,
-                            "frac_of_bf16_peak": flops / (pms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                            "tokens_per_s": Tp / (pms * 1e-3), "algorithmic_flop": flops}
+                            "frac_of_f16_peak": flops / (pms * 1e-3) / 1e12 / F16_PEAK_TFLOPS,
+                            "tokens_per_s": Tp / (pms * 1e-3), "algorithmic_flop": flops,
+                            "operands": "fp16 (per-token power-of-two scaled) x +-1, fp32 accumulate",
+                            "includes": "prep kernels (row scaling, fp16 conversion) and both GEMMs of all 560 linears"}
         log(f"[bench] prefill {pms:.1f} ms/pass, {extra['prefill']['tflops']:.0f} TFLOP/s")
     del stack
     torch.cuda.empty_cache()
@@ -240,8 +277,9 @@ def main() -> int:
                    "global_batch": T, "layers": args.layers, "parallelism": "single-gpu"},
         "hbm_gbs": gbs,
         "algorithmic_bytes_per_step": bytes_step,
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": "lut_persistent_kernel<1> (one launch per step)",
+                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic()},
         "parity_rel_err": err,
     }
     out.update(extra)

@@ -360,12 +360,17 @@ __global__ __launch_bounds__(kRows) void lut_stage_kernel(StageDesc S, int* err)
   lut_tile<T>(S, blockIdx.x, lut, &s_flag, err);
 }
 
+// ints: [0] error flag (sticky), [1] next tile, [2] workgroups exited,
+// [3 .. n_ints) per-linear counters.  The last workgroup to exit zeroes
+// [1 .. n_ints), so consecutive runs need no separate reset launch.
 template <int T>
 __global__ __launch_bounds__(kRows) void lut_persistent_kernel(const StageDesc* __restrict__ segs, int nseg,
-                                                               int ntiles, int* next_tile, int* err) {
+                                                               int ntiles, int* ints, int n_ints) {
   __shared__ __attribute__((aligned(16))) float lut[kLutFloats];
   __shared__ int s_flag;
   __shared__ int s_tile;
+  int* err = ints;
+  int* next_tile = ints + 1;
   if (threadIdx.x == 0) s_tile = atomicAdd(next_tile, 1);
   __syncthreads();
   int tile = s_tile;
@@ -381,6 +386,16 @@ __global__ __launch_bounds__(kRows) void lut_persistent_kernel(const StageDesc* 
     tile = s_tile;
     __syncthreads();
   }
+  // every counter access of this workgroup is done: count the exit; the last
+  // workgroup out resets the counters for the next run
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    s_flag = atomicAdd(ints + 2, 1) == (int)gridDim.x - 1;
+    if (s_flag) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  if (s_flag)
+    for (int i = 1 + threadIdx.x; i < n_ints; i += kRows) ints[i] = 0;
 }
 
 __global__ void zero_ints_kernel(int* p, int64_t n) {
@@ -449,13 +464,13 @@ int lut_persistent_grid(int64_t T) {
   return cus * per;
 }
 
-hipError_t launch_lut_persistent(const StageDesc* segs, int nseg, int ntiles, int* next_tile, int* err,
+hipError_t launch_lut_persistent(const StageDesc* segs, int nseg, int ntiles, int* ints, int n_ints,
                                  int64_t T, int grid, hipStream_t s) {
   switch (T) {
 #define NQ_CASE(TT)                                                                                     \
   case TT:                                                                                              \
     hipLaunchKernelGGL(lut_persistent_kernel<TT>, dim3(grid), dim3(kRows), 0, s, segs, nseg, ntiles, \
-                       next_tile, err);                                                                 \
+                       ints, n_ints);                                                                   \
     break;
     NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
 #undef NQ_CASE

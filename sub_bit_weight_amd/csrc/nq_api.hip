@@ -105,13 +105,14 @@ struct nq_seq {
   // persistent decode schedule (T <= 8)
   bool persistent = false;
   int grid = 0, ntiles = 0;
-  int64_t n_ints = 0;                 // [error flag][next tile][per-linear counters]
+  int64_t n_ints = 0;                 // [error flag][next tile][exited][per-linear counters]
   std::vector<int64_t> ctr_off;       // per linear, in ints from the start of the workspace
   std::vector<size_t> buf_off;        // per linear, in bytes
   std::vector<std::pair<int, int>> order;  // (linear, stage) in schedule order
   size_t off_sched = 0;
   std::vector<nq::StageDesc> segs;    // host copy of the uploaded schedule
   void* uploaded_for = nullptr;
+  bool needs_zero = true;
 };
 
 namespace {
@@ -129,7 +130,7 @@ void plan_persistent(nq_seq* s) {
   using namespace nq;
   const int64_t n = (int64_t)s->layers.size();
   s->persistent = true;
-  int64_t ints = 2;
+  int64_t ints = 3;
   size_t bufs = 0;
   for (int64_t i = 0; i < n; ++i) {
     s->ctr_off.push_back(ints);
@@ -174,6 +175,7 @@ nq_status build_and_upload(nq_seq* s, void* ws, hipStream_t stream) {
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_status(e, "nq_seq_run schedule upload");
   s->uploaded_for = ws;
+  s->needs_zero = true;
   return NQ_OK;
 }
 
@@ -295,10 +297,14 @@ nq_status nq_seq_run(nq_seq* s, void* workspace, size_t workspace_bytes, void* s
       if (r != NQ_OK) return r;
     }
     int* ints = static_cast<int*>(workspace);
-    hipError_t e = launch_zero_ints(ints, s->n_ints, st);
+    hipError_t e = hipSuccess;
+    if (s->needs_zero) {  // first run on this workspace; later runs leave the counters zeroed
+      e = launch_zero_ints(ints, s->n_ints, st);
+      s->needs_zero = false;
+    }
     if (e == hipSuccess)
       e = launch_lut_persistent(reinterpret_cast<const StageDesc*>(static_cast<char*>(workspace) + s->off_sched),
-                                (int)s->segs.size(), s->ntiles, ints + 1, ints, s->T, s->grid, st);
+                                (int)s->segs.size(), s->ntiles, ints, (int)s->n_ints, s->T, s->grid, st);
     return hip_status(e, "nq_seq_run launch");
   }
   for (size_t i = 0; i < s->layers.size(); ++i) {
