@@ -111,8 +111,10 @@ size_t nq_lrb_workspace_bytes(const nq_lrb* L, int64_t T);
  *   x: [T][d_in] row-major, fp32 or bf16 (x_dtype);  y: [T][d_out] fp32.
  *   workspace: at least nq_lrb_workspace_bytes(L, T) bytes, 256-byte aligned.
  * Regimes: T <= 8 runs the decode kernels (fp32 arithmetic throughout);
- * T > 8 runs the matrix-core kernels (bf16 operands, fp32 accumulation, one
- * operand of the cheaper stage split into two bf16 terms).
+ * T > 8 runs the matrix-core kernels: each token row of a stage's activations
+ * is scaled by an exact power of two and rounded to fp16 (two fp16 terms for
+ * fp32 x), multiplied by the exact +-1 signs with fp32 accumulation, and
+ * scaled back.
  * y is fully overwritten.  Summation order is fixed: results are run-to-run
  * deterministic, but not bitwise equal across regimes.
  * Errors: NQ_ERR_ARG for null pointers, dims < 1, ldu < d_out, ldv < r, T < 1,
@@ -128,7 +130,7 @@ nq_status nq_lrb_linear(const nq_lrb* L, const void* x, nq_dtype x_dtype, int64_
  *   w[i*d_in + j] = fl32( fl32(s1[i] * m) * s2[j] ),  m = sum_k U[i,k] V[j,k]
  * with m an exact integer and both products rounded to nearest even, so the
  * result is unique bit for bit.  w is [d_out][d_in] fp32.
- * Errors: NQ_ERR_ARG as for nq_lrb_linear; NQ_ERR_UNSUPPORTED for r > 65536.
+ * Errors: NQ_ERR_ARG as for nq_lrb_linear; NQ_ERR_UNSUPPORTED for r > 2^24.
  */
 nq_status nq_reconstruct(const nq_lrb* L, float* w, void* stream);
 
@@ -153,7 +155,10 @@ uint64_t nq_storage_bits(int64_t d_out, int64_t d_in, int64_t r);
  * nq_seq_workspace_bytes: device workspace the plan needs.
  * nq_seq_run: runs the whole sequence on `stream`.  The workspace must stay
  *   the same buffer across runs of one plan (the first run uploads the
- *   schedule into it) and must not be shared by plans running concurrently.
+ *   schedule into it, synchronising `stream` once) and must not be shared by
+ *   plans running concurrently.  In the decode regime the first 4 bytes of the
+ *   workspace are a device error word: 0, or non-zero (sticky) if a
+ *   dependency wait inside the kernel gave up; read it after synchronising.
  * nq_seq_destroy: frees the host plan.
  */
 typedef struct nq_seq nq_seq;
