@@ -119,8 +119,9 @@ size_t nq_lrb_workspace_bytes(const nq_lrb* L, int64_t T);
  * deterministic, but not bitwise equal across regimes.
  * Errors: NQ_ERR_ARG for null pointers, dims < 1, ldu < d_out, ldv < r, T < 1,
  * an unknown dtype or a misaligned pointer (x, y: 4 bytes; bits, scales: 4
- * bytes); NQ_ERR_WORKSPACE when workspace_bytes is too small;
- * NQ_ERR_HIP when a launch fails.
+ * bytes); NQ_ERR_UNSUPPORTED when r > 2^24, d_out or d_in > 2^31, or a
+ * sign-word buffer exceeds 2 GiB; NQ_ERR_WORKSPACE when workspace_bytes is too
+ * small; NQ_ERR_HIP when a launch fails.
  */
 nq_status nq_lrb_linear(const nq_lrb* L, const void* x, nq_dtype x_dtype, int64_t T,
                         float* y, void* workspace, size_t workspace_bytes, void* stream);

@@ -223,13 +223,28 @@ __device__ inline void add_entries(const float (&e)[8][Geo<T>::NQ * Geo<T>::TT],
 // past the end of a tile's reduction span only select table entries of groups
 // past the span, which are all zero, so loads need no masking: the word index
 // is clamped (uniformly) to stay inside the matrix.
+// Sign words are read with buffer loads: the word row's byte offset is a scalar
+// (uniform) operand and the lane's column a 32-bit vector offset, so a load
+// costs no vector ALU work.  Sign-word buffers are below 2 GiB (checked by the
+// host), so both offsets fit.
+__device__ inline __amdgpu_buffer_rsrc_t word_rsrc(const uint32_t* bits) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(bits), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ inline uint32_t load_word(__amdgpu_buffer_rsrc_t r, uint32_t lane_bytes, int64_t w, int64_t ld) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)lane_bytes, (int)(w * ld * 4), 0);
+}
+
 template <int T, int WI>
-__device__ inline void chunk_words(const uint32_t* wp, int64_t ld, int64_t wnext, int64_t wlast,
-                                   uint32_t (&ring)[Geo<T>::D][Geo<T>::B], const float* lut, float* acc,
+__device__ inline void chunk_words(__amdgpu_buffer_rsrc_t bits, uint32_t lane_bytes, int64_t ld, int64_t wnext, int64_t wlast,
+                                   int nwords, uint32_t (&ring)[Geo<T>::D][Geo<T>::B], const float* lut, float* acc,
                                    float (&cur)[8][Geo<T>::NQ * Geo<T>::TT]) {
   using G = Geo<T>;
   if constexpr (WI < G::CW) {
     constexpr int b = WI / G::B, j = WI % G::B;
+    // a short last chunk stops at the first batch past its words (uniform
+    // branch); the tile ends there, so the ring is not needed any more
+    if constexpr (j == 0 && WI > 0)
+      if (WI >= nwords) return;
     float nxt[8][G::NQ * G::TT];
     if constexpr (WI + 1 < G::CW) {
       constexpr int b1 = (WI + 1) / G::B, j1 = (WI + 1) % G::B;
@@ -239,12 +254,12 @@ __device__ inline void chunk_words(const uint32_t* wp, int64_t ld, int64_t wnext
 #pragma unroll
       for (int jj = 0; jj < G::B; ++jj) {
         const int64_t w = imin(wnext + (int64_t)b * G::B + jj, wlast);
-        ring[b % G::D][jj] = gload(wp + w * ld);
+        ring[b % G::D][jj] = load_word(bits, lane_bytes, w, ld);
       }
     }
     add_entries<T>(cur, acc);
     __builtin_amdgcn_sched_barrier(0);  // one word per scheduling region: bounded registers
-    if constexpr (WI + 1 < G::CW) chunk_words<T, WI + 1>(wp, ld, wnext, wlast, ring, lut, acc, nxt);
+    if constexpr (WI + 1 < G::CW) chunk_words<T, WI + 1>(bits, lane_bytes, ld, wnext, wlast, nwords, ring, lut, acc, nxt);
   }
 }
 
@@ -262,7 +277,8 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
   const int64_t w0 = span0 / kWordBits;
   const int64_t wlast = cdiv(S.n_red, kWordBits) - 1;  // last word row of the matrix
   // lanes past the last row read row n_rows-1 and store nothing
-  const uint32_t* wp = S.bits + (valid ? o : S.n_rows - 1);
+  const uint32_t lane_bytes = 4u * (uint32_t)(valid ? o : S.n_rows - 1);
+  const __amdgpu_buffer_rsrc_t wrsrc = word_rsrc(S.bits);
   const int nchunks = (int)cdiv(span1 - span0, 4 * G::GMAX);
 
   if (S.wait_ctr) {
@@ -287,7 +303,7 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
 #pragma unroll
   for (int d = 0; d < G::D; ++d)
 #pragma unroll
-    for (int j = 0; j < G::B; ++j) ring[d][j] = gload(wp + imin(w0 + d * G::B + j, wlast) * S.ld);
+    for (int j = 0; j < G::B; ++j) ring[d][j] = load_word(wrsrc, lane_bytes, imin(w0 + d * G::B + j, wlast), S.ld);
 
   TableInputs<T> in;
   load_inputs<T>(S, span0, span1, in);
@@ -305,7 +321,8 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
     const int64_t wnext = c0 / kWordBits + (int64_t)G::D * G::B;  // first word not yet in the ring
     float first[8][G::NQ * G::TT];
     read_entries<T, 0>(ring[0][0], lut, first);
-    chunk_words<T, 0>(wp, S.ld, wnext, wlast, ring, lut, acc, first);
+    const int nwords = (int)imin(G::CW, cdiv(span1 - c0, kWordBits));  // words of this chunk
+    chunk_words<T, 0>(wrsrc, lane_bytes, S.ld, wnext, wlast, nwords, ring, lut, acc, first);
   }
 #pragma unroll
   for (int t = 0; t < G::NQ * G::TT; ++t) acc[t] += acc[G::NQ * G::TT + t];
@@ -483,9 +500,15 @@ hipError_t launch_lut_persistent(const StageDesc* segs, int nseg, int ntiles, in
 
 namespace {
 
+// Sequences give each tile its row block's whole reduction: no partial sums
+// and one release per row block.  (Capping the span at 8K or 16K elements to
+// shorten the longest tiles measured slower: the extra fixups cost more than
+// the shorter dependency waits they buy.)
+constexpr int64_t kSeqSpan = 0;
+
 void plans(const nq_lrb& L, int64_t T, bool split, StagePlan* p1, StagePlan* p2) {
-  *p1 = lut_stage_plan(L.r, L.d_in, T, split ? lut_single_span(L.r, L.d_in) : 0);
-  *p2 = lut_stage_plan(L.d_out, L.r, T, split ? lut_single_span(L.d_out, L.r) : 0);
+  *p1 = lut_stage_plan(L.r, L.d_in, T, split ? lut_single_span(L.r, L.d_in) : kSeqSpan);
+  *p2 = lut_stage_plan(L.d_out, L.r, T, split ? lut_single_span(L.d_out, L.r) : kSeqSpan);
 }
 
 size_t part_bytes(const StagePlan& p, int64_t T) {

@@ -53,6 +53,9 @@ nq_status check_lrb(const char* who, const nq_lrb* L) {
     return set_error("%s: r=%lld exceeds 2^24", who, (long long)L->r), NQ_ERR_UNSUPPORTED;
   if (L->d_out > (int64_t(1) << 31) || L->d_in > (int64_t(1) << 31))
     return set_error("%s: dimension exceeds 2^31", who), NQ_ERR_UNSUPPORTED;
+  // sign-word buffers are addressed with 32-bit byte offsets inside the kernels
+  if (cdiv(L->r, kWordBits) * L->ldu >= (int64_t(1) << 29) || cdiv(L->d_in, kWordBits) * L->ldv >= (int64_t(1) << 29))
+    return set_error("%s: a sign-word buffer exceeds 2 GiB", who), NQ_ERR_UNSUPPORTED;
   nq_status st;
   if ((st = check_words(who, L->u_bits, L->d_out, L->r, L->ldu)) != NQ_OK) return st;
   if ((st = check_words(who, L->vt_bits, L->r, L->d_in, L->ldv)) != NQ_OK) return st;
@@ -122,7 +125,7 @@ namespace {
 // enough independent tiles are ready to keep every workgroup streaming.
 int seq_lag() {
   const char* e = getenv("NQ_SEQ_LAG");
-  const int v = e ? atoi(e) : 64;
+  const int v = e ? atoi(e) : 128;
   return v < 0 ? 0 : v;
 }
 
