@@ -16,9 +16,9 @@
 // For fp32 activations A is kept as two fp16 terms (hi + lo), ~22 bits.
 //
 // Kernels per stage: a prep kernel (row maxima, exponents, fp16 terms) and the
-// GEMM.  GEMM tiles are 256 (tokens) x 128 (outputs) x 64 (reduction) per
-// workgroup of 8 waves (two per SIMD), each wave 64 x 64 as 2 x 2
-// v_mfma_f32_32x32x16_f16 tiles.  A streams into a ring of LDS stages with direct global->LDS loads
+// GEMM.  GEMM tiles are 128 (tokens) x 256 (outputs) x 64 (reduction) per
+// workgroup of 8 waves, each wave 64 x 64 as 2 x 2 v_mfma_f32_32x32x16_f16
+// tiles; two workgroups fit a CU (four waves per SIMD).  A streams into a ring of LDS stages with direct global->LDS loads
 // issued several 64-deep steps ahead; the +-1 operand is built in registers
 // straight from the sign words: a 32x32x16 MFMA lane needs 8 signs
 // of one column, and with the reduction order below two signs 16 bits apart
@@ -34,8 +34,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 256, kBN = 128, kBK = 64;
-constexpr int kWaves = 8;                 // 4 (tokens) x 2 (outputs); each wave owns 64 x 64
+constexpr int kBM = 128, kBN = 256, kBK = 64;
+constexpr int kWaves = 8;                 // 2 (tokens) x 4 (outputs); each wave owns 64 x 64
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPrepThreads = 256;
 
@@ -121,10 +121,11 @@ struct Pipe {
 
 // A stage holds NT tiles of kBM rows x kBK fp16 (128 bytes per row) written by
 // direct global->LDS loads: one instruction moves 64 lanes x 16 bytes = 8 rows.
-// The 16-byte chunk c of row r is stored at chunk c ^ (r & 7), which makes the
-// 32-row fragment reads below conflict-free.
+// The 16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7): any 16
+// consecutive rows read at the same logical chunk hit 16 distinct 16-byte bank
+// groups, so the 32-row fragment reads below are conflict-free.
 template <int NT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const _Float16* __restrict__ A, const int* __restrict__ erow,
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const _Float16* __restrict__ A, const int* __restrict__ erow,
                                                            const uint32_t* __restrict__ bits, int64_t ldb,
                                                            int64_t M, int64_t N, int64_t K, int64_t Kpad,
                                                            int tiles_m, int tiles_n, const float* __restrict__ colscale,
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const _Float16* __res
   extern __shared__ __attribute__((aligned(16))) char lds[];  // [S][NT][kBM][128 bytes]
   const int tid = threadIdx.x;
   const int lane = tid % 64, wave = tid / 64;
-  const int wm = wave / 2, wn = wave % 2;  // wave tile: rows 64*wm .., columns 64*wn ..
+  const int wm = wave / 4, wn = wave % 4;  // wave tile: rows 64*wm .., columns 64*wn ..
   const int l32 = lane % 32, h = lane / 32;
 
   // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const _Float16* __res
       for (int j = 0; j < P::ROWS_PER_WAVE / 8; ++j) {
         const int r = wave * P::ROWS_PER_WAVE + j * 8 + drow;
         const int64_t m = m0 + r < M ? m0 + r : M - 1;  // rows past M load row M-1 (never stored)
-        const int c = dchunk ^ (r & 7);
+        const int c = dchunk ^ ((r >> 1) & 7);
         const _Float16* src = A + ((int64_t)term * M + m) * Kpad + (int64_t)kt * kBK + c * 8;
         char* dst = stage + ((int64_t)term * kBM + wave * P::ROWS_PER_WAVE + j * 8) * 128;
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const _Float16* __res
       const uint32_t* bws = reinterpret_cast<const uint32_t*>(stage + P::A_BYTES) + wave * 2 * 64;
       f16x8 af[2][NT][2];
       auto read_a = [&](int s, f16x8 (&dst)[NT][2]) {
-        const int chunk = (4 * (s / 2) + 2 * (s % 2) + h) ^ (l32 & 7);
+        const int chunk = (4 * (s / 2) + 2 * (s % 2) + h) ^ ((l32 >> 1) & 7);
 #pragma unroll
         for (int term = 0; term < NT; ++term)
 #pragma unroll
