@@ -38,31 +38,97 @@ constexpr int kBM = 128, kBN = 256, kBK = 64;
 constexpr int kWaves = 8;                 // 2 (tokens) x 4 (outputs); each wave owns 64 x 64
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPrepThreads = 256;
+constexpr uint32_t kSignMask = 0x80008000u;
 
 enum ASrc { kAF32Scaled = 0, kABF16Scaled = 1, kAF32 = 2 };
 
+// Activations of one 32-element block of row m, already multiplied by the
+// column scale (zero past K).  Stage 2 may hold `nsplit` partial sums of t,
+// added here in split order.
 template <int SRC>
-__device__ inline float act(const void* a, const float* cs, int64_t m, int64_t K, int64_t k) {
-  const int64_t g = m * K + k;
-  if (SRC == kAF32Scaled) return static_cast<const float*>(a)[g] * cs[k];
-  if (SRC == kABF16Scaled) return __uint_as_float((uint32_t) static_cast<const uint16_t*>(a)[g] << 16) * cs[k];
-  return static_cast<const float*>(a)[g];
+__device__ inline void load_block(const void* __restrict__ a, const float* __restrict__ cs, int64_t M, int64_t K,
+                                  int nsplit, bool vec, int64_t m, int64_t blk, float (&v)[32]) {
+  const int64_t k0 = blk * 32;
+  const bool full = vec && k0 + 32 <= K;
+  if (SRC == kABF16Scaled && full) {
+    const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a) + m * K + k0);
+    const float4* sp = reinterpret_cast<const float4*>(cs + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 w = xp[i];
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+      const float4 s0 = sp[2 * i], s1 = sp[2 * i + 1];
+      const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = __uint_as_float(u[j] << 16) * sc[2 * j];
+        v[8 * i + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u) * sc[2 * j + 1];
+      }
+    }
+    return;
+  }
+  if (SRC != kABF16Scaled && full) {
+    const float* base = static_cast<const float*>(a) + m * K + k0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float4 acc = reinterpret_cast<const float4*>(base)[i];
+      for (int sp = 1; sp < nsplit; ++sp) {
+        const float4 p = reinterpret_cast<const float4*>(base + (int64_t)sp * M * K)[i];
+        acc.x += p.x;
+        acc.y += p.y;
+        acc.z += p.z;
+        acc.w += p.w;
+      }
+      float4 sc = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (SRC == kAF32Scaled) sc = reinterpret_cast<const float4*>(cs + k0)[i];
+      v[4 * i] = acc.x * sc.x;
+      v[4 * i + 1] = acc.y * sc.y;
+      v[4 * i + 2] = acc.z * sc.z;
+      v[4 * i + 3] = acc.w * sc.w;
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {  // ragged tail or unaligned data: element by element
+    const int64_t k = k0 + i;
+    float x = 0.0f;
+    if (k < K) {
+      if (SRC == kABF16Scaled) {
+        x = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a)[m * K + k] << 16) * cs[k];
+      } else {
+        for (int sp = 0; sp < nsplit; ++sp) x += static_cast<const float*>(a)[(int64_t)sp * M * K + m * K + k];
+        if (SRC == kAF32Scaled) x *= cs[k];
+      }
+    }
+    v[i] = x;
+  }
 }
 
 // One workgroup per token row m:
 //   e[m] = 14 - exponent(max_k |a[m][k]|)  (0 for an all-zero row)
 //   out[term][m][2p], out[term][m][2p+1] = fp16 terms of a[m][k]*2^e for the
 //   element pair p (block p/16, elements q and q+16 with q = p%16); zero past K.
+// A thread handles whole 32-element blocks: 16-byte loads when `vec` (rows and
+// scales 16-byte aligned), 16 output dwords.
+// Rows of up to 256 blocks (8192 elements) stay in registers between the two
+// passes; longer rows are read twice.
 template <int SRC>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restrict__ a,
                                                             const float* __restrict__ cs, int64_t M,
-                                                            int64_t K, int64_t Kpad, int nt,
+                                                            int64_t K, int64_t Kpad, int nt, int nsplit, int vec,
                                                             _Float16* __restrict__ out, int* __restrict__ e_out) {
   __shared__ float red[kPrepThreads / 64];
   const int64_t m = blockIdx.x;
   const int tid = threadIdx.x;
+  const int64_t nblk = Kpad / 32;
+  const bool in_regs = nblk <= kPrepThreads;
+  float v[32];
   float mx = 0.0f;
-  for (int64_t k = tid; k < K; k += kPrepThreads) mx = fmaxf(mx, fabsf(act<SRC>(a, cs, m, K, k)));
+  for (int64_t blk = tid; blk < nblk; blk += kPrepThreads) {
+    load_block<SRC>(a, cs, M, K, nsplit, vec != 0, m, blk, v);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(v[i]));
+  }
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (tid % 64 == 0) red[tid / 64] = mx;
   __syncthreads();
@@ -74,30 +140,54 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restri
     e = 14 - ex;      // mx * 2^e in [2^13, 2^14)
   }
   if (tid == 0) e_out[m] = e;
-  const int64_t npairs = Kpad / 2;
-  uint32_t* hi = reinterpret_cast<uint32_t*>(out + m * Kpad);
-  uint32_t* lo = reinterpret_cast<uint32_t*>(out + (M + m) * Kpad);
-  for (int64_t p = tid; p < npairs; p += kPrepThreads) {
-    const int64_t k0 = (p / 16) * 32 + (p % 16);
-    const int64_t k1 = k0 + 16;
-    const float v0 = k0 < K ? ldexpf(act<SRC>(a, cs, m, K, k0), e) : 0.0f;
-    const float v1 = k1 < K ? ldexpf(act<SRC>(a, cs, m, K, k1), e) : 0.0f;
-    const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-    hi[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    if (nt == 2) {
+  for (int64_t blk = tid; blk < nblk; blk += kPrepThreads) {
+    if (!in_regs) load_block<SRC>(a, cs, M, K, nsplit, vec != 0, m, blk, v);
+    uint32_t hi[16], lo[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float v0 = ldexpf(v[q], e), v1 = ldexpf(v[q + 16], e);
+      const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+      hi[q] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
       const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
-      lo[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      lo[q] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+    uint4* dh = reinterpret_cast<uint4*>(out + m * Kpad + blk * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dh[i] = make_uint4(hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]);
+    if (nt == 2) {
+      uint4* dl = reinterpret_cast<uint4*>(out + (M + m) * Kpad + blk * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dl[i] = make_uint4(lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]);
     }
   }
 }
 
 // +-1 fp16 operand of a 32x32x16 MFMA lane: 8 signs of one column, the pairs
 // (b+d, b+d+16) for d = 0..3 of sign word w; fp16 1.0 = 0x3C00, sign bit 15.
-__device__ inline f16x8 signs_f16(uint32_t w, int b) {
+// Each dword is one shift and one v_and_or_b32 (VOP3 takes no literal, so the
+// two constants come in registers).
+__device__ inline f16x8 signs_f16(uint32_t w, int b, uint32_t mask, uint32_t one) {
   u32x4 v;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) v[d] = ((w << (15 - b - d)) & 0x80008000u) | 0x3C003C00u;
+  for (int d = 0; d < 4; ++d) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w << (15 - b - d)), "s"(mask), "v"(one));
+    v[d] = r;
+  }
   return __builtin_bit_cast(f16x8, v);
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() (and any
+// workgroup fence) waits for every outstanding global->LDS load of the wave,
+// which would drain the loads issued for later pipeline stages.  Here the
+// stage being consumed is waited for explicitly (wait_vmcnt) before the
+// barrier, and every LDS read of the previous stage has been consumed by an
+// MFMA (so has completed) before it; the empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ inline void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // s_waitcnt that waits until at most n vector-memory operations of this wave
@@ -125,10 +215,11 @@ struct Pipe {
 // consecutive rows read at the same logical chunk hit 16 distinct 16-byte bank
 // groups, so the 32-row fragment reads below are conflict-free.
 template <int NT>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const _Float16* __restrict__ A, const int* __restrict__ erow,
+__global__ __launch_bounds__(kThreads, 4) void gemm_kernel(const _Float16* __restrict__ A, const int* __restrict__ erow,
                                                            const uint32_t* __restrict__ bits, int64_t ldb,
                                                            int64_t M, int64_t N, int64_t K, int64_t Kpad,
-                                                           int tiles_m, int tiles_n, const float* __restrict__ colscale,
+                                                           int tiles_m, int tiles_n, int nsplit, int kts,
+                                                           const float* __restrict__ colscale,
                                                            float* __restrict__ out) {
   using P = Pipe<NT>;
   extern __shared__ __attribute__((aligned(16))) char lds[];  // [S][NT][kBM][128 bytes]
@@ -138,15 +229,19 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const _Float16* __res
   const int l32 = lane % 32, h = lane / 32;
 
   // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a
-  // contiguous range of tiles (N fastest) so concurrent tiles share A rows in L2.
+  // contiguous range of tiles (N fastest, then M, then the reduction split) so
+  // concurrent tiles share A rows in L2.
   const int ntiles = tiles_m * tiles_n;
-  const int per_xcd = (ntiles + 7) / 8;
+  const int per_xcd = (ntiles * nsplit + 7) / 8;
   const int t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (t >= ntiles) return;
-  const int64_t m0 = (int64_t)(t / tiles_n) * kBM;
-  const int64_t n0 = (int64_t)(t % tiles_n) * kBN;
+  if (t >= ntiles * nsplit) return;
+  const int split = t / ntiles, tt = t % ntiles;
+  const int64_t m0 = (int64_t)(tt / tiles_n) * kBM;
+  const int64_t n0 = (int64_t)(tt % tiles_n) * kBN;
   const int64_t nwords = cdiv(K, kWordBits);
-  const int nk = (int)(Kpad / kBK);
+  // this workgroup's reduction tiles: [kt_base, kt_base + nk) of the 64-deep tiles
+  const int kt_base = split * kts;
+  const int nk = imin((int)(Kpad / kBK) - kt_base, kts);
 
   // this lane's DMA source rows: wave w fills rows ROWS_PER_WAVE*w .., 8 per instruction
   const int drow = lane / 8, dchunk = lane % 8;
@@ -155,7 +250,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const _Float16* __res
   // is exactly PER_STAGE such instructions per wave.  Sign words past the last
   // word row or column are clamped: they only ever meet zero-padded A columns
   // or produce outputs that are not stored.
-  auto issue = [&](int kt, int st) {
+  auto issue = [&](int ktl, int st) {
+    const int kt = kt_base + ktl;
     char* stage = lds + (int64_t)st * P::STAGE_BYTES;
 #pragma unroll
     for (int term = 0; term < NT; ++term)
@@ -205,43 +301,48 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const _Float16* __res
       } else {
         wait_vmcnt<0>();
       }
-      __syncthreads();  // every wave's DMA for stage kt landed; stage kt-1 fully consumed
+      stage_barrier();  // every wave's DMA for stage kt landed; stage kt-1 fully consumed
       if (kt + P::S - 1 < nk) issue(kt + P::S - 1, (st + P::S - 1) % P::S);
 
-      // 16-deep MFMA steps within the 64-deep tile; the A fragments of step
-      // s+1 are read from LDS while the MFMAs of step s run
+      // 16-deep MFMA steps within the 64-deep tile, one fp16 term at a time
+      // (j = NT*step + term); the A fragments of j+1 are read from LDS while
+      // the MFMAs of j run
       const char* stage = lds + (int64_t)st * P::STAGE_BYTES;
       const uint32_t* bws = reinterpret_cast<const uint32_t*>(stage + P::A_BYTES) + wave * 2 * 64;
-      f16x8 af[2][NT][2];
-      auto read_a = [&](int s, f16x8 (&dst)[NT][2]) {
+      f16x8 af[2][2];
+      auto read_a = [&](int j, f16x8 (&dst)[2]) {
+        const int s = j / NT, term = j % NT;
         const int chunk = (4 * (s / 2) + 2 * (s % 2) + h) ^ ((l32 >> 1) & 7);
 #pragma unroll
-        for (int term = 0; term < NT; ++term)
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-            dst[term][mb] = *reinterpret_cast<const f16x8*>(
-                stage + ((int64_t)term * kBM + wm * 64 + mb * 32 + l32) * 128 + chunk * 16);
+        for (int mb = 0; mb < 2; ++mb)
+          dst[mb] = *reinterpret_cast<const f16x8*>(stage + ((int64_t)term * kBM + wm * 64 + mb * 32 + l32) * 128 +
+                                                    chunk * 16);
       };
       read_a(0, af[0]);
+      f16x8 bf[2];
+      const uint32_t one = __builtin_amdgcn_readfirstlane(0x3C003C00u);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (s + 1 < 4) read_a(s + 1, af[(s + 1) & 1]);
-        const int q = s / 2, b = 8 * (s % 2) + 4 * h;
-        f16x8 bf[2];
+      for (int j = 0; j < 4 * NT; ++j) {
+        if (j + 1 < 4 * NT) read_a(j + 1, af[(j + 1) & 1]);
+        const int s = j / NT;
+        if (j % NT == 0) {
+          const int q = s / 2, b = 8 * (s % 2) + 4 * h;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) bf[nb] = signs_f16(bws[q * 64 + nb * 32 + l32], b);
+          for (int nb = 0; nb < 2; ++nb) bf[nb] = signs_f16(bws[q * 64 + nb * 32 + l32], b, kSignMask, one);
+        }
 #pragma unroll
-        for (int term = 0; term < NT; ++term)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][term][mb], bf[nb], acc[mb][nb], 0, 0, 0);
+          for (int nb = 0; nb < 2; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mb], bf[nb], acc[mb][nb], 0, 0, 0);
       }
     }
   }
 
   // 32x32 MFMA result layout: lane l, register 4a+c -> row 8a + 4(l/32) + c, column l%32.
+  // A split reduction writes its partial sums to out[split] (colscale is then
+  // applied by whoever adds the partials).
+  float* dst = out + (int64_t)split * M * N;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -253,9 +354,20 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const _Float16* __res
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int64_t m = m0 + wm * 64 + mb * 32 + 8 * a + 4 * h + c;
-          if (m < M && n < N) out[m * N + n] = sc * ldexpf(acc[mb][nb][4 * a + c], -erow[m]);
+          if (m < M && n < N) dst[m * N + n] = sc * ldexpf(acc[mb][nb][4 * a + c], -erow[m]);
         }
     }
+}
+
+// y[m][n] = colscale[n] * sum over splits of part[split][m][n], in split order.
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, int nsplit, int64_t MN,
+                                                        int64_t N, const float* __restrict__ colscale,
+                                                        float* __restrict__ y) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += (int64_t)gridDim.x * 256) {
+    float acc = part[i];
+    for (int sp = 1; sp < nsplit; ++sp) acc += part[(int64_t)sp * MN + i];
+    y[i] = colscale[i % N] * acc;
+  }
 }
 
 size_t gemm_lds_bytes(int nt) {
@@ -263,47 +375,80 @@ size_t gemm_lds_bytes(int nt) {
 }
 
 template <int SRC>
-hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int64_t Kpad, int nt, _Float16* out,
-                       int* e, hipStream_t s) {
-  hipLaunchKernelGGL(prep_kernel<SRC>, dim3((unsigned)M), dim3(kPrepThreads), 0, s, a, cs, M, K, Kpad, nt, out, e);
+hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int64_t Kpad, int nt, int nsplit,
+                       _Float16* out, int* e, hipStream_t s) {
+  const int esize = SRC == kABF16Scaled ? 2 : 4;
+  const int vec = (reinterpret_cast<uintptr_t>(a) % 16 == 0) && (reinterpret_cast<uintptr_t>(cs) % 16 == 0) &&
+                  ((K * esize) % 16 == 0);
+  hipLaunchKernelGGL(prep_kernel<SRC>, dim3((unsigned)M), dim3(kPrepThreads), 0, s, a, cs, M, K, Kpad, nt, nsplit,
+                     vec, out, e);
   return hipGetLastError();
 }
 
+// Reduction split of one GEMM: workgroups are 128 x 256 output tiles and two
+// fit a CU, so a GEMM with fewer than 512 tiles leaves CUs idle; its reduction
+// is then cut into up to kMaxSplit pieces of at least kMinSplitTiles 64-deep
+// tiles, the partial sums going through the workspace.
+constexpr int kSlots = 512, kMaxSplit = 8, kMinSplitTiles = 4;
+
+struct Split {
+  int n;    // number of pieces
+  int kts;  // 64-deep reduction tiles per piece
+};
+
+Split split_plan(int64_t M, int64_t N, int64_t Kpad) {
+  const int64_t tiles = cdiv(M, kBM) * cdiv(N, kBN);
+  const int nk = (int)(Kpad / kBK);
+  int n = 1;
+  while (n < kMaxSplit && tiles * n * 2 <= kSlots && nk / (n * 2) >= kMinSplitTiles) n *= 2;
+  const int kts = (int)cdiv(nk, n);
+  return {(int)cdiv(nk, kts), kts};
+}
+
 hipError_t launch_gemm(int nt, const _Float16* A, const int* e, const uint32_t* bits, int64_t ldb, int64_t M,
-                       int64_t N, int64_t K, int64_t Kpad, const float* colscale, float* out, hipStream_t s) {
+                       int64_t N, int64_t K, int64_t Kpad, Split sp, const float* colscale, float* out,
+                       hipStream_t s) {
   const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
-  const unsigned grid = (unsigned)(8 * ((tiles_m * tiles_n + 7) / 8));
+  const unsigned grid = (unsigned)(8 * ((tiles_m * tiles_n * sp.n + 7) / 8));
   if (nt == 1)
     hipLaunchKernelGGL(gemm_kernel<1>, dim3(grid), dim3(kThreads), gemm_lds_bytes(1), s, A, e, bits, ldb, M, N, K,
-                       Kpad, tiles_m, tiles_n, colscale, out);
+                       Kpad, tiles_m, tiles_n, sp.n, sp.kts, colscale, out);
   else
     hipLaunchKernelGGL(gemm_kernel<2>, dim3(grid), dim3(kThreads), gemm_lds_bytes(2), s, A, e, bits, ldb, M, N, K,
-                       Kpad, tiles_m, tiles_n, colscale, out);
+                       Kpad, tiles_m, tiles_n, sp.n, sp.kts, colscale, out);
   return hipGetLastError();
 }
 
 struct PrefillLayout {
   int nt;
   int64_t kpad1, kpad2;
-  size_t off_z, off_e1, off_t, off_t16, off_e2, total;
+  Split sp1, sp2;
+  size_t off_z, off_e1, off_t, off_t16, off_e2, off_y2, total;
 };
 
+// Workspace: fp16 terms of stage 1's activations, their exponents, t (one copy
+// per reduction piece of stage 1), fp16 terms of t, their exponents, and the
+// partial outputs of stage 2 when its reduction is split.
 PrefillLayout prefill_layout(const nq_lrb& L, int64_t T, nq_dtype xd) {
   PrefillLayout d;
   d.nt = xd == NQ_F32 ? 2 : 1;
   d.kpad1 = round_up(L.d_in, kBK);
   d.kpad2 = round_up(L.r, kBK);
+  d.sp1 = split_plan(T, L.r, d.kpad1);
+  d.sp2 = split_plan(T, L.d_out, d.kpad2);
   size_t off = 0;
   d.off_z = off;
   off = align_up(off + (size_t)d.nt * T * d.kpad1 * sizeof(_Float16));
   d.off_e1 = off;
   off = align_up(off + (size_t)T * sizeof(int));
   d.off_t = off;
-  off = align_up(off + (size_t)T * L.r * sizeof(float));
+  off = align_up(off + (size_t)d.sp1.n * T * L.r * sizeof(float));
   d.off_t16 = off;
   off = align_up(off + (size_t)d.nt * T * d.kpad2 * sizeof(_Float16));
   d.off_e2 = off;
   off = align_up(off + (size_t)T * sizeof(int));
+  d.off_y2 = off;
+  if (d.sp2.n > 1) off = align_up(off + (size_t)d.sp2.n * T * L.d_out * sizeof(float));
   d.total = off;
   return d;
 }
@@ -335,15 +480,24 @@ hipError_t launch_prefill(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T
   float* t = reinterpret_cast<float*>(base + d.off_t);
   _Float16* t16 = reinterpret_cast<_Float16*>(base + d.off_t16);
   int* e2 = reinterpret_cast<int*>(base + d.off_e2);
+  float* y2 = reinterpret_cast<float*>(base + d.off_y2);
   hipError_t e;
   if (xd == NQ_BF16)
-    e = launch_prep<kABF16Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, z, e1, s);
+    e = launch_prep<kABF16Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, 1, z, e1, s);
   else
-    e = launch_prep<kAF32Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, z, e1, s);
+    e = launch_prep<kAF32Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, 1, z, e1, s);
   if (e != hipSuccess) return e;
-  if ((e = launch_gemm(d.nt, z, e1, L.vt_bits, L.ldv, T, L.r, L.d_in, d.kpad1, nullptr, t, s)) != hipSuccess) return e;
-  if ((e = launch_prep<kAF32>(t, nullptr, T, L.r, d.kpad2, d.nt, t16, e2, s)) != hipSuccess) return e;
-  return launch_gemm(d.nt, t16, e2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, L.s1, y, s);
+  if ((e = launch_gemm(d.nt, z, e1, L.vt_bits, L.ldv, T, L.r, L.d_in, d.kpad1, d.sp1, nullptr, t, s)) != hipSuccess)
+    return e;
+  // the stage-2 prep adds stage 1's partial sums while it reads t
+  if ((e = launch_prep<kAF32>(t, nullptr, T, L.r, d.kpad2, d.nt, d.sp1.n, t16, e2, s)) != hipSuccess) return e;
+  if (d.sp2.n == 1) return launch_gemm(d.nt, t16, e2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, L.s1, y, s);
+  if ((e = launch_gemm(d.nt, t16, e2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, nullptr, y2, s)) != hipSuccess)
+    return e;
+  const int64_t MN = T * L.d_out;
+  const unsigned grid = (unsigned)imin(cdiv(MN, 256), (int64_t)4096);
+  hipLaunchKernelGGL(split_sum_kernel, dim3(grid), dim3(256), 0, s, y2, d.sp2.n, MN, L.d_out, L.s1, y);
+  return hipGetLastError();
 }
 
 }  // namespace nq

@@ -199,8 +199,8 @@ def test_sequence_many_linears_parity(T):
 # ---------------------------------------------------------------- 70B shapes (sampled rows)
 
 
-def _sampled_err(dev, ref, x_np, rows):
-    y = nq.lrb_linear(dev, G.to_device_x(x_np, "bf16")).cpu().numpy()
+def _sampled_err(dev, ref, x_np, rows, x_dtype="bf16"):
+    y = nq.lrb_linear(dev, G.to_device_x(x_np, x_dtype)).cpu().numpy()
     assert np.all(np.isfinite(y))
     return O.rel_err(y[:, rows], O.sampled_linear_ref(ref, x_np, rows))
 
@@ -217,12 +217,31 @@ def test_70b_decode_sampled_rows(name):
     assert err <= 1e-5
 
 
-def test_70b_prefill_sampled_rows():
+# q: 256 output tiles (reduction split in two); k: few tiles (split eight ways in
+# stage 1, two in stage 2); down: no split; q with fp32 x: two fp16 terms.
+@pytest.mark.parametrize("name,x_dtype", [("q", "bf16"), ("k", "bf16"), ("down", "bf16"), ("q", "f32")])
+def test_70b_prefill_sampled_rows(name, x_dtype):
     cfg = synth.CONFIGS["70b_prefill"]
-    shape = next(s for s in cfg.layers if s.name == "q")
+    shape = next(s for s in cfg.layers if s.name == name)
     dev, ref = G.splitmix_layer(cfg, shape, layer_idx=0)
-    rows = np.sort(synth.rng("rows/prefill/q").choice(shape.d_out, 64, replace=False))
-    x = synth.x_for(cfg, shape.d_in, 2048)
-    err = _sampled_err(dev, ref, x, rows)
-    print(f"70b q T2048 sampled 64 rows: rel err {err:.3e}")
-    assert err <= 2e-3
+    rows = np.sort(synth.rng(f"rows/prefill/{name}").choice(shape.d_out, 64, replace=False))
+    if x_dtype == "bf16":
+        x = synth.x_for(cfg, shape.d_in, 2048)
+    else:  # full fp32 mantissas, same distribution
+        x = synth.activations(f"{cfg.key}/x32/{shape.d_in}/2048", 2048, shape.d_in, "f32", cfg.outlier_frac)
+    err = _sampled_err(dev, ref, x, rows, x_dtype)
+    print(f"70b {name} T2048 {x_dtype} sampled 64 rows: rel err {err:.3e}")
+    assert err <= G.tol_for(2048, x_dtype)
+
+
+# Reduction lengths that split unevenly: stage 1 has 13 tiles of 64 (pieces of
+# 7 and 6), stage 2 has 10 (two pieces of 5); rows and outputs ragged too.
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_linear_uneven_split(x_dtype):
+    shape = synth.LayerShape("split", 700, 800, 600)
+    cfg = G.tiny_config(f"split/{x_dtype}", x_dtype=x_dtype)
+    dev, ref, _ = G.latent_layer(cfg, shape)
+    x = synth.activations(f"split/x/{x_dtype}", 200, shape.d_in, x_dtype)
+    err = _linear_err(dev, ref, x, x_dtype)
+    print(f"uneven split {x_dtype}: rel err {err:.3e}")
+    assert err <= G.tol_for(200, x_dtype), err
