@@ -154,10 +154,11 @@ def time_prefill(stack, T: int, device: str, warmup_layers: int = 1):
     return t0.elapsed_time(t1)
 
 
-def cpu_baseline(cfg, budget_s: float = 20.0) -> dict:
+def cpu_baseline(cfg, min_s: float = 10.0) -> dict:
     """The oracle (reconstruct in fp64, then multiply) on the host cores, on a
-    bounded sample of the decode step: the k, v and q matrices of layer 0,
-    then extrapolated to the 560-linear step by reconstruction flops."""
+    bounded sample of the decode step: the linears of layer 0, then layer 1,
+    ... in stack order until at least `min_s` seconds of oracle work are done,
+    extrapolated to the 560-linear step by reconstruction flops."""
     import numpy as np
 
     import synth
@@ -168,27 +169,30 @@ def cpu_baseline(cfg, budget_s: float = 20.0) -> dict:
                       default=1)
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    sample = [s for s in cfg.layers if s.name in ("k", "v", "q")]
-    done_flops, elapsed = 0, 0.0
-    for s in sample:
-        inp = synth.lrb_inputs(cfg, s, 0)
-        nwu, nwv = (s.r + 31) // 32, (s.d_in + 31) // 32
-        ref = O.LRB(synth.random_words(inp["u_seed"], np.arange(nwu * s.d_out, dtype=np.uint64)).reshape(nwu, s.d_out),
-                    synth.random_words(inp["v_seed"], np.arange(nwv * s.r, dtype=np.uint64)).reshape(nwv, s.r),
-                    inp["s1"], inp["s2"], s.d_out, s.d_in, s.r)
-        x = synth.x_for(cfg, s.d_in, 1)
-        t = time.perf_counter()
-        O.linear_ref(ref, x)
-        elapsed += time.perf_counter() - t
-        done_flops += 2 * s.d_out * s.d_in * s.r + 2 * s.d_out * s.d_in
-        if elapsed > budget_s:
+    done, done_flops, elapsed = [], 0, 0.0
+    for l in range(80):
+        for s in cfg.layers:
+            inp = synth.lrb_inputs(cfg, s, l)
+            nwu, nwv = (s.r + 31) // 32, (s.d_in + 31) // 32
+            ref = O.LRB(synth.random_words(inp["u_seed"], np.arange(nwu * s.d_out, dtype=np.uint64)).reshape(nwu, s.d_out),
+                        synth.random_words(inp["v_seed"], np.arange(nwv * s.r, dtype=np.uint64)).reshape(nwv, s.r),
+                        inp["s1"], inp["s2"], s.d_out, s.d_in, s.r)
+            x = synth.x_for(cfg, s.d_in, 1)
+            t = time.perf_counter()
+            O.linear_ref(ref, x)
+            elapsed += time.perf_counter() - t
+            done_flops += 2 * s.d_out * s.d_in * s.r + 2 * s.d_out * s.d_in
+            done.append(f"{l}.{s.name}")
+            if elapsed >= min_s:
+                break
+        if elapsed >= min_s:
             break
     step_flops = 80 * sum(2 * s.d_out * s.d_in * s.r + 2 * s.d_out * s.d_in for s in cfg.layers)
     step_s = elapsed * step_flops / done_flops
     return {"value": 1.0 / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"oracle linear_ref (fp64 reconstruct-then-multiply) on layer-0 {'/'.join(s.name for s in sample)} "
-                       f"({elapsed:.1f} s), extrapolated by reconstruction flops to the 560-linear T=1 step "
-                       f"({step_s:.0f} s/token)")}
+            "sample": (f"oracle linear_ref (fp64 reconstruct-then-multiply, T=1) on {len(done)} linears "
+                       f"({done[0]} .. {done[-1]}, {elapsed:.1f} s), extrapolated by reconstruction flops to "
+                       f"the 560-linear T=1 step ({step_s:.0f} s/token)")}
 
 
 def main() -> int:

@@ -16,15 +16,17 @@
 // For fp32 activations A is kept as two fp16 terms (hi + lo), ~22 bits.
 //
 // Kernels per stage: a prep kernel (row maxima, exponents, fp16 terms) and the
-// GEMM.  GEMM tiles are 128 (tokens) x 256 (outputs) x 64 (reduction) per
-// workgroup of 8 waves, each wave 64 x 64 as 2 x 2 v_mfma_f32_32x32x16_f16
-// tiles; two workgroups fit a CU (four waves per SIMD).  A streams into a ring of LDS stages with direct global->LDS loads
-// issued several 64-deep steps ahead; the +-1 operand is built in registers
-// straight from the sign words: a 32x32x16 MFMA lane needs 8 signs
-// of one column, and with the reduction order below two signs 16 bits apart
-// become one fp16 pair with a shift and a v_and_or_b32:
+// GEMM.  GEMM workgroups are 8 waves over an output tile of 64*MB tokens x 256
+// outputs (2 x 4 waves, each 32*MB x 64 as MB x 2 v_mfma_f32_32x32x16_f16
+// tiles), stepping through the reduction 64 deep.  A streams into a ring of
+// LDS stages with direct global->LDS loads issued several steps ahead; the
+// +-1 operand is built in registers straight from the sign words: a 32x32x16
+// MFMA lane needs 8 signs of one column, and with the reduction order below
+// two signs 16 bits apart become one fp16 pair with a shift and a v_and_or_b32:
 //   pair q (0..15) of each 32-element block holds elements (q, q+16);
 //   the prep kernel writes A in that interleaved order.
+// A GEMM with too few output tiles to fill the chip splits its reduction;
+// the partial sums are added in fixed order by the next kernel.
 #include "nq_internal.h"
 
 namespace nq {
@@ -34,11 +36,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128, kBN = 256, kBK = 64;
+constexpr int kBN = 256, kBK = 64;
 constexpr int kWaves = 8;                 // 2 (tokens) x 4 (outputs); each wave owns 64 x 64
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPrepThreads = 256;
-constexpr uint32_t kSignMask = 0x80008000u;
+constexpr uint32_t kSignMask = 0x80008000u, kOnePair = 0x3C003C00u;  // fp16 pair: sign bits, +1.0
 
 enum ASrc { kAF32Scaled = 0, kABF16Scaled = 1, kAF32 = 2 };
 
@@ -164,16 +166,14 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restri
 
 // +-1 fp16 operand of a 32x32x16 MFMA lane: 8 signs of one column, the pairs
 // (b+d, b+d+16) for d = 0..3 of sign word w; fp16 1.0 = 0x3C00, sign bit 15.
-// Each dword is one shift and one v_and_or_b32 (VOP3 takes no literal, so the
-// two constants come in registers).
+// `mask` (0x80008000) and `one` (0x3C003C00) arrive as kernel arguments: held
+// in registers they let each dword compile to a shift and one v_and_or_b32
+// (a VOP3 operand cannot be a literal).  Plain C is used rather than inline
+// asm so the compiler's MFMA hazard tracking sees every VGPR write.
 __device__ inline f16x8 signs_f16(uint32_t w, int b, uint32_t mask, uint32_t one) {
   u32x4 v;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w << (15 - b - d)), "s"(mask), "v"(one));
-    v[d] = r;
-  }
+  for (int d = 0; d < 4; ++d) v[d] = ((w << (15 - b - d)) & mask) | one;
   return __builtin_bit_cast(f16x8, v);
 }
 
@@ -198,34 +198,37 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int NT>
+// Workgroup tile BM x kBN x kBK: 8 waves as 2 (rows) x 4 (columns), each wave
+// 32*MB rows x 64 columns as MB x 2 v_mfma_f32_32x32x16_f16 tiles.
+template <int NT, int MB>
 struct Pipe {
+  static constexpr int BM = 2 * 32 * MB;                          // tile rows (tokens)
   static constexpr int S = NT == 1 ? 4 : 2;                       // LDS stages
-  static constexpr int A_BYTES = NT * kBM * kBK * 2;              // A tile(s) of one stage
-  static constexpr int B_BYTES = kWaves * 2 * 64 * 4;             // per wave: 2 word rows x 64 columns
+  static constexpr int A_BYTES = NT * BM * kBK * 2;               // A tile(s) of one stage
+  static constexpr int B_BYTES = 2 * kBN * 4;                     // 2 sign-word rows x kBN columns
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int ROWS_PER_WAVE = kBM / kWaves;              // A rows each wave moves
-  static constexpr int DMA_PER_WAVE = NT * ROWS_PER_WAVE / 8;     // 8 rows (1 KiB) per 16-byte DMA
-  static constexpr int PER_STAGE = DMA_PER_WAVE + 2;              // + 2 sign-word DMA instructions
+  static constexpr int ROWS_PER_WAVE = BM / kWaves;               // A rows each wave moves
+  static constexpr int A_DMA = NT * ROWS_PER_WAVE / 8;            // 8 rows (1 KiB) per 16-byte DMA
+  static constexpr int PER_STAGE = A_DMA + 1;                     // + 1 sign-word DMA instruction
+  static constexpr int LDS = S * STAGE_BYTES;
 };
 
-// A stage holds NT tiles of kBM rows x kBK fp16 (128 bytes per row) written by
+// A stage holds NT tiles of BM rows x kBK fp16 (128 bytes per row) written by
 // direct global->LDS loads: one instruction moves 64 lanes x 16 bytes = 8 rows.
 // The 16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7): any 16
 // consecutive rows read at the same logical chunk hit 16 distinct 16-byte bank
-// groups, so the 32-row fragment reads below are conflict-free.
-template <int NT>
-__global__ __launch_bounds__(kThreads, 4) void gemm_kernel(const _Float16* __restrict__ A, const int* __restrict__ erow,
-                                                           const uint32_t* __restrict__ bits, int64_t ldb,
-                                                           int64_t M, int64_t N, int64_t K, int64_t Kpad,
-                                                           int tiles_m, int tiles_n, int nsplit, int kts,
-                                                           const float* __restrict__ colscale,
-                                                           float* __restrict__ out) {
-  using P = Pipe<NT>;
-  extern __shared__ __attribute__((aligned(16))) char lds[];  // [S][NT][kBM][128 bytes]
-  const int tid = threadIdx.x;
-  const int lane = tid % 64, wave = tid / 64;
-  const int wm = wave / 4, wn = wave % 4;  // wave tile: rows 64*wm .., columns 64*wn ..
+// groups, so the 32-row fragment reads below are conflict-free.  The stage's
+// sign words follow: word row q (of the tile's two) at [q][kBN columns].
+template <int NT, int MB>
+__global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
+    const _Float16* __restrict__ A, const int* __restrict__ erow, const uint32_t* __restrict__ bits, int64_t ldb,
+    int64_t M, int64_t N, int64_t K, int64_t Kpad, int tiles_m, int tiles_n, int nsplit, int kts,
+    uint32_t sign_mask, uint32_t one, const float* __restrict__ colscale, float* __restrict__ out) {
+  using P = Pipe<NT, MB>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];  // [S][A tiles | sign words]
+  const int lane = threadIdx.x % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int wm = wave / 4, wn = wave % 4;  // wave tile: rows 32*MB*wm .., columns 64*wn ..
   const int l32 = lane % 32, h = lane / 32;
 
   // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a
@@ -236,46 +239,52 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(const _Float16* __res
   const int t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
   if (t >= ntiles * nsplit) return;
   const int split = t / ntiles, tt = t % ntiles;
-  const int64_t m0 = (int64_t)(tt / tiles_n) * kBM;
+  const int64_t m0 = (int64_t)(tt / tiles_n) * P::BM;
   const int64_t n0 = (int64_t)(tt % tiles_n) * kBN;
   const int64_t nwords = cdiv(K, kWordBits);
   // this workgroup's reduction tiles: [kt_base, kt_base + nk) of the 64-deep tiles
   const int kt_base = split * kts;
   const int nk = imin((int)(Kpad / kBK) - kt_base, kts);
 
-  // this lane's DMA source rows: wave w fills rows ROWS_PER_WAVE*w .., 8 per instruction
+  // Per-lane DMA source offsets, fixed over the reduction: A rows past M load
+  // row M-1 and sign-word columns past N load column N-1 (neither is stored).
   const int drow = lane / 8, dchunk = lane % 8;
+  uint32_t a_off[P::ROWS_PER_WAVE / 8];
+#pragma unroll
+  for (int j = 0; j < P::ROWS_PER_WAVE / 8; ++j) {
+    const int r = wave * P::ROWS_PER_WAVE + j * 8 + drow;
+    const int64_t m = imin(m0 + r, M - 1);
+    a_off[j] = (uint32_t)((m - m0) * Kpad + ((dchunk ^ ((r >> 1) & 7)) * 8));
+  }
+  const uint32_t b_off = (uint32_t)imin(n0 + wn * 64 + lane, N - 1);
+  const _Float16* a_tile = A + m0 * Kpad;
+
   // Every global read is a direct global->LDS load, so no register waits on a
   // global load and the explicit vmcnt waits below are the only ones.  A stage
-  // is exactly PER_STAGE such instructions per wave.  Sign words past the last
-  // word row or column are clamped: they only ever meet zero-padded A columns
-  // or produce outputs that are not stored.
+  // is exactly PER_STAGE such instructions per wave.  Sign-word rows past the
+  // last are clamped: they only ever meet zero-padded A columns.
   auto issue = [&](int ktl, int st) {
     const int kt = kt_base + ktl;
-    char* stage = lds + (int64_t)st * P::STAGE_BYTES;
+    char* stage = lds + st * P::STAGE_BYTES;
 #pragma unroll
-    for (int term = 0; term < NT; ++term)
+    for (int term = 0; term < NT; ++term) {
+      const _Float16* base = a_tile + (int64_t)term * M * Kpad + (int64_t)kt * kBK;
 #pragma unroll
       for (int j = 0; j < P::ROWS_PER_WAVE / 8; ++j) {
-        const int r = wave * P::ROWS_PER_WAVE + j * 8 + drow;
-        const int64_t m = m0 + r < M ? m0 + r : M - 1;  // rows past M load row M-1 (never stored)
-        const int c = dchunk ^ ((r >> 1) & 7);
-        const _Float16* src = A + ((int64_t)term * M + m) * Kpad + (int64_t)kt * kBK + c * 8;
-        char* dst = stage + ((int64_t)term * kBM + wave * P::ROWS_PER_WAVE + j * 8) * 128;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        char* dst = stage + (term * P::BM + wave * P::ROWS_PER_WAVE + j * 8) * 128;
+        __builtin_amdgcn_global_load_lds((const void*)(base + a_off[j]), (__attribute__((address_space(3))) void*)dst, 16,
+                                         0, 0);
       }
-    const int64_t n = imin(n0 + wn * 64 + lane, N - 1);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int64_t kw = imin((int64_t)kt * 2 + q, nwords - 1);
-      char* dst = stage + P::A_BYTES + (wave * 2 + q) * 64 * 4;
-      __builtin_amdgcn_global_load_lds(bits + kw * ldb + n, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
     }
+    const int64_t kw = imin((int64_t)kt * 2 + wm, nwords - 1);
+    char* dst = stage + P::A_BYTES + (wm * kBN + wn * 64) * 4;
+    __builtin_amdgcn_global_load_lds((const void*)(bits + kw * ldb + b_off), (__attribute__((address_space(3))) void*)dst,
+                                     4, 0, 0);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[MB][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -285,8 +294,15 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(const _Float16* __res
   for (int kt = 0; kt < P::S - 1; ++kt)
     if (kt < nk) issue(kt, kt);
 
-  // the ring index is kept compile-time (kt = kt0 + st, st < S) so the sign
-  // words stay in registers
+  asm volatile("" : "+v"(one));  // keep `one` in a VGPR: one SGPR operand per VOP3 (sign_mask)
+
+  // lane offsets of the A fragments for the four 16-deep steps of a tile
+  uint32_t frag_off[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    frag_off[s] = (uint32_t)((wm * 32 * MB + l32) * 128 + (((4 * (s / 2) + 2 * (s % 2) + h) ^ ((l32 >> 1) & 7)) * 16));
+
+  // the ring index is kept compile-time (kt = kt0 + st, st < S)
   for (int kt0 = 0; kt0 < nk; kt0 += P::S) {
 #pragma unroll
     for (int st = 0; st < P::S; ++st) {
@@ -305,36 +321,44 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(const _Float16* __res
       if (kt + P::S - 1 < nk) issue(kt + P::S - 1, (st + P::S - 1) % P::S);
 
       // 16-deep MFMA steps within the 64-deep tile, one fp16 term at a time
-      // (j = NT*step + term); the A fragments of j+1 are read from LDS while
-      // the MFMAs of j run
-      const char* stage = lds + (int64_t)st * P::STAGE_BYTES;
-      const uint32_t* bws = reinterpret_cast<const uint32_t*>(stage + P::A_BYTES) + wave * 2 * 64;
-      f16x8 af[2][2];
-      auto read_a = [&](int j, f16x8 (&dst)[2]) {
-        const int s = j / NT, term = j % NT;
-        const int chunk = (4 * (s / 2) + 2 * (s % 2) + h) ^ ((l32 >> 1) & 7);
+      // (j = NT*step + term), software-pipelined by hand: the A fragments of
+      // j+1 are read from LDS before the MFMAs of j are issued, and the +-1
+      // operands of the next step are built while those MFMAs run.  The
+      // scheduling barriers keep the compiler from regrouping the phases.
+      const char* stage = lds + st * P::STAGE_BYTES;
+      const uint32_t* bws = reinterpret_cast<const uint32_t*>(stage + P::A_BYTES) + wn * 64 + l32;
+      uint32_t words[2][2];  // [q][nb]: this lane's sign words of the tile
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          dst[mb] = *reinterpret_cast<const f16x8*>(stage + ((int64_t)term * kBM + wm * 64 + mb * 32 + l32) * 128 +
-                                                    chunk * 16);
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) words[q][nb] = bws[q * kBN + nb * 32];
+      f16x8 af[2][MB];
+      auto read_a = [&](int j, f16x8 (&dst)[MB]) {
+        const int s = j / NT, term = j % NT;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          dst[mb] = *reinterpret_cast<const f16x8*>(stage + frag_off[s] + (term * P::BM + mb * 32) * 128);
+      };
+      auto build_b = [&](int s, f16x8 (&dst)[2]) {
+        const int q = s / 2, b = 8 * (s % 2) + 4 * h;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) dst[nb] = signs_f16(words[q][nb], b, sign_mask, one);
       };
       read_a(0, af[0]);
-      f16x8 bf[2];
-      const uint32_t one = __builtin_amdgcn_readfirstlane(0x3C003C00u);
+      f16x8 bf[2][2];
+      build_b(0, bf[0]);
 #pragma unroll
       for (int j = 0; j < 4 * NT; ++j) {
-        if (j + 1 < 4 * NT) read_a(j + 1, af[(j + 1) & 1]);
         const int s = j / NT;
-        if (j % NT == 0) {
-          const int q = s / 2, b = 8 * (s % 2) + 4 * h;
+        if (j + 1 < 4 * NT) read_a(j + 1, af[(j + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) bf[nb] = signs_f16(bws[q * 64 + nb * 32 + l32], b, kSignMask, one);
-        }
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mb], bf[nb], acc[mb][nb], 0, 0, 0);
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mb], bf[s & 1][nb], acc[mb][nb], 0, 0, 0);
+        if (j % NT == NT - 1 && s + 1 < 4) build_b(s + 1, bf[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -344,7 +368,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(const _Float16* __res
   // applied by whoever adds the partials).
   float* dst = out + (int64_t)split * M * N;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int64_t n = n0 + wn * 64 + nb * 32 + l32;
@@ -353,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(const _Float16* __res
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int64_t m = m0 + wm * 64 + mb * 32 + 8 * a + 4 * h + c;
+          const int64_t m = m0 + wm * 32 * MB + mb * 32 + 8 * a + 4 * h + c;
           if (m < M && n < N) dst[m * N + n] = sc * ldexpf(acc[mb][nb][4 * a + c], -erow[m]);
         }
     }
@@ -370,10 +394,6 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
   }
 }
 
-size_t gemm_lds_bytes(int nt) {
-  return nt == 1 ? (size_t)Pipe<1>::S * Pipe<1>::STAGE_BYTES : (size_t)Pipe<2>::S * Pipe<2>::STAGE_BYTES;
-}
-
 template <int SRC>
 hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int64_t Kpad, int nt, int nsplit,
                        _Float16* out, int* e, hipStream_t s) {
@@ -385,11 +405,19 @@ hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int
   return hipGetLastError();
 }
 
-// Reduction split of one GEMM: workgroups are 128 x 256 output tiles and two
-// fit a CU, so a GEMM with fewer than 512 tiles leaves CUs idle; its reduction
-// is then cut into up to kMaxSplit pieces of at least kMinSplitTiles 64-deep
-// tiles, the partial sums going through the workspace.
-constexpr int kSlots = 512, kMaxSplit = 8, kMinSplitTiles = 4;
+// MFMA tiles per wave along the rows.  2: 128 x 256 workgroup tiles, two
+// workgroups (16 waves) per CU.  4 (256 x 256, one workgroup of 8 waves per
+// CU) halves the sign expansion per MFMA but measured slower on the 70B
+// shapes: two waves per SIMD hide too little LDS and barrier latency.
+constexpr int kTileMB = 2;
+constexpr int kTileRows = 64 * kTileMB;
+constexpr int kWgSlots = kTileMB == 2 ? 512 : 256;  // resident workgroups on 256 CUs
+
+// Reduction split of one GEMM: a GEMM with fewer output tiles than resident
+// workgroup slots leaves CUs idle; its reduction is then cut into up to
+// kMaxSplit pieces of at least kMinSplitTiles 64-deep tiles, the partial sums
+// going through the workspace.
+constexpr int kMaxSplit = 8, kMinSplitTiles = 4;
 
 struct Split {
   int n;    // number of pieces
@@ -397,26 +425,39 @@ struct Split {
 };
 
 Split split_plan(int64_t M, int64_t N, int64_t Kpad) {
-  const int64_t tiles = cdiv(M, kBM) * cdiv(N, kBN);
+  const int64_t tiles = cdiv(M, kTileRows) * cdiv(N, kBN);
   const int nk = (int)(Kpad / kBK);
   int n = 1;
-  while (n < kMaxSplit && tiles * n * 2 <= kSlots && nk / (n * 2) >= kMinSplitTiles) n *= 2;
+  while (n < kMaxSplit && tiles * n * 2 <= kWgSlots && nk / (n * 2) >= kMinSplitTiles) n *= 2;
   const int kts = (int)cdiv(nk, n);
   return {(int)cdiv(nk, kts), kts};
+}
+
+template <int NT, int MB>
+hipError_t launch_gemm_t(decltype(&gemm_kernel<NT, MB>) kernel, const _Float16* A, const int* e,
+                         const uint32_t* bits, int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t Kpad, Split sp,
+                         const float* colscale, float* out, hipStream_t s) {
+  using P = Pipe<NT, MB>;
+  static bool configured = false;
+  if (!configured) {
+    const hipError_t err =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, P::LDS);
+    if (err != hipSuccess) return err;
+    configured = true;
+  }
+  const int tiles_m = (int)cdiv(M, P::BM), tiles_n = (int)cdiv(N, kBN);
+  const unsigned grid = (unsigned)(8 * ((tiles_m * tiles_n * sp.n + 7) / 8));
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), P::LDS, s, A, e, bits, ldb, M, N, K, Kpad, tiles_m, tiles_n,
+                     sp.n, sp.kts, kSignMask, kOnePair, colscale, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int nt, const _Float16* A, const int* e, const uint32_t* bits, int64_t ldb, int64_t M,
                        int64_t N, int64_t K, int64_t Kpad, Split sp, const float* colscale, float* out,
                        hipStream_t s) {
-  const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
-  const unsigned grid = (unsigned)(8 * ((tiles_m * tiles_n * sp.n + 7) / 8));
-  if (nt == 1)
-    hipLaunchKernelGGL(gemm_kernel<1>, dim3(grid), dim3(kThreads), gemm_lds_bytes(1), s, A, e, bits, ldb, M, N, K,
-                       Kpad, tiles_m, tiles_n, sp.n, sp.kts, colscale, out);
-  else
-    hipLaunchKernelGGL(gemm_kernel<2>, dim3(grid), dim3(kThreads), gemm_lds_bytes(2), s, A, e, bits, ldb, M, N, K,
-                       Kpad, tiles_m, tiles_n, sp.n, sp.kts, colscale, out);
-  return hipGetLastError();
+  constexpr int MB = kTileMB;
+  return nt == 1 ? launch_gemm_t<1, MB>(gemm_kernel<1, MB>, A, e, bits, ldb, M, N, K, Kpad, sp, colscale, out, s)
+                 : launch_gemm_t<2, MB>(gemm_kernel<2, MB>, A, e, bits, ldb, M, N, K, Kpad, sp, colscale, out, s);
 }
 
 struct PrefillLayout {
@@ -453,8 +494,6 @@ PrefillLayout prefill_layout(const nq_lrb& L, int64_t T, nq_dtype xd) {
   return d;
 }
 
-bool lds_configured = false;
-
 }  // namespace
 
 size_t prefill_workspace_bytes(const nq_lrb& L, int64_t T) {
@@ -464,15 +503,6 @@ size_t prefill_workspace_bytes(const nq_lrb& L, int64_t T) {
 
 hipError_t launch_prefill(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
                           hipStream_t s) {
-  if (!lds_configured) {
-    hipError_t e1 = hipFuncSetAttribute((const void*)gemm_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        (int)gemm_lds_bytes(1));
-    hipError_t e2 = hipFuncSetAttribute((const void*)gemm_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        (int)gemm_lds_bytes(2));
-    if (e1 != hipSuccess) return e1;
-    if (e2 != hipSuccess) return e2;
-    lds_configured = true;
-  }
   const PrefillLayout d = prefill_layout(L, T, xd);
   char* base = static_cast<char*>(ws);
   _Float16* z = reinterpret_cast<_Float16*>(base + d.off_z);
