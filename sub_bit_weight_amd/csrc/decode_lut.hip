@@ -32,20 +32,26 @@ namespace nq {
 namespace {
 
 constexpr int kRows = 256;           // rows (outputs) per tile = threads per workgroup
-constexpr int kLutFloats = 8192;     // 32 KiB of tables per workgroup
+constexpr int kLutFloats = 8192;     // 32 KiB of table entries per workgroup (plus padding)
 constexpr unsigned kSpinLimit = 1u << 21;  // ~1 s of polling, then give up and flag
 
 // Table geometry for T tokens.  Entries are token-innermost: the TT tokens of
 // one (group, nibble) entry are adjacent, so one ds_read_b32/b64/b128 fetches
-// them together; T > 4 uses NQ = 2 such arrays.  The reduction is walked in
-// chunks of GMAX groups (4*GMAX elements, 32 KiB of tables), each chunk in NB
-// batches of B sign words; D batches of words are kept in flight per lane.
+// them together; T > 4 uses NQ = 2 such arrays.  Each group's 16 entries are
+// followed by 16 bytes of padding: the 16-byte stores that build the tables
+// (one group per thread) then fall into distinct banks for 8 consecutive
+// threads, while a group's 16 entries still occupy 16 distinct banks for the
+// lookups.  The reduction is walked in chunks of GMAX groups (4*GMAX elements),
+// each chunk in NB batches of B sign words; D batches of words are kept in
+// flight per lane.
 template <int T>
 struct Geo {
   static constexpr int TT = T == 1 ? 1 : (T == 2 ? 2 : 4);
   static constexpr int NQ = (T + TT - 1) / TT;
-  static constexpr int QF = kLutFloats / NQ;                 // floats per array
-  static constexpr int GMAX = QF / (16 * TT);                // groups per chunk
+  static constexpr int QF = (kLutFloats / NQ) / (16 * TT) * (16 * TT + 4);  // floats per array
+  static constexpr int GMAX = kLutFloats / NQ / (16 * TT);  // groups per chunk
+  static constexpr int GS = 16 * TT + 4;                     // floats per group (with padding)
+  static constexpr int LUT = NQ * GMAX * GS;                 // floats of tables per workgroup
   static constexpr int CW = GMAX / 8;                        // words per chunk
   static constexpr int B = CW >= 32 ? 8 : (CW >= 16 ? 4 : 2);  // words per batch
   static constexpr int NB = CW / B;                          // batches per chunk
@@ -153,7 +159,7 @@ __device__ inline void build_tables(const TableInputs<T>& in, int64_t c0, int64_
 #pragma unroll
         for (int n = 0; n < 16; ++n) ent[n][tt] = p01[n & 3] + p23[n >> 2];
       }
-      float4* dst = reinterpret_cast<float4*>(lut + q * G::QF + g * 16 * G::TT);
+      float4* dst = reinterpret_cast<float4*>(lut + q * G::QF + g * G::GS);
       const float* src = &ent[0][0];
 #pragma unroll
       for (int k = 0; k < 4 * G::TT; ++k)
@@ -183,11 +189,10 @@ __device__ inline void read_entries(uint32_t w, const float* lut, float (&e)[8][
   a[7] = and_byte<3>(mask, hi);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    constexpr int kEntryBytes = 4 * G::TT;
     const int group = WI * 8 + k;
 #pragma unroll
     for (int q = 0; q < G::NQ; ++q) {
-      const char* p = base + (q * G::QF * 4) + group * 16 * kEntryBytes + a[k];
+      const char* p = base + (q * G::QF * 4) + group * G::GS * 4 + a[k];
       if constexpr (G::TT == 1) {
         e[k][q] = *reinterpret_cast<const float*>(p);
       } else if constexpr (G::TT == 2) {
@@ -230,12 +235,14 @@ __device__ inline void add_entries(const float (&e)[8][Geo<T>::NQ * Geo<T>::TT],
 __device__ inline __amdgpu_buffer_rsrc_t word_rsrc(const uint32_t* bits) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(bits), (short)0, 0x7fffffff, 0x00020000);
 }
-__device__ inline uint32_t load_word(__amdgpu_buffer_rsrc_t r, uint32_t lane_bytes, int64_t w, int64_t ld) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)lane_bytes, (int)(w * ld * 4), 0);
+// w < 2^26 and w * ld4 < 2^31 (the host checks the buffer size), so 32-bit
+// scalar arithmetic suffices for the offsets.
+__device__ inline uint32_t load_word(__amdgpu_buffer_rsrc_t r, uint32_t lane_bytes, int w, uint32_t ld4) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)lane_bytes, (int)((uint32_t)w * ld4), 0);
 }
 
 template <int T, int WI>
-__device__ inline void chunk_words(__amdgpu_buffer_rsrc_t bits, uint32_t lane_bytes, int64_t ld, int64_t wnext, int64_t wlast,
+__device__ inline void chunk_words(__amdgpu_buffer_rsrc_t bits, uint32_t lane_bytes, uint32_t ld4, int wnext, int wlast,
                                    int nwords, uint32_t (&ring)[Geo<T>::D][Geo<T>::B], const float* lut, float* acc,
                                    float (&cur)[8][Geo<T>::NQ * Geo<T>::TT]) {
   using G = Geo<T>;
@@ -253,13 +260,13 @@ __device__ inline void chunk_words(__amdgpu_buffer_rsrc_t bits, uint32_t lane_by
     if constexpr (j == G::B - 1) {
 #pragma unroll
       for (int jj = 0; jj < G::B; ++jj) {
-        const int64_t w = imin(wnext + (int64_t)b * G::B + jj, wlast);
-        ring[b % G::D][jj] = load_word(bits, lane_bytes, w, ld);
+        const int w = min(wnext + b * G::B + jj, wlast);
+        ring[b % G::D][jj] = load_word(bits, lane_bytes, w, ld4);
       }
     }
     add_entries<T>(cur, acc);
     __builtin_amdgcn_sched_barrier(0);  // one word per scheduling region: bounded registers
-    if constexpr (WI + 1 < G::CW) chunk_words<T, WI + 1>(bits, lane_bytes, ld, wnext, wlast, nwords, ring, lut, acc, nxt);
+    if constexpr (WI + 1 < G::CW) chunk_words<T, WI + 1>(bits, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, nxt);
   }
 }
 
@@ -274,8 +281,10 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
   const int64_t span1 = imin(span0 + S.kc, S.n_red);
   const int64_t o = (int64_t)rb * kRows + tid;
   const bool valid = o < S.n_rows;
-  const int64_t w0 = span0 / kWordBits;
-  const int64_t wlast = cdiv(S.n_red, kWordBits) - 1;  // last word row of the matrix
+  // word-row indices and the row stride in bytes, as wave-uniform 32-bit values
+  const int w0 = __builtin_amdgcn_readfirstlane((int)(span0 / kWordBits));
+  const int wlast = __builtin_amdgcn_readfirstlane((int)(cdiv(S.n_red, kWordBits) - 1));  // last word row
+  const uint32_t ld4 = __builtin_amdgcn_readfirstlane((uint32_t)(S.ld * 4));
   // lanes past the last row read row n_rows-1 and store nothing
   const uint32_t lane_bytes = 4u * (uint32_t)(valid ? o : S.n_rows - 1);
   const __amdgpu_buffer_rsrc_t wrsrc = word_rsrc(S.bits);
@@ -303,7 +312,7 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
 #pragma unroll
   for (int d = 0; d < G::D; ++d)
 #pragma unroll
-    for (int j = 0; j < G::B; ++j) ring[d][j] = load_word(wrsrc, lane_bytes, imin(w0 + d * G::B + j, wlast), S.ld);
+    for (int j = 0; j < G::B; ++j) ring[d][j] = load_word(wrsrc, lane_bytes, min(w0 + d * G::B + j, wlast), ld4);
 
   TableInputs<T> in;
   load_inputs<T>(S, span0, span1, in);
@@ -318,11 +327,11 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
     build_tables<T>(in, c0, span1, S.x_bf16, lut);
     if (c + 1 < nchunks) load_inputs<T>(S, c0 + 4 * G::GMAX, span1, in);  // next chunk's inputs
     lds_barrier();
-    const int64_t wnext = c0 / kWordBits + (int64_t)G::D * G::B;  // first word not yet in the ring
+    const int wnext = w0 + c * (G::CW) + G::D * G::B;  // first word not yet in the ring
     float first[8][G::NQ * G::TT];
     read_entries<T, 0>(ring[0][0], lut, first);
     const int nwords = (int)imin(G::CW, cdiv(span1 - c0, kWordBits));  // words of this chunk
-    chunk_words<T, 0>(wrsrc, lane_bytes, S.ld, wnext, wlast, nwords, ring, lut, acc, first);
+    chunk_words<T, 0>(wrsrc, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, first);
   }
 #pragma unroll
   for (int t = 0; t < G::NQ * G::TT; ++t) acc[t] += acc[G::NQ * G::TT + t];
@@ -370,11 +379,15 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
   __syncthreads();
 }
 
+// The workgroup's two shared flag words live in the first entries of the
+// table array: every write to them follows a barrier after the last table
+// read of a tile, and every read precedes the barrier before the next tables
+// are built.
 template <int T>
 __global__ __launch_bounds__(kRows) void lut_stage_kernel(StageDesc S, int* err) {
-  __shared__ __attribute__((aligned(16))) float lut[kLutFloats];
-  __shared__ int s_flag;
-  lut_tile<T>(S, blockIdx.x, lut, &s_flag, err);
+  __shared__ __attribute__((aligned(16))) float lut[Geo<T>::LUT];
+  int* s_flag = reinterpret_cast<int*>(lut);
+  lut_tile<T>(S, blockIdx.x, lut, s_flag, err);
 }
 
 // ints: [0] error flag (sticky), [1] next tile, [2] workgroups exited,
@@ -383,9 +396,9 @@ __global__ __launch_bounds__(kRows) void lut_stage_kernel(StageDesc S, int* err)
 template <int T>
 __global__ __launch_bounds__(kRows) void lut_persistent_kernel(const StageDesc* __restrict__ segs, int nseg,
                                                                int ntiles, int* ints, int n_ints) {
-  __shared__ __attribute__((aligned(16))) float lut[kLutFloats];
-  __shared__ int s_flag;
-  __shared__ int s_tile;
+  __shared__ __attribute__((aligned(16))) float lut[Geo<T>::LUT];
+  int& s_flag = reinterpret_cast<int*>(lut)[0];  // aliases table entries (see lut_stage_kernel)
+  int& s_tile = reinterpret_cast<int*>(lut)[1];
   int* err = ints;
   int* next_tile = ints + 1;
   if (threadIdx.x == 0) s_tile = atomicAdd(next_tile, 1);
