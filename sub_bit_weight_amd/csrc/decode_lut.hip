@@ -270,6 +270,39 @@ __device__ inline void chunk_words(__amdgpu_buffer_rsrc_t bits, uint32_t lane_by
   }
 }
 
+// The same with the table reads two words ahead (more LDS latency hidden, at
+// the cost of one more set of entries in registers): used for T = 1, where
+// the entries are single floats.
+template <int T, int WI>
+__device__ inline void chunk_words2(__amdgpu_buffer_rsrc_t bits, uint32_t lane_bytes, uint32_t ld4, int wnext,
+                                    int wlast, int nwords, uint32_t (&ring)[Geo<T>::D][Geo<T>::B], const float* lut,
+                                    float* acc, float (&cur)[8][Geo<T>::NQ * Geo<T>::TT],
+                                    float (&nx1)[8][Geo<T>::NQ * Geo<T>::TT]) {
+  using G = Geo<T>;
+  if constexpr (WI < G::CW) {
+    constexpr int b = WI / G::B, j = WI % G::B;
+    if constexpr (j == 0 && WI > 0)
+      if (WI >= nwords) return;
+    float nx2[8][G::NQ * G::TT];
+    if constexpr (WI + 2 < G::CW) {
+      constexpr int b2 = (WI + 2) / G::B, j2 = (WI + 2) % G::B;
+      read_entries<T, WI + 2>(ring[b2 % G::D][j2], lut, nx2);
+    }
+    // every word of batch b has had its entries read (word WI two steps ago)
+    if constexpr (j == G::B - 1) {
+#pragma unroll
+      for (int jj = 0; jj < G::B; ++jj) {
+        const int w = min(wnext + b * G::B + jj, wlast);
+        ring[b % G::D][jj] = load_word(bits, lane_bytes, w, ld4);
+      }
+    }
+    add_entries<T>(cur, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (WI + 1 < G::CW)
+      chunk_words2<T, WI + 1>(bits, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, nx1, nx2);
+  }
+}
+
 // One tile: row block rb (one row per lane) over reduction span ks of stage S.
 template <int T>
 __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag, int* err) {
@@ -328,10 +361,16 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
     if (c + 1 < nchunks) load_inputs<T>(S, c0 + 4 * G::GMAX, span1, in);  // next chunk's inputs
     lds_barrier();
     const int wnext = w0 + c * (G::CW) + G::D * G::B;  // first word not yet in the ring
+    const int nwords = (int)imin(G::CW, cdiv(span1 - c0, kWordBits));  // words of this chunk
     float first[8][G::NQ * G::TT];
     read_entries<T, 0>(ring[0][0], lut, first);
-    const int nwords = (int)imin(G::CW, cdiv(span1 - c0, kWordBits));  // words of this chunk
-    chunk_words<T, 0>(wrsrc, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, first);
+    if constexpr (T == 1) {
+      float second[8][G::NQ * G::TT];
+      read_entries<T, 1>(ring[0][1], lut, second);
+      chunk_words2<T, 0>(wrsrc, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, first, second);
+    } else {
+      chunk_words<T, 0>(wrsrc, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, first);
+    }
   }
 #pragma unroll
   for (int t = 0; t < G::NQ * G::TT; ++t) acc[t] += acc[G::NQ * G::TT + t];

@@ -106,52 +106,97 @@ __device__ inline void load_block(const void* __restrict__ a, const float* __res
   }
 }
 
-// One workgroup per token row m:
-//   e[m] = 14 - exponent(max_k |a[m][k]|)  (0 for an all-zero row)
-//   out[term][m][2p], out[term][m][2p+1] = fp16 terms of a[m][k]*2^e for the
-//   element pair p (block p/16, elements q and q+16 with q = p%16); zero past K.
+// Reduction order within a 32-element block (one sign word) for the two
+// operand encodings of the GEMM.
+//  * Pair order (fp32 activations): k-slot j holds element j/2 + 16*(j%2).
+//  * Rotated order (bf16 activations): k-slot j = 16*sg + 8*h + 2*d + half
+//    (sg: which 16-deep step of the word, h: lane half of the 32x32x16 MFMA,
+//    d: dword of the lane's operand, half: fp16 within it) holds element
+//    (kPos[d] + 16*half + 8*h + 4*sg) mod 32.  The GEMM rotates the sign word
+//    right by 8*h + 4*sg and takes bit kPos[d] (and kPos[d]+16) of it: bit 15
+//    is the fp16 sign (value -1 or +1), bits 10, 9, 8 turn 1.0 into 0.5, 1.5
+//    or 1.25.  So slot j's operand is 1 + c*bit with c = -2, -1/2, +1/2, +1/4,
+//    and with A prescaled by f = 1, 4, -4, -8 (exact powers of two) the MFMA
+//    sums a*sign + (f - 1)*a per slot; the prep kernel returns the second
+//    part, C = sum (f - 1)*a, per row and reduction piece, and the GEMM
+//    subtracts it.  One rotation and four v_bitop3_b32 build a 16-deep step's
+//    operand instead of four shifts and four v_and_or_b32.
+constexpr int kPos[4] = {15, 10, 9, 8};
+constexpr int kPre[4] = {1, 4, -4, -8};
+
+__device__ constexpr int rot_element(int j) {
+  return (kPos[(j / 2) % 4] + 16 * (j % 2) + 8 * ((j / 8) % 2) + 4 * (j / 16)) % 32;
+}
+
+// One workgroup per (token row m, reduction piece sp); the piece covers
+// blocks [sp*bps, min((sp+1)*bps, nblk)) of 32 elements.
+//   e[sp][m] = E_TOP - exponent(max |a[m][k]| over the piece)  (0 if all zero);
+//   E_TOP = 14 puts the maximum in [2^13, 2^14), 11 leaves room for the x8
+//   prescale of the rotated order.
+//   out[term][m][slot] = fp16 terms of a[m][k]*2^e in the block's slot order
+//   (zero past K); fp32 activations get two terms (hi + lo).
+//   c[sp][m] = sum over the piece of (f - 1) * (fp16 of a*2^e)  (rotated order).
 // A thread handles whole 32-element blocks: 16-byte loads when `vec` (rows and
-// scales 16-byte aligned), 16 output dwords.
-// Rows of up to 256 blocks (8192 elements) stay in registers between the two
-// passes; longer rows are read twice.
-template <int SRC>
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restrict__ a,
-                                                            const float* __restrict__ cs, int64_t M,
-                                                            int64_t K, int64_t Kpad, int nt, int nsplit, int vec,
-                                                            _Float16* __restrict__ out, int* __restrict__ e_out) {
-  __shared__ float red[kPrepThreads / 64];
+// scales 16-byte aligned), 16 output dwords.  Pieces of up to 256 blocks stay
+// in registers between the two passes; longer ones are read twice.
+template <int SRC, bool ROT, int NTH>
+__global__ __launch_bounds__(NTH) void prep_kernel(const void* __restrict__ a, const float* __restrict__ cs,
+                                                   int64_t M, int64_t K, int64_t Kpad, int nt, int nsum, int vec,
+                                                   int bps, _Float16* __restrict__ out, int* __restrict__ e_out,
+                                                   float* __restrict__ c_out) {
+  constexpr int NW = NTH / 64;
+  __shared__ float red[NW];
   const int64_t m = blockIdx.x;
+  const int sp = blockIdx.y;
   const int tid = threadIdx.x;
   const int64_t nblk = Kpad / 32;
-  const bool in_regs = nblk <= kPrepThreads;
+  const int64_t b0 = (int64_t)sp * bps, b1 = imin(b0 + bps, nblk);
+  const bool in_regs = b1 - b0 <= NTH;
   float v[32];
   float mx = 0.0f;
-  for (int64_t blk = tid; blk < nblk; blk += kPrepThreads) {
-    load_block<SRC>(a, cs, M, K, nsplit, vec != 0, m, blk, v);
+  for (int64_t blk = b0 + tid; blk < b1; blk += NTH) {
+    load_block<SRC>(a, cs, M, K, nsum, vec != 0, m, blk, v);
 #pragma unroll
     for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(v[i]));
   }
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (tid % 64 == 0) red[tid / 64] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (NW > 1) {
+    if (tid % 64 == 0) red[tid / 64] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red[w]);
+    __syncthreads();  // red is reused below
+  }
   int e = 0;
   if (mx > 0.0f && isfinite(mx)) {
     int ex;
     frexpf(mx, &ex);  // mx = f * 2^ex, f in [0.5, 1)
-    e = 14 - ex;      // mx * 2^e in [2^13, 2^14)
+    e = (ROT ? 11 : 14) - ex;
   }
-  if (tid == 0) e_out[m] = e;
-  for (int64_t blk = tid; blk < nblk; blk += kPrepThreads) {
-    if (!in_regs) load_block<SRC>(a, cs, M, K, nsplit, vec != 0, m, blk, v);
+  if (tid == 0) e_out[(int64_t)sp * M + m] = e;
+  float csum = 0.0f;
+  for (int64_t blk = b0 + tid; blk < b1; blk += NTH) {
+    if (!in_regs) load_block<SRC>(a, cs, M, K, nsum, vec != 0, m, blk, v);
     uint32_t hi[16], lo[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const float v0 = ldexpf(v[q], e), v1 = ldexpf(v[q + 16], e);
-      const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-      hi[q] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-      const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
-      lo[q] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    for (int p = 0; p < 16; ++p) {
+      _Float16 h2[2], l2[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int j = 2 * p + half;
+        const float x = ldexpf(v[ROT ? rot_element(j) : p + 16 * half], e);
+        const _Float16 hx = (_Float16)x;
+        if (ROT) {
+          h2[half] = (_Float16)(kPre[p % 4] * (float)hx);
+          l2[half] = (_Float16)0.0f;
+          csum += (float)(kPre[p % 4] - 1) * (float)hx;
+        } else {
+          h2[half] = hx;
+          l2[half] = (_Float16)(x - (float)hx);
+        }
+      }
+      hi[p] = (uint32_t)__builtin_bit_cast(uint16_t, h2[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, h2[1]) << 16);
+      lo[p] = (uint32_t)__builtin_bit_cast(uint16_t, l2[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, l2[1]) << 16);
     }
     uint4* dh = reinterpret_cast<uint4*>(out + m * Kpad + blk * 32);
 #pragma unroll
@@ -161,6 +206,17 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restri
 #pragma unroll
       for (int i = 0; i < 4; ++i) dl[i] = make_uint4(lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]);
     }
+  }
+  if (ROT) {  // fixed-order reduction of the correction sums
+    for (int off = 32; off > 0; off >>= 1) csum += __shfl_xor(csum, off);
+    if (NW > 1) {
+      if (tid % 64 == 0) red[tid / 64] = csum;
+      __syncthreads();
+      csum = red[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) csum += red[w];
+    }
+    if (tid == 0) c_out[(int64_t)sp * M + m] = csum;
   }
 }
 
@@ -174,6 +230,20 @@ __device__ inline f16x8 signs_f16(uint32_t w, int b, uint32_t mask, uint32_t one
   u32x4 v;
 #pragma unroll
   for (int d = 0; d < 4; ++d) v[d] = ((w << (15 - b - d)) & mask) | one;
+  return __builtin_bit_cast(f16x8, v);
+}
+
+// The same operand in the rotated order (see rot_element): rotate the sign
+// word right by 8*h + 4*sg, then dword d = (x & (bit kPos[d] | bit kPos[d]+16))
+// ^ 1.0 pair, one v_bitop3_b32 each.
+__device__ inline f16x8 signs_rot(uint32_t w, uint32_t rot, uint32_t one) {
+  const uint32_t x = __builtin_amdgcn_alignbit(w, w, rot);
+  u32x4 v;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t mask = __builtin_amdgcn_readfirstlane((1u << kPos[d]) | (1u << (kPos[d] + 16)));
+    v[d] = __builtin_amdgcn_bitop3_b32(x, mask, one, (0xF0 & 0xCC) ^ 0xAA);  // (x & mask) ^ one
+  }
   return __builtin_bit_cast(f16x8, v);
 }
 
@@ -221,10 +291,12 @@ struct Pipe {
 // sign words follow: word row q (of the tile's two) at [q][kBN columns].
 template <int NT, int MB>
 __global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
-    const _Float16* __restrict__ A, const int* __restrict__ erow, const uint32_t* __restrict__ bits, int64_t ldb,
+    const _Float16* __restrict__ A, const int* __restrict__ erow, const float* __restrict__ crow,
+    const uint32_t* __restrict__ bits, int64_t ldb,
     int64_t M, int64_t N, int64_t K, int64_t Kpad, int tiles_m, int tiles_n, int nsplit, int kts,
     uint32_t sign_mask, uint32_t one, const float* __restrict__ colscale, float* __restrict__ out) {
   using P = Pipe<NT, MB>;
+  constexpr bool ROT = NT == 1;  // rotated operand encoding (see rot_element)
   extern __shared__ __attribute__((aligned(16))) char lds[];  // [S][A tiles | sign words]
   const int lane = threadIdx.x % 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -322,9 +394,9 @@ __global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
 
       // 16-deep MFMA steps within the 64-deep tile, one fp16 term at a time
       // (j = NT*step + term), software-pipelined by hand: the A fragments of
-      // j+1 are read from LDS before the MFMAs of j are issued, and the +-1
-      // operands of the next step are built while those MFMAs run.  The
-      // scheduling barriers keep the compiler from regrouping the phases.
+      // j+1 are read from LDS and the +-1 operands of the next step are built
+      // between the MFMAs of j (scheduling-group barriers fix the interleave:
+      // one MFMA, one fragment read, a share of the sign expansion).
       const char* stage = lds + st * P::STAGE_BYTES;
       const uint32_t* bws = reinterpret_cast<const uint32_t*>(stage + P::A_BYTES) + wn * 64 + l32;
       uint32_t words[2][2];  // [q][nb]: this lane's sign words of the tile
@@ -340,9 +412,16 @@ __global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
           dst[mb] = *reinterpret_cast<const f16x8*>(stage + frag_off[s] + (term * P::BM + mb * 32) * 128);
       };
       auto build_b = [&](int s, f16x8 (&dst)[2]) {
-        const int q = s / 2, b = 8 * (s % 2) + 4 * h;
+        const int q = s / 2;
+        if constexpr (ROT) {
+          const uint32_t rot = 8 * h + 4 * (s % 2);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) dst[nb] = signs_f16(words[q][nb], b, sign_mask, one);
+          for (int nb = 0; nb < 2; ++nb) dst[nb] = signs_rot(words[q][nb], rot, one);
+        } else {
+          const int b = 8 * (s % 2) + 4 * h;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) dst[nb] = signs_f16(words[q][nb], b, sign_mask, one);
+        }
       };
       read_a(0, af[0]);
       f16x8 bf[2][2];
@@ -350,14 +429,23 @@ __global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
 #pragma unroll
       for (int j = 0; j < 4 * NT; ++j) {
         const int s = j / NT;
-        if (j + 1 < 4 * NT) read_a(j + 1, af[(j + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
+        const bool rd = j + 1 < 4 * NT, bld = j % NT == NT - 1 && s + 1 < 4;
+        if (rd) read_a(j + 1, af[(j + 1) & 1]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mb], bf[s & 1][nb], acc[mb][nb], 0, 0, 0);
-        if (j % NT == NT - 1 && s + 1 < 4) build_b(s + 1, bf[(s + 1) & 1]);
+        if (bld) build_b(s + 1, bf[(s + 1) & 1]);
+        // one MFMA, then (first MB of them) one A-fragment read, then a share of
+        // the sign expansion for the next step
+#pragma unroll
+        for (int i = 0; i < 2 * MB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (rd && i < MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (bld) __builtin_amdgcn_sched_group_barrier(0x002, 16 / (2 * MB), 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -366,7 +454,11 @@ __global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
   // 32x32 MFMA result layout: lane l, register 4a+c -> row 8a + 4(l/32) + c, column l%32.
   // A split reduction writes its partial sums to out[split] (colscale is then
   // applied by whoever adds the partials).
+  // Exponents (and, in the rotated encoding, the correction sums) are per
+  // reduction piece and row.
   float* dst = out + (int64_t)split * M * N;
+  const int* ep = erow + (int64_t)split * M;
+  const float* cp = crow + (int64_t)split * M;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -378,7 +470,10 @@ __global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int64_t m = m0 + wm * 32 * MB + mb * 32 + 8 * a + 4 * h + c;
-          if (m < M && n < N) dst[m * N + n] = sc * ldexpf(acc[mb][nb][4 * a + c], -erow[m]);
+          if (m < M && n < N) {
+            const float v = ROT ? acc[mb][nb][4 * a + c] - cp[m] : acc[mb][nb][4 * a + c];
+            dst[m * N + n] = sc * ldexpf(v, -ep[m]);
+          }
         }
     }
 }
@@ -394,14 +489,29 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
   }
 }
 
+// Prep of one GEMM operand: grid (rows, reduction pieces); bps = blocks of 32
+// per piece.  nt == 1 uses the rotated encoding (with correction sums in c).
 template <int SRC>
-hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int64_t Kpad, int nt, int nsplit,
-                       _Float16* out, int* e, hipStream_t s) {
+hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int64_t Kpad, int nt, int nsum,
+                       int npieces, int bps, _Float16* out, int* e, float* c, hipStream_t s) {
   const int esize = SRC == kABF16Scaled ? 2 : 4;
   const int vec = (reinterpret_cast<uintptr_t>(a) % 16 == 0) && (reinterpret_cast<uintptr_t>(cs) % 16 == 0) &&
                   ((K * esize) % 16 == 0);
-  hipLaunchKernelGGL(prep_kernel<SRC>, dim3((unsigned)M), dim3(kPrepThreads), 0, s, a, cs, M, K, Kpad, nt, nsplit,
-                     vec, out, e);
+  const dim3 grid((unsigned)M, (unsigned)npieces);
+  // one wave per (row, piece) for short pieces, four for long ones
+  const int64_t pblk = imin((int64_t)bps, Kpad / 32);
+  if (nt == 1 && pblk <= 64)
+    hipLaunchKernelGGL((prep_kernel<SRC, true, 64>), grid, dim3(64), 0, s, a, cs, M, K, Kpad, nt, nsum, vec, bps, out,
+                       e, c);
+  else if (nt == 1)
+    hipLaunchKernelGGL((prep_kernel<SRC, true, kPrepThreads>), grid, dim3(kPrepThreads), 0, s, a, cs, M, K, Kpad, nt,
+                       nsum, vec, bps, out, e, c);
+  else if (pblk <= 64)
+    hipLaunchKernelGGL((prep_kernel<SRC, false, 64>), grid, dim3(64), 0, s, a, cs, M, K, Kpad, nt, nsum, vec, bps,
+                       out, e, c);
+  else
+    hipLaunchKernelGGL((prep_kernel<SRC, false, kPrepThreads>), grid, dim3(kPrepThreads), 0, s, a, cs, M, K, Kpad,
+                       nt, nsum, vec, bps, out, e, c);
   return hipGetLastError();
 }
 
@@ -434,7 +544,7 @@ Split split_plan(int64_t M, int64_t N, int64_t Kpad) {
 }
 
 template <int NT, int MB>
-hipError_t launch_gemm_t(decltype(&gemm_kernel<NT, MB>) kernel, const _Float16* A, const int* e,
+hipError_t launch_gemm_t(decltype(&gemm_kernel<NT, MB>) kernel, const _Float16* A, const int* e, const float* c,
                          const uint32_t* bits, int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t Kpad, Split sp,
                          const float* colscale, float* out, hipStream_t s) {
   using P = Pipe<NT, MB>;
@@ -447,29 +557,31 @@ hipError_t launch_gemm_t(decltype(&gemm_kernel<NT, MB>) kernel, const _Float16* 
   }
   const int tiles_m = (int)cdiv(M, P::BM), tiles_n = (int)cdiv(N, kBN);
   const unsigned grid = (unsigned)(8 * ((tiles_m * tiles_n * sp.n + 7) / 8));
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), P::LDS, s, A, e, bits, ldb, M, N, K, Kpad, tiles_m, tiles_n,
-                     sp.n, sp.kts, kSignMask, kOnePair, colscale, out);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), P::LDS, s, A, e, c, bits, ldb, M, N, K, Kpad, tiles_m,
+                     tiles_n, sp.n, sp.kts, kSignMask, kOnePair, colscale, out);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int nt, const _Float16* A, const int* e, const uint32_t* bits, int64_t ldb, int64_t M,
-                       int64_t N, int64_t K, int64_t Kpad, Split sp, const float* colscale, float* out,
+hipError_t launch_gemm(int nt, const _Float16* A, const int* e, const float* c, const uint32_t* bits, int64_t ldb,
+                       int64_t M, int64_t N, int64_t K, int64_t Kpad, Split sp, const float* colscale, float* out,
                        hipStream_t s) {
   constexpr int MB = kTileMB;
-  return nt == 1 ? launch_gemm_t<1, MB>(gemm_kernel<1, MB>, A, e, bits, ldb, M, N, K, Kpad, sp, colscale, out, s)
-                 : launch_gemm_t<2, MB>(gemm_kernel<2, MB>, A, e, bits, ldb, M, N, K, Kpad, sp, colscale, out, s);
+  return nt == 1
+             ? launch_gemm_t<1, MB>(gemm_kernel<1, MB>, A, e, c, bits, ldb, M, N, K, Kpad, sp, colscale, out, s)
+             : launch_gemm_t<2, MB>(gemm_kernel<2, MB>, A, e, c, bits, ldb, M, N, K, Kpad, sp, colscale, out, s);
 }
 
 struct PrefillLayout {
   int nt;
   int64_t kpad1, kpad2;
   Split sp1, sp2;
-  size_t off_z, off_e1, off_t, off_t16, off_e2, off_y2, total;
+  size_t off_z, off_e1, off_c1, off_t, off_t16, off_e2, off_c2, off_y2, total;
 };
 
-// Workspace: fp16 terms of stage 1's activations, their exponents, t (one copy
-// per reduction piece of stage 1), fp16 terms of t, their exponents, and the
-// partial outputs of stage 2 when its reduction is split.
+// Workspace: fp16 terms of stage 1's activations, their exponents and
+// correction sums (per reduction piece and row), t (one copy per reduction
+// piece of stage 1), the same three for t, and the partial outputs of stage 2
+// when its reduction is split.
 PrefillLayout prefill_layout(const nq_lrb& L, int64_t T, nq_dtype xd) {
   PrefillLayout d;
   d.nt = xd == NQ_F32 ? 2 : 1;
@@ -481,13 +593,17 @@ PrefillLayout prefill_layout(const nq_lrb& L, int64_t T, nq_dtype xd) {
   d.off_z = off;
   off = align_up(off + (size_t)d.nt * T * d.kpad1 * sizeof(_Float16));
   d.off_e1 = off;
-  off = align_up(off + (size_t)T * sizeof(int));
+  off = align_up(off + (size_t)d.sp1.n * T * sizeof(int));
+  d.off_c1 = off;
+  off = align_up(off + (size_t)d.sp1.n * T * sizeof(float));
   d.off_t = off;
   off = align_up(off + (size_t)d.sp1.n * T * L.r * sizeof(float));
   d.off_t16 = off;
   off = align_up(off + (size_t)d.nt * T * d.kpad2 * sizeof(_Float16));
   d.off_e2 = off;
-  off = align_up(off + (size_t)T * sizeof(int));
+  off = align_up(off + (size_t)d.sp2.n * T * sizeof(int));
+  d.off_c2 = off;
+  off = align_up(off + (size_t)d.sp2.n * T * sizeof(float));
   d.off_y2 = off;
   if (d.sp2.n > 1) off = align_up(off + (size_t)d.sp2.n * T * L.d_out * sizeof(float));
   d.total = off;
@@ -507,22 +623,30 @@ hipError_t launch_prefill(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T
   char* base = static_cast<char*>(ws);
   _Float16* z = reinterpret_cast<_Float16*>(base + d.off_z);
   int* e1 = reinterpret_cast<int*>(base + d.off_e1);
+  float* c1 = reinterpret_cast<float*>(base + d.off_c1);
   float* t = reinterpret_cast<float*>(base + d.off_t);
   _Float16* t16 = reinterpret_cast<_Float16*>(base + d.off_t16);
   int* e2 = reinterpret_cast<int*>(base + d.off_e2);
+  float* c2 = reinterpret_cast<float*>(base + d.off_c2);
   float* y2 = reinterpret_cast<float*>(base + d.off_y2);
+  const int bps1 = 2 * d.sp1.kts, bps2 = 2 * d.sp2.kts;  // 32-element blocks per reduction piece
   hipError_t e;
   if (xd == NQ_BF16)
-    e = launch_prep<kABF16Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, 1, z, e1, s);
+    e = launch_prep<kABF16Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, 1, d.sp1.n, bps1, z, e1, c1, s);
   else
-    e = launch_prep<kAF32Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, 1, z, e1, s);
+    e = launch_prep<kAF32Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, 1, d.sp1.n, bps1, z, e1, c1, s);
   if (e != hipSuccess) return e;
-  if ((e = launch_gemm(d.nt, z, e1, L.vt_bits, L.ldv, T, L.r, L.d_in, d.kpad1, d.sp1, nullptr, t, s)) != hipSuccess)
+  if ((e = launch_gemm(d.nt, z, e1, c1, L.vt_bits, L.ldv, T, L.r, L.d_in, d.kpad1, d.sp1, nullptr, t, s)) !=
+      hipSuccess)
     return e;
   // the stage-2 prep adds stage 1's partial sums while it reads t
-  if ((e = launch_prep<kAF32>(t, nullptr, T, L.r, d.kpad2, d.nt, d.sp1.n, t16, e2, s)) != hipSuccess) return e;
-  if (d.sp2.n == 1) return launch_gemm(d.nt, t16, e2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, L.s1, y, s);
-  if ((e = launch_gemm(d.nt, t16, e2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, nullptr, y2, s)) != hipSuccess)
+  if ((e = launch_prep<kAF32>(t, nullptr, T, L.r, d.kpad2, d.nt, d.sp1.n, d.sp2.n, bps2, t16, e2, c2, s)) !=
+      hipSuccess)
+    return e;
+  if (d.sp2.n == 1)
+    return launch_gemm(d.nt, t16, e2, c2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, L.s1, y, s);
+  if ((e = launch_gemm(d.nt, t16, e2, c2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, nullptr, y2, s)) !=
+      hipSuccess)
     return e;
   const int64_t MN = T * L.d_out;
   const unsigned grid = (unsigned)imin(cdiv(MN, 256), (int64_t)4096);

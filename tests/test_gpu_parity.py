@@ -245,3 +245,19 @@ def test_linear_uneven_split(x_dtype):
     err = _linear_err(dev, ref, x, x_dtype)
     print(f"uneven split {x_dtype}: rel err {err:.3e}")
     assert err <= G.tol_for(200, x_dtype), err
+
+
+# All-positive activations with a large mean: the matrix-core path's rotated
+# operand encoding leaves a per-row correction sum that is then large next to
+# the result (it must cancel exactly up to fp32 rounding).
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_linear_biased_inputs(x_dtype):
+    shape = synth.LayerShape("biased", 512, 1024, 256)
+    cfg = G.tiny_config(f"biased/{x_dtype}", x_dtype=x_dtype)
+    dev, ref, _ = G.latent_layer(cfg, shape)
+    x = np.abs(synth.activations(f"biased/x/{x_dtype}", 100, shape.d_in, "f32")) + np.float32(4.0)
+    if x_dtype == "bf16":
+        x = synth.round_bf16(x)
+    err = _linear_err(dev, ref, x, x_dtype)
+    print(f"biased inputs {x_dtype}: rel err {err:.3e}")
+    assert err <= G.tol_for(100, x_dtype), err
