@@ -63,6 +63,9 @@ struct Geo {
 
 __device__ inline float bf16_bits(uint32_t h) { return __uint_as_float(h << 16); }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // Loads through pointers held in a descriptor: tell the compiler they are
 // global memory (plain global_load, not flat).
 template <typename V>
@@ -113,6 +116,35 @@ __device__ inline void load_inputs(const StageDesc& S, int64_t c0, int64_t cend,
 #pragma unroll
   for (int i = 0; i < G::GPT; ++i) {
     const int g = threadIdx.x + i * kRows;
+    const int64_t j0 = c0 + 4 * g;
+    // a whole group in range: one 8- or 16-byte load per token, one for the
+    // scales (T <= 2 only: for more tokens the extra registers cost occupancy)
+    if (T <= 2 && S.x_vec && g < G::GMAX && j0 + 4 <= cend) {
+      if (S.colscale) {
+        const u32x4 c = gload(reinterpret_cast<const u32x4*>(S.colscale + j0));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) in.cs[i][b] = __uint_as_float(c[b]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) in.cs[i][b] = 1.0f;
+      }
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int64_t idx = (int64_t)t * S.n_red + j0;
+        if (S.x_bf16) {
+          const u32x2 w = gload(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(S.xin) + idx));
+          in.x[i][t][0] = w[0] & 0xFFFFu;
+          in.x[i][t][1] = w[0] >> 16;
+          in.x[i][t][2] = w[1] & 0xFFFFu;
+          in.x[i][t][3] = w[1] >> 16;
+        } else {
+          const u32x4 w = gload(reinterpret_cast<const u32x4*>(static_cast<const uint32_t*>(S.xin) + idx));
+#pragma unroll
+          for (int b = 0; b < 4; ++b) in.x[i][t][b] = w[b];
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int64_t j = c0 + 4 * g + b;
@@ -614,6 +646,8 @@ void lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, flo
   a.nks = p1.nks;
   a.nrb = p1.nrb;
   a.x_bf16 = xd == NQ_BF16;
+  a.x_vec = reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(L.s2) % 16 == 0 &&
+            L.d_in % 4 == 0;
   a.tile0 = 0;
   StageDesc b = a;
   b.bits = L.u_bits;
@@ -633,6 +667,7 @@ void lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, flo
   b.nks = p2.nks;
   b.nrb = p2.nrb;
   b.x_bf16 = 0;
+  b.x_vec = L.r % 4 == 0;  // t sits 256-byte aligned in the workspace
   *s1 = a;
   *s2 = b;
 }

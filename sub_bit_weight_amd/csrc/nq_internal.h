@@ -59,6 +59,7 @@ struct StageDesc {
   int n_rows, n_red;
   int kc, nks, nrb;       // reduction span per tile (elements), spans, row blocks
   int x_bf16;
+  int x_vec;              // xin and colscale 16-byte aligned and n_red % 4 == 0: vector loads
   int tile0;              // first tile of this stage in a persistent schedule
 };
 struct StagePlan {
