@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16/bf16 matrix cores, TFLOP/s
+VALU_LANE_OPS = 256 * 64 * 2.4e9  # MI355X vector ALU lane-ops per second (256 CUs, 2.4 GHz)
 DECODE_SRC = os.path.join(ROOT, "sub_bit_weight_amd", "csrc", "decode_lut.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_lut_persistent_70b_stack_hbm_traffic.md")
 
@@ -154,6 +155,35 @@ def time_prefill(stack, T: int, device: str, warmup_layers: int = 1):
     return t0.elapsed_time(t1)
 
 
+def vendor_gemm_reference(shapes, T: int, device: str) -> dict:
+    """Context for the matrix-core roofline: torch.matmul (hipBLASLt) on dense
+    bf16 operands of the same GEMM shapes as the two LRB stages (M = T,
+    N = r or d_out, K = d_in or r), TFLOP/s per distinct shape.  The LRB
+    kernels read 1-bit B operands instead of bf16 ones."""
+    import torch
+    out = {}
+    for s in shapes:
+        for stage, (N, K) in (("stage1", (s.r, s.d_in)), ("stage2", (s.d_out, s.r))):
+            key = f"{T}x{N}x{K}"
+            if key in out:
+                continue
+            a = torch.randn(T, K, device=device, dtype=torch.bfloat16)
+            b = torch.randn(K, N, device=device, dtype=torch.bfloat16)
+            for _ in range(3):
+                a @ b
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                a @ b
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            out[key] = round(2 * T * N * K / (ms * 1e-3) / 1e12, 1)
+            del a, b
+    return out
+
+
 def cpu_baseline(cfg, min_s: float = 10.0) -> dict:
     """The oracle (reconstruct in fp64, then multiply) on the host cores, on a
     bounded sample of the decode step: the linears of layer 0, then layer 1,
@@ -255,6 +285,8 @@ def main() -> int:
                             "operands": "fp16 (per-token power-of-two scaled) x +-1, fp32 accumulate",
                             "includes": "prep kernels (row scaling, fp16 conversion) and both GEMMs of all 560 linears"}
         log(f"[bench] prefill {pms:.1f} ms/pass, {extra['prefill']['tflops']:.0f} TFLOP/s")
+        extra["prefill"]["vendor_dense_bf16_gemm_tflops"] = vendor_gemm_reference(stack.shapes[:len(cfg.layers)],
+                                                                                  Tp, device)
     del stack
     torch.cuda.empty_cache()
 
@@ -284,6 +316,10 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "lut_persistent_kernel<1> (one launch per step)",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic()},
+        # The decode kernel's own ceiling: 18 VALU lane-ops per 32-weight sign
+        # word (2 shifts, 8 nibble address selects, 8 fp32 adds) against
+        # 256 CUs x 64 lanes x 2.4 GHz of VALU lane-ops.
+        "decode_valu_ceiling_gbs": VALU_LANE_OPS / 18.0 * 4 / 1e9,
         "parity_rel_err": err,
     }
     out.update(extra)

@@ -70,23 +70,37 @@ __device__ inline void load_block(const void* __restrict__ a, const float* __res
     return;
   }
   if (SRC != kABF16Scaled && full) {
-    const float* base = static_cast<const float*>(a) + m * K + k0;
+    const float4* base = reinterpret_cast<const float4*>(static_cast<const float*>(a) + m * K + k0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float4 acc = reinterpret_cast<const float4*>(base)[i];
-      for (int sp = 1; sp < nsplit; ++sp) {
-        const float4 p = reinterpret_cast<const float4*>(base + (int64_t)sp * M * K)[i];
-        acc.x += p.x;
-        acc.y += p.y;
-        acc.z += p.z;
-        acc.w += p.w;
+      const float4 p = base[i];
+      v[4 * i] = p.x;
+      v[4 * i + 1] = p.y;
+      v[4 * i + 2] = p.z;
+      v[4 * i + 3] = p.w;
+    }
+#pragma unroll 1
+    for (int sp = 1; sp < nsplit; ++sp) {  // partial sums of a split reduction, in order
+      const float4* ps = base + (int64_t)sp * M * K / 4;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 p = ps[i];
+        v[4 * i] += p.x;
+        v[4 * i + 1] += p.y;
+        v[4 * i + 2] += p.z;
+        v[4 * i + 3] += p.w;
       }
-      float4 sc = make_float4(1.f, 1.f, 1.f, 1.f);
-      if (SRC == kAF32Scaled) sc = reinterpret_cast<const float4*>(cs + k0)[i];
-      v[4 * i] = acc.x * sc.x;
-      v[4 * i + 1] = acc.y * sc.y;
-      v[4 * i + 2] = acc.z * sc.z;
-      v[4 * i + 3] = acc.w * sc.w;
+    }
+    if (SRC == kAF32Scaled) {
+      const float4* sp4 = reinterpret_cast<const float4*>(cs + k0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 c = sp4[i];
+        v[4 * i] *= c.x;
+        v[4 * i + 1] *= c.y;
+        v[4 * i + 2] *= c.z;
+        v[4 * i + 3] *= c.w;
+      }
     }
     return;
   }
@@ -139,7 +153,64 @@ __device__ constexpr int rot_element(int j) {
 // A thread handles whole 32-element blocks: 16-byte loads when `vec` (rows and
 // scales 16-byte aligned), 16 output dwords.  Pieces of up to 256 blocks stay
 // in registers between the two passes; longer ones are read twice.
-template <int SRC, bool ROT, int NTH>
+// Convert one 32-element block (values v, already in registers) to its fp16
+// terms in the block's slot order and store them; returns the block's part of
+// the correction sum (rotated order).
+template <bool ROT>
+__device__ inline float convert_block(const float (&v)[32], int e, int64_t M, int64_t Kpad, int nt, int64_t m,
+                                      int64_t blk, _Float16* __restrict__ out) {
+  float csum = 0.0f;
+  uint32_t hi[16], lo[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    _Float16 h2[2], l2[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int j = 2 * p + half;
+      const float x = ldexpf(v[ROT ? rot_element(j) : p + 16 * half], e);
+      const _Float16 hx = (_Float16)x;
+      if (ROT) {
+        h2[half] = (_Float16)(kPre[p % 4] * (float)hx);
+        l2[half] = (_Float16)0.0f;
+        csum += (float)(kPre[p % 4] - 1) * (float)hx;
+      } else {
+        h2[half] = hx;
+        l2[half] = (_Float16)(x - (float)hx);
+      }
+    }
+    hi[p] = (uint32_t)__builtin_bit_cast(uint16_t, h2[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, h2[1]) << 16);
+    lo[p] = (uint32_t)__builtin_bit_cast(uint16_t, l2[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, l2[1]) << 16);
+  }
+  uint4* dh = reinterpret_cast<uint4*>(out + m * Kpad + blk * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dh[i] = make_uint4(hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]);
+  if (!ROT && nt == 2) {
+    uint4* dl = reinterpret_cast<uint4*>(out + (M + m) * Kpad + blk * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dl[i] = make_uint4(lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]);
+  }
+  return csum;
+}
+
+// Workgroup-wide reduction (max or sum) in a fixed order.
+template <int NW, bool MAX>
+__device__ inline float wg_reduce(float x, float* red) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const float o = __shfl_xor(x, off);
+    x = MAX ? fmaxf(x, o) : x + o;
+  }
+  if (NW > 1) {
+    __syncthreads();  // red may still be read by an earlier reduction
+    if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = x;
+    __syncthreads();
+    x = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) x = MAX ? fmaxf(x, red[w]) : x + red[w];
+  }
+  return x;
+}
+
+template <int SRC, bool ROT, int NTH, int BPT>
 __global__ __launch_bounds__(NTH) void prep_kernel(const void* __restrict__ a, const float* __restrict__ cs,
                                                    int64_t M, int64_t K, int64_t Kpad, int nt, int nsum, int vec,
                                                    int bps, _Float16* __restrict__ out, int* __restrict__ e_out,
@@ -151,22 +222,24 @@ __global__ __launch_bounds__(NTH) void prep_kernel(const void* __restrict__ a, c
   const int tid = threadIdx.x;
   const int64_t nblk = Kpad / 32;
   const int64_t b0 = (int64_t)sp * bps, b1 = imin(b0 + bps, nblk);
-  const bool in_regs = b1 - b0 <= NTH;
-  float v[32];
+  // this thread's blocks: b0 + tid + i*NTH; up to BPT of them stay in registers,
+  // longer pieces are read a second time for the conversion
+  const bool in_regs = b1 - b0 <= (int64_t)NTH * BPT;
+  float v[BPT][32];
   float mx = 0.0f;
-  for (int64_t blk = b0 + tid; blk < b1; blk += NTH) {
-    load_block<SRC>(a, cs, M, K, nsum, vec != 0, m, blk, v);
+  for (int64_t base = b0 + tid; base < b1; base += (int64_t)NTH * BPT) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(v[i]));
-  }
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (NW > 1) {
-    if (tid % 64 == 0) red[tid / 64] = mx;
-    __syncthreads();
+    for (int i = 0; i < BPT; ++i) {
+      const int64_t blk = base + (int64_t)i * NTH;
+      if (blk < b1) load_block<SRC>(a, cs, M, K, nsum, vec != 0, m, blk, v[i]);
+    }
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red[w]);
-    __syncthreads();  // red is reused below
+    for (int i = 0; i < BPT; ++i)
+      if (base + (int64_t)i * NTH < b1)
+#pragma unroll
+        for (int k = 0; k < 32; ++k) mx = fmaxf(mx, fabsf(v[i][k]));
   }
+  mx = wg_reduce<NW, true>(mx, red);
   int e = 0;
   if (mx > 0.0f && isfinite(mx)) {
     int ex;
@@ -175,47 +248,18 @@ __global__ __launch_bounds__(NTH) void prep_kernel(const void* __restrict__ a, c
   }
   if (tid == 0) e_out[(int64_t)sp * M + m] = e;
   float csum = 0.0f;
-  for (int64_t blk = b0 + tid; blk < b1; blk += NTH) {
-    if (!in_regs) load_block<SRC>(a, cs, M, K, nsum, vec != 0, m, blk, v);
-    uint32_t hi[16], lo[16];
+  for (int64_t base = b0 + tid; base < b1; base += (int64_t)NTH * BPT) {
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      _Float16 h2[2], l2[2];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int j = 2 * p + half;
-        const float x = ldexpf(v[ROT ? rot_element(j) : p + 16 * half], e);
-        const _Float16 hx = (_Float16)x;
-        if (ROT) {
-          h2[half] = (_Float16)(kPre[p % 4] * (float)hx);
-          l2[half] = (_Float16)0.0f;
-          csum += (float)(kPre[p % 4] - 1) * (float)hx;
-        } else {
-          h2[half] = hx;
-          l2[half] = (_Float16)(x - (float)hx);
-        }
+    for (int i = 0; i < BPT; ++i) {
+      const int64_t blk = base + (int64_t)i * NTH;
+      if (blk < b1) {
+        if (!in_regs) load_block<SRC>(a, cs, M, K, nsum, vec != 0, m, blk, v[i]);
+        csum += convert_block<ROT>(v[i], e, M, Kpad, nt, m, blk, out);
       }
-      hi[p] = (uint32_t)__builtin_bit_cast(uint16_t, h2[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, h2[1]) << 16);
-      lo[p] = (uint32_t)__builtin_bit_cast(uint16_t, l2[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, l2[1]) << 16);
-    }
-    uint4* dh = reinterpret_cast<uint4*>(out + m * Kpad + blk * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dh[i] = make_uint4(hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]);
-    if (nt == 2) {
-      uint4* dl = reinterpret_cast<uint4*>(out + (M + m) * Kpad + blk * 32);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dl[i] = make_uint4(lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]);
     }
   }
-  if (ROT) {  // fixed-order reduction of the correction sums
-    for (int off = 32; off > 0; off >>= 1) csum += __shfl_xor(csum, off);
-    if (NW > 1) {
-      if (tid % 64 == 0) red[tid / 64] = csum;
-      __syncthreads();
-      csum = red[0];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) csum += red[w];
-    }
+  if (ROT) {
+    csum = wg_reduce<NW, false>(csum, red);
     if (tid == 0) c_out[(int64_t)sp * M + m] = csum;
   }
 }
@@ -498,20 +542,34 @@ hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int
   const int vec = (reinterpret_cast<uintptr_t>(a) % 16 == 0) && (reinterpret_cast<uintptr_t>(cs) % 16 == 0) &&
                   ((K * esize) % 16 == 0);
   const dim3 grid((unsigned)M, (unsigned)npieces);
-  // one wave per (row, piece) for short pieces, four for long ones
+  // 1 to 8 waves per (row, piece), the fewest that hold the piece in registers
   const int64_t pblk = imin((int64_t)bps, Kpad / 32);
-  if (nt == 1 && pblk <= 64)
-    hipLaunchKernelGGL((prep_kernel<SRC, true, 64>), grid, dim3(64), 0, s, a, cs, M, K, Kpad, nt, nsum, vec, bps, out,
-                       e, c);
-  else if (nt == 1)
-    hipLaunchKernelGGL((prep_kernel<SRC, true, kPrepThreads>), grid, dim3(kPrepThreads), 0, s, a, cs, M, K, Kpad, nt,
-                       nsum, vec, bps, out, e, c);
-  else if (pblk <= 64)
-    hipLaunchKernelGGL((prep_kernel<SRC, false, 64>), grid, dim3(64), 0, s, a, cs, M, K, Kpad, nt, nsum, vec, bps,
-                       out, e, c);
-  else
-    hipLaunchKernelGGL((prep_kernel<SRC, false, kPrepThreads>), grid, dim3(kPrepThreads), 0, s, a, cs, M, K, Kpad,
-                       nt, nsum, vec, bps, out, e, c);
+#define NQ_PREP(ROT, NTH, BPT)                                                                                    \
+  hipLaunchKernelGGL((prep_kernel<SRC, ROT, NTH, BPT>), grid, dim3(NTH), 0, s, a, cs, M, K, Kpad, nt, nsum, vec, bps, \
+                     out, e, c)
+  // bf16 sources: two blocks per thread in registers; fp32 sources (whose
+  // loads need more registers): one
+  constexpr int BPT = SRC == kABF16Scaled ? 2 : 1;
+  if (nt == 1) {
+    if (pblk <= 64 * BPT)
+      NQ_PREP(true, 64, BPT);
+    else if (pblk <= 128 * BPT)
+      NQ_PREP(true, 128, BPT);
+    else if (pblk <= 256 * BPT)
+      NQ_PREP(true, 256, BPT);
+    else
+      NQ_PREP(true, 512, BPT);
+  } else {
+    if (pblk <= 64 * BPT)
+      NQ_PREP(false, 64, BPT);
+    else if (pblk <= 128 * BPT)
+      NQ_PREP(false, 128, BPT);
+    else if (pblk <= 256 * BPT)
+      NQ_PREP(false, 256, BPT);
+    else
+      NQ_PREP(false, 512, BPT);
+  }
+#undef NQ_PREP
   return hipGetLastError();
 }
 
