@@ -132,27 +132,27 @@ def parity_sample(stack, xs, ys, idx: int, n_rows: int = 16) -> float:
     return O.rel_err(y[:, rows], O.sampled_linear_ref(ref, x, rows))
 
 
-def time_prefill(stack, T: int, device: str, warmup_layers: int = 1):
+def time_prefill(stack, T: int, device: str):
+    """One T-token pass over every linear of the stack as one sequence plan
+    (entries run round-robin on the plan's streams).  Returns (ms, seq, xs,
+    ys); each linear has its own output."""
     import torch
 
     import sub_bit_weight_amd as nq
     import synth
-    per = len(stack.cfg.layers)
     xs_by_din = {d: torch.from_numpy(synth.x_for(stack.cfg, d, T)).to(device).to(torch.bfloat16)
                  for d in sorted({s.d_in for s in stack.shapes})}
-    ys = [torch.empty((T, s.d_out), dtype=torch.float32, device=device) for s in stack.shapes[:per]]
-    ws = torch.empty(max(nq.lrb_workspace_bytes(L, T) for L in stack.layers[:per]), dtype=torch.uint8,
-                     device=device)
-    for i in range(warmup_layers * per):
-        nq.lrb_linear(stack.layers[i], xs_by_din[stack.shapes[i].d_in], ys[i % per], ws)
+    xs = [xs_by_din[s.d_in] for s in stack.shapes]
+    ys = [torch.empty((T, s.d_out), dtype=torch.float32, device=device) for s in stack.shapes]
+    seq = nq.Seq(stack.layers, xs, ys)
+    seq.run()  # warm-up pass
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
-    for i, L in enumerate(stack.layers):
-        nq.lrb_linear(L, xs_by_din[stack.shapes[i].d_in], ys[i % per], ws)
+    seq.run()
     t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1)
+    return t0.elapsed_time(t1), seq, xs, ys
 
 
 def vendor_gemm_reference(shapes, T: int, device: str) -> dict:
@@ -277,13 +277,17 @@ def main() -> int:
     if not args.no_prefill:
         Tp = 2048
         log("[bench] prefill T=2048")
-        pms = time_prefill(stack, Tp, device)
+        pms, pseq, pxs, pys = time_prefill(stack, Tp, device)
+        perr = parity_sample(stack, pxs, pys, idx=0)  # layer 0 q, 16 rows, all 2048 tokens
+        log(f"[bench] prefill parity (layer 0 q, 16 rows) rel err {perr:.2e}")
+        del pseq, pys
         flops = algorithmic_flops(stack.shapes, Tp)
         extra["prefill"] = {"T": Tp, "ms_per_pass": pms, "tflops": flops / (pms * 1e-3) / 1e12,
                             "frac_of_f16_peak": flops / (pms * 1e-3) / 1e12 / F16_PEAK_TFLOPS,
                             "tokens_per_s": Tp / (pms * 1e-3), "algorithmic_flop": flops,
                             "operands": "fp16 (per-token power-of-two scaled) x +-1, fp32 accumulate",
-                            "includes": "prep kernels (row scaling, fp16 conversion) and both GEMMs of all 560 linears"}
+                            "includes": "prep kernels (row scaling, fp16 conversion) and both GEMMs of all 560 linears",
+                            "parity_rel_err": perr}
         log(f"[bench] prefill {pms:.1f} ms/pass, {extra['prefill']['tflops']:.0f} TFLOP/s")
         extra["prefill"]["vendor_dense_bf16_gemm_tflops"] = vendor_gemm_reference(stack.shapes[:len(cfg.layers)],
                                                                                   Tp, device)

@@ -144,23 +144,28 @@ uint64_t nq_storage_bits(int64_t d_out, int64_t d_in, int64_t r);
 
 /*
  * Sequences of independent LRB linears (e.g. every linear of a decoder stack)
- * run as one device-side schedule.  Running the sequence is equivalent to
- * calling nq_lrb_linear on each entry in order, except that consecutive entries
- * may overlap (each entry's inputs must not depend on another entry's output).
+ * run as one schedule.  Running the sequence is equivalent to calling
+ * nq_lrb_linear on each entry in order, except that entries may run
+ * concurrently: no entry's input may be another entry's output, and no two
+ * entries' outputs may overlap.
  *
  * nq_seq_create: host-only planning.  `layers`, `xs`, `ys` are host arrays of
  *   n entries (the nq_lrb structs are copied; xs[i], ys[i] are device
  *   pointers).  All entries share T and x_dtype.  The decode regime (T <= 8)
- *   runs as one persistent kernel; T > 8 runs the per-entry kernels.
- *   Errors: as for nq_lrb_linear, per entry.
+ *   runs as one persistent kernel; T > 8 runs the per-entry kernels
+ *   round-robin on three streams owned by the plan (created on the first run
+ *   on the device current then), each entry with its own part of the
+ *   workspace.  Errors: as for nq_lrb_linear, per entry.
  * nq_seq_workspace_bytes: device workspace the plan needs.
- * nq_seq_run: runs the whole sequence on `stream`.  The workspace must stay
- *   the same buffer across runs of one plan (the first run uploads the
- *   schedule into it, synchronising `stream` once) and must not be shared by
- *   plans running concurrently.  In the decode regime the first 4 bytes of the
- *   workspace are a device error word: 0, or non-zero (sticky) if a
- *   dependency wait inside the kernel gave up; read it after synchronising.
- * nq_seq_destroy: frees the host plan.
+ * nq_seq_run: runs the whole sequence, ordered after the work already on
+ *   `stream`; work queued on `stream` afterwards waits for all of it.  The
+ *   workspace must stay the same buffer across runs of one plan (the first
+ *   decode-regime run uploads the schedule into it, synchronising `stream`
+ *   once) and must not be shared by plans running concurrently.  In the decode
+ *   regime the first 4 bytes of the workspace are a device error word: 0, or
+ *   non-zero (sticky) if a dependency wait inside the kernel gave up; read it
+ *   after synchronising.
+ * nq_seq_destroy: frees the plan (and its streams).
  */
 typedef struct nq_seq nq_seq;
 nq_status nq_seq_create(const nq_lrb* layers, const void* const* xs, float* const* ys, int64_t n,

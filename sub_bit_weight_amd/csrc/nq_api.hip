@@ -76,6 +76,7 @@ nq_status check_io(const char* who, const nq_lrb* L, const void* x, nq_dtype xd,
 }
 
 constexpr int64_t kDecodeMaxT = 8;
+constexpr int64_t kSeqLanes = 3;  // streams of a sequence plan in the matrix-core regime
 
 // NQ_DECODE_VARIANT=xor selects the per-weight sign-XOR decode kernels (kept
 // for comparison); the default is the table-lookup kernels.
@@ -116,6 +117,20 @@ struct nq_seq {
   std::vector<nq::StageDesc> segs;    // host copy of the uploaded schedule
   void* uploaded_for = nullptr;
   bool needs_zero = true;
+  // per-entry kernels (T > 8): entries run round-robin on `nlanes` streams of
+  // the plan, each with its own slice of the workspace, so that one entry's
+  // memory-bound prep kernels and partly filled last GEMM waves overlap the
+  // next entries' GEMMs.  The streams and events are created on the first run.
+  int nlanes = 0;
+  size_t lane_ws = 0;
+  std::vector<hipStream_t> lanes;
+  std::vector<hipEvent_t> lane_done;
+  hipEvent_t start = nullptr;
+  ~nq_seq() {
+    for (hipStream_t l : lanes) (void)hipStreamDestroy(l);
+    for (hipEvent_t e : lane_done) (void)hipEventDestroy(e);
+    if (start) (void)hipEventDestroy(start);
+  }
 };
 
 namespace {
@@ -279,7 +294,13 @@ nq_status nq_seq_create(const nq_lrb* layers, const void* const* xs, float* cons
     s->ys.push_back(ys[i]);
     s->ws_bytes = std::max<size_t>(s->ws_bytes, linear_workspace(layers[i], T));
   }
-  if (T <= kDecodeMaxT && !decode_xor()) plan_persistent(s);
+  if (T <= kDecodeMaxT && !decode_xor()) {
+    plan_persistent(s);
+  } else {
+    s->nlanes = (int)std::min<int64_t>(kSeqLanes, n);
+    s->lane_ws = align_up(s->ws_bytes);
+    s->ws_bytes = s->lane_ws * s->nlanes;
+  }
   *out = s;
   return NQ_OK;
 }
@@ -310,11 +331,33 @@ nq_status nq_seq_run(nq_seq* s, void* workspace, size_t workspace_bytes, void* s
                                 (int)s->segs.size(), s->ntiles, ints, (int)s->n_ints, s->T, s->grid, st);
     return hip_status(e, "nq_seq_run launch");
   }
-  for (size_t i = 0; i < s->layers.size(); ++i) {
-    hipError_t e = launch_linear(s->layers[i], s->xs[i], s->xd, s->T, s->ys[i], workspace, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e, "nq_seq_run launch");
+  if (s->lanes.empty()) {  // first run: the plan's streams (default priority) and events
+    for (int l = 0; l < s->nlanes; ++l) {
+      hipStream_t ls = nullptr;
+      hipEvent_t ev = nullptr;
+      hipError_t e = hipStreamCreateWithFlags(&ls, hipStreamNonBlocking);
+      if (e == hipSuccess) s->lanes.push_back(ls);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e == hipSuccess) s->lane_done.push_back(ev);
+      if (e != hipSuccess) return hip_status(e, "nq_seq_run stream setup");
+    }
+    hipError_t e = hipEventCreateWithFlags(&s->start, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_status(e, "nq_seq_run stream setup");
   }
-  return NQ_OK;
+  // fork: every lane waits for the work already queued on the caller's stream
+  hipError_t e = hipEventRecord(s->start, st);
+  for (int l = 0; l < s->nlanes && e == hipSuccess; ++l) e = hipStreamWaitEvent(s->lanes[l], s->start, 0);
+  for (size_t i = 0; i < s->layers.size() && e == hipSuccess; ++i) {
+    const int l = (int)(i % s->nlanes);
+    e = launch_linear(s->layers[i], s->xs[i], s->xd, s->T, s->ys[i], static_cast<char*>(workspace) + l * s->lane_ws,
+                      s->lanes[l]);
+  }
+  // join: the caller's stream waits for every lane
+  for (int l = 0; l < s->nlanes && e == hipSuccess; ++l) {
+    e = hipEventRecord(s->lane_done[l], s->lanes[l]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, s->lane_done[l], 0);
+  }
+  return hip_status(e, "nq_seq_run launch");
 }
 
 void nq_seq_destroy(nq_seq* s) { delete s; }

@@ -176,6 +176,33 @@ def test_sequence_matches_single_calls():
         seq.close()
 
 
+def test_sequence_prefill_streams():
+    # more entries than the plan's streams, shapes with and without split
+    # reductions; inputs written and outputs read on the caller's stream right
+    # before and after the run (the plan forks from and joins back to it)
+    cfg = G.tiny_config("seqpf")
+    shapes = [synth.LayerShape("a", 300, 200, 64), synth.LayerShape("b", 700, 800, 600),
+              synth.LayerShape("c", 200, 96, 33), synth.LayerShape("d", 1024, 768, 256),
+              synth.LayerShape("e", 96, 300, 40), synth.LayerShape("f", 512, 1024, 256),
+              synth.LayerShape("g", 65, 129, 31)]
+    layers = [G.latent_layer(cfg, s, i)[0] for i, s in enumerate(shapes)]
+    T = 100
+    src = [G.to_device_x(synth.activations(f"seqpf/x/{i}", T, s.d_in, "bf16"), "bf16") for i, s in enumerate(shapes)]
+    xs = [torch.zeros_like(x) for x in src]
+    ys = [torch.full((T, s.d_out), float("nan"), device=G.DEV) for s in shapes]
+    seq = nq.Seq(layers, xs, ys)
+    for rep in range(2):
+        for x, x0 in zip(xs, src):
+            x.copy_(x0 * (rep + 1))
+        seq.run()
+        got = [y.clone() for y in ys]
+        torch.cuda.synchronize()
+        for L, x0, g in zip(layers, src, got):
+            want = nq.lrb_linear(L, x0 * (rep + 1))
+            assert torch.equal(g.view(torch.int32), want.view(torch.int32))
+    seq.close()
+
+
 @pytest.mark.parametrize("T", [1, 3, 8])
 def test_sequence_many_linears_parity(T):
     """A persistent schedule over many linears of mixed shapes (ragged row blocks,
