@@ -132,6 +132,31 @@ def parity_sample(stack, xs, ys, idx: int, n_rows: int = 16) -> float:
     return O.rel_err(y[:, rows], O.sampled_linear_ref(ref, x, rows))
 
 
+def time_prefill_serial(stack, T: int, device: str) -> float:
+    """The same pass with one nq_lrb_linear call per linear on one stream
+    (kernels never overlap: per-kernel durations in a trace are standalone)."""
+    import torch
+
+    import sub_bit_weight_amd as nq
+    import synth
+    per = len(stack.cfg.layers)
+    xs_by_din = {d: torch.from_numpy(synth.x_for(stack.cfg, d, T)).to(device).to(torch.bfloat16)
+                 for d in sorted({s.d_in for s in stack.shapes})}
+    ys = [torch.empty((T, s.d_out), dtype=torch.float32, device=device) for s in stack.shapes[:per]]
+    ws = torch.empty(max(nq.lrb_workspace_bytes(L, T) for L in stack.layers[:per]), dtype=torch.uint8,
+                     device=device)
+    for i in range(per):  # warm-up layer
+        nq.lrb_linear(stack.layers[i], xs_by_din[stack.shapes[i].d_in], ys[i], ws)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i, L in enumerate(stack.layers):
+        nq.lrb_linear(L, xs_by_din[stack.shapes[i].d_in], ys[i % per], ws)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
 def time_prefill(stack, T: int, device: str):
     """One T-token pass over every linear of the stack as one sequence plan
     (entries run round-robin on the plan's streams).  Returns (ms, seq, xs,
@@ -234,6 +259,8 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-055", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--prefill-serial", action="store_true",
+                    help="also time the prefill pass as serial single-linear calls on one stream")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -289,6 +316,11 @@ def main() -> int:
                             "includes": "prep kernels (row scaling, fp16 conversion) and both GEMMs of all 560 linears",
                             "parity_rel_err": perr}
         log(f"[bench] prefill {pms:.1f} ms/pass, {extra['prefill']['tflops']:.0f} TFLOP/s")
+        if args.prefill_serial:
+            sms = time_prefill_serial(stack, Tp, device)
+            extra["prefill"]["serial_ms_per_pass"] = sms
+            extra["prefill"]["serial_tflops"] = flops / (sms * 1e-3) / 1e12
+            log(f"[bench] prefill serial {sms:.1f} ms/pass")
         extra["prefill"]["vendor_dense_bf16_gemm_tflops"] = vendor_gemm_reference(stack.shapes[:len(cfg.layers)],
                                                                                   Tp, device)
     del stack
