@@ -146,8 +146,10 @@ uint64_t nq_storage_bits(int64_t d_out, int64_t d_in, int64_t r);
  * Sequences of independent LRB linears (e.g. every linear of a decoder stack)
  * run as one schedule.  Running the sequence is equivalent to calling
  * nq_lrb_linear on each entry in order, except that entries may run
- * concurrently: no entry's input may be another entry's output, and no two
- * entries' outputs may overlap.
+ * concurrently (no entry's input may be another entry's output, and no two
+ * entries' outputs may overlap) and that in the matrix-core regime an entry
+ * never splits its reduction, so its sums may be ordered differently from a
+ * single call (equal up to rounding; each plan is run-to-run deterministic).
  *
  * nq_seq_create: host-only planning.  `layers`, `xs`, `ys` are host arrays of
  *   n entries (the nq_lrb structs are copied; xs[i], ys[i] are device

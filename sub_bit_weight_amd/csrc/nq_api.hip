@@ -85,14 +85,17 @@ bool decode_xor() {
   return e && strcmp(e, "xor") == 0;
 }
 
-size_t linear_workspace(const nq_lrb& L, int64_t T) {
-  if (T > kDecodeMaxT) return prefill_workspace_bytes(L, T);
+// in_seq: the linear is an entry of a sequence plan, whose entries run
+// concurrently; the matrix-core regime then never splits a reduction (the
+// entries fill the chip together, and a split only adds partial-sum traffic).
+size_t linear_workspace(const nq_lrb& L, int64_t T, bool in_seq = false) {
+  if (T > kDecodeMaxT) return prefill_workspace_bytes(L, T, !in_seq);
   return decode_xor() ? decode_workspace_bytes(L, T) : lut_workspace_bytes(L, T);
 }
 
 hipError_t launch_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
-                         hipStream_t s) {
-  if (T > kDecodeMaxT) return launch_prefill(L, x, xd, T, y, ws, s);
+                         hipStream_t s, bool in_seq = false) {
+  if (T > kDecodeMaxT) return launch_prefill(L, x, xd, T, y, ws, s, !in_seq);
   return decode_xor() ? launch_decode(L, x, xd, T, y, ws, s) : launch_lut_linear(L, x, xd, T, y, ws, s);
 }
 
@@ -292,7 +295,7 @@ nq_status nq_seq_create(const nq_lrb* layers, const void* const* xs, float* cons
     s->layers.push_back(layers[i]);
     s->xs.push_back(xs[i]);
     s->ys.push_back(ys[i]);
-    s->ws_bytes = std::max<size_t>(s->ws_bytes, linear_workspace(layers[i], T));
+    s->ws_bytes = std::max<size_t>(s->ws_bytes, linear_workspace(layers[i], T, true));
   }
   if (T <= kDecodeMaxT && !decode_xor()) {
     plan_persistent(s);
@@ -350,7 +353,7 @@ nq_status nq_seq_run(nq_seq* s, void* workspace, size_t workspace_bytes, void* s
   for (size_t i = 0; i < s->layers.size() && e == hipSuccess; ++i) {
     const int l = (int)(i % s->nlanes);
     e = launch_linear(s->layers[i], s->xs[i], s->xd, s->T, s->ys[i], static_cast<char*>(workspace) + l * s->lane_ws,
-                      s->lanes[l]);
+                      s->lanes[l], true);
   }
   // join: the caller's stream waits for every lane
   for (int l = 0; l < s->nlanes && e == hipSuccess; ++l) {

@@ -84,8 +84,10 @@ hipError_t launch_lut_persistent(const StageDesc* segs, int nseg, int ntiles, in
                                  int64_t T, int grid, hipStream_t s);
 
 // Matrix-core regime (T > 8).
-size_t prefill_workspace_bytes(const nq_lrb& L, int64_t T);
+// split = false: never split a GEMM's reduction (entries of a sequence run
+// concurrently and fill the chip together).
+size_t prefill_workspace_bytes(const nq_lrb& L, int64_t T, bool split = true);
 hipError_t launch_prefill(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y,
-                          void* ws, hipStream_t s);
+                          void* ws, hipStream_t s, bool split = true);
 
 }  // namespace nq

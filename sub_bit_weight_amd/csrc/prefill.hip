@@ -592,11 +592,11 @@ struct Split {
   int kts;  // 64-deep reduction tiles per piece
 };
 
-Split split_plan(int64_t M, int64_t N, int64_t Kpad) {
+Split split_plan(int64_t M, int64_t N, int64_t Kpad, bool allow) {
   const int64_t tiles = cdiv(M, kTileRows) * cdiv(N, kBN);
   const int nk = (int)(Kpad / kBK);
   int n = 1;
-  while (n < kMaxSplit && tiles * n * 2 <= kWgSlots && nk / (n * 2) >= kMinSplitTiles) n *= 2;
+  while (allow && n < kMaxSplit && tiles * n * 2 <= kWgSlots && nk / (n * 2) >= kMinSplitTiles) n *= 2;
   const int kts = (int)cdiv(nk, n);
   return {(int)cdiv(nk, kts), kts};
 }
@@ -640,13 +640,13 @@ struct PrefillLayout {
 // correction sums (per reduction piece and row), t (one copy per reduction
 // piece of stage 1), the same three for t, and the partial outputs of stage 2
 // when its reduction is split.
-PrefillLayout prefill_layout(const nq_lrb& L, int64_t T, nq_dtype xd) {
+PrefillLayout prefill_layout(const nq_lrb& L, int64_t T, nq_dtype xd, bool split) {
   PrefillLayout d;
   d.nt = xd == NQ_F32 ? 2 : 1;
   d.kpad1 = round_up(L.d_in, kBK);
   d.kpad2 = round_up(L.r, kBK);
-  d.sp1 = split_plan(T, L.r, d.kpad1);
-  d.sp2 = split_plan(T, L.d_out, d.kpad2);
+  d.sp1 = split_plan(T, L.r, d.kpad1, split);
+  d.sp2 = split_plan(T, L.d_out, d.kpad2, split);
   size_t off = 0;
   d.off_z = off;
   off = align_up(off + (size_t)d.nt * T * d.kpad1 * sizeof(_Float16));
@@ -670,14 +670,14 @@ PrefillLayout prefill_layout(const nq_lrb& L, int64_t T, nq_dtype xd) {
 
 }  // namespace
 
-size_t prefill_workspace_bytes(const nq_lrb& L, int64_t T) {
+size_t prefill_workspace_bytes(const nq_lrb& L, int64_t T, bool split) {
   // sized for the larger (fp32 activation) plan so one size serves both dtypes
-  return prefill_layout(L, T, NQ_F32).total;
+  return prefill_layout(L, T, NQ_F32, split).total;
 }
 
 hipError_t launch_prefill(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
-                          hipStream_t s) {
-  const PrefillLayout d = prefill_layout(L, T, xd);
+                          hipStream_t s, bool split) {
+  const PrefillLayout d = prefill_layout(L, T, xd, split);
   char* base = static_cast<char*>(ws);
   _Float16* z = reinterpret_cast<_Float16*>(base + d.off_z);
   int* e1 = reinterpret_cast<int*>(base + d.off_e1);

@@ -185,21 +185,28 @@ def test_sequence_prefill_streams():
               synth.LayerShape("c", 200, 96, 33), synth.LayerShape("d", 1024, 768, 256),
               synth.LayerShape("e", 96, 300, 40), synth.LayerShape("f", 512, 1024, 256),
               synth.LayerShape("g", 65, 129, 31)]
-    layers = [G.latent_layer(cfg, s, i)[0] for i, s in enumerate(shapes)]
+    built = [G.latent_layer(cfg, s, i) for i, s in enumerate(shapes)]
     T = 100
-    src = [G.to_device_x(synth.activations(f"seqpf/x/{i}", T, s.d_in, "bf16"), "bf16") for i, s in enumerate(shapes)]
+    x_np = [synth.activations(f"seqpf/x/{i}", T, s.d_in, "bf16") for i, s in enumerate(shapes)]
+    src = [G.to_device_x(x, "bf16") for x in x_np]
     xs = [torch.zeros_like(x) for x in src]
     ys = [torch.full((T, s.d_out), float("nan"), device=G.DEV) for s in shapes]
-    seq = nq.Seq(layers, xs, ys)
+    seq = nq.Seq([b[0] for b in built], xs, ys)
+    first = None
     for rep in range(2):
         for x, x0 in zip(xs, src):
-            x.copy_(x0 * (rep + 1))
+            x.copy_(x0 * (rep + 1))  # exact in bf16
         seq.run()
         got = [y.clone() for y in ys]
         torch.cuda.synchronize()
-        for L, x0, g in zip(layers, src, got):
-            want = nq.lrb_linear(L, x0 * (rep + 1))
-            assert torch.equal(g.view(torch.int32), want.view(torch.int32))
+        for (dev, ref, _), x, g in zip(built, x_np, got):
+            err = O.rel_err(g.cpu().numpy(), O.linear_ref(ref, x * (rep + 1)))
+            assert err <= G.tol_for(T, "bf16"), err
+        if rep == 0:
+            first = got
+    # run-to-run determinism of the plan (inputs doubled: outputs exactly doubled)
+    for a, b in zip(first, got):
+        assert torch.equal((a * 2).view(torch.int32), b.view(torch.int32))
     seq.close()
 
 
