@@ -74,6 +74,23 @@ __device__ inline V gload(const V* p) {
   return *(gptr)(p);
 }
 
+// Values that other workgroups read during the same launch (partial sums and
+// the stage-1 result t) are written with agent-scope stores (sc1).  Such a
+// store writes through to the device coherence point by itself, so once every
+// thread's stores have completed (vmcnt 0) and the workgroup has met at a
+// barrier, a relaxed counter increment hands them over; the readers still
+// acquire (invalidate) before reading.  An agent-scope release fence would
+// instead write back every dirty line of the XCD's L2 on each tile.
+__device__ inline void store_agent(float* p, float v) {
+  typedef __attribute__((address_space(1))) float* gptr;
+  __hip_atomic_store((gptr)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this thread's stores have completed, then meet the workgroup.
+__device__ inline void stores_done_barrier() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+  __syncthreads();
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
 // outstanding global load, which would drain the sign words kept in flight.
 __device__ inline void lds_barrier() {
@@ -411,16 +428,21 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
     if (valid) {
       const float sc = S.rowscale ? S.rowscale[o] : 1.0f;
 #pragma unroll
-      for (int t = 0; t < T; ++t) S.out[(int64_t)t * S.n_rows + o] = sc * acc[t];
+      for (int t = 0; t < T; ++t) {
+        float* dst = S.out + (int64_t)t * S.n_rows + o;
+        if (S.signal)
+          store_agent(dst, sc * acc[t]);
+        else
+          *dst = sc * acc[t];
+      }
     }
   } else {
     if (valid) {
 #pragma unroll
-      for (int t = 0; t < T; ++t) S.part[((int64_t)ks * T + t) * S.n_rows + o] = acc[t];
+      for (int t = 0; t < T; ++t) store_agent(S.part + ((int64_t)ks * T + t) * S.n_rows + o, acc[t]);
     }
-    __syncthreads();
+    stores_done_barrier();  // this workgroup's partial sums are at the coherence point
     if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // publish this workgroup's partial sums
       *s_flag = (atomicAdd(&S.rb_count[rb], 1) == S.nks - 1);
       if (*s_flag) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see the other spans' sums
     }
@@ -435,17 +457,18 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
       for (int t = 0; t < T; ++t) {
         float sum = 0.0f;
         for (int c = 0; c < S.nks; ++c) sum += S.part[((int64_t)c * T + t) * S.n_rows + o];
-        S.out[(int64_t)t * S.n_rows + o] = sc * sum;
+        float* dst = S.out + (int64_t)t * S.n_rows + o;
+        if (S.signal)
+          store_agent(dst, sc * sum);
+        else
+          *dst = sc * sum;
       }
     }
     if (tid == 0) S.rb_count[rb] = 0;  // all arrivals happened: ready for the next run
   }
   if (S.signal) {
-    __syncthreads();
-    if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // publish the final row block
-      atomicAdd(S.signal, 1);
-    }
+    stores_done_barrier();  // the final row block is at the coherence point
+    if (tid == 0) atomicAdd(S.signal, 1);
   }
   __syncthreads();
 }
