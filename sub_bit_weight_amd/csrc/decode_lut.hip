@@ -352,78 +352,33 @@ __device__ inline void chunk_words2(__amdgpu_buffer_rsrc_t bits, uint32_t lane_b
   }
 }
 
-// One tile: row block rb (one row per lane) over reduction span ks of stage S.
-template <int T>
-__device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag, int* err) {
-  using G = Geo<T>;
-  const int tid = threadIdx.x;
-  const int rb = local % S.nrb;
-  const int ks = local / S.nrb;
-  const int64_t span0 = (int64_t)ks * S.kc;                 // this tile's reduction span
-  const int64_t span1 = imin(span0 + S.kc, S.n_red);
-  const int64_t o = (int64_t)rb * kRows + tid;
-  const bool valid = o < S.n_rows;
-  // word-row indices and the row stride in bytes, as wave-uniform 32-bit values
-  const int w0 = __builtin_amdgcn_readfirstlane((int)(span0 / kWordBits));
-  const int wlast = __builtin_amdgcn_readfirstlane((int)(cdiv(S.n_red, kWordBits) - 1));  // last word row
-  const uint32_t ld4 = __builtin_amdgcn_readfirstlane((uint32_t)(S.ld * 4));
-  // lanes past the last row read row n_rows-1 and store nothing
-  const uint32_t lane_bytes = 4u * (uint32_t)(valid ? o : S.n_rows - 1);
-  const __amdgpu_buffer_rsrc_t wrsrc = word_rsrc(S.bits);
-  const int nchunks = (int)cdiv(span1 - span0, 4 * G::GMAX);
-
-  if (S.wait_ctr) {
-    if (tid == 0) {
-      // poll with relaxed loads (an acquire per poll would invalidate caches
-      // that streaming workgroups are using), then acquire once
-      unsigned spins = 0;
-      while (__hip_atomic_load(S.wait_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < S.wait_target) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > kSpinLimit) {
-          atomicOr(err, 1);
-          break;
-        }
+// A stage-2 tile of a sequence waits until every row block of its linear's
+// stage 1 is final.  Thread 0 polls with relaxed loads (an acquire per poll
+// would invalidate caches that streaming workgroups are using), then acquires
+// once; the barrier releases the workgroup.
+__device__ inline void wait_input(const StageDesc& S, int* err) {
+  if (!S.wait_ctr) return;
+  if (threadIdx.x == 0) {
+    unsigned spins = 0;
+    while (__hip_atomic_load(S.wait_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < S.wait_target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) {
+        atomicOr(err, 1);
+        break;
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
+  __syncthreads();
+}
 
-  // fill the ring with the first D batches (independent of the tables)
-  uint32_t ring[G::D][G::B];
-#pragma unroll
-  for (int d = 0; d < G::D; ++d)
-#pragma unroll
-    for (int j = 0; j < G::B; ++j) ring[d][j] = load_word(wrsrc, lane_bytes, min(w0 + d * G::B + j, wlast), ld4);
-
-  TableInputs<T> in;
-  load_inputs<T>(S, span0, span1, in);
-
-  float acc[2 * G::NQ * G::TT];  // [even/odd nibbles][token]
-#pragma unroll
-  for (int t = 0; t < 2 * G::NQ * G::TT; ++t) acc[t] = 0.0f;
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int64_t c0 = span0 + (int64_t)c * 4 * G::GMAX;
-    lds_barrier();  // everyone is done with the previous chunk's tables
-    build_tables<T>(in, c0, span1, S.x_bf16, lut);
-    if (c + 1 < nchunks) load_inputs<T>(S, c0 + 4 * G::GMAX, span1, in);  // next chunk's inputs
-    lds_barrier();
-    const int wnext = w0 + c * (G::CW) + G::D * G::B;  // first word not yet in the ring
-    const int nwords = (int)imin(G::CW, cdiv(span1 - c0, kWordBits));  // words of this chunk
-    float first[8][G::NQ * G::TT];
-    read_entries<T, 0>(ring[0][0], lut, first);
-    if constexpr (T == 1) {
-      float second[8][G::NQ * G::TT];
-      read_entries<T, 1>(ring[0][1], lut, second);
-      chunk_words2<T, 0>(wrsrc, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, first, second);
-    } else {
-      chunk_words<T, 0>(wrsrc, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, first);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < G::NQ * G::TT; ++t) acc[t] += acc[G::NQ * G::TT + t];
-
+// End of a tile, one output row per thread (acc[t] = this tile's sum for row o,
+// token t): store the row (times the row scale), or publish the span's partial
+// sums and let the last span of the row block add them in span order.  Every
+// thread of the workgroup must call it; it ends with a barrier.
+template <int T>
+__device__ void finish_rows(const StageDesc& S, int rb, int ks, int64_t o, bool valid, const float* acc, int* s_flag) {
+  const int tid = threadIdx.x;
   if (S.nks == 1) {
     if (valid) {
       const float sc = S.rowscale ? S.rowscale[o] : 1.0f;
@@ -473,15 +428,409 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
   __syncthreads();
 }
 
+// One tile: row block rb (one row per lane) over reduction span ks of stage S.
+template <int T>
+__device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag, int* err) {
+  using G = Geo<T>;
+  const int tid = threadIdx.x;
+  const int rb = local % S.nrb;
+  const int ks = local / S.nrb;
+  const int64_t span0 = (int64_t)ks * S.kc;                 // this tile's reduction span
+  const int64_t span1 = imin(span0 + S.kc, S.n_red);
+  const int64_t o = (int64_t)rb * kRows + tid;
+  const bool valid = o < S.n_rows;
+  // word-row indices and the row stride in bytes, as wave-uniform 32-bit values
+  const int w0 = __builtin_amdgcn_readfirstlane((int)(span0 / kWordBits));
+  const int wlast = __builtin_amdgcn_readfirstlane((int)(cdiv(S.n_red, kWordBits) - 1));  // last word row
+  const uint32_t ld4 = __builtin_amdgcn_readfirstlane((uint32_t)(S.ld * 4));
+  // lanes past the last row read row n_rows-1 and store nothing
+  const uint32_t lane_bytes = 4u * (uint32_t)(valid ? o : S.n_rows - 1);
+  const __amdgpu_buffer_rsrc_t wrsrc = word_rsrc(S.bits);
+  const int nchunks = (int)cdiv(span1 - span0, 4 * G::GMAX);
+
+  wait_input(S, err);
+
+  // fill the ring with the first D batches (independent of the tables)
+  uint32_t ring[G::D][G::B];
+#pragma unroll
+  for (int d = 0; d < G::D; ++d)
+#pragma unroll
+    for (int j = 0; j < G::B; ++j) ring[d][j] = load_word(wrsrc, lane_bytes, min(w0 + d * G::B + j, wlast), ld4);
+
+  TableInputs<T> in;
+  load_inputs<T>(S, span0, span1, in);
+
+  float acc[2 * G::NQ * G::TT];  // [even/odd nibbles][token]
+#pragma unroll
+  for (int t = 0; t < 2 * G::NQ * G::TT; ++t) acc[t] = 0.0f;
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int64_t c0 = span0 + (int64_t)c * 4 * G::GMAX;
+    lds_barrier();  // everyone is done with the previous chunk's tables
+    build_tables<T>(in, c0, span1, S.x_bf16, lut);
+    if (c + 1 < nchunks) load_inputs<T>(S, c0 + 4 * G::GMAX, span1, in);  // next chunk's inputs
+    lds_barrier();
+    const int wnext = w0 + c * (G::CW) + G::D * G::B;  // first word not yet in the ring
+    const int nwords = (int)imin(G::CW, cdiv(span1 - c0, kWordBits));  // words of this chunk
+    float first[8][G::NQ * G::TT];
+    read_entries<T, 0>(ring[0][0], lut, first);
+    if constexpr (T == 1) {
+      float second[8][G::NQ * G::TT];
+      read_entries<T, 1>(ring[0][1], lut, second);
+      chunk_words2<T, 0>(wrsrc, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, first, second);
+    } else {
+      chunk_words<T, 0>(wrsrc, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, first);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < G::NQ * G::TT; ++t) acc[t] += acc[G::NQ * G::TT + t];
+
+  finish_rows<T>(S, rb, ks, o, valid, acc, s_flag);
+}
+
+
+// ------------------------------------------------- matrix-core tiles (T <= 2)
+//
+// For one or two tokens the lookups above are bound by the LDS instruction
+// rate (eight 4-byte lookups per sign word and lane).  These tiles run the
+// sign matrix through the matrix cores instead:
+//  * A sign word becomes four dwords of fp4 (e2m1) values: dword j holds, in
+//    nibble i, element 4i+3-j as +1.0 (0x2) or -1.0 (0xA): the word shifted
+//    left by j (j adds), masked to bit 3 of every nibble, ORed with 0x2 in
+//    every nibble.  That is eleven full-rate VALU operations per word.
+//  * The inputs v = colscale (.) x are cut into fp8 (e4m3) pieces:
+//    v * 2^s = q0 + q1/16 + q2/256 + ... (each q the round-to-nearest fp8 of
+//    the scaled remainder), six pieces per token, each piece a matrix column.
+//    2^s brings the chunk's largest |v| into [64, 128), so no piece saturates;
+//    the six pieces carry v to about 2^-24 of that largest value.
+//  * One v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 A, fp8 B, unit scales) then
+//    gives, for 16 rows and 128 reduction elements, the signed sums of every
+//    piece of every token.  Products of +-1 and fp8 values are exact and
+//    accumulate in fp32; each chunk's sums are scaled back by 2^-(s+4p) and
+//    added up per column, the pieces of a token are added across lanes at the
+//    end of the tile.
+// Operand layouts of the 16x16x128 fp4 x fp8 form (measured on the device):
+// lane l holds A row l%16, reduction elements 32*(l/16) + [0, 32) as nibbles
+// (dword d, nibble i = element 8d+i); B column l%16, elements 16*(l/16) +
+// [0, 16) in bytes 0..15 and 64 + 16*(l/16) + [0, 16) in bytes 16..31; C
+// column l%16, rows 4*(l/16) + [0, 4).
+//
+// A workgroup covers 256 rows: each wave 64 rows as four sets of 16.  Lane
+// l of set q reads the word of row 16q + l%16 in word row 4k + l/16 for MFMA
+// step k (128 elements), so one word per lane and step feeds one MFMA.  The B
+// fragments of a chunk of 8 steps are built in LDS by the whole workgroup.
+
+constexpr int kMfmaMaxT = 2;
+constexpr int kPieces = 6;                            // fp8 pieces per token
+constexpr int kStepWords = 4;                         // word rows per MFMA step
+constexpr int kChunkSteps = 8;                        // steps per staged chunk
+constexpr int kChunkWords = kChunkSteps * kStepWords;  // 32 word rows
+constexpr int kStepInts = 64 * 8;                     // B fragments of one step (64 lanes x 32 bytes)
+constexpr int kBInts = kChunkSteps * kStepInts;       // B fragments of a chunk (16 KiB)
+constexpr int kSlotOff = kBInts;                      // per-chunk maxima: [2 slots][kMfmaMaxT]
+constexpr int kSumOff = kBInts + 16;                  // row sums [kMfmaMaxT][kRows]
+constexpr int kMfmaLds = kSumOff + kMfmaMaxT * kRows;  // 4-byte words of LDS per workgroup
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int T>
+struct MfmaIn {
+  uint32_t x[T][4];  // raw bf16 / fp32 bits of this thread's 4 elements
+  float cs[4];
+};
+
+// This thread's build task within a chunk: word row wr (0..31), dword j of
+// the A expansion, half ih of the nibbles: elements 32*wr + 4*(4*ih + k) +
+// 3 - j, k = 0..3, i.e. one B dword (4 consecutive reduction positions).
+__device__ inline int task_element(int k) {
+  const int tid = threadIdx.x;
+  const int wr = tid >> 3, j = (tid >> 1) & 3, ih = tid & 1;
+  return 32 * wr + 4 * (4 * ih + k) + 3 - j;
+}
+
+template <int T>
+__device__ inline void mfma_load_inputs(const StageDesc& S, int64_t c0, int64_t cend, MfmaIn<T>& in) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t e = c0 + task_element(k);
+    const int64_t ec = e < cend ? e : c0;  // in-bounds index; the value is dropped when e >= cend
+    in.cs[k] = S.colscale ? gload(S.colscale + ec) : 1.0f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int64_t idx = (int64_t)t * S.n_red + ec;
+      in.x[t][k] = S.x_bf16 ? (uint32_t)gload(static_cast<const uint16_t*>(S.xin) + idx)
+                            : gload(static_cast<const uint32_t*>(S.xin) + idx);
+    }
+  }
+}
+
+template <int T>
+__device__ inline float mfma_value(const StageDesc& S, const MfmaIn<T>& in, int64_t c0, int64_t cend, int t, int k) {
+  const float x = S.x_bf16 ? bf16_bits(in.x[t][k]) : __uint_as_float(in.x[t][k]);
+  return c0 + task_element(k) < cend ? x * in.cs[k] : 0.0f;
+}
+
+// Largest |v| of the chunk per token into slot[t] (float bits of a
+// non-negative value order like unsigned integers; NaN orders above inf).
+template <int T>
+__device__ inline void mfma_chunk_max(const StageDesc& S, const MfmaIn<T>& in, int64_t c0, int64_t cend,
+                                      unsigned* slot) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    unsigned m = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, __float_as_uint(fabsf(mfma_value<T>(S, in, c0, cend, t, k))));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off));
+    if ((threadIdx.x & 63) == 0) atomicMax(slot + t, m);
+  }
+}
+
+// Scale exponent for a chunk maximum (bits): max * 2^s in [64, 128).
+__device__ inline int chunk_shift(unsigned mbits) {
+  const int e = (int)((mbits >> 23) & 0xFF);
+  return e == 255 ? 0 : 133 - e;
+}
+
+// Zero the subnormal bytes (exponent field 0) of four packed e4m3 values.
+// The matrix cores do not count subnormal fp8 inputs at full value, so a
+// piece keeps only normal values; what it drops stays in the remainder and
+// reaches a later piece (scaled by 16 per piece) instead.
+__device__ inline int drop_subnormal_fp8(int d) {
+  const uint32_t u = (uint32_t)d;
+  const uint32_t normal = ((u & 0x78787878u) + 0x78787878u) & 0x80808080u;  // bit 7: exponent != 0
+  return (int)(u & (normal | (normal - (normal >> 7))));
+}
+
+// Write this thread's B dwords of the chunk: one per piece and token.
+template <int T>
+__device__ inline void mfma_build(const StageDesc& S, const MfmaIn<T>& in, int64_t c0, int64_t cend,
+                                  const int (&shift)[T], int* lds) {
+  const int tid = threadIdx.x;
+  const int wr = tid >> 3, j = (tid >> 1) & 3, ih = tid & 1;
+  const int kk = wr >> 2, gw = wr & 3;
+  const int gp = 2 * (gw & 1) + (j >> 1);
+  int* dst = lds + kk * kStepInts + (gw >> 1) * 256 + 16 * gp * 4 + 2 * (j & 1) + ih;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = ldexpf(mfma_value<T>(S, in, c0, cend, t, k), shift[t]);
+#pragma unroll
+    for (int p = 0; p < kPieces; ++p) {
+      int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+      d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
+      d = drop_subnormal_fp8(d);
+      dst[(t * kPieces + p) * 4] = d;
+      if (p + 1 < kPieces) {
+        typedef float v2f __attribute__((ext_vector_type(2)));
+        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
+        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
+        r[0] = (r[0] - lo.x) * 16.0f;
+        r[1] = (r[1] - lo.y) * 16.0f;
+        r[2] = (r[2] - hi.x) * 16.0f;
+        r[3] = (r[3] - hi.y) * 16.0f;
+      }
+    }
+  }
+}
+
+// B columns past the last piece of the last token stay zero for the life of
+// the kernel (the builds never write them): clear them once.
+template <int T>
+__device__ inline void mfma_lds_init(int* lds) {
+  constexpr int NC = T * kPieces;
+  if constexpr (NC < 16) {
+    // per step and half: 64 lanes x 4 dwords; lane = column + 16 * group
+    for (int i = threadIdx.x; i < kChunkSteps * 2 * 64 * 4; i += kRows) {
+      const int lane = (i >> 2) & 63;
+      if ((lane & 15) >= NC) lds[i] = 0;
+    }
+  }
+}
+
+// Four fp4 dwords of one sign word (see above).
+// x + x as an add (the compiler would turn it into a shift, which issues at
+// half the rate of an add on this chip).
+__device__ inline uint32_t twice(uint32_t x) {
+  uint32_t y;
+  asm("v_add_u32_e32 %0, %1, %1" : "=v"(y) : "v"(x));
+  return y;
+}
+
+__device__ inline v8i expand_word(uint32_t x) {
+  const uint32_t x1 = twice(x), x2 = twice(x1), x3 = twice(x2);
+  v8i a;
+  a[0] = (int)((x & 0x88888888u) | 0x22222222u);
+  a[1] = (int)((x1 & 0x88888888u) | 0x22222222u);
+  a[2] = (int)((x2 & 0x88888888u) | 0x22222222u);
+  a[3] = (int)((x3 & 0x88888888u) | 0x22222222u);
+  a[4] = a[5] = a[6] = a[7] = 0;
+  return a;
+}
+
+// Sum over the 16 lanes of a row of the wavefront (DPP rotations).
+__device__ inline float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));  // row_ror:2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));  // row_ror:1
+  return v;
+}
+
+template <int T>
+__device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_flag, int* err) {
+  static_assert(T <= kMfmaMaxT && T * kPieces <= 16, "columns");
+  int* lds = reinterpret_cast<int*>(ldsf);
+  unsigned* slots = reinterpret_cast<unsigned*>(lds + kSlotOff);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, col = lane & 15, grp = lane >> 4;
+  const int rb = local % S.nrb;
+  const int ks = local / S.nrb;
+  const int64_t span0 = (int64_t)ks * S.kc;
+  const int64_t span1 = imin(span0 + S.kc, S.n_red);
+  const int w0 = __builtin_amdgcn_readfirstlane((int)(span0 / kWordBits));
+  const uint32_t ld4 = __builtin_amdgcn_readfirstlane((uint32_t)(S.ld * 4));
+  const int nw = (int)cdiv(span1 - span0, kWordBits);
+  const int nk = (nw + kStepWords - 1) / kStepWords;
+  const int nchunks = (nw + kChunkWords - 1) / kChunkWords;
+
+  // per row set: byte offset of this lane's word from word row 4k (rows past
+  // the last read row n_rows-1; their sums are never stored)
+  uint32_t voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t row = (int64_t)rb * kRows + wv * 64 + q * 16 + col;
+    voff[q] = 4u * (uint32_t)(row < S.n_rows ? row : S.n_rows - 1) + (uint32_t)grp * ld4;
+  }
+  // step k reads word row 4k + grp of the span for every row set, through a
+  // buffer resource that starts at word row 4k and ends with the span: word
+  // rows past the span (a partial last step, or steps past the last) are out
+  // of range and read as 0 without touching memory, and meet zero B entries.
+  // Everything but the lane offsets is scalar.
+  auto load_step = [&](int k, uint32_t (&dst)[4]) {
+    const int wb = kStepWords * k;  // from the span start
+    const int rows_left = max(nw - wb, 0);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(S.bits) + (int64_t)(w0 + wb) * S.ld, (short)0, (int)((uint32_t)rows_left * ld4),
+        0x00020000);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff[q], 0, 0);
+  };
+
+  uint32_t ring[kChunkSteps][4];
+#pragma unroll
+  for (int k = 0; k < kChunkSteps; ++k) load_step(k, ring[k]);
+
+  wait_input(S, err);
+  MfmaIn<T> in;
+  mfma_load_inputs<T>(S, span0, span1, in);
+  if (tid < 2 * kMfmaMaxT) slots[tid] = 0;
+  __syncthreads();
+  mfma_chunk_max<T>(S, in, span0, span1, slots);
+  __syncthreads();
+
+  float total[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) total[q][r] = 0.0f;
+  const int tcol = col / kPieces, pcol = col % kPieces;  // this lane's column: token, piece
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int64_t c0 = span0 + (int64_t)c * kChunkWords * kWordBits;
+    int shift[T];
+    float fscale = 0.0f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const unsigned mb = slots[(c & 1) * kMfmaMaxT + t];
+      shift[t] = chunk_shift(mb);
+      if (tcol == t) fscale = ((mb >> 23) & 0xFF) == 255 ? __int_as_float(0x7FC00000) : ldexpf(1.0f, -(shift[t] + 4 * pcol));
+    }
+    mfma_build<T>(S, in, c0, span1, shift, lds);
+    if (c + 1 < nchunks) mfma_load_inputs<T>(S, c0 + kChunkWords * kWordBits, span1, in);
+    __syncthreads();  // B fragments of chunk c are in LDS
+    if (tid == 0)
+#pragma unroll
+      for (int t = 0; t < T; ++t) slots[(c & 1) * kMfmaMaxT + t] = 0;  // reused by chunk c+2
+
+    v4f acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < kChunkSteps; ++kk) {
+      const int k = c * kChunkSteps + kk;
+      if (k >= nk) break;
+      const uint4 blo = reinterpret_cast<const uint4*>(lds)[kk * (kStepInts / 4) + lane];
+      const uint4 bhi = reinterpret_cast<const uint4*>(lds)[kk * (kStepInts / 4) + 64 + lane];
+      v8i b;
+      b[0] = (int)blo.x; b[1] = (int)blo.y; b[2] = (int)blo.z; b[3] = (int)blo.w;
+      b[4] = (int)bhi.x; b[5] = (int)bhi.y; b[6] = (int)bhi.z; b[7] = (int)bhi.w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(expand_word(ring[kk][q]), b, acc[q], 4, 0, 0, 127, 0,
+                                                                  127);
+      load_step(k + kChunkSteps, ring[kk]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) total[q][r] = fmaf(acc[q][r], fscale, total[q][r]);
+    if (c + 1 < nchunks)
+      mfma_chunk_max<T>(S, in, c0 + kChunkWords * kWordBits, span1, slots + ((c + 1) & 1) * kMfmaMaxT);
+    __syncthreads();  // every wave is done with chunk c's B fragments
+  }
+
+  // add the pieces of each token across the lanes of a row; lane col == 0
+  // of every row group writes its 4 rows of every set
+  float* sums = ldsf + kSumOff;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = row16_sum(tcol == t ? total[q][r] : 0.0f);
+      if (col == 0)
+        *reinterpret_cast<float4*>(sums + t * kRows + wv * 64 + q * 16 + grp * 4) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+  __syncthreads();
+  float accr[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) accr[t] = sums[t * kRows + tid];
+  const int64_t o = (int64_t)rb * kRows + tid;
+  finish_rows<T>(S, rb, ks, o, o < S.n_rows, accr, s_flag);
+}
+
 // The workgroup's two shared flag words live in the first entries of the
 // table array: every write to them follows a barrier after the last table
 // read of a tile, and every read precedes the barrier before the next tables
 // are built.
 template <int T>
+constexpr bool use_mfma() { return T <= kMfmaMaxT; }
+template <int T>
+constexpr int stage_lds_floats() { return use_mfma<T>() ? kMfmaLds : Geo<T>::LUT; }
+
+template <int T>
+__device__ inline void stage_init(float* lds) {
+  if constexpr (use_mfma<T>()) mfma_lds_init<T>(reinterpret_cast<int*>(lds));
+}
+template <int T>
+__device__ inline void stage_tile(const StageDesc& S, int local, float* lds, int* s_flag, int* err) {
+  if constexpr (use_mfma<T>())
+    mfma_tile<T>(S, local, lds, s_flag, err);
+  else
+    lut_tile<T>(S, local, lds, s_flag, err);
+}
+
+template <int T>
 __global__ __launch_bounds__(kRows) void lut_stage_kernel(StageDesc S, int* err) {
-  __shared__ __attribute__((aligned(16))) float lut[Geo<T>::LUT];
+  __shared__ __attribute__((aligned(16))) float lut[stage_lds_floats<T>()];
   int* s_flag = reinterpret_cast<int*>(lut);
-  lut_tile<T>(S, blockIdx.x, lut, s_flag, err);
+  stage_init<T>(lut);
+  __syncthreads();
+  stage_tile<T>(S, blockIdx.x, lut, s_flag, err);
 }
 
 // ints: [0] error flag (sticky), [1] next tile, [2] workgroups exited,
@@ -490,11 +839,12 @@ __global__ __launch_bounds__(kRows) void lut_stage_kernel(StageDesc S, int* err)
 template <int T>
 __global__ __launch_bounds__(kRows) void lut_persistent_kernel(const StageDesc* __restrict__ segs, int nseg,
                                                                int ntiles, int* ints, int n_ints) {
-  __shared__ __attribute__((aligned(16))) float lut[Geo<T>::LUT];
+  __shared__ __attribute__((aligned(16))) float lut[stage_lds_floats<T>()];
   int& s_flag = reinterpret_cast<int*>(lut)[0];  // aliases table entries (see lut_stage_kernel)
   int& s_tile = reinterpret_cast<int*>(lut)[1];
   int* err = ints;
   int* next_tile = ints + 1;
+  stage_init<T>(lut);
   if (threadIdx.x == 0) s_tile = atomicAdd(next_tile, 1);
   __syncthreads();
   int tile = s_tile;
@@ -504,7 +854,7 @@ __global__ __launch_bounds__(kRows) void lut_persistent_kernel(const StageDesc* 
     if (threadIdx.x == 0) nxt = atomicAdd(next_tile, 1);  // prefetch the next tile id
     while (seg + 1 < nseg && tile >= segs[seg + 1].tile0) ++seg;
     const StageDesc S = segs[seg];
-    lut_tile<T>(S, tile - S.tile0, lut, &s_flag, err);
+    stage_tile<T>(S, tile - S.tile0, lut, &s_flag, err);
     if (threadIdx.x == 0) s_tile = nxt;
     __syncthreads();
     tile = s_tile;
