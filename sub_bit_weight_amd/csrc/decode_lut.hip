@@ -363,7 +363,7 @@ __device__ inline void wait_input(const StageDesc& S, int* err) {
     while (__hip_atomic_load(S.wait_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < S.wait_target) {
       __builtin_amdgcn_s_sleep(2);
       if (++spins > kSpinLimit) {
-        atomicOr(err, 1);
+        if (err) atomicOr(err, 1);
         break;
       }
     }
@@ -515,21 +515,35 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
 // [0, 16) in bytes 0..15 and 64 + 16*(l/16) + [0, 16) in bytes 16..31; C
 // column l%16, rows 4*(l/16) + [0, 4).
 //
-// A workgroup covers 256 rows: each wave 64 rows as four sets of 16.  Lane
-// l of set q reads the word of row 16q + l%16 in word row 4k + l/16 for MFMA
-// step k (128 elements), so one word per lane and step feeds one MFMA.  The B
-// fragments of a chunk of 8 steps are built in LDS by the whole workgroup.
+// The pieces of a stage's input are made once per stage, by input-piece
+// tiles (one per chunk of 1024 elements), and stored in the workspace in a
+// compact form (only the 16-byte fragment blocks of the T*6 used columns);
+// every row-block tile of the stage copies them into LDS chunk by chunk.
+// (Making them in every row-block tile took about a fifth of the stream
+// rate: the loads of x and s2, the chunk maxima and the conversions.)
+//
+// A workgroup covers 256 rows: each wave 64 rows as four sets of 16, set q
+// holding rows 4m + q (m = 0..15) of the wave's 64.  For MFMA step k (128
+// elements) lane l reads the words of rows 4*(l%16) + [0, 4) in word row
+// 4k + l/16 (one 16-byte load; 16 lanes cover 256 contiguous bytes of a word
+// row), and component q feeds the MFMA of set q.
 
 constexpr int kMfmaMaxT = 2;
 constexpr int kPieces = 6;                            // fp8 pieces per token
 constexpr int kStepWords = 4;                         // word rows per MFMA step
 constexpr int kChunkSteps = 8;                        // steps per staged chunk
 constexpr int kChunkWords = kChunkSteps * kStepWords;  // 32 word rows
+constexpr int kRingSteps = 8;                         // steps of sign words in flight per lane
+static_assert(kChunkSteps % kRingSteps == 0, "ring slots are compile-time within a chunk");
 constexpr int kStepInts = 64 * 8;                     // B fragments of one step (64 lanes x 32 bytes)
 constexpr int kBInts = kChunkSteps * kStepInts;       // B fragments of a chunk (16 KiB)
-constexpr int kSlotOff = kBInts;                      // per-chunk maxima: [2 slots][kMfmaMaxT]
-constexpr int kSumOff = kBInts + 16;                  // row sums [kMfmaMaxT][kRows]
-constexpr int kMfmaLds = kSumOff + kMfmaMaxT * kRows;  // 4-byte words of LDS per workgroup
+// LDS of a workgroup, in 4-byte words: [B fragments, two chunk buffers]
+// [chunk scale exponents, two buffers of kMfmaMaxT][per-chunk maxima of an
+// input-piece tile][row sums [kMfmaMaxT][kRows]]
+constexpr int kSigOff = 2 * kBInts;
+constexpr int kSlotOff = kSigOff + 2 * kMfmaMaxT;
+constexpr int kSumOff = kSlotOff + 2 * kMfmaMaxT;
+constexpr int kMfmaLds = kSumOff + kMfmaMaxT * kRows;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -549,12 +563,15 @@ __device__ inline int task_element(int k) {
   return 32 * wr + 4 * (4 * ih + k) + 3 - j;
 }
 
+// Loads of a chunk's inputs.  Elements at or past cend read element `safe`
+// (any in-bounds index) and are dropped later, so chunks past the span can be
+// loaded too: the loads keep a fixed count and position in the pipeline.
 template <int T>
-__device__ inline void mfma_load_inputs(const StageDesc& S, int64_t c0, int64_t cend, MfmaIn<T>& in) {
+__device__ inline void mfma_load_inputs(const StageDesc& S, int64_t c0, int64_t cend, int64_t safe, MfmaIn<T>& in) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int64_t e = c0 + task_element(k);
-    const int64_t ec = e < cend ? e : c0;  // in-bounds index; the value is dropped when e >= cend
+    const int64_t ec = e < cend ? e : safe;
     in.cs[k] = S.colscale ? gload(S.colscale + ec) : 1.0f;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -587,42 +604,82 @@ __device__ inline void mfma_chunk_max(const StageDesc& S, const MfmaIn<T>& in, i
   }
 }
 
-// Scale exponent for a chunk maximum (bits): max * 2^s in [64, 128).
+// Scale exponent s for a chunk maximum (float bits): max * 2^s in [64, 128).
+// s is capped at 107 so that the MFMA scale of the last piece, 2^-(s+20),
+// stays within the E8M0 range; only chunks whose largest |v| is below 2^-81
+// start below 64 and so keep fewer significant bits.  A non-finite maximum
+// gives kShiftNaN: the chunk's pieces are NaN.
+constexpr int kShiftNaN = 1 << 20;
 __device__ inline int chunk_shift(unsigned mbits) {
   const int e = (int)((mbits >> 23) & 0xFF);
-  return e == 255 ? 0 : 133 - e;
+  return e == 255 ? kShiftNaN : min(133 - e, 107);
 }
 
-// Zero the subnormal bytes (exponent field 0) of four packed e4m3 values.
-// The matrix cores do not count subnormal fp8 inputs at full value, so a
-// piece keeps only normal values; what it drops stays in the remainder and
-// reaches a later piece (scaled by 16 per piece) instead.
-__device__ inline int drop_subnormal_fp8(int d) {
+// The 16x16x128 fp4 x fp8 MFMA adds each group of 8 consecutive products
+// (reduction positions 8m..8m+7) in a window of about 13 binades below the
+// group's leading bit, truncating what lies below it (measured on the device:
+// 128 + 7 * 1.875*2^-4 comes out 128.765625).  So a piece keeps, per group,
+// only values whose exponent is within 7 of the group's largest (their last
+// bit then lies inside the window even after the group sum carries 3 binades
+// up), and no subnormals; what it leaves stays in the remainder and reaches a
+// later piece, scaled by 16 per piece.
+// Bytes of four packed e4m3 values with exponent field < lo (1 <= lo <= 15)
+// become 0.
+__device__ inline int keep_fp8_exponents(int d, int lo) {
   const uint32_t u = (uint32_t)d;
-  const uint32_t normal = ((u & 0x78787878u) + 0x78787878u) & 0x80808080u;  // bit 7: exponent != 0
-  return (int)(u & (normal | (normal - (normal >> 7))));
+  const uint32_t bias = (uint32_t)(0x80 - 8 * lo) * 0x01010101u;  // bit 7 of (field*8 + bias): field >= lo
+  const uint32_t keep = ((u & 0x78787878u) + bias) & 0x80808080u;
+  return (int)(u & (keep | (keep - (keep >> 7))));
+}
+// Largest exponent field among the four bytes of d.
+__device__ inline int max_fp8_exponent(int d) {
+  const uint32_t u = (uint32_t)d & 0x78787878u;
+  return (int)(max(max(u & 0xFFu, (u >> 8) & 0xFFu), max((u >> 16) & 0xFFu, u >> 24)) >> 3);
 }
 
-// Write this thread's B dwords of the chunk: one per piece and token.
+// Compact piece layout of one chunk: 16-byte blocks, block
+// ((step*2 + half)*4 + group)*NC + column holds the fragment bytes of LDS
+// lane column + 16*group, half `half`, of MFMA step `step` (NC = T*6 used
+// columns; column t*6 + p is piece p of token t).
 template <int T>
-__device__ inline void mfma_build(const StageDesc& S, const MfmaIn<T>& in, int64_t c0, int64_t cend,
-                                  const int (&shift)[T], int* lds) {
+constexpr int chunk_blocks() { return kChunkSteps * 2 * 4 * T * kPieces; }
+
+// One input-piece tile: chunk `chunk` of the stage input.  Each thread makes
+// one B dword (4 consecutive reduction positions) per piece and token.
+template <int T>
+__device__ void mfma_prep_tile(const StageDesc& S, int chunk, float* ldsf, int* err) {
+  constexpr int NC = T * kPieces;
+  unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + kSlotOff);
   const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)chunk * kChunkWords * kWordBits;
+  wait_input(S, err);
+  MfmaIn<T> in;
+  mfma_load_inputs<T>(S, c0, S.n_red, 0, in);
+  if (tid < T) slots[tid] = 0;
+  __syncthreads();
+  mfma_chunk_max<T>(S, in, c0, S.n_red, slots);
+  __syncthreads();
   const int wr = tid >> 3, j = (tid >> 1) & 3, ih = tid & 1;
   const int kk = wr >> 2, gw = wr & 3;
   const int gp = 2 * (gw & 1) + (j >> 1);
-  int* dst = lds + kk * kStepInts + (gw >> 1) * 256 + 16 * gp * 4 + 2 * (j & 1) + ih;
+  uint32_t* dst = S.bfrag + ((int64_t)chunk * chunk_blocks<T>() + ((kk * 2 + (gw >> 1)) * 4 + gp) * NC) * 4 +
+                  2 * (j & 1) + ih;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
+    const int shift = chunk_shift(slots[t]);
     float r[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) r[k] = ldexpf(mfma_value<T>(S, in, c0, cend, t, k), shift[t]);
+    for (int k = 0; k < 4; ++k)
+      r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000) : ldexpf(mfma_value<T>(S, in, c0, S.n_red, t, k), shift);
 #pragma unroll
     for (int p = 0; p < kPieces; ++p) {
       int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
       d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
-      d = drop_subnormal_fp8(d);
-      dst[(t * kPieces + p) * 4] = d;
+      // this dword and the partner thread's (tid ^ 1) form one group of 8
+      int emax = max_fp8_exponent(d);
+      emax = max(emax, __shfl_xor(emax, 1));
+      d = keep_fp8_exponents(d, max(1, emax - 7));
+      store_agent(reinterpret_cast<float*>(dst + (t * kPieces + p) * 4), __int_as_float(d));
       if (p + 1 < kPieces) {
         typedef float v2f __attribute__((ext_vector_type(2)));
         const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
@@ -633,7 +690,13 @@ __device__ inline void mfma_build(const StageDesc& S, const MfmaIn<T>& in, int64
         r[3] = (r[3] - hi.y) * 16.0f;
       }
     }
+    if (tid == 0) store_agent(reinterpret_cast<float*>(S.bsig + (int64_t)chunk * T + t), __int_as_float(shift));
   }
+  if (S.signal) {
+    stores_done_barrier();  // the chunk's pieces are at the coherence point
+    if (tid == 0) atomicAdd(S.signal, 1);
+  }
+  __syncthreads();  // the slots are reused by the next tile
 }
 
 // B columns past the last piece of the last token stay zero for the life of
@@ -643,7 +706,7 @@ __device__ inline void mfma_lds_init(int* lds) {
   constexpr int NC = T * kPieces;
   if constexpr (NC < 16) {
     // per step and half: 64 lanes x 4 dwords; lane = column + 16 * group
-    for (int i = threadIdx.x; i < kChunkSteps * 2 * 64 * 4; i += kRows) {
+    for (int i = threadIdx.x; i < 2 * kBInts; i += kRows) {  // both chunk buffers
       const int lane = (i >> 2) & 63;
       if ((lane & 15) >= NC) lds[i] = 0;
     }
@@ -679,11 +742,12 @@ __device__ inline float row16_sum(float v) {
   return v;
 }
 
-template <int T>
+// W4: sign words are read 4 rows at a time (16-byte loads); otherwise one
+// word per load (row counts or strides that are not multiples of 4).
+template <int T, bool W4>
 __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_flag, int* err) {
   static_assert(T <= kMfmaMaxT && T * kPieces <= 16, "columns");
   int* lds = reinterpret_cast<int*>(ldsf);
-  unsigned* slots = reinterpret_cast<unsigned*>(lds + kSlotOff);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int rb = local % S.nrb;
   const int ks = local / S.nrb;
@@ -695,90 +759,110 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   const int nk = (nw + kStepWords - 1) / kStepWords;
   const int nchunks = (nw + kChunkWords - 1) / kChunkWords;
 
-  // per row set: byte offset of this lane's word from word row 4k (rows past
-  // the last read row n_rows-1; their sums are never stored)
-  uint32_t voff[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t row = (int64_t)rb * kRows + wv * 64 + q * 16 + col;
-    voff[q] = 4u * (uint32_t)(row < S.n_rows ? row : S.n_rows - 1) + (uint32_t)grp * ld4;
-  }
-  // step k reads word row 4k + grp of the span for every row set, through a
-  // buffer resource that starts at word row 4k and ends with the span: word
-  // rows past the span (a partial last step, or steps past the last) are out
-  // of range and read as 0 without touching memory, and meet zero B entries.
-  // Everything but the lane offsets is scalar.
-  auto load_step = [&](int k, uint32_t (&dst)[4]) {
+  // byte offset of this lane's first word from word row 4k (rows at or past
+  // n_rows are read where in range and never stored)
+  const uint32_t voff = 4u * (uint32_t)((int64_t)rb * kRows + wv * 64 + 4 * col) + (uint32_t)grp * ld4;
+  // Step k reads word row 4k + grp of the span through a buffer resource that
+  // starts at word row 4k and ends with row n_rows-1 of the span's last word
+  // row: words past the span (a partial last step, steps past the last) or
+  // past the last row are out of range and read as 0 without touching memory
+  // (with W4, n_rows is a multiple of 4, so a 16-byte load is entirely in or
+  // out of range).  Everything but the lane offset is scalar.
+  auto load_step = [&](int k, u32x4& dst) {
     const int wb = kStepWords * k;  // from the span start
     const int rows_left = max(nw - wb, 0);
+    const uint32_t nrec = rows_left > 0 ? (uint32_t)(rows_left - 1) * ld4 + 4u * (uint32_t)S.n_rows : 0u;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint32_t*>(S.bits) + (int64_t)(w0 + wb) * S.ld, (short)0, (int)((uint32_t)rows_left * ld4),
-        0x00020000);
+        const_cast<uint32_t*>(S.bits) + (int64_t)(w0 + wb) * S.ld, (short)0, (int)nrec, 0x00020000);
+    if constexpr (W4) {
+      dst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+    } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff[q], 0, 0);
+      for (int q = 0; q < 4; ++q) dst[q] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(voff + 4u * q), 0, 0);
+    }
   };
 
-  uint32_t ring[kChunkSteps][4];
+  // This thread's compact blocks of a chunk (see mfma_prep_tile) and their
+  // LDS places.  Every thread loads NBT blocks (past the chunk's last block:
+  // the last one again, written to the row-sum area, unused until the tile's
+  // end) and thread 0 the chunk's scale exponents, so no branch surrounds the
+  // loads.  Chunk c+1 is loaded during chunk c and written to the other LDS
+  // buffer half-way through it (the loads are then waited for with the sign
+  // words issued after them still in flight); one barrier per chunk.  A chunk
+  // past the stage's last loads the last one again.
+  constexpr int NB = chunk_blocks<T>();
+  constexpr int NBT = (NB + kRows - 1) / kRows;  // blocks per thread
+  constexpr int NC = T * kPieces;
+  int lds_at[NBT], blk_at[NBT];
 #pragma unroll
-  for (int k = 0; k < kChunkSteps; ++k) load_step(k, ring[k]);
-
-  wait_input(S, err);
-  MfmaIn<T> in;
-  mfma_load_inputs<T>(S, span0, span1, in);
-  if (tid < 2 * kMfmaMaxT) slots[tid] = 0;
-  __syncthreads();
-  mfma_chunk_max<T>(S, in, span0, span1, slots);
-  __syncthreads();
-
-  float total[4][4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) total[q][r] = 0.0f;
+  for (int m = 0; m < NBT; ++m) {
+    const int bi = tid + m * kRows;
+    const int n = bi % NC, rest = bi / NC;
+    const int g = rest % 4, h = (rest / 4) % 2, kk = rest / 8;
+    lds_at[m] = bi < NB ? kk * kStepInts + h * 256 + (n + 16 * g) * 4 : kSumOff;
+    blk_at[m] = min(bi, NB - 1);
+  }
+  const int chunk0 = (int)(span0 / (kChunkWords * kWordBits));
+  const int last_chunk = (int)((S.n_red - 1) / (kChunkWords * kWordBits));
+  const u32x4* bsrc = reinterpret_cast<const u32x4*>(S.bfrag);
   const int tcol = col / kPieces, pcol = col % kPieces;  // this lane's column: token, piece
+  u32x4 blk[NBT];
+  int sig;
+  auto load_chunk = [&](int ch) {
+    ch = min(ch, last_chunk);
+#pragma unroll
+    for (int m = 0; m < NBT; ++m) blk[m] = gload(bsrc + (int64_t)ch * NB + blk_at[m]);
+    sig = gload(S.bsig + (int64_t)ch * T + min(tid, T - 1));
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int m = 0; m < NBT; ++m) *reinterpret_cast<u32x4*>(lds + buf * kBInts + lds_at[m]) = blk[m];
+    if (tid < T) lds[kSigOff + buf * kMfmaMaxT + tid] = sig;
+  };
+  wait_input(S, err);  // the stage's pieces are final
+  load_chunk(chunk0);
+  store_chunk(0);
+  u32x4 ring[kRingSteps];
+#pragma unroll
+  for (int k = 0; k < kRingSteps; ++k) load_step(k, ring[k]);
+  __syncthreads();  // chunk 0's fragments are in LDS buffer 0
+
+  // the sums of all chunks accumulate in acc: each chunk's B column (token t,
+  // piece p) carries the MFMA scale 2^-(s_t + 4p) of that chunk
+  v4f acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int c = 0; c < nchunks; ++c) {
-    const int64_t c0 = span0 + (int64_t)c * kChunkWords * kWordBits;
-    int shift[T];
-    float fscale = 0.0f;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const unsigned mb = slots[(c & 1) * kMfmaMaxT + t];
-      shift[t] = chunk_shift(mb);
-      if (tcol == t) fscale = ((mb >> 23) & 0xFF) == 255 ? __int_as_float(0x7FC00000) : ldexpf(1.0f, -(shift[t] + 4 * pcol));
-    }
-    mfma_build<T>(S, in, c0, span1, shift, lds);
-    if (c + 1 < nchunks) mfma_load_inputs<T>(S, c0 + kChunkWords * kWordBits, span1, in);
-    __syncthreads();  // B fragments of chunk c are in LDS
-    if (tid == 0)
-#pragma unroll
-      for (int t = 0; t < T; ++t) slots[(c & 1) * kMfmaMaxT + t] = 0;  // reused by chunk c+2
+    const int buf = c & 1;
+    // E8M0 scale of this lane's column (2^0 for columns past the last piece,
+    // whose B entries are 0; a NaN chunk has NaN pieces)
+    const int sg = lds[kSigOff + buf * kMfmaMaxT + min(tcol, T - 1)];
+    const int bscale = tcol < T ? 127 - (sg == kShiftNaN ? 0 : sg) - 4 * pcol : 127;
+    load_chunk(chunk0 + c + 1);  // next chunk's pieces (or none)
 
-    v4f acc[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    const u32x4* bfrag = reinterpret_cast<const u32x4*>(lds + buf * kBInts) + lane;
+    u32x4 blo = bfrag[0], bhi = bfrag[64];
 #pragma unroll
     for (int kk = 0; kk < kChunkSteps; ++kk) {
       const int k = c * kChunkSteps + kk;
-      if (k >= nk) break;
-      const uint4 blo = reinterpret_cast<const uint4*>(lds)[kk * (kStepInts / 4) + lane];
-      const uint4 bhi = reinterpret_cast<const uint4*>(lds)[kk * (kStepInts / 4) + 64 + lane];
       v8i b;
       b[0] = (int)blo.x; b[1] = (int)blo.y; b[2] = (int)blo.z; b[3] = (int)blo.w;
       b[4] = (int)bhi.x; b[5] = (int)bhi.y; b[6] = (int)bhi.z; b[7] = (int)bhi.w;
+      if (kk + 1 < kChunkSteps) {  // next step's fragments (stale past the span; then unused)
+        blo = bfrag[(kk + 1) * (kStepInts / 4)];
+        bhi = bfrag[(kk + 1) * (kStepInts / 4) + 64];
+      }
+      if (k < nk) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(expand_word(ring[kk][q]), b, acc[q], 4, 0, 0, 127, 0,
-                                                                  127);
-      load_step(k + kChunkSteps, ring[kk]);
+        for (int q = 0; q < 4; ++q)
+          acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(expand_word(ring[kk % kRingSteps][q]), b, acc[q], 4,
+                                                                    0, 0, 127, 0, bscale);
+      }
+      load_step(k + kRingSteps, ring[kk % kRingSteps]);  // past the span: out of range, no memory access
+      if (kk == kChunkSteps / 2) store_chunk(buf ^ 1);    // the other buffer was last read in chunk c-1
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) total[q][r] = fmaf(acc[q][r], fscale, total[q][r]);
-    if (c + 1 < nchunks)
-      mfma_chunk_max<T>(S, in, c0 + kChunkWords * kWordBits, span1, slots + ((c + 1) & 1) * kMfmaMaxT);
-    __syncthreads();  // every wave is done with chunk c's B fragments
+    __syncthreads();  // chunk c+1's fragments are in LDS; every wave is done with chunk c's
   }
 
   // add the pieces of each token across the lanes of a row; lane col == 0
@@ -787,12 +871,12 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
 #pragma unroll
   for (int t = 0; t < T; ++t) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int r = 0; r < 4; ++r) {  // C row 4*grp + r of set q is row 16*grp + 4r + q of the wave
       float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = row16_sum(tcol == t ? total[q][r] : 0.0f);
+      for (int q = 0; q < 4; ++q) v[q] = row16_sum(tcol == t ? acc[q][r] : 0.0f);
       if (col == 0)
-        *reinterpret_cast<float4*>(sums + t * kRows + wv * 64 + q * 16 + grp * 4) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(sums + t * kRows + wv * 64 + grp * 16 + 4 * r) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
   __syncthreads();
@@ -818,9 +902,14 @@ __device__ inline void stage_init(float* lds) {
 }
 template <int T>
 __device__ inline void stage_tile(const StageDesc& S, int local, float* lds, int* s_flag, int* err) {
-  if constexpr (use_mfma<T>())
-    mfma_tile<T>(S, local, lds, s_flag, err);
-  else
+  if constexpr (use_mfma<T>()) {
+    if (S.kind == 1)
+      mfma_prep_tile<T>(S, local, lds, err);
+    else if (S.w_vec)
+      mfma_tile<T, true>(S, local, lds, s_flag, err);
+    else
+      mfma_tile<T, false>(S, local, lds, s_flag, err);
+  } else
     lut_tile<T>(S, local, lds, s_flag, err);
 }
 
@@ -887,9 +976,11 @@ StagePlan lut_stage_plan(int64_t n_rows, int64_t n_red, int64_t T, int64_t kspan
   p.nrb = (int)cdiv(n_rows, kRows);
   const int64_t span = kspan_max > 0 ? imin(kspan_max, n_red) : n_red;
   p.nks = (int)cdiv(n_red, span);
-  p.kc = (int)round_up(cdiv(n_red, p.nks), kWordBits);
+  // balanced spans, in whole sign words; on the matrix cores in whole chunks
+  // of input pieces (a span starts at a chunk)
+  const int64_t grain = T <= kMfmaMaxT ? kChunkWords * kWordBits : kWordBits;
+  p.kc = (int)round_up(cdiv(n_red, p.nks), grain);
   p.nks = (int)cdiv(n_red, p.kc);
-  (void)T;
   return p;
 }
 
@@ -974,24 +1065,46 @@ size_t part_bytes(const StagePlan& p, int64_t T) {
 
 }  // namespace
 
-// Per-linear device buffers: [part1][t][part2].
+namespace {
+
+// Matrix-core pieces of a stage input of n_red elements: compact blocks and
+// per-chunk scale exponents.
+int64_t piece_chunks(int64_t n_red) { return cdiv(n_red, kChunkWords * kWordBits); }
+size_t piece_bytes(int64_t n_red, int64_t T) {
+  if (T > kMfmaMaxT) return 0;
+  const int64_t nch = piece_chunks(n_red);
+  return align_up((size_t)nch * 64 * T * kPieces * 16) + align_up((size_t)nch * T * sizeof(int));
+}
+
+}  // namespace
+
+// Per-linear device buffers: [part1][t][part2][pieces of x][pieces of t].
 size_t lut_linear_bytes(const nq_lrb& L, int64_t T, bool split) {
   StagePlan p1, p2;
   plans(L, T, split, &p1, &p2);
   size_t off = align_up(part_bytes(p1, T));
   off = align_up(off + (size_t)T * L.r * sizeof(float));
-  return align_up(off + part_bytes(p2, T));
+  off = align_up(off + part_bytes(p2, T));
+  return off + piece_bytes(L.d_in, T) + piece_bytes(L.r, T);
 }
 
-// Per-linear counters: [stage-1 row blocks][stage-2 row blocks][t-ready].
+// Per-linear counters: [stage-1 row blocks][stage-2 row blocks][t ready]
+// [pieces of x ready][pieces of t ready].
 int lut_linear_counters(const nq_lrb& L, int64_t T, bool split) {
   StagePlan p1, p2;
   plans(L, T, split, &p1, &p2);
-  return p1.nrb + p2.nrb + 1;
+  return p1.nrb + p2.nrb + 3;
 }
 
-void lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, bool split,
-                     char* ws_linear, int* ctr_base, StageDesc* s1, StageDesc* s2) {
+bool lut_uses_pieces(int64_t T) { return T <= kMfmaMaxT; }
+
+// Sign words of a stage can be read 4 rows at a time (16-byte loads).
+bool words_vec(const uint32_t* bits, int64_t ld, int64_t n_rows) {
+  return reinterpret_cast<uintptr_t>(bits) % 16 == 0 && ld % 4 == 0 && n_rows % 4 == 0;
+}
+
+int lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, bool split,
+                    char* ws_linear, int* ctr_base, StageDesc* d) {
   StagePlan p1, p2;
   plans(L, T, split, &p1, &p2);
   size_t off = 0;
@@ -1000,6 +1113,11 @@ void lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, flo
   float* tbuf = reinterpret_cast<float*>(ws_linear + off);
   off = align_up(off + (size_t)T * L.r * sizeof(float));
   float* part2 = reinterpret_cast<float*>(ws_linear + off);
+  off = align_up(off + part_bytes(p2, T));
+  char* pieces1 = ws_linear + off;
+  off += piece_bytes(L.d_in, T);
+  char* pieces2 = ws_linear + off;
+  int* t_ready = ctr_base + p1.nrb + p2.nrb;
 
   StageDesc a{};
   a.bits = L.vt_bits;
@@ -1010,7 +1128,7 @@ void lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, flo
   a.out = tbuf;
   a.part = part1;
   a.rb_count = ctr_base;
-  a.signal = ctr_base + p1.nrb + p2.nrb;
+  a.signal = t_ready;
   a.wait_ctr = nullptr;
   a.wait_target = 0;
   a.n_rows = (int)L.r;
@@ -1021,6 +1139,8 @@ void lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, flo
   a.x_bf16 = xd == NQ_BF16;
   a.x_vec = reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(L.s2) % 16 == 0 &&
             L.d_in % 4 == 0;
+  a.w_vec = words_vec(L.vt_bits, L.ldv, L.r);
+  a.kind = 0;
   a.tile0 = 0;
   StageDesc b = a;
   b.bits = L.u_bits;
@@ -1032,7 +1152,7 @@ void lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, flo
   b.part = part2;
   b.rb_count = ctr_base + p1.nrb;
   b.signal = nullptr;
-  b.wait_ctr = a.signal;
+  b.wait_ctr = t_ready;
   b.wait_target = p1.nrb;
   b.n_rows = (int)L.d_out;
   b.n_red = (int)L.r;
@@ -1041,8 +1161,40 @@ void lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, flo
   b.nrb = p2.nrb;
   b.x_bf16 = 0;
   b.x_vec = L.r % 4 == 0;  // t sits 256-byte aligned in the workspace
-  *s1 = a;
-  *s2 = b;
+  b.w_vec = words_vec(L.u_bits, L.ldu, L.d_out);
+  if (T > kMfmaMaxT) {
+    d[0] = a;
+    d[1] = b;
+    return 2;
+  }
+  // matrix cores: input-piece tiles before each stage; each stage waits for
+  // its pieces, the pieces of t wait for stage 1
+  auto pieces = [&](const StageDesc& st, char* buf, int* ready) {
+    StageDesc pc = st;
+    const int64_t nch = piece_chunks(st.n_red);
+    pc.kind = 1;
+    pc.bfrag = reinterpret_cast<uint32_t*>(buf);
+    pc.bsig = reinterpret_cast<int*>(buf + align_up((size_t)nch * 64 * T * kPieces * 16));
+    pc.nrb = (int)nch;
+    pc.nks = 1;
+    pc.signal = ready;
+    return pc;
+  };
+  int* x_ready = t_ready + 1;
+  int* tp_ready = t_ready + 2;
+  d[0] = pieces(a, pieces1, x_ready);  // no wait
+  d[2] = pieces(b, pieces2, tp_ready);  // waits for t (b's wait)
+  a.bfrag = d[0].bfrag;
+  a.bsig = d[0].bsig;
+  a.wait_ctr = x_ready;
+  a.wait_target = d[0].nrb;
+  b.bfrag = d[2].bfrag;
+  b.bsig = d[2].bsig;
+  b.wait_ctr = tp_ready;
+  b.wait_target = d[2].nrb;
+  d[1] = a;
+  d[3] = b;
+  return 4;
 }
 
 size_t lut_workspace_bytes(const nq_lrb& L, int64_t T) {
@@ -1056,14 +1208,16 @@ hipError_t launch_lut_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_
   int* ctr = err + 1;
   const int nctr = lut_linear_counters(L, T, true);
   char* lin = base + align_up((size_t)(1 + nctr) * sizeof(int));
-  StageDesc a, b;
-  lut_stage_descs(L, x, xd, T, y, true, lin, ctr, &a, &b);
-  a.signal = nullptr;  // stream order separates the two launches
-  b.wait_ctr = nullptr;
+  StageDesc d[kMaxLinearDescs];
+  const int nd = lut_stage_descs(L, x, xd, T, y, true, lin, ctr, d);
   hipError_t e;
   if ((e = launch_zero_ints(err, 1 + nctr, s)) != hipSuccess) return e;
-  if ((e = launch_lut_stage(a, T, err, s)) != hipSuccess) return e;
-  return launch_lut_stage(b, T, err, s);
+  for (int i = 0; i < nd; ++i) {
+    d[i].signal = nullptr;  // stream order separates the launches
+    d[i].wait_ctr = nullptr;
+    if ((e = launch_lut_stage(d[i], T, err, s)) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace nq

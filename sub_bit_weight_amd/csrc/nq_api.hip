@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <new>
+#include <array>
 #include <vector>
 
 #include "nq_internal.h"
@@ -140,7 +141,10 @@ namespace {
 
 // Stage 2 of linear i is scheduled after stage 1 of linear i+lag, so that its
 // inputs are usually final by the time a workgroup takes its first tile and
-// enough independent tiles are ready to keep every workgroup streaming.
+// enough independent tiles are ready to keep every workgroup streaming.  On
+// the matrix cores the input-piece tiles of linear i's stage 1 come lag/2
+// linears ahead of its stage 1 (its stage-1 tiles then find them final), those
+// of its stage 2 lag/2 linears after it.
 int seq_lag() {
   const char* e = getenv("NQ_SEQ_LAG");
   const int v = e ? atoi(e) : 128;
@@ -160,12 +164,25 @@ void plan_persistent(nq_seq* s) {
     bufs = align_up(bufs + lut_linear_bytes(s->layers[i], s->T, false));
   }
   s->n_ints = ints;
-  const int lag = seq_lag();
-  for (int64_t i = 0; i < n; ++i) {
-    s->order.push_back({(int)i, 1});
-    if (i >= lag) s->order.push_back({(int)(i - lag), 2});
+  const int64_t lag = seq_lag();
+  if (!lut_uses_pieces(s->T)) {  // descriptors: stage 1, stage 2
+    for (int64_t i = 0; i < n; ++i) {
+      s->order.push_back({(int)i, 0});
+      if (i >= lag) s->order.push_back({(int)(i - lag), 1});
+    }
+    for (int64_t i = std::max<int64_t>(0, n - lag); i < n; ++i) s->order.push_back({(int)i, 1});
+  } else {  // descriptors: pieces of x, stage 1, pieces of t, stage 2
+    const int64_t pre = std::max<int64_t>(lag / 2, 1), lag2 = lag / 2;
+    for (int64_t i = 0; i < std::min(pre, n); ++i) s->order.push_back({(int)i, 0});
+    for (int64_t i = 0; i < n; ++i) {
+      if (i + pre < n) s->order.push_back({(int)(i + pre), 0});
+      s->order.push_back({(int)i, 1});
+      if (i >= lag2) s->order.push_back({(int)(i - lag2), 2});
+      if (i >= lag) s->order.push_back({(int)(i - lag), 3});
+    }
+    for (int64_t i = std::max<int64_t>(0, n - lag2); i < n; ++i) s->order.push_back({(int)i, 2});
+    for (int64_t i = std::max<int64_t>(0, n - lag); i < n; ++i) s->order.push_back({(int)i, 3});
   }
-  for (int64_t i = std::max<int64_t>(0, n - lag); i < n; ++i) s->order.push_back({(int)i, 2});
   s->off_sched = align_up((size_t)ints * sizeof(int));
   const size_t off_bufs = align_up(s->off_sched + s->order.size() * sizeof(StageDesc));
   for (auto& b : s->buf_off) b += off_bufs;
@@ -177,14 +194,14 @@ nq_status build_and_upload(nq_seq* s, void* ws, hipStream_t stream) {
   using namespace nq;
   char* base = static_cast<char*>(ws);
   int* ints = reinterpret_cast<int*>(base);
-  std::vector<StageDesc> st1(s->layers.size()), st2(s->layers.size());
+  std::vector<std::array<StageDesc, kMaxLinearDescs>> st(s->layers.size());
   for (size_t i = 0; i < s->layers.size(); ++i)
     lut_stage_descs(s->layers[i], s->xs[i], s->xd, s->T, s->ys[i], false, base + s->buf_off[i], ints + s->ctr_off[i],
-                    &st1[i], &st2[i]);
+                    st[i].data());
   s->segs.clear();
   int tile = 0;
   for (auto& o : s->order) {
-    StageDesc d = o.second == 1 ? st1[o.first] : st2[o.first];
+    StageDesc d = st[o.first][o.second];
     d.tile0 = tile;
     tile += d.nrb * d.nks;
     s->segs.push_back(d);

@@ -60,6 +60,10 @@ struct StageDesc {
   int kc, nks, nrb;       // reduction span per tile (elements), spans, row blocks
   int x_bf16;
   int x_vec;              // xin and colscale 16-byte aligned and n_red % 4 == 0: vector loads
+  int w_vec;              // bits 16-byte aligned, ld and n_rows multiples of 4: 16-byte word loads
+  int kind;               // 0: stage tiles (nrb x nks); 1: input-piece tiles (nrb = chunks, nks = 1)
+  uint32_t* bfrag;        // matrix-core operand pieces of the stage input (written by kind 1, read by kind 0)
+  int* bsig;              // per chunk and token: scale exponent of the pieces
   int tile0;              // first tile of this stage in a persistent schedule
 };
 struct StagePlan {
@@ -72,8 +76,13 @@ size_t lut_workspace_bytes(const nq_lrb& L, int64_t T);
 // split = true: single-call plan (reduction split over workgroups); false: sequence plan
 size_t lut_linear_bytes(const nq_lrb& L, int64_t T, bool split);
 int lut_linear_counters(const nq_lrb& L, int64_t T, bool split);
-void lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, bool split,
-                     char* ws_linear, int* ctr_base, StageDesc* s1, StageDesc* s2);
+// Descriptors of one linear in dependency order (each waits only on earlier
+// ones): stage 1, stage 2 for table lookups; pieces of x, stage 1, pieces of
+// t, stage 2 on the matrix cores (T <= 2).  Returns their number (2 or 4).
+constexpr int kMaxLinearDescs = 4;
+bool lut_uses_pieces(int64_t T);  // the matrix-core form (4 descriptors) serves T tokens
+int lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, bool split,
+                    char* ws_linear, int* ctr_base, StageDesc* d);
 hipError_t launch_lut_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
                              hipStream_t s);
 hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t s);
