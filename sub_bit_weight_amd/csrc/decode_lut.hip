@@ -529,7 +529,7 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
 // row), and component q feeds the MFMA of set q.
 
 constexpr int kMfmaMaxT = 2;
-constexpr int kPieces = 6;                            // fp8 pieces per token
+constexpr int kPieces = 5;                            // fp8 pieces per token
 constexpr int kStepWords = 4;                         // word rows per MFMA step
 constexpr int kChunkSteps = 8;                        // steps per staged chunk
 constexpr int kChunkWords = kChunkSteps * kStepWords;  // 32 word rows
@@ -644,56 +644,71 @@ __device__ inline int max_fp8_exponent(int d) {
 template <int T>
 constexpr int chunk_blocks() { return kChunkSteps * 2 * 4 * T * kPieces; }
 
-// One input-piece tile: chunk `chunk` of the stage input.  Each thread makes
-// one B dword (4 consecutive reduction positions) per piece and token.
+// One input-piece tile: chunks [kPrepChunks*tile, ...) of the stage input
+// (fewer tiles, each with its own latency, fences and barriers, cost less
+// than one tile per chunk).  Per chunk each thread makes one B dword (4
+// consecutive reduction positions) per piece and token; the next chunk's
+// inputs load while the current one is converted.
+constexpr int kPrepChunks = 8;
+
 template <int T>
-__device__ void mfma_prep_tile(const StageDesc& S, int chunk, float* ldsf, int* err) {
+__device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* err) {
   constexpr int NC = T * kPieces;
+  constexpr int64_t kChunkElems = kChunkWords * kWordBits;
   unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + kSlotOff);
   const int tid = threadIdx.x;
-  const int64_t c0 = (int64_t)chunk * kChunkWords * kWordBits;
+  const int ch0 = tile * kPrepChunks;
+  const int ch1 = min(ch0 + kPrepChunks, (int)cdiv(S.n_red, kChunkElems));
   wait_input(S, err);
-  MfmaIn<T> in;
-  mfma_load_inputs<T>(S, c0, S.n_red, 0, in);
-  if (tid < T) slots[tid] = 0;
-  __syncthreads();
-  mfma_chunk_max<T>(S, in, c0, S.n_red, slots);
-  __syncthreads();
   const int wr = tid >> 3, j = (tid >> 1) & 3, ih = tid & 1;
   const int kk = wr >> 2, gw = wr & 3;
   const int gp = 2 * (gw & 1) + (j >> 1);
-  uint32_t* dst = S.bfrag + ((int64_t)chunk * chunk_blocks<T>() + ((kk * 2 + (gw >> 1)) * 4 + gp) * NC) * 4 +
-                  2 * (j & 1) + ih;
+  const int64_t task_off = (int64_t)(((kk * 2 + (gw >> 1)) * 4 + gp) * NC) * 4 + 2 * (j & 1) + ih;
+  if (tid < 2 * T) slots[tid] = 0;
+  MfmaIn<T> in, nxt;
+  mfma_load_inputs<T>(S, ch0 * kChunkElems, S.n_red, 0, in);
+  __syncthreads();
+  for (int ch = ch0; ch < ch1; ++ch) {
+    const int64_t c0 = ch * kChunkElems;
+    unsigned* slot = slots + (ch & 1) * T;
+    mfma_chunk_max<T>(S, in, c0, S.n_red, slot);
+    mfma_load_inputs<T>(S, c0 + kChunkElems, S.n_red, 0, nxt);  // next chunk (or none)
+    __syncthreads();  // the chunk's maxima are complete
+    uint32_t* dst = S.bfrag + (int64_t)ch * chunk_blocks<T>() * 4 + task_off;
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int shift = chunk_shift(slots[t]);
-    float r[4];
+    for (int t = 0; t < T; ++t) {
+      const int shift = chunk_shift(slot[t]);
+      float r[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000) : ldexpf(mfma_value<T>(S, in, c0, S.n_red, t, k), shift);
+      for (int k = 0; k < 4; ++k)
+        r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000) : ldexpf(mfma_value<T>(S, in, c0, S.n_red, t, k), shift);
 #pragma unroll
-    for (int p = 0; p < kPieces; ++p) {
-      int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
-      d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
-      // this dword and the partner thread's (tid ^ 1) form one group of 8
-      int emax = max_fp8_exponent(d);
-      emax = max(emax, __shfl_xor(emax, 1));
-      d = keep_fp8_exponents(d, max(1, emax - 7));
-      store_agent(reinterpret_cast<float*>(dst + (t * kPieces + p) * 4), __int_as_float(d));
-      if (p + 1 < kPieces) {
-        typedef float v2f __attribute__((ext_vector_type(2)));
-        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
-        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
-        r[0] = (r[0] - lo.x) * 16.0f;
-        r[1] = (r[1] - lo.y) * 16.0f;
-        r[2] = (r[2] - hi.x) * 16.0f;
-        r[3] = (r[3] - hi.y) * 16.0f;
+      for (int p = 0; p < kPieces; ++p) {
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+        d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
+        // this dword and the partner thread's (tid ^ 1) form one group of 8
+        int emax = max_fp8_exponent(d);
+        emax = max(emax, __shfl_xor(emax, 1));
+        d = keep_fp8_exponents(d, max(1, emax - 7));
+        store_agent(reinterpret_cast<float*>(dst + (t * kPieces + p) * 4), __int_as_float(d));
+        if (p + 1 < kPieces) {
+          typedef float v2f __attribute__((ext_vector_type(2)));
+          const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
+          const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
+          r[0] = (r[0] - lo.x) * 16.0f;
+          r[1] = (r[1] - lo.y) * 16.0f;
+          r[2] = (r[2] - hi.x) * 16.0f;
+          r[3] = (r[3] - hi.y) * 16.0f;
+        }
       }
+      if (tid == 0) store_agent(reinterpret_cast<float*>(S.bsig + (int64_t)ch * T + t), __int_as_float(shift));
     }
-    if (tid == 0) store_agent(reinterpret_cast<float*>(S.bsig + (int64_t)chunk * T + t), __int_as_float(shift));
+    __syncthreads();  // every thread has read this chunk's maxima
+    if (tid < T) slot[tid] = 0;  // reused by chunk ch+2 (its maxima come after the next barrier)
+    in = nxt;
   }
   if (S.signal) {
-    stores_done_barrier();  // the chunk's pieces are at the coherence point
+    stores_done_barrier();  // the tile's pieces are at the coherence point
     if (tid == 0) atomicAdd(S.signal, 1);
   }
   __syncthreads();  // the slots are reused by the next tile
@@ -1175,7 +1190,7 @@ int lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
     pc.kind = 1;
     pc.bfrag = reinterpret_cast<uint32_t*>(buf);
     pc.bsig = reinterpret_cast<int*>(buf + align_up((size_t)nch * 64 * T * kPieces * 16));
-    pc.nrb = (int)nch;
+    pc.nrb = (int)cdiv(nch, kPrepChunks);  // tiles
     pc.nks = 1;
     pc.signal = ready;
     return pc;

@@ -144,7 +144,9 @@ namespace {
 // enough independent tiles are ready to keep every workgroup streaming.  On
 // the matrix cores the input-piece tiles of linear i's stage 1 come lag/2
 // linears ahead of its stage 1 (its stage-1 tiles then find them final), those
-// of its stage 2 lag/2 linears after it.
+// of its stage 2 3*lag/4 linears after it (late enough that stage 1, whose
+// tiles can be long, has usually finished, early enough to be done before
+// stage 2).
 int seq_lag() {
   const char* e = getenv("NQ_SEQ_LAG");
   const int v = e ? atoi(e) : 128;
@@ -172,7 +174,7 @@ void plan_persistent(nq_seq* s) {
     }
     for (int64_t i = std::max<int64_t>(0, n - lag); i < n; ++i) s->order.push_back({(int)i, 1});
   } else {  // descriptors: pieces of x, stage 1, pieces of t, stage 2
-    const int64_t pre = std::max<int64_t>(lag / 2, 1), lag2 = lag / 2;
+    const int64_t pre = std::max<int64_t>(lag / 2, 1), lag2 = lag * 3 / 4;
     for (int64_t i = 0; i < std::min(pre, n); ++i) s->order.push_back({(int)i, 0});
     for (int64_t i = 0; i < n; ++i) {
       if (i + pre < n) s->order.push_back({(int)(i + pre), 0});
