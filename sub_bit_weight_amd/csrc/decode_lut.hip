@@ -800,7 +800,7 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   // This thread's compact blocks of a chunk (see mfma_prep_tile) and their
   // LDS places.  Every thread loads NBT blocks (past the chunk's last block:
   // the last one again, written to the row-sum area, unused until the tile's
-  // end) and thread 0 the chunk's scale exponents, so no branch surrounds the
+  // end) and the chunk's scale exponents, so no branch surrounds the
   // loads.  Chunk c+1 is loaded during chunk c and written to the other LDS
   // buffer half-way through it (the loads are then waited for with the sign
   // words issued after them still in flight); one barrier per chunk.  A chunk
@@ -834,12 +834,14 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
     for (int m = 0; m < NBT; ++m) *reinterpret_cast<u32x4*>(lds + buf * kBInts + lds_at[m]) = blk[m];
     if (tid < T) lds[kSigOff + buf * kMfmaMaxT + tid] = sig;
   };
-  wait_input(S, err);  // the stage's pieces are final
-  load_chunk(chunk0);
-  store_chunk(0);
+  // the first sign words do not depend on the stage input: in flight while
+  // the wait and the first chunk's pieces complete
   u32x4 ring[kRingSteps];
 #pragma unroll
   for (int k = 0; k < kRingSteps; ++k) load_step(k, ring[k]);
+  wait_input(S, err);  // the stage's pieces are final
+  load_chunk(chunk0);
+  store_chunk(0);
   __syncthreads();  // chunk 0's fragments are in LDS buffer 0
 
   // the sums of all chunks accumulate in acc: each chunk's B column (token t,
