@@ -295,3 +295,65 @@ def test_linear_biased_inputs(x_dtype):
     err = _linear_err(dev, ref, x, x_dtype)
     print(f"biased inputs {x_dtype}: rel err {err:.3e}")
     assert err <= G.tol_for(100, x_dtype), err
+
+
+# Decode on the matrix cores cuts each input into fp8 pieces per 1024-element
+# chunk, scaled by the chunk's largest value; these cases stress that: strong
+# outliers (wide dynamic range inside one group of 8 products), magnitudes
+# spread over many binades, tiny and huge overall scales, all-zero chunks
+# next to non-zero ones, and all-positive inputs.
+def _decode_inputs(kind: str, T: int, d: int, x_dtype: str) -> np.ndarray:
+    tag = f"decode-edge/{kind}/{T}/{d}/{x_dtype}"
+    if kind == "outliers":
+        x = synth.activations(tag, T, d, "f32", outlier_frac=0.01, outlier_mag=3.0e3)
+    elif kind == "spread":  # |x| log-uniform over 2^-40 .. 2^10
+        g = synth.rng(tag)
+        x = (np.exp2(g.uniform(-40.0, 10.0, (T, d))) * np.where(g.random((T, d)) < 0.5, -1.0, 1.0)).astype(np.float32)
+    elif kind == "tiny":
+        x = synth.activations(tag, T, d, "f32") * np.float32(1e-20)
+    elif kind == "huge":
+        x = synth.activations(tag, T, d, "f32") * np.float32(1e12)
+    elif kind == "zero_chunks":  # every other 1024-element chunk is zero
+        x = synth.activations(tag, T, d, "f32")
+        for c in range(0, d, 2048):
+            x[:, c:c + 1024] = 0.0
+    elif kind == "biased":
+        x = np.abs(synth.activations(tag, T, d, "f32")) + np.float32(4.0)
+    else:
+        raise ValueError(kind)
+    return synth.round_bf16(x) if x_dtype == "bf16" else x.astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["outliers", "spread", "tiny", "huge", "zero_chunks", "biased"])
+@pytest.mark.parametrize("T,x_dtype", [(1, "bf16"), (1, "f32"), (2, "f32")])
+def test_decode_input_ranges(kind, T, x_dtype):
+    shape = synth.LayerShape("ranges", 320, 4096, 1088)  # ragged rows and rank, 4 chunks of x, 2 of t
+    cfg = G.tiny_config(f"ranges/{x_dtype}", x_dtype=x_dtype)
+    dev, ref, _ = G.latent_layer(cfg, shape)
+    x = _decode_inputs(kind, T, shape.d_in, x_dtype)
+    err = _linear_err(dev, ref, x, x_dtype, factored=True)
+    print(f"decode {kind} T{T} {x_dtype}: rel err {err:.3e}")
+    assert err <= 1e-5, err
+
+
+def test_decode_all_zero_input():
+    shape = synth.LayerShape("zeros", 200, 3000, 300)
+    cfg = G.tiny_config("zeros")
+    dev, ref, _ = G.latent_layer(cfg, shape)
+    y = nq.lrb_linear(dev, G.to_device_x(np.zeros((1, shape.d_in), np.float32), "bf16")).cpu().numpy()
+    assert np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf])
+def test_decode_non_finite_input(bad):
+    # one non-finite element reaches every output: the oracle's sums are NaN
+    # or +-inf; the decode result must not be finite anywhere
+    shape = synth.LayerShape("nonfinite", 256, 2048, 256)
+    cfg = G.tiny_config("nonfinite")
+    dev, ref, _ = G.latent_layer(cfg, shape)
+    x = synth.activations("nonfinite/x", 1, shape.d_in, "f32")
+    x[0, 1500] = bad
+    y = nq.lrb_linear(dev, G.to_device_x(x, "f32")).cpu().numpy()
+    y_ref = O.linear_factored_ref(ref, x)
+    assert not np.any(np.isfinite(y_ref))
+    assert not np.any(np.isfinite(y))
