@@ -522,13 +522,14 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
 // (Making them in every row-block tile took about a fifth of the stream
 // rate: the loads of x and s2, the chunk maxima and the conversions.)
 //
-// A workgroup covers 256 rows: each wave 64 rows as four sets of 16, set q
+// A workgroup covers 512 rows: each of 8 waves 64 rows as four sets of 16, set q
 // holding rows 4m + q (m = 0..15) of the wave's 64.  For MFMA step k (128
 // elements) lane l reads the words of rows 4*(l%16) + [0, 4) in word row
 // 4k + l/16 (one 16-byte load; 16 lanes cover 256 contiguous bytes of a word
 // row), and component q feeds the MFMA of set q.
 
 constexpr int kMfmaMaxT = 2;
+constexpr int kMRows = 512;                            // rows per tile = threads per workgroup (8 waves)
 constexpr int kPieces = 5;                            // fp8 pieces per token
 constexpr int kStepWords = 4;                         // word rows per MFMA step
 constexpr int kChunkSteps = 8;                        // steps per staged chunk
@@ -539,11 +540,11 @@ constexpr int kStepInts = 64 * 8;                     // B fragments of one step
 constexpr int kBInts = kChunkSteps * kStepInts;       // B fragments of a chunk (16 KiB)
 // LDS of a workgroup, in 4-byte words: [B fragments, two chunk buffers]
 // [chunk scale exponents, two buffers of kMfmaMaxT][per-chunk maxima of an
-// input-piece tile][row sums [kMfmaMaxT][kRows]]
+// input-piece tile][row sums [kMfmaMaxT][kMRows]]
 constexpr int kSigOff = 2 * kBInts;
 constexpr int kSlotOff = kSigOff + 2 * kMfmaMaxT;
-constexpr int kSumOff = kSlotOff + 2 * kMfmaMaxT;
-constexpr int kMfmaLds = kSumOff + kMfmaMaxT * kRows;
+constexpr int kSumOff = kSlotOff + 4 * kMfmaMaxT;
+constexpr int kMfmaLds = kSumOff + kMfmaMaxT * kMRows;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -557,9 +558,8 @@ struct MfmaIn {
 // This thread's build task within a chunk: word row wr (0..31), dword j of
 // the A expansion, half ih of the nibbles: elements 32*wr + 4*(4*ih + k) +
 // 3 - j, k = 0..3, i.e. one B dword (4 consecutive reduction positions).
-__device__ inline int task_element(int k) {
-  const int tid = threadIdx.x;
-  const int wr = tid >> 3, j = (tid >> 1) & 3, ih = tid & 1;
+__device__ inline int task_element(int task, int k) {
+  const int wr = task >> 3, j = (task >> 1) & 3, ih = task & 1;
   return 32 * wr + 4 * (4 * ih + k) + 3 - j;
 }
 
@@ -567,10 +567,11 @@ __device__ inline int task_element(int k) {
 // (any in-bounds index) and are dropped later, so chunks past the span can be
 // loaded too: the loads keep a fixed count and position in the pipeline.
 template <int T>
-__device__ inline void mfma_load_inputs(const StageDesc& S, int64_t c0, int64_t cend, int64_t safe, MfmaIn<T>& in) {
+__device__ inline void mfma_load_inputs(const StageDesc& S, int task, int64_t c0, int64_t cend, int64_t safe,
+                                        MfmaIn<T>& in) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int64_t e = c0 + task_element(k);
+    const int64_t e = c0 + task_element(task, k);
     const int64_t ec = e < cend ? e : safe;
     in.cs[k] = S.colscale ? gload(S.colscale + ec) : 1.0f;
 #pragma unroll
@@ -583,21 +584,22 @@ __device__ inline void mfma_load_inputs(const StageDesc& S, int64_t c0, int64_t 
 }
 
 template <int T>
-__device__ inline float mfma_value(const StageDesc& S, const MfmaIn<T>& in, int64_t c0, int64_t cend, int t, int k) {
+__device__ inline float mfma_value(const StageDesc& S, const MfmaIn<T>& in, int task, int64_t c0, int64_t cend, int t,
+                                  int k) {
   const float x = S.x_bf16 ? bf16_bits(in.x[t][k]) : __uint_as_float(in.x[t][k]);
-  return c0 + task_element(k) < cend ? x * in.cs[k] : 0.0f;
+  return c0 + task_element(task, k) < cend ? x * in.cs[k] : 0.0f;
 }
 
 // Largest |v| of the chunk per token into slot[t] (float bits of a
 // non-negative value order like unsigned integers; NaN orders above inf).
 template <int T>
-__device__ inline void mfma_chunk_max(const StageDesc& S, const MfmaIn<T>& in, int64_t c0, int64_t cend,
+__device__ inline void mfma_chunk_max(const StageDesc& S, const MfmaIn<T>& in, int task, int64_t c0, int64_t cend,
                                       unsigned* slot) {
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     unsigned m = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) m = max(m, __float_as_uint(fabsf(mfma_value<T>(S, in, c0, cend, t, k))));
+    for (int k = 0; k < 4; ++k) m = max(m, __float_as_uint(fabsf(mfma_value<T>(S, in, task, c0, cend, t, k))));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off));
     if ((threadIdx.x & 63) == 0) atomicMax(slot + t, m);
@@ -646,65 +648,70 @@ constexpr int chunk_blocks() { return kChunkSteps * 2 * 4 * T * kPieces; }
 
 // One input-piece tile: chunks [kPrepChunks*tile, ...) of the stage input
 // (fewer tiles, each with its own latency, fences and barriers, cost less
-// than one tile per chunk).  Per chunk each thread makes one B dword (4
-// consecutive reduction positions) per piece and token; the next chunk's
-// inputs load while the current one is converted.
+// than one tile per chunk).  The two halves of the workgroup (256 threads
+// each) take a chunk each per round; per chunk each thread makes one B dword
+// (4 consecutive reduction positions) per piece and token; the next round's
+// inputs load while the current ones are converted.
 constexpr int kPrepChunks = 8;
 
 template <int T>
 __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* err) {
   constexpr int NC = T * kPieces;
   constexpr int64_t kChunkElems = kChunkWords * kWordBits;
-  unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + kSlotOff);
-  const int tid = threadIdx.x;
+  unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + kSlotOff);  // [round&1][half][T]
+  const int tid = threadIdx.x, half = tid >> 8, task = tid & 255;
   const int ch0 = tile * kPrepChunks;
   const int ch1 = min(ch0 + kPrepChunks, (int)cdiv(S.n_red, kChunkElems));
   wait_input(S, err);
-  const int wr = tid >> 3, j = (tid >> 1) & 3, ih = tid & 1;
+  const int wr = task >> 3, j = (task >> 1) & 3, ih = task & 1;
   const int kk = wr >> 2, gw = wr & 3;
   const int gp = 2 * (gw & 1) + (j >> 1);
   const int64_t task_off = (int64_t)(((kk * 2 + (gw >> 1)) * 4 + gp) * NC) * 4 + 2 * (j & 1) + ih;
-  if (tid < 2 * T) slots[tid] = 0;
+  if (tid < 4 * T) slots[tid] = 0;
   MfmaIn<T> in, nxt;
-  mfma_load_inputs<T>(S, ch0 * kChunkElems, S.n_red, 0, in);
+  mfma_load_inputs<T>(S, task, (ch0 + half) * kChunkElems, S.n_red, 0, in);
   __syncthreads();
-  for (int ch = ch0; ch < ch1; ++ch) {
+  for (int r0 = ch0, round = 0; r0 < ch1; r0 += 2, ++round) {
+    const int ch = r0 + half;  // this half's chunk (past ch1: loads clamp, nothing is stored)
     const int64_t c0 = ch * kChunkElems;
-    unsigned* slot = slots + (ch & 1) * T;
-    mfma_chunk_max<T>(S, in, c0, S.n_red, slot);
-    mfma_load_inputs<T>(S, c0 + kChunkElems, S.n_red, 0, nxt);  // next chunk (or none)
-    __syncthreads();  // the chunk's maxima are complete
-    uint32_t* dst = S.bfrag + (int64_t)ch * chunk_blocks<T>() * 4 + task_off;
+    unsigned* slot = slots + ((round & 1) * 2 + half) * T;
+    mfma_chunk_max<T>(S, in, task, c0, S.n_red, slot);
+    mfma_load_inputs<T>(S, task, c0 + 2 * kChunkElems, S.n_red, 0, nxt);  // next round (or none)
+    __syncthreads();  // the chunks' maxima are complete
+    if (ch < ch1) {   // wave-uniform: a half is 4 whole waves
+      uint32_t* dst = S.bfrag + (int64_t)ch * chunk_blocks<T>() * 4 + task_off;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int shift = chunk_shift(slot[t]);
-      float r[4];
+      for (int t = 0; t < T; ++t) {
+        const int shift = chunk_shift(slot[t]);
+        float r[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000) : ldexpf(mfma_value<T>(S, in, c0, S.n_red, t, k), shift);
+        for (int k = 0; k < 4; ++k)
+          r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000)
+                                    : ldexpf(mfma_value<T>(S, in, task, c0, S.n_red, t, k), shift);
 #pragma unroll
-      for (int p = 0; p < kPieces; ++p) {
-        int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
-        d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
-        // this dword and the partner thread's (tid ^ 1) form one group of 8
-        int emax = max_fp8_exponent(d);
-        emax = max(emax, __shfl_xor(emax, 1));
-        d = keep_fp8_exponents(d, max(1, emax - 7));
-        store_agent(reinterpret_cast<float*>(dst + (t * kPieces + p) * 4), __int_as_float(d));
-        if (p + 1 < kPieces) {
-          typedef float v2f __attribute__((ext_vector_type(2)));
-          const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
-          const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
-          r[0] = (r[0] - lo.x) * 16.0f;
-          r[1] = (r[1] - lo.y) * 16.0f;
-          r[2] = (r[2] - hi.x) * 16.0f;
-          r[3] = (r[3] - hi.y) * 16.0f;
+        for (int p = 0; p < kPieces; ++p) {
+          int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+          d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
+          // this dword and the partner thread's (task ^ 1, same wave) form one group of 8
+          int emax = max_fp8_exponent(d);
+          emax = max(emax, __shfl_xor(emax, 1));
+          d = keep_fp8_exponents(d, max(1, emax - 7));
+          store_agent(reinterpret_cast<float*>(dst + (t * kPieces + p) * 4), __int_as_float(d));
+          if (p + 1 < kPieces) {
+            typedef float v2f __attribute__((ext_vector_type(2)));
+            const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
+            const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
+            r[0] = (r[0] - lo.x) * 16.0f;
+            r[1] = (r[1] - lo.y) * 16.0f;
+            r[2] = (r[2] - hi.x) * 16.0f;
+            r[3] = (r[3] - hi.y) * 16.0f;
+          }
         }
+        if (task == 0) store_agent(reinterpret_cast<float*>(S.bsig + (int64_t)ch * T + t), __int_as_float(shift));
       }
-      if (tid == 0) store_agent(reinterpret_cast<float*>(S.bsig + (int64_t)ch * T + t), __int_as_float(shift));
     }
-    __syncthreads();  // every thread has read this chunk's maxima
-    if (tid < T) slot[tid] = 0;  // reused by chunk ch+2 (its maxima come after the next barrier)
+    __syncthreads();  // every thread has read this round's maxima
+    if (task < T) slot[task] = 0;  // reused two rounds on (its maxima come after the next barrier)
     in = nxt;
   }
   if (S.signal) {
@@ -721,7 +728,7 @@ __device__ inline void mfma_lds_init(int* lds) {
   constexpr int NC = T * kPieces;
   if constexpr (NC < 16) {
     // per step and half: 64 lanes x 4 dwords; lane = column + 16 * group
-    for (int i = threadIdx.x; i < 2 * kBInts; i += kRows) {  // both chunk buffers
+    for (int i = threadIdx.x; i < 2 * kBInts; i += kMRows) {  // both chunk buffers
       const int lane = (i >> 2) & 63;
       if ((lane & 15) >= NC) lds[i] = 0;
     }
@@ -776,7 +783,7 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
 
   // byte offset of this lane's first word from word row 4k (rows at or past
   // n_rows are read where in range and never stored)
-  const uint32_t voff = 4u * (uint32_t)((int64_t)rb * kRows + wv * 64 + 4 * col) + (uint32_t)grp * ld4;
+  const uint32_t voff = 4u * (uint32_t)((int64_t)rb * kMRows + wv * 64 + 4 * col) + (uint32_t)grp * ld4;
   // Step k reads word row 4k + grp of the span through a buffer resource that
   // starts at word row 4k and ends with row n_rows-1 of the span's last word
   // row: words past the span (a partial last step, steps past the last) or
@@ -806,12 +813,12 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   // words issued after them still in flight); one barrier per chunk.  A chunk
   // past the stage's last loads the last one again.
   constexpr int NB = chunk_blocks<T>();
-  constexpr int NBT = (NB + kRows - 1) / kRows;  // blocks per thread
+  constexpr int NBT = (NB + kMRows - 1) / kMRows;  // blocks per thread
   constexpr int NC = T * kPieces;
   int lds_at[NBT], blk_at[NBT];
 #pragma unroll
   for (int m = 0; m < NBT; ++m) {
-    const int bi = tid + m * kRows;
+    const int bi = tid + m * kMRows;
     const int n = bi % NC, rest = bi / NC;
     const int g = rest % 4, h = (rest / 4) % 2, kk = rest / 8;
     lds_at[m] = bi < NB ? kk * kStepInts + h * 256 + (n + 16 * g) * 4 : kSumOff;
@@ -893,14 +900,14 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[q] = row16_sum(tcol == t ? acc[q][r] : 0.0f);
       if (col == 0)
-        *reinterpret_cast<float4*>(sums + t * kRows + wv * 64 + grp * 16 + 4 * r) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(sums + t * kMRows + wv * 64 + grp * 16 + 4 * r) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
   __syncthreads();
   float accr[T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) accr[t] = sums[t * kRows + tid];
-  const int64_t o = (int64_t)rb * kRows + tid;
+  for (int t = 0; t < T; ++t) accr[t] = sums[t * kMRows + tid];
+  const int64_t o = (int64_t)rb * kMRows + tid;
   finish_rows<T>(S, rb, ks, o, o < S.n_rows, accr, s_flag);
 }
 
@@ -910,6 +917,12 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
 // are built.
 template <int T>
 constexpr bool use_mfma() { return T <= kMfmaMaxT; }
+// rows per tile = threads per workgroup
+template <int T>
+constexpr int tile_rows() { return use_mfma<T>() ? kMRows : kRows; }
+// matrix-core kernels: 4 waves per SIMD (at most 128 VGPRs), 2 workgroups per CU
+template <int T>
+constexpr int min_waves() { return use_mfma<T>() ? 4 : 1; }
 template <int T>
 constexpr int stage_lds_floats() { return use_mfma<T>() ? kMfmaLds : Geo<T>::LUT; }
 
@@ -931,7 +944,8 @@ __device__ inline void stage_tile(const StageDesc& S, int local, float* lds, int
 }
 
 template <int T>
-__global__ __launch_bounds__(kRows) void lut_stage_kernel(StageDesc S, int* err) {
+__global__ __launch_bounds__(tile_rows<T>()) __attribute__((amdgpu_waves_per_eu(min_waves<T>())))
+void lut_stage_kernel(StageDesc S, int* err) {
   __shared__ __attribute__((aligned(16))) float lut[stage_lds_floats<T>()];
   int* s_flag = reinterpret_cast<int*>(lut);
   stage_init<T>(lut);
@@ -943,8 +957,8 @@ __global__ __launch_bounds__(kRows) void lut_stage_kernel(StageDesc S, int* err)
 // [3 .. n_ints) per-linear counters.  The last workgroup to exit zeroes
 // [1 .. n_ints), so consecutive runs need no separate reset launch.
 template <int T>
-__global__ __launch_bounds__(kRows) void lut_persistent_kernel(const StageDesc* __restrict__ segs, int nseg,
-                                                               int ntiles, int* ints, int n_ints) {
+__global__ __launch_bounds__(tile_rows<T>()) __attribute__((amdgpu_waves_per_eu(min_waves<T>())))
+void lut_persistent_kernel(const StageDesc* __restrict__ segs, int nseg, int ntiles, int* ints, int n_ints) {
   __shared__ __attribute__((aligned(16))) float lut[stage_lds_floats<T>()];
   int& s_flag = reinterpret_cast<int*>(lut)[0];  // aliases table entries (see lut_stage_kernel)
   int& s_tile = reinterpret_cast<int*>(lut)[1];
@@ -975,7 +989,7 @@ __global__ __launch_bounds__(kRows) void lut_persistent_kernel(const StageDesc* 
   }
   __syncthreads();
   if (s_flag)
-    for (int i = 1 + threadIdx.x; i < n_ints; i += kRows) ints[i] = 0;
+    for (int i = 1 + threadIdx.x; i < n_ints; i += blockDim.x) ints[i] = 0;
 }
 
 __global__ void zero_ints_kernel(int* p, int64_t n) {
@@ -986,11 +1000,13 @@ __global__ void zero_ints_kernel(int* p, int64_t n) {
 }  // namespace
 
 // Reduction spans per row block: `kspan_max` bounds a span (0 = whole reduction).
+int64_t lut_tile_rows(int64_t T) { return T <= kMfmaMaxT ? kMRows : kRows; }
+
 StagePlan lut_stage_plan(int64_t n_rows, int64_t n_red, int64_t T, int64_t kspan_max) {
   StagePlan p;
   p.n_rows = n_rows;
   p.n_red = n_red;
-  p.nrb = (int)cdiv(n_rows, kRows);
+  p.nrb = (int)cdiv(n_rows, lut_tile_rows(T));
   const int64_t span = kspan_max > 0 ? imin(kspan_max, n_red) : n_red;
   p.nks = (int)cdiv(n_red, span);
   // balanced spans, in whole sign words; on the matrix cores in whole chunks
@@ -1003,8 +1019,8 @@ StagePlan lut_stage_plan(int64_t n_rows, int64_t n_red, int64_t T, int64_t kspan
 
 // Single calls split the reduction until the two stages have enough tiles to
 // fill the GPU; sequences keep whole reductions (no partial sums).
-int64_t lut_single_span(int64_t n_rows, int64_t n_red) {
-  const int64_t nrb = cdiv(n_rows, kRows);
+int64_t lut_single_span(int64_t n_rows, int64_t n_red, int64_t T) {
+  const int64_t nrb = cdiv(n_rows, lut_tile_rows(T));
   const int64_t want = cdiv(512, nrb);
   const int64_t span = round_up(cdiv(n_red, want), 1024);
   return span;
@@ -1021,7 +1037,7 @@ hipError_t launch_lut_stage(const StageDesc& S, int64_t T, int* err, hipStream_t
   const unsigned grid = (unsigned)(S.nrb * S.nks);
   switch (T) {
 #define NQ_CASE(TT) \
-  case TT: hipLaunchKernelGGL(lut_stage_kernel<TT>, dim3(grid), dim3(kRows), 0, s, S, err); break;
+  case TT: hipLaunchKernelGGL(lut_stage_kernel<TT>, dim3(grid), dim3(tile_rows<TT>()), 0, s, S, err); break;
     NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
 #undef NQ_CASE
     default: return hipErrorInvalidValue;
@@ -1038,7 +1054,7 @@ int lut_persistent_grid(int64_t T) {
   hipError_t e = hipErrorInvalidValue;
   switch (T) {
 #define NQ_CASE(TT) \
-  case TT: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, lut_persistent_kernel<TT>, kRows, 0); break;
+  case TT: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, lut_persistent_kernel<TT>, tile_rows<TT>(), 0); break;
     NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
 #undef NQ_CASE
   }
@@ -1051,7 +1067,7 @@ hipError_t launch_lut_persistent(const StageDesc* segs, int nseg, int ntiles, in
   switch (T) {
 #define NQ_CASE(TT)                                                                                     \
   case TT:                                                                                              \
-    hipLaunchKernelGGL(lut_persistent_kernel<TT>, dim3(grid), dim3(kRows), 0, s, segs, nseg, ntiles, \
+    hipLaunchKernelGGL(lut_persistent_kernel<TT>, dim3(grid), dim3(tile_rows<TT>()), 0, s, segs, nseg, ntiles, \
                        ints, n_ints);                                                                   \
     break;
     NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
@@ -1072,8 +1088,8 @@ namespace {
 constexpr int64_t kSeqSpan = 0;
 
 void plans(const nq_lrb& L, int64_t T, bool split, StagePlan* p1, StagePlan* p2) {
-  *p1 = lut_stage_plan(L.r, L.d_in, T, split ? lut_single_span(L.r, L.d_in) : kSeqSpan);
-  *p2 = lut_stage_plan(L.d_out, L.r, T, split ? lut_single_span(L.d_out, L.r) : kSeqSpan);
+  *p1 = lut_stage_plan(L.r, L.d_in, T, split ? lut_single_span(L.r, L.d_in, T) : kSeqSpan);
+  *p2 = lut_stage_plan(L.d_out, L.r, T, split ? lut_single_span(L.d_out, L.r, T) : kSeqSpan);
 }
 
 size_t part_bytes(const StagePlan& p, int64_t T) {

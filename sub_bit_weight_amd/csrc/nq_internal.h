@@ -71,7 +71,7 @@ struct StagePlan {
   int kc, nks, nrb;
 };
 StagePlan lut_stage_plan(int64_t n_rows, int64_t n_red, int64_t T, int64_t kspan_max);
-int64_t lut_single_span(int64_t n_rows, int64_t n_red);
+int64_t lut_single_span(int64_t n_rows, int64_t n_red, int64_t T);
 size_t lut_workspace_bytes(const nq_lrb& L, int64_t T);
 // split = true: single-call plan (reduction split over workgroups); false: sequence plan
 size_t lut_linear_bytes(const nq_lrb& L, int64_t T, bool split);
