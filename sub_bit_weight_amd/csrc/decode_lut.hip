@@ -542,8 +542,9 @@ constexpr int kBInts = kChunkSteps * kStepInts;       // B fragments of a chunk 
 // [chunk scale exponents, two buffers of kMfmaMaxT][per-chunk maxima of an
 // input-piece tile][row sums [kMfmaMaxT][kMRows]]
 constexpr int kSigOff = 2 * kBInts;
+constexpr int kPrepGroups = kMRows / 256;           // chunks per round of an input-piece tile
 constexpr int kSlotOff = kSigOff + 2 * kMfmaMaxT;
-constexpr int kSumOff = kSlotOff + 4 * kMfmaMaxT;
+constexpr int kSumOff = kSlotOff + 2 * kPrepGroups * kMfmaMaxT;
 constexpr int kMfmaLds = kSumOff + kMfmaMaxT * kMRows;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -648,8 +649,8 @@ constexpr int chunk_blocks() { return kChunkSteps * 2 * 4 * T * kPieces; }
 
 // One input-piece tile: chunks [kPrepChunks*tile, ...) of the stage input
 // (fewer tiles, each with its own latency, fences and barriers, cost less
-// than one tile per chunk).  The two halves of the workgroup (256 threads
-// each) take a chunk each per round; per chunk each thread makes one B dword
+// than one tile per chunk).  Each group of 256 threads of the workgroup takes
+// a chunk per round; per chunk each thread makes one B dword
 // (4 consecutive reduction positions) per piece and token; the next round's
 // inputs load while the current ones are converted.
 constexpr int kPrepChunks = 8;
@@ -658,8 +659,8 @@ template <int T>
 __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* err) {
   constexpr int NC = T * kPieces;
   constexpr int64_t kChunkElems = kChunkWords * kWordBits;
-  unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + kSlotOff);  // [round&1][half][T]
-  const int tid = threadIdx.x, half = tid >> 8, task = tid & 255;
+  unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + kSlotOff);  // [round&1][group][T]
+  const int tid = threadIdx.x, half = tid >> 8, task = tid & 255;  // half: this thread's group
   const int ch0 = tile * kPrepChunks;
   const int ch1 = min(ch0 + kPrepChunks, (int)cdiv(S.n_red, kChunkElems));
   wait_input(S, err);
@@ -667,18 +668,18 @@ __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* e
   const int kk = wr >> 2, gw = wr & 3;
   const int gp = 2 * (gw & 1) + (j >> 1);
   const int64_t task_off = (int64_t)(((kk * 2 + (gw >> 1)) * 4 + gp) * NC) * 4 + 2 * (j & 1) + ih;
-  if (tid < 4 * T) slots[tid] = 0;
+  if (tid < 2 * kPrepGroups * T) slots[tid] = 0;
   MfmaIn<T> in, nxt;
   mfma_load_inputs<T>(S, task, (ch0 + half) * kChunkElems, S.n_red, 0, in);
   __syncthreads();
-  for (int r0 = ch0, round = 0; r0 < ch1; r0 += 2, ++round) {
-    const int ch = r0 + half;  // this half's chunk (past ch1: loads clamp, nothing is stored)
+  for (int r0 = ch0, round = 0; r0 < ch1; r0 += kPrepGroups, ++round) {
+    const int ch = r0 + half;  // this group's chunk (past ch1: loads clamp, nothing is stored)
     const int64_t c0 = ch * kChunkElems;
-    unsigned* slot = slots + ((round & 1) * 2 + half) * T;
+    unsigned* slot = slots + ((round & 1) * kPrepGroups + half) * T;
     mfma_chunk_max<T>(S, in, task, c0, S.n_red, slot);
-    mfma_load_inputs<T>(S, task, c0 + 2 * kChunkElems, S.n_red, 0, nxt);  // next round (or none)
+    mfma_load_inputs<T>(S, task, c0 + kPrepGroups * kChunkElems, S.n_red, 0, nxt);  // next round (or none)
     __syncthreads();  // the chunks' maxima are complete
-    if (ch < ch1) {   // wave-uniform: a half is 4 whole waves
+    if (ch < ch1) {   // wave-uniform: a group is 4 whole waves
       uint32_t* dst = S.bfrag + (int64_t)ch * chunk_blocks<T>() * 4 + task_off;
 #pragma unroll
       for (int t = 0; t < T; ++t) {
