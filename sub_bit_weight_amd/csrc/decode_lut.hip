@@ -959,7 +959,8 @@ void lut_stage_kernel(StageDesc S, int* err) {
 // [1 .. n_ints), so consecutive runs need no separate reset launch.
 template <int T>
 __global__ __launch_bounds__(tile_rows<T>()) __attribute__((amdgpu_waves_per_eu(min_waves<T>())))
-void lut_persistent_kernel(const StageDesc* __restrict__ segs, int nseg, int ntiles, int* ints, int n_ints) {
+void lut_persistent_kernel(const StageDesc* __restrict__ segs, const int* __restrict__ tile_seg, int ntiles, int* ints,
+                           int n_ints) {
   __shared__ __attribute__((aligned(16))) float lut[stage_lds_floats<T>()];
   int& s_flag = reinterpret_cast<int*>(lut)[0];  // aliases table entries (see lut_stage_kernel)
   int& s_tile = reinterpret_cast<int*>(lut)[1];
@@ -968,17 +969,15 @@ void lut_persistent_kernel(const StageDesc* __restrict__ segs, int nseg, int nti
   stage_init<T>(lut);
   if (threadIdx.x == 0) s_tile = atomicAdd(next_tile, 1);
   __syncthreads();
-  int tile = s_tile;
-  int seg = 0;
+  int tile = __builtin_amdgcn_readfirstlane(s_tile);
   while (tile < ntiles) {
     int nxt = 0;
     if (threadIdx.x == 0) nxt = atomicAdd(next_tile, 1);  // prefetch the next tile id
-    while (seg + 1 < nseg && tile >= segs[seg + 1].tile0) ++seg;
-    const StageDesc S = segs[seg];
+    const StageDesc S = segs[tile_seg[tile]];  // one lookup (a scan over the segments stalled for microseconds)
     stage_tile<T>(S, tile - S.tile0, lut, &s_flag, err);
     if (threadIdx.x == 0) s_tile = nxt;
     __syncthreads();
-    tile = s_tile;
+    tile = __builtin_amdgcn_readfirstlane(s_tile);
     __syncthreads();
   }
   // every counter access of this workgroup is done: count the exit; the last
@@ -1063,12 +1062,12 @@ int lut_persistent_grid(int64_t T) {
   return cus * per;
 }
 
-hipError_t launch_lut_persistent(const StageDesc* segs, int nseg, int ntiles, int* ints, int n_ints,
+hipError_t launch_lut_persistent(const StageDesc* segs, const int* tile_seg, int ntiles, int* ints, int n_ints,
                                  int64_t T, int grid, hipStream_t s) {
   switch (T) {
 #define NQ_CASE(TT)                                                                                     \
   case TT:                                                                                              \
-    hipLaunchKernelGGL(lut_persistent_kernel<TT>, dim3(grid), dim3(tile_rows<TT>()), 0, s, segs, nseg, ntiles, \
+    hipLaunchKernelGGL(lut_persistent_kernel<TT>, dim3(grid), dim3(tile_rows<TT>()), 0, s, segs, tile_seg, ntiles, \
                        ints, n_ints);                                                                   \
     break;
     NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)

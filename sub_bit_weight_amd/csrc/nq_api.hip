@@ -117,8 +117,10 @@ struct nq_seq {
   std::vector<int64_t> ctr_off;       // per linear, in ints from the start of the workspace
   std::vector<size_t> buf_off;        // per linear, in bytes
   std::vector<std::pair<int, int>> order;  // (linear, stage) in schedule order
-  size_t off_sched = 0;
-  std::vector<nq::StageDesc> segs;    // host copy of the uploaded schedule
+  size_t off_sched = 0;                // descriptors in schedule order
+  size_t off_tseg = 0;                 // per tile: index of its descriptor
+  std::vector<nq::StageDesc> segs;    // host copies of the uploaded schedule
+  std::vector<int> tile_seg;
   void* uploaded_for = nullptr;
   bool needs_zero = true;
   // per-entry kernels (T > 8): entries run round-robin on `nlanes` streams of
@@ -185,8 +187,19 @@ void plan_persistent(nq_seq* s) {
     for (int64_t i = std::max<int64_t>(0, n - lag2); i < n; ++i) s->order.push_back({(int)i, 2});
     for (int64_t i = std::max<int64_t>(0, n - lag); i < n; ++i) s->order.push_back({(int)i, 3});
   }
+  // tile counts do not depend on where the buffers are: count them with the
+  // descriptors of a stand-in workspace address
+  s->ntiles = 0;
+  char* const stand_in = reinterpret_cast<char*>(uintptr_t{1} << 40);
+  for (auto& o : s->order) {
+    StageDesc d[kMaxLinearDescs];
+    lut_stage_descs(s->layers[o.first], s->xs[o.first], s->xd, s->T, s->ys[o.first], false, stand_in,
+                    reinterpret_cast<int*>(stand_in), d);
+    s->ntiles += d[o.second].nrb * d[o.second].nks;
+  }
   s->off_sched = align_up((size_t)ints * sizeof(int));
-  const size_t off_bufs = align_up(s->off_sched + s->order.size() * sizeof(StageDesc));
+  s->off_tseg = align_up(s->off_sched + s->order.size() * sizeof(StageDesc));
+  const size_t off_bufs = align_up(s->off_tseg + (size_t)s->ntiles * sizeof(int));
   for (auto& b : s->buf_off) b += off_bufs;
   s->ws_bytes = off_bufs + bufs;
   s->grid = 0;
@@ -201,17 +214,20 @@ nq_status build_and_upload(nq_seq* s, void* ws, hipStream_t stream) {
     lut_stage_descs(s->layers[i], s->xs[i], s->xd, s->T, s->ys[i], false, base + s->buf_off[i], ints + s->ctr_off[i],
                     st[i].data());
   s->segs.clear();
-  int tile = 0;
+  s->tile_seg.clear();
   for (auto& o : s->order) {
     StageDesc d = st[o.first][o.second];
-    d.tile0 = tile;
-    tile += d.nrb * d.nks;
+    d.tile0 = (int)s->tile_seg.size();
+    s->tile_seg.insert(s->tile_seg.end(), (size_t)d.nrb * d.nks, (int)s->segs.size());
     s->segs.push_back(d);
   }
-  s->ntiles = tile;
+  if ((int64_t)s->tile_seg.size() != s->ntiles) return set_error("nq_seq_run: tile count changed"), NQ_ERR_ARG;
   if (s->grid == 0) s->grid = lut_persistent_grid(s->T);
   hipError_t e = hipMemcpyAsync(base + s->off_sched, s->segs.data(), s->segs.size() * sizeof(StageDesc),
                                 hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(base + s->off_tseg, s->tile_seg.data(), s->tile_seg.size() * sizeof(int),
+                       hipMemcpyHostToDevice, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_status(e, "nq_seq_run schedule upload");
   s->uploaded_for = ws;
@@ -350,7 +366,8 @@ nq_status nq_seq_run(nq_seq* s, void* workspace, size_t workspace_bytes, void* s
     }
     if (e == hipSuccess)
       e = launch_lut_persistent(reinterpret_cast<const StageDesc*>(static_cast<char*>(workspace) + s->off_sched),
-                                (int)s->segs.size(), s->ntiles, ints, (int)s->n_ints, s->T, s->grid, st);
+                                reinterpret_cast<const int*>(static_cast<char*>(workspace) + s->off_tseg), s->ntiles,
+                                ints, (int)s->n_ints, s->T, s->grid, st);
     return hip_status(e, "nq_seq_run launch");
   }
   if (s->lanes.empty()) {  // first run: the plan's streams (default priority) and events

@@ -89,7 +89,8 @@ hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t s);
 int lut_persistent_grid(int64_t T);
 // ints: [0] error flag, [1] next tile, [2] exited workgroups, [3..n_ints) counters;
 // [1..n_ints) must be zero before the first run and are left zero by each run.
-hipError_t launch_lut_persistent(const StageDesc* segs, int nseg, int ntiles, int* ints, int n_ints,
+// tile_seg[i] (device) is the index in segs of the descriptor of tile i.
+hipError_t launch_lut_persistent(const StageDesc* segs, const int* tile_seg, int ntiles, int* ints, int n_ints,
                                  int64_t T, int grid, hipStream_t s);
 
 // Matrix-core regime (T > 8).
