@@ -21,6 +21,9 @@ COMMON = [
     "-I", INCLUDE, "-I", CSRC,
     # keep the compiler from emitting packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # single-lane atomics only: the atomic optimizer would turn a counter fetch
+    # into a wave reduction whose result is waited for at once
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
 ]
 
