@@ -553,7 +553,7 @@ __device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag,
 // 4k + l/16 (one 16-byte load; 16 lanes cover 256 contiguous bytes of a word
 // row), and component q feeds the MFMA of set q.
 
-constexpr int kMfmaMaxT = 2;
+constexpr int kMfmaMaxT = 8;
 constexpr int kMRows = 512;                            // rows per tile = threads per workgroup (8 waves)
 constexpr int kPieces = 5;                            // fp8 pieces per token
 constexpr int kStepWords = 4;                         // word rows per MFMA step
@@ -561,16 +561,26 @@ constexpr int kChunkSteps = 8;                        // steps per staged chunk
 constexpr int kChunkWords = kChunkSteps * kStepWords;  // 32 word rows
 constexpr int kRingSteps = 8;                         // steps of sign words in flight per lane
 static_assert(kChunkSteps % kRingSteps == 0, "ring slots are compile-time within a chunk");
-constexpr int kStepInts = 64 * 8;                     // B fragments of one step (64 lanes x 32 bytes)
-constexpr int kBInts = kChunkSteps * kStepInts;       // B fragments of a chunk (16 KiB)
-// LDS of a workgroup, in 4-byte words: [B fragments, two chunk buffers]
-// [chunk scale exponents, two buffers of kMfmaMaxT][per-chunk maxima of an
-// input-piece tile][row sums [kMfmaMaxT][kMRows]]
-constexpr int kSigOff = 2 * kBInts;
-constexpr int kPrepGroups = kMRows / 256;           // chunks per round of an input-piece tile
-constexpr int kSlotOff = kSigOff + 2 * kMfmaMaxT;
-constexpr int kSumOff = kSlotOff + 2 * kPrepGroups * kMfmaMaxT;
-constexpr int kMfmaLds = kSumOff + kMfmaMaxT * kMRows;
+constexpr int kStepInts = 64 * 8;                     // B fragments of one step and MFMA (64 lanes x 32 bytes)
+constexpr int kPrepGroups = kMRows / 256;            // chunks per round of an input-piece tile
+// B columns are (token t, piece p) -> t*kPieces + p; every 16 of them form
+// one MFMA column group (T*kPieces columns: 1 group up to T = 3, 2 up to 6,
+// 3 up to 8).
+template <int T>
+constexpr int col_groups() { return (T * kPieces + 15) / 16; }
+// LDS of a workgroup, in 4-byte words: [B fragments, two chunk buffers of
+// kChunkSteps x col_groups x kStepInts] [chunk scale exponents, two buffers of
+// T] [per-chunk maxima of an input-piece tile] [row sums [T][kMRows]]
+template <int T>
+constexpr int b_ints() { return kChunkSteps * col_groups<T>() * kStepInts; }
+template <int T>
+constexpr int sig_off() { return 2 * b_ints<T>(); }
+template <int T>
+constexpr int slot_off() { return sig_off<T>() + 2 * T; }
+template <int T>
+constexpr int sum_off() { return slot_off<T>() + 2 * kPrepGroups * T; }
+template <int T>
+constexpr int mfma_lds() { return sum_off<T>() + T * kMRows; }
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -684,7 +694,7 @@ template <int T>
 __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* err) {
   constexpr int NC = T * kPieces;
   constexpr int64_t kChunkElems = kChunkWords * kWordBits;
-  unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + kSlotOff);  // [round&1][group][T]
+  unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + slot_off<T>());  // [round&1][group][T]
   const int tid = threadIdx.x, half = tid >> 8, task = tid & 255;  // half: this thread's group
   const int ch0 = tile * kPrepChunks;
   const int ch1 = min(ch0 + kPrepChunks, (int)cdiv(S.n_red, kChunkElems));
@@ -748,15 +758,15 @@ __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* e
 }
 
 // B columns past the last piece of the last token stay zero for the life of
-// the kernel (the builds never write them): clear them once.
+// the kernel (the chunk copies never write them): clear them once.
 template <int T>
 __device__ inline void mfma_lds_init(int* lds) {
-  constexpr int NC = T * kPieces;
-  if constexpr (NC < 16) {
-    // per step and half: 64 lanes x 4 dwords; lane = column + 16 * group
-    for (int i = threadIdx.x; i < 2 * kBInts; i += kMRows) {  // both chunk buffers
-      const int lane = (i >> 2) & 63;
-      if ((lane & 15) >= NC) lds[i] = 0;
+  constexpr int NC = T * kPieces, G = col_groups<T>();
+  if constexpr (NC < 16 * G) {
+    // per step and column group, per half: 64 lanes x 4 dwords; lane = column + 16 * lane group
+    for (int i = threadIdx.x; i < 2 * b_ints<T>(); i += kMRows) {  // both chunk buffers
+      const int lane = (i >> 2) & 63, cg = (i / kStepInts) % G;
+      if (16 * cg + (lane & 15) >= NC) lds[i] = 0;
     }
   }
 }
@@ -794,7 +804,8 @@ __device__ inline float row16_sum(float v) {
 // word per load (row counts or strides that are not multiples of 4).
 template <int T, bool W4>
 __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_flag, int* err) {
-  static_assert(T <= kMfmaMaxT && T * kPieces <= 16, "columns");
+  static_assert(T <= kMfmaMaxT, "tokens");
+  constexpr int G = col_groups<T>();
   int* lds = reinterpret_cast<int*>(ldsf);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int rb = local % S.nrb;
@@ -848,13 +859,12 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
     const int bi = tid + m * kMRows;
     const int n = bi % NC, rest = bi / NC;
     const int g = rest % 4, h = (rest / 4) % 2, kk = rest / 8;
-    lds_at[m] = bi < NB ? kk * kStepInts + h * 256 + (n + 16 * g) * 4 : kSumOff;
+    lds_at[m] = bi < NB ? (kk * G + n / 16) * kStepInts + h * 256 + (n % 16 + 16 * g) * 4 : sum_off<T>();
     blk_at[m] = min(bi, NB - 1);
   }
   const int chunk0 = (int)(span0 / (kChunkWords * kWordBits));
   const int last_chunk = (int)((S.n_red - 1) / (kChunkWords * kWordBits));
   const u32x4* bsrc = reinterpret_cast<const u32x4*>(S.bfrag);
-  const int tcol = col / kPieces, pcol = col % kPieces;  // this lane's column: token, piece
   u32x4 blk[NBT];
   int sig;
   auto load_chunk = [&](int ch) {
@@ -865,11 +875,11 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   };
   auto store_chunk = [&](int buf) {
 #pragma unroll
-    for (int m = 0; m < NBT; ++m) *reinterpret_cast<u32x4*>(lds + buf * kBInts + lds_at[m]) = blk[m];
+    for (int m = 0; m < NBT; ++m) *reinterpret_cast<u32x4*>(lds + buf * b_ints<T>() + lds_at[m]) = blk[m];
     // every thread stores (threads past T into the row-sum area, unused until
     // the tile's end), so the compiler cannot move the load into a branch
     // behind later sign-word loads
-    lds[tid < T ? kSigOff + buf * kMfmaMaxT + tid : kSumOff + tid] = sig;
+    lds[tid < T ? sig_off<T>() + buf * T + tid : sum_off<T>() + tid] = sig;
   };
   // the first sign words do not depend on the stage input: in flight while
   // the wait and the first chunk's pieces complete (loads complete in issue
@@ -885,35 +895,54 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
 
   // the sums of all chunks accumulate in acc: each chunk's B column (token t,
   // piece p) carries the MFMA scale 2^-(s_t + 4p) of that chunk
-  v4f acc[4];
+  v4f acc[4][G];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int cg = 0; cg < G; ++cg) acc[q][cg] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int c = 0; c < nchunks; ++c) {
     const int buf = c & 1;
-    // E8M0 scale of this lane's column (2^0 for columns past the last piece,
-    // whose B entries are 0; a NaN chunk has NaN pieces)
-    const int sg = lds[kSigOff + buf * kMfmaMaxT + min(tcol, T - 1)];
-    const int bscale = tcol < T ? 127 - (sg == kShiftNaN ? 0 : sg) - 4 * pcol : 127;
+    // E8M0 scale of this lane's column in every group (2^0 for columns past
+    // the last piece, whose B entries are 0; a NaN chunk has NaN pieces)
+    int bscale[G];
+#pragma unroll
+    for (int cg = 0; cg < G; ++cg) {
+      const int n = 16 * cg + col, tc = n / kPieces, pc = n % kPieces;
+      const int sg = lds[sig_off<T>() + buf * T + min(tc, T - 1)];
+      bscale[cg] = tc < T ? 127 - (sg == kShiftNaN ? 0 : sg) - 4 * pc : 127;
+    }
     load_chunk(chunk0 + c + 1);  // next chunk's pieces (or none)
 
-    const u32x4* bfrag = reinterpret_cast<const u32x4*>(lds + buf * kBInts) + lane;
-    u32x4 blo = bfrag[0], bhi = bfrag[64];
+    const u32x4* bfrag = reinterpret_cast<const u32x4*>(lds + buf * b_ints<T>()) + lane;
+    u32x4 blo[G], bhi[G];
+#pragma unroll
+    for (int cg = 0; cg < G; ++cg) {
+      blo[cg] = bfrag[cg * (kStepInts / 4)];
+      bhi[cg] = bfrag[cg * (kStepInts / 4) + 64];
+    }
 #pragma unroll
     for (int kk = 0; kk < kChunkSteps; ++kk) {
       const int k = c * kChunkSteps + kk;
-      v8i b;
-      b[0] = (int)blo.x; b[1] = (int)blo.y; b[2] = (int)blo.z; b[3] = (int)blo.w;
-      b[4] = (int)bhi.x; b[5] = (int)bhi.y; b[6] = (int)bhi.z; b[7] = (int)bhi.w;
-      if (kk + 1 < kChunkSteps) {  // next step's fragments (stale past the span; then unused)
-        blo = bfrag[(kk + 1) * (kStepInts / 4)];
-        bhi = bfrag[(kk + 1) * (kStepInts / 4) + 64];
+      v8i b[G];
+#pragma unroll
+      for (int cg = 0; cg < G; ++cg) {
+        b[cg][0] = (int)blo[cg].x; b[cg][1] = (int)blo[cg].y; b[cg][2] = (int)blo[cg].z; b[cg][3] = (int)blo[cg].w;
+        b[cg][4] = (int)bhi[cg].x; b[cg][5] = (int)bhi[cg].y; b[cg][6] = (int)bhi[cg].z; b[cg][7] = (int)bhi[cg].w;
+        if (kk + 1 < kChunkSteps) {  // next step's fragments (stale past the span; then unused)
+          blo[cg] = bfrag[((kk + 1) * G + cg) * (kStepInts / 4)];
+          bhi[cg] = bfrag[((kk + 1) * G + cg) * (kStepInts / 4) + 64];
+        }
       }
       if (k < nk) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(expand_word(ring[kk % kRingSteps][q]), b, acc[q], 4,
-                                                                    0, 0, 127, 0, bscale);
+        for (int q = 0; q < 4; ++q) {
+          const v8i a = expand_word(ring[kk % kRingSteps][q]);
+#pragma unroll
+          for (int cg = 0; cg < G; ++cg)
+            acc[q][cg] =
+                __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[cg], acc[q][cg], 4, 0, 0, 127, 0, bscale[cg]);
+        }
       }
       load_step(k + kRingSteps, ring[kk % kRingSteps]);  // past the span: out of range, no memory access
       if (kk == kChunkSteps / 2) store_chunk(buf ^ 1);    // the other buffer was last read in chunk c-1
@@ -921,16 +950,23 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
     __syncthreads();  // chunk c+1's fragments are in LDS; every wave is done with chunk c's
   }
 
-  // add the pieces of each token across the lanes of a row; lane col == 0
-  // of every row group writes its 4 rows of every set
-  float* sums = ldsf + kSumOff;
+  // add the pieces of each token across the lanes of a row (and the column
+  // groups); lane col == 0 of every row group writes its 4 rows of every set
+  float* sums = ldsf + sum_off<T>();
 #pragma unroll
   for (int t = 0; t < T; ++t) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {  // C row 4*grp + r of set q is row 16*grp + 4r + q of the wave
       float v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = row16_sum(tcol == t ? acc[q][r] : 0.0f);
+      for (int q = 0; q < 4; ++q) {
+        float u = 0.0f;
+#pragma unroll
+        for (int cg = 0; cg < G; ++cg)
+          if ((16 * cg + 15) / kPieces >= t && (16 * cg) / kPieces <= t)  // the group holds columns of token t
+            u += (16 * cg + col) / kPieces == t ? acc[q][cg][r] : 0.0f;
+        v[q] = row16_sum(u);
+      }
       if (col == 0)
         *reinterpret_cast<float4*>(sums + t * kMRows + wv * 64 + grp * 16 + 4 * r) = make_float4(v[0], v[1], v[2], v[3]);
     }
@@ -952,11 +988,13 @@ constexpr bool use_mfma() { return T <= kMfmaMaxT; }
 // rows per tile = threads per workgroup
 template <int T>
 constexpr int tile_rows() { return use_mfma<T>() ? kMRows : kRows; }
-// matrix-core kernels: 4 waves per SIMD (at most 128 VGPRs), 2 workgroups per CU
+// matrix-core kernels: with one column group 4 waves per SIMD (at most 128
+// VGPRs) and 2 workgroups per CU; with more (accumulators and B fragments of
+// every group) 2 waves per SIMD, one workgroup per CU
 template <int T>
-constexpr int min_waves() { return use_mfma<T>() ? 4 : 1; }
+constexpr int min_waves() { return use_mfma<T>() ? (col_groups<T>() == 1 ? 4 : 2) : 1; }
 template <int T>
-constexpr int stage_lds_floats() { return use_mfma<T>() ? kMfmaLds : Geo<T>::LUT; }
+constexpr int stage_lds_floats() { return use_mfma<T>() ? mfma_lds<T>() : Geo<T>::LUT; }
 
 template <int T>
 __device__ inline void stage_init(float* lds) {

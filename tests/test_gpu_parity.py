@@ -325,7 +325,8 @@ def _decode_inputs(kind: str, T: int, d: int, x_dtype: str) -> np.ndarray:
 
 
 @pytest.mark.parametrize("kind", ["outliers", "spread", "tiny", "huge", "zero_chunks", "biased"])
-@pytest.mark.parametrize("T,x_dtype", [(1, "bf16"), (1, "f32"), (2, "f32")])
+# T = 4 and 7: a token's pieces straddle two MFMA column groups
+@pytest.mark.parametrize("T,x_dtype", [(1, "bf16"), (1, "f32"), (2, "f32"), (4, "f32"), (7, "f32"), (8, "bf16")])
 def test_decode_input_ranges(kind, T, x_dtype):
     shape = synth.LayerShape("ranges", 320, 4096, 1088)  # ragged rows and rank, 4 chunks of x, 2 of t
     cfg = G.tiny_config(f"ranges/{x_dtype}", x_dtype=x_dtype)
@@ -345,15 +346,19 @@ def test_decode_all_zero_input():
 
 
 @pytest.mark.parametrize("bad", [np.nan, np.inf])
-def test_decode_non_finite_input(bad):
-    # one non-finite element reaches every output: the oracle's sums are NaN
-    # or +-inf; the decode result must not be finite anywhere
+@pytest.mark.parametrize("T", [1, 6])
+def test_decode_non_finite_input(bad, T):
+    # one non-finite element of the last token reaches every output of that
+    # token: the oracle's sums are NaN or +-inf; the decode result must not be
+    # finite anywhere in that token, and the other tokens stay exact
     shape = synth.LayerShape("nonfinite", 256, 2048, 256)
     cfg = G.tiny_config("nonfinite")
     dev, ref, _ = G.latent_layer(cfg, shape)
-    x = synth.activations("nonfinite/x", 1, shape.d_in, "f32")
-    x[0, 1500] = bad
+    x = synth.activations("nonfinite/x", T, shape.d_in, "f32")
+    x[T - 1, 1500] = bad
     y = nq.lrb_linear(dev, G.to_device_x(x, "f32")).cpu().numpy()
     y_ref = O.linear_factored_ref(ref, x)
-    assert not np.any(np.isfinite(y_ref))
-    assert not np.any(np.isfinite(y))
+    assert not np.any(np.isfinite(y_ref[T - 1]))
+    assert not np.any(np.isfinite(y[T - 1]))
+    if T > 1:
+        assert O.rel_err(y[: T - 1], y_ref[: T - 1]) <= 1e-5
