@@ -25,8 +25,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16/bf16 matrix cores, TFLOP/s
 VALU_LANE_OPS = 256 * 64 * 2.4e9  # MI355X vector ALU lane-ops per second (256 CUs, 2.4 GHz)
-DECODE_SRC = os.path.join(ROOT, "sub_bit_weight_amd", "csrc", "decode_lut.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_lut_persistent_70b_stack_hbm_traffic.md")
+DECODE_SRC = os.path.join(ROOT, "sub_bit_weight_amd", "csrc", "decode_mfma.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_persistent_70b_stack_hbm_traffic.md")
 
 
 def log(msg: str) -> None:
@@ -82,7 +82,7 @@ def measured_traffic():
     fields = dict(line.split(":", 1) for line in text.splitlines() if ":" in line and line.startswith("- "))
     fields = {k[2:].strip(): v.strip() for k, v in fields.items()}
     src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-    if fields.get("decode_lut.hip sha256") != src_hash:
+    if fields.get("decode_mfma.hip sha256") != src_hash:
         return None
     try:
         return float(fields["hbm bytes per launch"])
@@ -349,7 +349,7 @@ def main() -> int:
                    "global_batch": T, "layers": args.layers, "parallelism": "single-gpu"},
         "hbm_gbs": gbs,
         "algorithmic_bytes_per_step": bytes_step,
-        "roofline": {"bound": "hbm", "kernel": "lut_persistent_kernel<1> (one launch per step)",
+        "roofline": {"bound": "hbm", "kernel": "dec_persistent_kernel<1> (one launch per step)",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic()},
         # The decode kernel's own ceiling: 18 VALU lane-ops per 32-weight sign

@@ -110,8 +110,11 @@ size_t nq_lrb_workspace_bytes(const nq_lrb* L, int64_t T);
  * kernels for batches (section 4 "Results", subsection "Inference Performance").
  *   x: [T][d_in] row-major, fp32 or bf16 (x_dtype);  y: [T][d_out] fp32.
  *   workspace: at least nq_lrb_workspace_bytes(L, T) bytes, 256-byte aligned.
- * Regimes: T <= 8 runs the decode kernels (fp32 arithmetic throughout);
- * T > 8 runs the matrix-core kernels: each token row of a stage's activations
+ * Regimes: T <= 8 runs the decode kernels: each token's stage input is scaled
+ * per chunk of 1024 elements by a power of two and split into five fp8 pieces
+ * that carry it to about 2^-20 of the chunk's largest value, multiplied by
+ * the exact +-1 signs on the matrix cores with fp32 accumulation;
+ * T > 8 runs the GEMM kernels: each token row of a stage's activations
  * is scaled by an exact power of two and rounded to fp16 (two fp16 terms for
  * fp32 x), multiplied by the exact +-1 signs with fp32 accumulation, and
  * scaled back.

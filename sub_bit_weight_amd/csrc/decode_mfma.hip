@@ -1,4 +1,4 @@
-// Decode regime (T <= 8), table-lookup kernels.
+// Decode regime (T <= 8): matrix-core tiles for the low-rank binary linear.
 //
 // The layer is evaluated in factored form, stage 1 t = V^T (s2 (.) x) and
 // stage 2 y = s1 (.) (U t) (research.samsung.com NanoQuant blog, section 2,
@@ -6,24 +6,21 @@
 // GEMV regime for token-by-token decoding is section 4, "Inference
 // Performance").  Both stages have the form
 //     out[t][o] = sum_e sign(o,e) * v[t][e],   sign from words[e/32][o] bit e%32.
+// The regime is bound by the sign-word bytes streamed from HBM.
 //
-// Design (gfx950):
-//  * One output row per lane: a wave reads one word row of 64 consecutive
-//    outputs (256 contiguous bytes) and every lane needs the same elements of v.
-//  * Per group of 4 reduction elements the workgroup builds, in LDS, the 16
-//    signed sums  L[g][n] = sum_b (bit b of n ? -v[4g+b] : +v[4g+b])  (the sign
-//    is applied by flipping the float sign bit).  A 4-bit nibble of a sign word
-//    then selects one entry: one LDS read and one fp32 add per 4 weights.  All
-//    lanes of a wave read the same group, so the 16 candidate entries sit in 16
-//    different banks and equal nibbles broadcast: the reads are conflict-free.
-//  * The reduction is split into chunks of at most kcmax(T) elements; each
-//    (row block, chunk) is one tile.  Partial sums go to the workspace; the last
-//    tile of a row block to finish (arrival counter) adds them in chunk order,
-//    so results are deterministic, then applies s1 for stage 2.
-//  * A persistent kernel runs a whole sequence of linears from one launch: tiles
-//    are taken in schedule order from an atomic counter, and a stage-2 tile
-//    first waits until its linear's stage-1 row blocks are all final.  Waits
-//    only target earlier tiles, which are already running, so the queue always
+// Structure:
+//  * A tile is a block of 512 output rows over a reduction span (single calls
+//    split the reduction; sequences give a tile the whole reduction).  Partial
+//    sums of split spans go to the workspace; the last span of a row block to
+//    finish (arrival counter) adds them in span order, so results are
+//    deterministic, then applies s1 for stage 2.
+//  * Each stage input is first cut into fp8 pieces by input-piece tiles; the
+//    row-block tiles multiply fp4 +-1 sign operands by those pieces on the
+//    matrix cores (details before mfma_tile below).
+//  * A persistent kernel runs a whole sequence of linears from one launch:
+//    tiles are taken in schedule order from an atomic counter, and a tile
+//    whose input is produced by other tiles first waits for them.  Waits only
+//    target earlier tiles, which are already running, so the queue always
 //    drains; each wait also has a spin limit that records an error and exits.
 #include "nq_internal.h"
 
@@ -31,35 +28,8 @@ namespace nq {
 
 namespace {
 
-constexpr int kRows = 256;           // rows (outputs) per tile = threads per workgroup
-constexpr int kLutFloats = 8192;     // 32 KiB of table entries per workgroup (plus padding)
 constexpr unsigned kSpinLimit = 1u << 21;  // ~1 s of polling, then give up and flag
 
-// Table geometry for T tokens.  Entries are token-innermost: the TT tokens of
-// one (group, nibble) entry are adjacent, so one ds_read_b32/b64/b128 fetches
-// them together; T > 4 uses NQ = 2 such arrays.  Each group's 16 entries are
-// followed by 16 bytes of padding: the 16-byte stores that build the tables
-// (one group per thread) then fall into distinct banks for 8 consecutive
-// threads, while a group's 16 entries still occupy 16 distinct banks for the
-// lookups.  The reduction is walked in chunks of GMAX groups (4*GMAX elements),
-// each chunk in NB batches of B sign words; D batches of words are kept in
-// flight per lane.
-template <int T>
-struct Geo {
-  static constexpr int TT = T == 1 ? 1 : (T == 2 ? 2 : 4);
-  static constexpr int NQ = (T + TT - 1) / TT;
-  static constexpr int QF = (kLutFloats / NQ) / (16 * TT) * (16 * TT + 4);  // floats per array
-  static constexpr int GMAX = kLutFloats / NQ / (16 * TT);  // groups per chunk
-  static constexpr int GS = 16 * TT + 4;                     // floats per group (with padding)
-  static constexpr int LUT = NQ * GMAX * GS;                 // floats of tables per workgroup
-  static constexpr int CW = GMAX / 8;                        // words per chunk
-  static constexpr int B = CW >= 32 ? 8 : (CW >= 16 ? 4 : 2);  // words per batch
-  static constexpr int NB = CW / B;                          // batches per chunk
-  static constexpr int D = 4;                                // batches in flight
-  static constexpr int SHIFT = TT == 1 ? 2 : (TT == 2 ? 3 : 4);  // log2 of the entry size in bytes
-  static constexpr int GPT = (GMAX + kRows - 1) / kRows;     // table groups built per thread
-  static_assert(NB % D == 0, "batches per chunk must be a multiple of the ring depth");
-};
 
 __device__ inline float bf16_bits(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -112,192 +82,6 @@ __device__ inline void stores_done_barrier() {
   __syncthreads();
 }
 
-// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
-// outstanding global load, which would drain the sign words kept in flight.
-__device__ inline void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// (selected byte BYTE of w) & mask, one VALU op (SDWA byte select).
-template <int BYTE>
-__device__ inline uint32_t and_byte(uint32_t mask, uint32_t w) {
-  uint32_t r;
-  if constexpr (BYTE == 0)
-    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
-        : "=v"(r) : "v"(mask), "v"(w));
-  if constexpr (BYTE == 1)
-    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
-        : "=v"(r) : "v"(mask), "v"(w));
-  if constexpr (BYTE == 2)
-    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
-        : "=v"(r) : "v"(mask), "v"(w));
-  if constexpr (BYTE == 3)
-    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
-        : "=v"(r) : "v"(mask), "v"(w));
-  return r;
-}
-
-// The raw activations and column scales one thread needs for its table groups
-// of one chunk (GPT groups x 4 elements).  They are kept raw until the tables
-// are built, so the loads stay in flight while the previous chunk is processed.
-template <int T>
-struct TableInputs {
-  uint32_t x[Geo<T>::GPT][T][4];  // bf16 or fp32 bit patterns
-  float cs[Geo<T>::GPT][4];
-};
-
-template <int T>
-__device__ inline void load_inputs(const StageDesc& S, int64_t c0, int64_t cend, TableInputs<T>& in) {
-  using G = Geo<T>;
-#pragma unroll
-  for (int i = 0; i < G::GPT; ++i) {
-    const int g = threadIdx.x + i * kRows;
-    const int64_t j0 = c0 + 4 * g;
-    // a whole group in range: one 8- or 16-byte load per token, one for the
-    // scales (T <= 2 only: for more tokens the extra registers cost occupancy)
-    if (T <= 2 && S.x_vec && g < G::GMAX && j0 + 4 <= cend) {
-      if (S.colscale) {
-        const u32x4 c = gload(reinterpret_cast<const u32x4*>(S.colscale + j0));
-#pragma unroll
-        for (int b = 0; b < 4; ++b) in.cs[i][b] = __uint_as_float(c[b]);
-      } else {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) in.cs[i][b] = 1.0f;
-      }
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int64_t idx = (int64_t)t * S.n_red + j0;
-        if (S.x_bf16) {
-          const u32x2 w = gload(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(S.xin) + idx));
-          in.x[i][t][0] = w[0] & 0xFFFFu;
-          in.x[i][t][1] = w[0] >> 16;
-          in.x[i][t][2] = w[1] & 0xFFFFu;
-          in.x[i][t][3] = w[1] >> 16;
-        } else {
-          const u32x4 w = gload(reinterpret_cast<const u32x4*>(static_cast<const uint32_t*>(S.xin) + idx));
-#pragma unroll
-          for (int b = 0; b < 4; ++b) in.x[i][t][b] = w[b];
-        }
-      }
-      continue;
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t j = c0 + 4 * g + b;
-      const bool ok = g < G::GMAX && j < cend;
-      const int64_t jc = ok ? j : 0;  // in-bounds index; the value is dropped when !ok
-      in.cs[i][b] = S.colscale ? gload(S.colscale + jc) : 1.0f;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int64_t idx = (int64_t)t * S.n_red + jc;
-        in.x[i][t][b] = S.x_bf16 ? (uint32_t)gload(static_cast<const uint16_t*>(S.xin) + idx)
-                                 : gload(static_cast<const uint32_t*>(S.xin) + idx);
-      }
-    }
-  }
-}
-
-// Write the 16 signed sums of each of this thread's groups:
-//   L[g][n] = sum_b (bit b of n ? -z[4g+b] : +z[4g+b])
-// (negation flips the float sign bit).
-template <int T>
-__device__ inline void build_tables(const TableInputs<T>& in, int64_t c0, int64_t cend, int x_bf16, float* lut) {
-  using G = Geo<T>;
-#pragma unroll
-  for (int i = 0; i < G::GPT; ++i) {
-    const int g = threadIdx.x + i * kRows;
-    if (g >= G::GMAX) break;
-#pragma unroll
-    for (int q = 0; q < G::NQ; ++q) {
-      float ent[16][G::TT];
-#pragma unroll
-      for (int tt = 0; tt < G::TT; ++tt) {
-        const int t = q * G::TT + tt;
-        float z[4] = {0.f, 0.f, 0.f, 0.f};
-        if (t < T) {
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t raw = in.x[i][t < T ? t : 0][b];
-            const float v = x_bf16 ? bf16_bits(raw) : __uint_as_float(raw);
-            z[b] = (c0 + 4 * g + b < cend) ? v * in.cs[i][b] : 0.0f;
-          }
-        }
-        const float p01[4] = {z[0] + z[1], -z[0] + z[1], z[0] - z[1], -z[0] - z[1]};
-        const float p23[4] = {z[2] + z[3], -z[2] + z[3], z[2] - z[3], -z[2] - z[3]};
-#pragma unroll
-        for (int n = 0; n < 16; ++n) ent[n][tt] = p01[n & 3] + p23[n >> 2];
-      }
-      float4* dst = reinterpret_cast<float4*>(lut + q * G::QF + g * G::GS);
-      const float* src = &ent[0][0];
-#pragma unroll
-      for (int k = 0; k < 4 * G::TT; ++k)
-        dst[k] = make_float4(src[4 * k], src[4 * k + 1], src[4 * k + 2], src[4 * k + 3]);
-    }
-  }
-}
-
-// Table reads for one sign word: the 8 nibbles of word WI (compile-time index
-// within the chunk, so table offsets are immediates) select 8 entries of T
-// floats each.
-template <int T, int WI>
-__device__ inline void read_entries(uint32_t w, const float* lut, float (&e)[8][Geo<T>::NQ * Geo<T>::TT]) {
-  using G = Geo<T>;
-  const uint32_t mask = 15u << G::SHIFT;
-  const char* base = reinterpret_cast<const char*>(lut);
-  const uint32_t lo = w << G::SHIFT;        // bytes -> nibbles 0,2,4,6 times the entry size
-  const uint32_t hi = w >> (4 - G::SHIFT);  // bytes -> nibbles 1,3,5,7 times the entry size
-  uint32_t a[8];
-  a[0] = and_byte<0>(mask, lo);
-  a[1] = and_byte<0>(mask, hi);
-  a[2] = and_byte<1>(mask, lo);
-  a[3] = and_byte<1>(mask, hi);
-  a[4] = and_byte<2>(mask, lo);
-  a[5] = and_byte<2>(mask, hi);
-  a[6] = and_byte<3>(mask, lo);
-  a[7] = and_byte<3>(mask, hi);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int group = WI * 8 + k;
-#pragma unroll
-    for (int q = 0; q < G::NQ; ++q) {
-      const char* p = base + (q * G::QF * 4) + group * G::GS * 4 + a[k];
-      if constexpr (G::TT == 1) {
-        e[k][q] = *reinterpret_cast<const float*>(p);
-      } else if constexpr (G::TT == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(p);
-        e[k][2 * q] = v.x;
-        e[k][2 * q + 1] = v.y;
-      } else {
-        const float4 v = *reinterpret_cast<const float4*>(p);
-        e[k][4 * q] = v.x;
-        e[k][4 * q + 1] = v.y;
-        e[k][4 * q + 2] = v.z;
-        e[k][4 * q + 3] = v.w;
-      }
-    }
-  }
-}
-
-// acc holds two partial sums per token (even / odd nibbles): shorter add chains.
-template <int T>
-__device__ inline void add_entries(const float (&e)[8][Geo<T>::NQ * Geo<T>::TT], float* acc) {
-  using G = Geo<T>;
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-#pragma unroll
-    for (int t = 0; t < G::NQ * G::TT; ++t)
-      if (t < T) acc[(k & 1) * G::NQ * G::TT + t] += e[k][t];
-}
-
-// One chunk, software-pipelined: while the entries of word WI are added, the
-// reads for word WI+1 are in flight.  Sign words come from a ring of D batches
-// of B words: when the last word of batch b has been read, its ring slot is
-// refilled with the words D batches ahead (possibly in the next chunk).  Words
-// past the end of a tile's reduction span only select table entries of groups
-// past the span, which are all zero, so loads need no masking: the word index
-// is clamped (uniformly) to stay inside the matrix.
 // Sign words are read with buffer loads: the word row's byte offset is a scalar
 // (uniform) operand and the lane's column a 32-bit vector offset, so a load
 // costs no vector ALU work.  Sign-word buffers are below 2 GiB (checked by the
@@ -306,81 +90,12 @@ __device__ inline void add_entries(const float (&e)[8][Geo<T>::NQ * Geo<T>::TT],
 // policy bit 1, "nt"), so they do not push the input pieces, which every row
 // block re-reads, out of the L2 (measured: 5.3 -> 5.6 TB/s on the 70B stack).
 constexpr int kStreamLoad = 2;
-__device__ inline __amdgpu_buffer_rsrc_t word_rsrc(const uint32_t* bits) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(bits), (short)0, 0x7fffffff, 0x00020000);
-}
-// w < 2^26 and w * ld4 < 2^31 (the host checks the buffer size), so 32-bit
-// scalar arithmetic suffices for the offsets.
-__device__ inline uint32_t load_word(__amdgpu_buffer_rsrc_t r, uint32_t lane_bytes, int w, uint32_t ld4) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)lane_bytes, (int)((uint32_t)w * ld4), kStreamLoad);
-}
 
-template <int T, int WI>
-__device__ inline void chunk_words(__amdgpu_buffer_rsrc_t bits, uint32_t lane_bytes, uint32_t ld4, int wnext, int wlast,
-                                   int nwords, uint32_t (&ring)[Geo<T>::D][Geo<T>::B], const float* lut, float* acc,
-                                   float (&cur)[8][Geo<T>::NQ * Geo<T>::TT]) {
-  using G = Geo<T>;
-  if constexpr (WI < G::CW) {
-    constexpr int b = WI / G::B, j = WI % G::B;
-    // a short last chunk stops at the first batch past its words (uniform
-    // branch); the tile ends there, so the ring is not needed any more
-    if constexpr (j == 0 && WI > 0)
-      if (WI >= nwords) return;
-    float nxt[8][G::NQ * G::TT];
-    if constexpr (WI + 1 < G::CW) {
-      constexpr int b1 = (WI + 1) / G::B, j1 = (WI + 1) % G::B;
-      read_entries<T, WI + 1>(ring[b1 % G::D][j1], lut, nxt);
-    }
-    if constexpr (j == G::B - 1) {
-#pragma unroll
-      for (int jj = 0; jj < G::B; ++jj) {
-        const int w = min(wnext + b * G::B + jj, wlast);
-        ring[b % G::D][jj] = load_word(bits, lane_bytes, w, ld4);
-      }
-    }
-    add_entries<T>(cur, acc);
-    __builtin_amdgcn_sched_barrier(0);  // one word per scheduling region: bounded registers
-    if constexpr (WI + 1 < G::CW) chunk_words<T, WI + 1>(bits, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, nxt);
-  }
-}
-
-// The same with the table reads two words ahead (more LDS latency hidden, at
-// the cost of one more set of entries in registers): used for T = 1, where
-// the entries are single floats.
-template <int T, int WI>
-__device__ inline void chunk_words2(__amdgpu_buffer_rsrc_t bits, uint32_t lane_bytes, uint32_t ld4, int wnext,
-                                    int wlast, int nwords, uint32_t (&ring)[Geo<T>::D][Geo<T>::B], const float* lut,
-                                    float* acc, float (&cur)[8][Geo<T>::NQ * Geo<T>::TT],
-                                    float (&nx1)[8][Geo<T>::NQ * Geo<T>::TT]) {
-  using G = Geo<T>;
-  if constexpr (WI < G::CW) {
-    constexpr int b = WI / G::B, j = WI % G::B;
-    if constexpr (j == 0 && WI > 0)
-      if (WI >= nwords) return;
-    float nx2[8][G::NQ * G::TT];
-    if constexpr (WI + 2 < G::CW) {
-      constexpr int b2 = (WI + 2) / G::B, j2 = (WI + 2) % G::B;
-      read_entries<T, WI + 2>(ring[b2 % G::D][j2], lut, nx2);
-    }
-    // every word of batch b has had its entries read (word WI two steps ago)
-    if constexpr (j == G::B - 1) {
-#pragma unroll
-      for (int jj = 0; jj < G::B; ++jj) {
-        const int w = min(wnext + b * G::B + jj, wlast);
-        ring[b % G::D][jj] = load_word(bits, lane_bytes, w, ld4);
-      }
-    }
-    add_entries<T>(cur, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (WI + 1 < G::CW)
-      chunk_words2<T, WI + 1>(bits, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, nx1, nx2);
-  }
-}
-
-// A stage-2 tile of a sequence waits until every row block of its linear's
-// stage 1 is final.  Thread 0 polls with relaxed loads (an acquire per poll
-// would invalidate caches that streaming workgroups are using), then acquires
-// once; the barrier releases the workgroup.
+// A tile whose input is made by other tiles of the same launch (a stage by
+// its input-piece tiles, the pieces of t by the stage-1 row blocks) waits
+// until their counter reaches its target.  Thread 0 polls with relaxed loads
+// (an acquire per poll would invalidate caches that streaming workgroups are
+// using), then acquires once; the barrier releases the workgroup.
 __device__ inline void wait_input(const StageDesc& S, int* err) {
   if (!S.wait_ctr) return;
   if (threadIdx.x == 0) {
@@ -453,105 +168,47 @@ __device__ void finish_rows(const StageDesc& S, int rb, int ks, int64_t o, bool 
   __syncthreads();
 }
 
-// One tile: row block rb (one row per lane) over reduction span ks of stage S.
-template <int T>
-__device__ void lut_tile(const StageDesc& S, int local, float* lut, int* s_flag, int* err) {
-  using G = Geo<T>;
-  const int tid = threadIdx.x;
-  const int rb = local % S.nrb;
-  const int ks = local / S.nrb;
-  const int64_t span0 = (int64_t)ks * S.kc;                 // this tile's reduction span
-  const int64_t span1 = imin(span0 + S.kc, S.n_red);
-  const int64_t o = (int64_t)rb * kRows + tid;
-  const bool valid = o < S.n_rows;
-  // word-row indices and the row stride in bytes, as wave-uniform 32-bit values
-  const int w0 = __builtin_amdgcn_readfirstlane((int)(span0 / kWordBits));
-  const int wlast = __builtin_amdgcn_readfirstlane((int)(cdiv(S.n_red, kWordBits) - 1));  // last word row
-  const uint32_t ld4 = __builtin_amdgcn_readfirstlane((uint32_t)(S.ld * 4));
-  // lanes past the last row read row n_rows-1 and store nothing
-  const uint32_t lane_bytes = 4u * (uint32_t)(valid ? o : S.n_rows - 1);
-  const __amdgpu_buffer_rsrc_t wrsrc = word_rsrc(S.bits);
-  const int nchunks = (int)cdiv(span1 - span0, 4 * G::GMAX);
 
-  wait_input(S, err);
-
-  // fill the ring with the first D batches (independent of the tables)
-  uint32_t ring[G::D][G::B];
-#pragma unroll
-  for (int d = 0; d < G::D; ++d)
-#pragma unroll
-    for (int j = 0; j < G::B; ++j) ring[d][j] = load_word(wrsrc, lane_bytes, min(w0 + d * G::B + j, wlast), ld4);
-
-  TableInputs<T> in;
-  load_inputs<T>(S, span0, span1, in);
-
-  float acc[2 * G::NQ * G::TT];  // [even/odd nibbles][token]
-#pragma unroll
-  for (int t = 0; t < 2 * G::NQ * G::TT; ++t) acc[t] = 0.0f;
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int64_t c0 = span0 + (int64_t)c * 4 * G::GMAX;
-    lds_barrier();  // everyone is done with the previous chunk's tables
-    build_tables<T>(in, c0, span1, S.x_bf16, lut);
-    if (c + 1 < nchunks) load_inputs<T>(S, c0 + 4 * G::GMAX, span1, in);  // next chunk's inputs
-    lds_barrier();
-    const int wnext = w0 + c * (G::CW) + G::D * G::B;  // first word not yet in the ring
-    const int nwords = (int)imin(G::CW, cdiv(span1 - c0, kWordBits));  // words of this chunk
-    float first[8][G::NQ * G::TT];
-    read_entries<T, 0>(ring[0][0], lut, first);
-    if constexpr (T == 1) {
-      float second[8][G::NQ * G::TT];
-      read_entries<T, 1>(ring[0][1], lut, second);
-      chunk_words2<T, 0>(wrsrc, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, first, second);
-    } else {
-      chunk_words<T, 0>(wrsrc, lane_bytes, ld4, wnext, wlast, nwords, ring, lut, acc, first);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < G::NQ * G::TT; ++t) acc[t] += acc[G::NQ * G::TT + t];
-
-  finish_rows<T>(S, rb, ks, o, valid, acc, s_flag);
-}
-
-
-// ------------------------------------------------- matrix-core tiles (T <= 2)
+// ------------------------------------------------------- matrix-core tiles
 //
-// For one or two tokens the lookups above are bound by the LDS instruction
-// rate (eight 4-byte lookups per sign word and lane).  These tiles run the
-// sign matrix through the matrix cores instead:
+// Evaluating the sign sums on the vector ALU costs an instruction or more per
+// weight bit, several times what HBM delivers per instruction slot (and table
+// lookups per 4-bit nibble are bound by the LDS instruction rate).  These
+// tiles run the sign matrix through the matrix cores instead:
 //  * A sign word becomes four dwords of fp4 (e2m1) values: dword j holds, in
-//    nibble i, element 4i+3-j as +1.0 (0x2) or -1.0 (0xA): the word shifted
-//    left by j (j adds), masked to bit 3 of every nibble, ORed with 0x2 in
-//    every nibble.  That is eleven full-rate VALU operations per word.
+//    nibble i, element 4i+3-j as +1.0 (0x2) or -1.0 (0xA): the word doubled j
+//    times, masked to bit 3 of every nibble, ORed with 0x2 in every nibble.
+//    That is eleven full-rate VALU operations per word.
 //  * The inputs v = colscale (.) x are cut into fp8 (e4m3) pieces:
 //    v * 2^s = q0 + q1/16 + q2/256 + ... (each q the round-to-nearest fp8 of
-//    the scaled remainder), six pieces per token, each piece a matrix column.
+//    the scaled remainder), kPieces per token, each piece a matrix column.
 //    2^s brings the chunk's largest |v| into [64, 128), so no piece saturates;
-//    the six pieces carry v to about 2^-24 of that largest value.
-//  * One v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 A, fp8 B, unit scales) then
-//    gives, for 16 rows and 128 reduction elements, the signed sums of every
-//    piece of every token.  Products of +-1 and fp8 values are exact and
-//    accumulate in fp32; each chunk's sums are scaled back by 2^-(s+4p) and
-//    added up per column, the pieces of a token are added across lanes at the
-//    end of the tile.
+//    five pieces carry v to about 2^-20 of that largest value.
+//  * One v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 A, fp8 B; the B scale of a
+//    column is the 2^-(s+4p) of its piece) then gives, for 16 rows and 128
+//    reduction elements, the signed sums of 16 piece columns (one column
+//    group; up to three groups for T <= 8).  Products of +-1 and fp8 values
+//    are exact and accumulate in fp32 across the chunks of the span; the
+//    pieces of a token are added across lanes at the end of the tile.
 // Operand layouts of the 16x16x128 fp4 x fp8 form (measured on the device):
 // lane l holds A row l%16, reduction elements 32*(l/16) + [0, 32) as nibbles
 // (dword d, nibble i = element 8d+i); B column l%16, elements 16*(l/16) +
 // [0, 16) in bytes 0..15 and 64 + 16*(l/16) + [0, 16) in bytes 16..31; C
-// column l%16, rows 4*(l/16) + [0, 4).
+// column l%16, rows 4*(l/16) + [0, 4).  The expansion above permutes the
+// elements within each lane's 32, and the B pieces follow the same order.
 //
 // The pieces of a stage's input are made once per stage, by input-piece
-// tiles (one per chunk of 1024 elements), and stored in the workspace in a
-// compact form (only the 16-byte fragment blocks of the T*6 used columns);
-// every row-block tile of the stage copies them into LDS chunk by chunk.
-// (Making them in every row-block tile took about a fifth of the stream
-// rate: the loads of x and s2, the chunk maxima and the conversions.)
+// tiles (eight chunks of 1024 elements each), and stored in the workspace in
+// a compact form (only the 16-byte fragment blocks of the T*kPieces used
+// columns); every row-block tile of the stage copies them into LDS chunk by
+// chunk.  (Making them in every row-block tile took about a fifth of the
+// stream rate: the loads of x and s2, the chunk maxima and the conversions.)
 //
 // A workgroup covers 512 rows: each of 8 waves 64 rows as four sets of 16, set q
 // holding rows 4m + q (m = 0..15) of the wave's 64.  For MFMA step k (128
 // elements) lane l reads the words of rows 4*(l%16) + [0, 4) in word row
 // 4k + l/16 (one 16-byte load; 16 lanes cover 256 contiguous bytes of a word
-// row), and component q feeds the MFMA of set q.
+// row), and component q feeds the MFMAs of set q.
 
 constexpr int kMfmaMaxT = 8;
 constexpr int kMRows = 512;                            // rows per tile = threads per workgroup (8 waves)
@@ -676,9 +333,10 @@ __device__ inline int max_fp8_exponent(int d) {
 }
 
 // Compact piece layout of one chunk: 16-byte blocks, block
-// ((step*2 + half)*4 + group)*NC + column holds the fragment bytes of LDS
-// lane column + 16*group, half `half`, of MFMA step `step` (NC = T*6 used
-// columns; column t*6 + p is piece p of token t).
+// ((step*2 + half)*4 + group)*NC + column holds half `half` of the B fragment
+// of lane (column % 16) + 16*group in column group column / 16, MFMA step
+// `step` (NC = T*kPieces used columns; column t*kPieces + p is piece p of
+// token t).
 template <int T>
 constexpr int chunk_blocks() { return kChunkSteps * 2 * 4 * T * kPieces; }
 
@@ -979,63 +637,49 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   finish_rows<T>(S, rb, ks, o, o < S.n_rows, accr, s_flag);
 }
 
-// The workgroup's two shared flag words live in the first entries of the
-// table array: every write to them follows a barrier after the last table
-// read of a tile, and every read precedes the barrier before the next tables
-// are built.
+// With one column group: 4 waves per SIMD (at most 128 VGPRs) and 2
+// workgroups per CU; with more (accumulators and B fragments of every group)
+// 2 waves per SIMD, one workgroup per CU.
 template <int T>
-constexpr bool use_mfma() { return T <= kMfmaMaxT; }
-// rows per tile = threads per workgroup
-template <int T>
-constexpr int tile_rows() { return use_mfma<T>() ? kMRows : kRows; }
-// matrix-core kernels: with one column group 4 waves per SIMD (at most 128
-// VGPRs) and 2 workgroups per CU; with more (accumulators and B fragments of
-// every group) 2 waves per SIMD, one workgroup per CU
-template <int T>
-constexpr int min_waves() { return use_mfma<T>() ? (col_groups<T>() == 1 ? 4 : 2) : 1; }
-template <int T>
-constexpr int stage_lds_floats() { return use_mfma<T>() ? mfma_lds<T>() : Geo<T>::LUT; }
+constexpr int min_waves() { return col_groups<T>() == 1 ? 4 : 2; }
 
-template <int T>
-__device__ inline void stage_init(float* lds) {
-  if constexpr (use_mfma<T>()) mfma_lds_init<T>(reinterpret_cast<int*>(lds));
-}
+// The workgroup's two shared flag words live in the first entries of LDS (B
+// fragments of column 0 in chunk buffer 0): every write to them follows the
+// barrier after a tile's last fragment read, and the next tile's first chunk
+// copy follows the barrier after their last read.
 template <int T>
 __device__ inline void stage_tile(const StageDesc& S, int local, float* lds, int* s_flag, int* err) {
-  if constexpr (use_mfma<T>()) {
-    if (S.kind == 1)
-      mfma_prep_tile<T>(S, local, lds, err);
-    else if (S.w_vec)
-      mfma_tile<T, true>(S, local, lds, s_flag, err);
-    else
-      mfma_tile<T, false>(S, local, lds, s_flag, err);
-  } else
-    lut_tile<T>(S, local, lds, s_flag, err);
+  if (S.kind == 1)
+    mfma_prep_tile<T>(S, local, lds, err);
+  else if (S.w_vec)
+    mfma_tile<T, true>(S, local, lds, s_flag, err);
+  else
+    mfma_tile<T, false>(S, local, lds, s_flag, err);
 }
 
 template <int T>
-__global__ __launch_bounds__(tile_rows<T>()) __attribute__((amdgpu_waves_per_eu(min_waves<T>())))
-void lut_stage_kernel(StageDesc S, int* err) {
-  __shared__ __attribute__((aligned(16))) float lut[stage_lds_floats<T>()];
-  int* s_flag = reinterpret_cast<int*>(lut);
-  stage_init<T>(lut);
+__global__ __launch_bounds__(kMRows) __attribute__((amdgpu_waves_per_eu(min_waves<T>())))
+void dec_stage_kernel(StageDesc S, int* err) {
+  __shared__ __attribute__((aligned(16))) float lds[mfma_lds<T>()];
+  int* s_flag = reinterpret_cast<int*>(lds);
+  mfma_lds_init<T>(reinterpret_cast<int*>(lds));
   __syncthreads();
-  stage_tile<T>(S, blockIdx.x, lut, s_flag, err);
+  stage_tile<T>(S, blockIdx.x, lds, s_flag, err);
 }
 
 // ints: [0] error flag (sticky), [1] next tile, [2] workgroups exited,
 // [3 .. n_ints) per-linear counters.  The last workgroup to exit zeroes
 // [1 .. n_ints), so consecutive runs need no separate reset launch.
 template <int T>
-__global__ __launch_bounds__(tile_rows<T>()) __attribute__((amdgpu_waves_per_eu(min_waves<T>())))
-void lut_persistent_kernel(const StageDesc* __restrict__ segs, const int* __restrict__ tile_seg, int ntiles, int* ints,
+__global__ __launch_bounds__(kMRows) __attribute__((amdgpu_waves_per_eu(min_waves<T>())))
+void dec_persistent_kernel(const StageDesc* __restrict__ segs, const int* __restrict__ tile_seg, int ntiles, int* ints,
                            int n_ints) {
-  __shared__ __attribute__((aligned(16))) float lut[stage_lds_floats<T>()];
-  int& s_flag = reinterpret_cast<int*>(lut)[0];  // aliases table entries (see lut_stage_kernel)
-  int& s_tile = reinterpret_cast<int*>(lut)[1];
+  __shared__ __attribute__((aligned(16))) float lds[mfma_lds<T>()];
+  int& s_flag = reinterpret_cast<int*>(lds)[0];  // aliases B fragments (see stage_tile)
+  int& s_tile = reinterpret_cast<int*>(lds)[1];
   int* err = ints;
   int* next_tile = ints + 1;
-  stage_init<T>(lut);
+  mfma_lds_init<T>(reinterpret_cast<int*>(lds));
   if (threadIdx.x == 0) s_tile = add_relaxed(next_tile, 1);
   __syncthreads();
   int tile = __builtin_amdgcn_readfirstlane(s_tile);
@@ -1043,7 +687,7 @@ void lut_persistent_kernel(const StageDesc* __restrict__ segs, const int* __rest
     int nxt;  // thread 0's (no initial value: a write would wait for loads in flight)
     if (threadIdx.x == 0) nxt = add_relaxed(next_tile, 1);  // prefetch the next tile id
     const StageDesc S = segs[tile_seg[tile]];  // one lookup (a scan over the segments stalled for microseconds)
-    stage_tile<T>(S, tile - S.tile0, lut, &s_flag, err);
+    stage_tile<T>(S, tile - S.tile0, lds, &s_flag, err);
     if (threadIdx.x == 0) s_tile = nxt;
     __syncthreads();
     tile = __builtin_amdgcn_readfirstlane(s_tile);
@@ -1068,19 +712,18 @@ __global__ void zero_ints_kernel(int* p, int64_t n) {
 
 }  // namespace
 
-// Reduction spans per row block: `kspan_max` bounds a span (0 = whole reduction).
-int64_t lut_tile_rows(int64_t T) { return T <= kMfmaMaxT ? kMRows : kRows; }
+int64_t dec_tile_rows(int64_t) { return kMRows; }
 
-StagePlan lut_stage_plan(int64_t n_rows, int64_t n_red, int64_t T, int64_t kspan_max) {
+// Reduction spans per row block: `kspan_max` bounds a span (0 = whole reduction).
+StagePlan dec_stage_plan(int64_t n_rows, int64_t n_red, int64_t T, int64_t kspan_max) {
   StagePlan p;
   p.n_rows = n_rows;
   p.n_red = n_red;
-  p.nrb = (int)cdiv(n_rows, lut_tile_rows(T));
+  p.nrb = (int)cdiv(n_rows, dec_tile_rows(T));
   const int64_t span = kspan_max > 0 ? imin(kspan_max, n_red) : n_red;
   p.nks = (int)cdiv(n_red, span);
-  // balanced spans, in whole sign words; on the matrix cores in whole chunks
-  // of input pieces (a span starts at a chunk)
-  const int64_t grain = T <= kMfmaMaxT ? kChunkWords * kWordBits : kWordBits;
+  // balanced spans in whole chunks of input pieces (a span starts at a chunk)
+  const int64_t grain = kChunkWords * kWordBits;
   p.kc = (int)round_up(cdiv(n_red, p.nks), grain);
   p.nks = (int)cdiv(n_red, p.kc);
   return p;
@@ -1088,8 +731,8 @@ StagePlan lut_stage_plan(int64_t n_rows, int64_t n_red, int64_t T, int64_t kspan
 
 // Single calls split the reduction until the two stages have enough tiles to
 // fill the GPU; sequences keep whole reductions (no partial sums).
-int64_t lut_single_span(int64_t n_rows, int64_t n_red, int64_t T) {
-  const int64_t nrb = cdiv(n_rows, lut_tile_rows(T));
+int64_t dec_single_span(int64_t n_rows, int64_t n_red, int64_t T) {
+  const int64_t nrb = cdiv(n_rows, dec_tile_rows(T));
   const int64_t want = cdiv(512, nrb);
   const int64_t span = round_up(cdiv(n_red, want), 1024);
   return span;
@@ -1102,11 +745,11 @@ hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_lut_stage(const StageDesc& S, int64_t T, int* err, hipStream_t s) {
+hipError_t launch_dec_stage(const StageDesc& S, int64_t T, int* err, hipStream_t s) {
   const unsigned grid = (unsigned)(S.nrb * S.nks);
   switch (T) {
 #define NQ_CASE(TT) \
-  case TT: hipLaunchKernelGGL(lut_stage_kernel<TT>, dim3(grid), dim3(tile_rows<TT>()), 0, s, S, err); break;
+  case TT: hipLaunchKernelGGL(dec_stage_kernel<TT>, dim3(grid), dim3(kMRows), 0, s, S, err); break;
     NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
 #undef NQ_CASE
     default: return hipErrorInvalidValue;
@@ -1114,7 +757,7 @@ hipError_t launch_lut_stage(const StageDesc& S, int64_t T, int* err, hipStream_t
   return hipGetLastError();
 }
 
-int lut_persistent_grid(int64_t T) {
+int dec_persistent_grid(int64_t T) {
   int dev = 0, cus = 256, per = 1;
   if (hipGetDevice(&dev) == hipSuccess) {
     hipDeviceProp_t prop;
@@ -1123,7 +766,7 @@ int lut_persistent_grid(int64_t T) {
   hipError_t e = hipErrorInvalidValue;
   switch (T) {
 #define NQ_CASE(TT) \
-  case TT: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, lut_persistent_kernel<TT>, tile_rows<TT>(), 0); break;
+  case TT: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, dec_persistent_kernel<TT>, kMRows, 0); break;
     NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
 #undef NQ_CASE
   }
@@ -1131,12 +774,12 @@ int lut_persistent_grid(int64_t T) {
   return cus * per;
 }
 
-hipError_t launch_lut_persistent(const StageDesc* segs, const int* tile_seg, int ntiles, int* ints, int n_ints,
+hipError_t launch_dec_persistent(const StageDesc* segs, const int* tile_seg, int ntiles, int* ints, int n_ints,
                                  int64_t T, int grid, hipStream_t s) {
   switch (T) {
 #define NQ_CASE(TT)                                                                                     \
   case TT:                                                                                              \
-    hipLaunchKernelGGL(lut_persistent_kernel<TT>, dim3(grid), dim3(tile_rows<TT>()), 0, s, segs, tile_seg, ntiles, \
+    hipLaunchKernelGGL(dec_persistent_kernel<TT>, dim3(grid), dim3(kMRows), 0, s, segs, tile_seg, ntiles, \
                        ints, n_ints);                                                                   \
     break;
     NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
@@ -1157,8 +800,8 @@ namespace {
 constexpr int64_t kSeqSpan = 0;
 
 void plans(const nq_lrb& L, int64_t T, bool split, StagePlan* p1, StagePlan* p2) {
-  *p1 = lut_stage_plan(L.r, L.d_in, T, split ? lut_single_span(L.r, L.d_in, T) : kSeqSpan);
-  *p2 = lut_stage_plan(L.d_out, L.r, T, split ? lut_single_span(L.d_out, L.r, T) : kSeqSpan);
+  *p1 = dec_stage_plan(L.r, L.d_in, T, split ? dec_single_span(L.r, L.d_in, T) : kSeqSpan);
+  *p2 = dec_stage_plan(L.d_out, L.r, T, split ? dec_single_span(L.d_out, L.r, T) : kSeqSpan);
 }
 
 size_t part_bytes(const StagePlan& p, int64_t T) {
@@ -1173,7 +816,6 @@ namespace {
 // per-chunk scale exponents.
 int64_t piece_chunks(int64_t n_red) { return cdiv(n_red, kChunkWords * kWordBits); }
 size_t piece_bytes(int64_t n_red, int64_t T) {
-  if (T > kMfmaMaxT) return 0;
   const int64_t nch = piece_chunks(n_red);
   return align_up((size_t)nch * 64 * T * kPieces * 16) + align_up((size_t)nch * T * sizeof(int));
 }
@@ -1181,7 +823,7 @@ size_t piece_bytes(int64_t n_red, int64_t T) {
 }  // namespace
 
 // Per-linear device buffers: [part1][t][part2][pieces of x][pieces of t].
-size_t lut_linear_bytes(const nq_lrb& L, int64_t T, bool split) {
+size_t dec_linear_bytes(const nq_lrb& L, int64_t T, bool split) {
   StagePlan p1, p2;
   plans(L, T, split, &p1, &p2);
   size_t off = align_up(part_bytes(p1, T));
@@ -1192,20 +834,19 @@ size_t lut_linear_bytes(const nq_lrb& L, int64_t T, bool split) {
 
 // Per-linear counters: [stage-1 row blocks][stage-2 row blocks][t ready]
 // [pieces of x ready][pieces of t ready].
-int lut_linear_counters(const nq_lrb& L, int64_t T, bool split) {
+int dec_linear_counters(const nq_lrb& L, int64_t T, bool split) {
   StagePlan p1, p2;
   plans(L, T, split, &p1, &p2);
   return p1.nrb + p2.nrb + 3;
 }
 
-bool lut_uses_pieces(int64_t T) { return T <= kMfmaMaxT; }
 
 // Sign words of a stage can be read 4 rows at a time (16-byte loads).
 bool words_vec(const uint32_t* bits, int64_t ld, int64_t n_rows) {
   return reinterpret_cast<uintptr_t>(bits) % 16 == 0 && ld % 4 == 0 && n_rows % 4 == 0;
 }
 
-int lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, bool split,
+int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, bool split,
                     char* ws_linear, int* ctr_base, StageDesc* d) {
   StagePlan p1, p2;
   plans(L, T, split, &p1, &p2);
@@ -1239,8 +880,6 @@ int lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
   a.nks = p1.nks;
   a.nrb = p1.nrb;
   a.x_bf16 = xd == NQ_BF16;
-  a.x_vec = reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(L.s2) % 16 == 0 &&
-            L.d_in % 4 == 0;
   a.w_vec = words_vec(L.vt_bits, L.ldv, L.r);
   a.kind = 0;
   a.tile0 = 0;
@@ -1262,15 +901,9 @@ int lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
   b.nks = p2.nks;
   b.nrb = p2.nrb;
   b.x_bf16 = 0;
-  b.x_vec = L.r % 4 == 0;  // t sits 256-byte aligned in the workspace
   b.w_vec = words_vec(L.u_bits, L.ldu, L.d_out);
-  if (T > kMfmaMaxT) {
-    d[0] = a;
-    d[1] = b;
-    return 2;
-  }
-  // matrix cores: input-piece tiles before each stage; each stage waits for
-  // its pieces, the pieces of t wait for stage 1
+  // input-piece tiles before each stage; each stage waits for its pieces,
+  // the pieces of t wait for stage 1
   auto pieces = [&](const StageDesc& st, char* buf, int* ready) {
     StageDesc pc = st;
     const int64_t nch = piece_chunks(st.n_red);
@@ -1299,25 +932,25 @@ int lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
   return 4;
 }
 
-size_t lut_workspace_bytes(const nq_lrb& L, int64_t T) {
-  return align_up((size_t)(1 + lut_linear_counters(L, T, true)) * sizeof(int)) + lut_linear_bytes(L, T, true);
+size_t dec_workspace_bytes(const nq_lrb& L, int64_t T) {
+  return align_up((size_t)(1 + dec_linear_counters(L, T, true)) * sizeof(int)) + dec_linear_bytes(L, T, true);
 }
 
-hipError_t launch_lut_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
+hipError_t launch_dec_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
                              hipStream_t s) {
   char* base = static_cast<char*>(ws);
   int* err = reinterpret_cast<int*>(base);
   int* ctr = err + 1;
-  const int nctr = lut_linear_counters(L, T, true);
+  const int nctr = dec_linear_counters(L, T, true);
   char* lin = base + align_up((size_t)(1 + nctr) * sizeof(int));
   StageDesc d[kMaxLinearDescs];
-  const int nd = lut_stage_descs(L, x, xd, T, y, true, lin, ctr, d);
+  const int nd = dec_stage_descs(L, x, xd, T, y, true, lin, ctr, d);
   hipError_t e;
   if ((e = launch_zero_ints(err, 1 + nctr, s)) != hipSuccess) return e;
   for (int i = 0; i < nd; ++i) {
     d[i].signal = nullptr;  // stream order separates the launches
     d[i].wait_ctr = nullptr;
-    if ((e = launch_lut_stage(d[i], T, err, s)) != hipSuccess) return e;
+    if ((e = launch_dec_stage(d[i], T, err, s)) != hipSuccess) return e;
   }
   return hipSuccess;
 }

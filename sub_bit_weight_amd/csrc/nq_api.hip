@@ -91,13 +91,13 @@ bool decode_xor() {
 // entries fill the chip together, and a split only adds partial-sum traffic).
 size_t linear_workspace(const nq_lrb& L, int64_t T, bool in_seq = false) {
   if (T > kDecodeMaxT) return prefill_workspace_bytes(L, T, !in_seq);
-  return decode_xor() ? decode_workspace_bytes(L, T) : lut_workspace_bytes(L, T);
+  return decode_xor() ? decode_workspace_bytes(L, T) : dec_workspace_bytes(L, T);
 }
 
 hipError_t launch_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
                          hipStream_t s, bool in_seq = false) {
   if (T > kDecodeMaxT) return launch_prefill(L, x, xd, T, y, ws, s, !in_seq);
-  return decode_xor() ? launch_decode(L, x, xd, T, y, ws, s) : launch_lut_linear(L, x, xd, T, y, ws, s);
+  return decode_xor() ? launch_decode(L, x, xd, T, y, ws, s) : launch_dec_linear(L, x, xd, T, y, ws, s);
 }
 
 }  // namespace
@@ -143,9 +143,9 @@ namespace {
 
 // Stage 2 of linear i is scheduled after stage 1 of linear i+lag, so that its
 // inputs are usually final by the time a workgroup takes its first tile and
-// enough independent tiles are ready to keep every workgroup streaming.  On
-// the matrix cores the input-piece tiles of linear i's stage 1 come lag/2
-// linears ahead of its stage 1 (its stage-1 tiles then find them final), those
+// enough independent tiles are ready to keep every workgroup streaming.  The
+// input-piece tiles of linear i's stage 1 come lag/2 linears ahead of its
+// stage 1 (its stage-1 tiles then find them final), those
 // of its stage 2 3*lag/4 linears after it (late enough that stage 1, whose
 // tiles can be long, has usually finished, early enough to be done before
 // stage 2).
@@ -163,37 +163,30 @@ void plan_persistent(nq_seq* s) {
   size_t bufs = 0;
   for (int64_t i = 0; i < n; ++i) {
     s->ctr_off.push_back(ints);
-    ints += lut_linear_counters(s->layers[i], s->T, false);
+    ints += dec_linear_counters(s->layers[i], s->T, false);
     s->buf_off.push_back(bufs);
-    bufs = align_up(bufs + lut_linear_bytes(s->layers[i], s->T, false));
+    bufs = align_up(bufs + dec_linear_bytes(s->layers[i], s->T, false));
   }
   s->n_ints = ints;
   const int64_t lag = seq_lag();
-  if (!lut_uses_pieces(s->T)) {  // descriptors: stage 1, stage 2
-    for (int64_t i = 0; i < n; ++i) {
-      s->order.push_back({(int)i, 0});
-      if (i >= lag) s->order.push_back({(int)(i - lag), 1});
-    }
-    for (int64_t i = std::max<int64_t>(0, n - lag); i < n; ++i) s->order.push_back({(int)i, 1});
-  } else {  // descriptors: pieces of x, stage 1, pieces of t, stage 2
-    const int64_t pre = std::max<int64_t>(lag / 2, 1), lag2 = lag * 3 / 4;
-    for (int64_t i = 0; i < std::min(pre, n); ++i) s->order.push_back({(int)i, 0});
-    for (int64_t i = 0; i < n; ++i) {
-      if (i + pre < n) s->order.push_back({(int)(i + pre), 0});
-      s->order.push_back({(int)i, 1});
-      if (i >= lag2) s->order.push_back({(int)(i - lag2), 2});
-      if (i >= lag) s->order.push_back({(int)(i - lag), 3});
-    }
-    for (int64_t i = std::max<int64_t>(0, n - lag2); i < n; ++i) s->order.push_back({(int)i, 2});
-    for (int64_t i = std::max<int64_t>(0, n - lag); i < n; ++i) s->order.push_back({(int)i, 3});
+  // descriptors: pieces of x, stage 1, pieces of t, stage 2
+  const int64_t pre = std::max<int64_t>(lag / 2, 1), lag2 = lag * 3 / 4;
+  for (int64_t i = 0; i < std::min(pre, n); ++i) s->order.push_back({(int)i, 0});
+  for (int64_t i = 0; i < n; ++i) {
+    if (i + pre < n) s->order.push_back({(int)(i + pre), 0});
+    s->order.push_back({(int)i, 1});
+    if (i >= lag2) s->order.push_back({(int)(i - lag2), 2});
+    if (i >= lag) s->order.push_back({(int)(i - lag), 3});
   }
+  for (int64_t i = std::max<int64_t>(0, n - lag2); i < n; ++i) s->order.push_back({(int)i, 2});
+  for (int64_t i = std::max<int64_t>(0, n - lag); i < n; ++i) s->order.push_back({(int)i, 3});
   // tile counts do not depend on where the buffers are: count them with the
   // descriptors of a stand-in workspace address
   s->ntiles = 0;
   char* const stand_in = reinterpret_cast<char*>(uintptr_t{1} << 40);
   for (auto& o : s->order) {
     StageDesc d[kMaxLinearDescs];
-    lut_stage_descs(s->layers[o.first], s->xs[o.first], s->xd, s->T, s->ys[o.first], false, stand_in,
+    dec_stage_descs(s->layers[o.first], s->xs[o.first], s->xd, s->T, s->ys[o.first], false, stand_in,
                     reinterpret_cast<int*>(stand_in), d);
     s->ntiles += d[o.second].nrb * d[o.second].nks;
   }
@@ -211,7 +204,7 @@ nq_status build_and_upload(nq_seq* s, void* ws, hipStream_t stream) {
   int* ints = reinterpret_cast<int*>(base);
   std::vector<std::array<StageDesc, kMaxLinearDescs>> st(s->layers.size());
   for (size_t i = 0; i < s->layers.size(); ++i)
-    lut_stage_descs(s->layers[i], s->xs[i], s->xd, s->T, s->ys[i], false, base + s->buf_off[i], ints + s->ctr_off[i],
+    dec_stage_descs(s->layers[i], s->xs[i], s->xd, s->T, s->ys[i], false, base + s->buf_off[i], ints + s->ctr_off[i],
                     st[i].data());
   s->segs.clear();
   s->tile_seg.clear();
@@ -222,7 +215,7 @@ nq_status build_and_upload(nq_seq* s, void* ws, hipStream_t stream) {
     s->segs.push_back(d);
   }
   if ((int64_t)s->tile_seg.size() != s->ntiles) return set_error("nq_seq_run: tile count changed"), NQ_ERR_ARG;
-  if (s->grid == 0) s->grid = lut_persistent_grid(s->T);
+  if (s->grid == 0) s->grid = dec_persistent_grid(s->T);
   hipError_t e = hipMemcpyAsync(base + s->off_sched, s->segs.data(), s->segs.size() * sizeof(StageDesc),
                                 hipMemcpyHostToDevice, stream);
   if (e == hipSuccess)
@@ -365,7 +358,7 @@ nq_status nq_seq_run(nq_seq* s, void* workspace, size_t workspace_bytes, void* s
       s->needs_zero = false;
     }
     if (e == hipSuccess)
-      e = launch_lut_persistent(reinterpret_cast<const StageDesc*>(static_cast<char*>(workspace) + s->off_sched),
+      e = launch_dec_persistent(reinterpret_cast<const StageDesc*>(static_cast<char*>(workspace) + s->off_sched),
                                 reinterpret_cast<const int*>(static_cast<char*>(workspace) + s->off_tseg), s->ntiles,
                                 ints, (int)s->n_ints, s->T, s->grid, st);
     return hip_status(e, "nq_seq_run launch");

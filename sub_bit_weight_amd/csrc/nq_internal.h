@@ -42,7 +42,7 @@ size_t decode_workspace_bytes(const nq_lrb& L, int64_t T);
 hipError_t launch_decode(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y,
                          void* ws, hipStream_t s);
 
-// Decode regime, table-lookup kernels.  One stage of one linear:
+// Decode regime, matrix-core kernels.  One stage of one linear:
 //   out[t][o] = rowscale[o] * sum_e sign(o,e) * xin[t][e] * colscale[e]
 struct StageDesc {
   const uint32_t* bits;   // words[e/32][o], row stride ld
@@ -59,9 +59,8 @@ struct StageDesc {
   int n_rows, n_red;
   int kc, nks, nrb;       // reduction span per tile (elements), spans, row blocks
   int x_bf16;
-  int x_vec;              // xin and colscale 16-byte aligned and n_red % 4 == 0: vector loads
   int w_vec;              // bits 16-byte aligned, ld and n_rows multiples of 4: 16-byte word loads
-  int kind;               // 0: stage tiles (nrb x nks); 1: input-piece tiles (nrb = chunks, nks = 1)
+  int kind;               // 0: stage tiles (nrb x nks); 1: input-piece tiles (nrb = tiles, nks = 1)
   uint32_t* bfrag;        // matrix-core operand pieces of the stage input (written by kind 1, read by kind 0)
   int* bsig;              // per chunk and token: scale exponent of the pieces
   int tile0;              // first tile of this stage in a persistent schedule
@@ -70,27 +69,25 @@ struct StagePlan {
   int64_t n_rows, n_red;
   int kc, nks, nrb;
 };
-StagePlan lut_stage_plan(int64_t n_rows, int64_t n_red, int64_t T, int64_t kspan_max);
-int64_t lut_single_span(int64_t n_rows, int64_t n_red, int64_t T);
-size_t lut_workspace_bytes(const nq_lrb& L, int64_t T);
+StagePlan dec_stage_plan(int64_t n_rows, int64_t n_red, int64_t T, int64_t kspan_max);
+int64_t dec_single_span(int64_t n_rows, int64_t n_red, int64_t T);
+size_t dec_workspace_bytes(const nq_lrb& L, int64_t T);
 // split = true: single-call plan (reduction split over workgroups); false: sequence plan
-size_t lut_linear_bytes(const nq_lrb& L, int64_t T, bool split);
-int lut_linear_counters(const nq_lrb& L, int64_t T, bool split);
+size_t dec_linear_bytes(const nq_lrb& L, int64_t T, bool split);
+int dec_linear_counters(const nq_lrb& L, int64_t T, bool split);
 // Descriptors of one linear in dependency order (each waits only on earlier
-// ones): stage 1, stage 2 for table lookups; pieces of x, stage 1, pieces of
-// t, stage 2 on the matrix cores (T <= 2).  Returns their number (2 or 4).
+// ones): pieces of x, stage 1, pieces of t, stage 2.  Returns their number.
 constexpr int kMaxLinearDescs = 4;
-bool lut_uses_pieces(int64_t T);  // the matrix-core form (4 descriptors) serves T tokens
-int lut_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, bool split,
+int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, bool split,
                     char* ws_linear, int* ctr_base, StageDesc* d);
-hipError_t launch_lut_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
+hipError_t launch_dec_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
                              hipStream_t s);
 hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t s);
-int lut_persistent_grid(int64_t T);
+int dec_persistent_grid(int64_t T);
 // ints: [0] error flag, [1] next tile, [2] exited workgroups, [3..n_ints) counters;
 // [1..n_ints) must be zero before the first run and are left zero by each run.
 // tile_seg[i] (device) is the index in segs of the descriptor of tile i.
-hipError_t launch_lut_persistent(const StageDesc* segs, const int* tile_seg, int ntiles, int* ints, int n_ints,
+hipError_t launch_dec_persistent(const StageDesc* segs, const int* tile_seg, int ntiles, int* ints, int n_ints,
                                  int64_t T, int grid, hipStream_t s);
 
 // Matrix-core regime (T > 8).
