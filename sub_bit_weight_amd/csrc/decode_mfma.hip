@@ -90,6 +90,7 @@ __device__ inline void stores_done_barrier() {
 // policy bit 1, "nt"), so they do not push the input pieces, which every row
 // block re-reads, out of the L2 (measured: 5.3 -> 5.6 TB/s on the 70B stack).
 constexpr int kStreamLoad = 2;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past every sign-word buffer (< 2 GiB)
 
 // A tile whose input is made by other tiles of the same launch (a stage by
 // its input-piece tiles, the pieces of t by the stage-1 row blocks) waits
@@ -476,9 +477,15 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   const int nk = (nw + kStepWords - 1) / kStepWords;
   const int nchunks = (nw + kChunkWords - 1) / kChunkWords;
 
-  // byte offset of this lane's first word from word row 4k (rows at or past
-  // n_rows are read where in range and never stored)
-  const uint32_t voff = 4u * (uint32_t)((int64_t)rb * kMRows + wv * 64 + 4 * col) + (uint32_t)grp * ld4;
+  // byte offset of this lane's q-th word from word row 4k; rows at or past
+  // n_rows (in the last row block) get an offset past any buffer (sign-word
+  // buffers are below 2 GiB), so their loads read 0 without memory traffic
+  // instead of words of the next word row
+  const int row0 = rb * kMRows + wv * 64 + 4 * col;
+  const uint32_t voff = 4u * (uint32_t)row0 + (uint32_t)grp * ld4;
+  uint32_t qoff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) qoff[q] = row0 + q < S.n_rows ? voff + 4u * q : kOutOfRange;
   // Step k reads word row 4k + grp of the span through a buffer resource that
   // starts at word row 4k and ends with row n_rows-1 of the span's last word
   // row: words past the span (a partial last step, steps past the last) or
@@ -491,12 +498,11 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
     const uint32_t nrec = rows_left > 0 ? (uint32_t)(rows_left - 1) * ld4 + 4u * (uint32_t)S.n_rows : 0u;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t*>(S.bits) + (int64_t)(w0 + wb) * S.ld, (short)0, (int)nrec, 0x00020000);
-    if constexpr (W4) {
-      dst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, kStreamLoad));
+    if constexpr (W4) {  // n_rows % 4 == 0: the lane's 4 rows are all valid or all past the end
+      dst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)qoff[0], 0, kStreamLoad));
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dst[q] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(voff + 4u * q), 0, kStreamLoad);
+      for (int q = 0; q < 4; ++q) dst[q] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)qoff[q], 0, kStreamLoad);
     }
   };
 
