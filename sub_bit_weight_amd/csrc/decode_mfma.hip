@@ -226,6 +226,11 @@ constexpr int kPrepGroups = kMRows / 256;            // chunks per round of an i
 // 3 up to 8).
 template <int T>
 constexpr int col_groups() { return (T * kPieces + 15) / 16; }
+// Steps of sign words in flight per lane: with two column groups the ring is
+// half as deep, so that two workgroups fit a CU (their registers); the CU
+// then keeps as many bytes in flight as one workgroup with the full ring.
+template <int T>
+constexpr int ring_steps() { return col_groups<T>() == 2 ? kRingSteps / 2 : kRingSteps; }
 // LDS of a workgroup, in 4-byte words: [B fragments, two chunk buffers of
 // kChunkSteps x col_groups x kStepInts] [chunk scale exponents, two buffers of
 // T] [per-chunk maxima of an input-piece tile] [row sums [T][kMRows]]
@@ -549,9 +554,10 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   // the wait and the first chunk's pieces complete (loads complete in issue
   // order for s_waitcnt, so the acquire and chunk 0's pieces wait for them;
   // issuing them after the wait measured slightly slower)
-  u32x4 ring[kRingSteps];
+  constexpr int R = ring_steps<T>();
+  u32x4 ring[R];
 #pragma unroll
-  for (int k = 0; k < kRingSteps; ++k) load_step(k, ring[k]);
+  for (int k = 0; k < R; ++k) load_step(k, ring[k]);
   wait_input(S, err);  // the stage's pieces are final
   load_chunk(chunk0);
   store_chunk(0);
@@ -579,11 +585,17 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
     load_chunk(chunk0 + c + 1);  // next chunk's pieces (or none)
 
     const u32x4* bfrag = reinterpret_cast<const u32x4*>(lds + buf * b_ints<T>()) + lane;
+    // B fragments: with one column group the next step's are read a step ahead;
+    // with two, at their own step (the registers a step ahead would cost the
+    // second workgroup per CU)
+    constexpr bool kAhead = G == 1;
     u32x4 blo[G], bhi[G];
+    if constexpr (kAhead) {
 #pragma unroll
-    for (int cg = 0; cg < G; ++cg) {
-      blo[cg] = bfrag[cg * (kStepInts / 4)];
-      bhi[cg] = bfrag[cg * (kStepInts / 4) + 64];
+      for (int cg = 0; cg < G; ++cg) {
+        blo[cg] = bfrag[cg * (kStepInts / 4)];
+        bhi[cg] = bfrag[cg * (kStepInts / 4) + 64];
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < kChunkSteps; ++kk) {
@@ -591,9 +603,13 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
       v8i b[G];
 #pragma unroll
       for (int cg = 0; cg < G; ++cg) {
+        if constexpr (!kAhead) {
+          blo[cg] = bfrag[(kk * G + cg) * (kStepInts / 4)];
+          bhi[cg] = bfrag[(kk * G + cg) * (kStepInts / 4) + 64];
+        }
         b[cg][0] = (int)blo[cg].x; b[cg][1] = (int)blo[cg].y; b[cg][2] = (int)blo[cg].z; b[cg][3] = (int)blo[cg].w;
         b[cg][4] = (int)bhi[cg].x; b[cg][5] = (int)bhi[cg].y; b[cg][6] = (int)bhi[cg].z; b[cg][7] = (int)bhi[cg].w;
-        if (kk + 1 < kChunkSteps) {  // next step's fragments (stale past the span; then unused)
+        if (kAhead && kk + 1 < kChunkSteps) {  // next step's fragments (stale past the span; then unused)
           blo[cg] = bfrag[((kk + 1) * G + cg) * (kStepInts / 4)];
           bhi[cg] = bfrag[((kk + 1) * G + cg) * (kStepInts / 4) + 64];
         }
@@ -601,14 +617,14 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
       if (k < nk) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const v8i a = expand_word(ring[kk % kRingSteps][q]);
+          const v8i a = expand_word(ring[kk % R][q]);
 #pragma unroll
           for (int cg = 0; cg < G; ++cg)
             acc[q][cg] =
                 __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[cg], acc[q][cg], 4, 0, 0, 127, 0, bscale[cg]);
         }
       }
-      load_step(k + kRingSteps, ring[kk % kRingSteps]);  // past the span: out of range, no memory access
+      load_step(k + R, ring[kk % R]);  // past the span: out of range, no memory access
       if (kk == kChunkSteps / 2) store_chunk(buf ^ 1);    // the other buffer was last read in chunk c-1
     }
     __syncthreads();  // chunk c+1's fragments are in LDS; every wave is done with chunk c's
@@ -643,11 +659,12 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   finish_rows<T>(S, rb, ks, o, o < S.n_rows, accr, s_flag);
 }
 
-// With one column group: 4 waves per SIMD (at most 128 VGPRs) and 2
-// workgroups per CU; with more (accumulators and B fragments of every group)
-// 2 waves per SIMD, one workgroup per CU.
+// With one or two column groups: 4 waves per SIMD (at most 128 VGPRs) and 2
+// workgroups per CU (two groups: a half-deep ring and B fragments read at
+// their step make room for the second group's accumulators); with three
+// (74-115 KB of LDS) 2 waves per SIMD, one workgroup per CU.
 template <int T>
-constexpr int min_waves() { return col_groups<T>() == 1 ? 4 : 2; }
+constexpr int min_waves() { return col_groups<T>() <= 2 ? 4 : 2; }
 
 // The workgroup's two shared flag words live in the first entries of LDS (B
 // fragments of column 0 in chunk buffer 0): every write to them follows the
