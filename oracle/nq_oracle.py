@@ -203,6 +203,58 @@ def sampled_linear_ref(L: LRB, x: np.ndarray, rows, chunk: int = 4096) -> np.nda
     return y
 
 
+# --------------------------------------------------------------------------
+# scale-only reconstruction (section 3, "Phase 3: Scale-Only Model
+# Reconstruction": with the binary factors frozen only s1 and s2 are tuned).
+# For a loss whose gradient with respect to the layer output is g (T x d_out),
+# the gradients with respect to s1, s2 and the input follow from the
+# factorization equation by the chain rule.
+# --------------------------------------------------------------------------
+
+
+def transpose_bits_ref(words: np.ndarray, n_out: int, n_red: int) -> np.ndarray:
+    """Sign words of the transposed sign matrix.
+
+    The input holds an (n_out x n_red) sign matrix S in the word layout above;
+    the result holds S^T (n_red outputs, reduction over the n_out positions),
+    shape (ceil(n_out/32), n_red).
+    """
+    S = unpack_ref(words, n_red, n_out)  # (n_out, n_red), +-1
+    return pack_ref(S.T)
+
+
+def scale_grads_ref(L: LRB, x: np.ndarray, g: np.ndarray):
+    """(dx, ds1, ds2) in float64 for y = W x with W[i,j] = s1[i] M[i,j] s2[j], M = U V^T.
+
+    dx[t,j]  = sum_i W[i,j] g[t,i]                      (the input gradient)
+    ds1[i]   = sum_t g[t,i] * sum_j M[i,j] s2[j] x[t,j]
+    ds2[j]   = sum_t x[t,j] * sum_i g[t,i] s1[i] M[i,j]
+    """
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    g64 = np.asarray(g, dtype=np.float32).astype(np.float64)
+    M = sign_product_ref(L)
+    s1 = L.s1.astype(np.float64)
+    s2 = L.s2.astype(np.float64)
+    dx = g64 @ reconstruct_ref(L)
+    ds1 = np.sum(g64 * ((x64 * s2[None, :]) @ M.T), axis=0)
+    ds2 = np.sum(x64 * ((g64 * s1[None, :]) @ M), axis=0)
+    return dx, ds1, ds2
+
+
+def scale_grads_factored_ref(L: LRB, x: np.ndarray, g: np.ndarray):
+    """The same gradients in factored order (no d_out x d_in matrix), float64:
+    u = U (V^T (s2 (.) x)), b = V (U^T (s1 (.) g)); dx = s2 (.) b,
+    ds1 = sum_t g (.) u, ds2 = sum_t x (.) b."""
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    g64 = np.asarray(g, dtype=np.float32).astype(np.float64)
+    s1 = L.s1.astype(np.float64)
+    s2 = L.s2.astype(np.float64)
+    U, Vt = L.U(), L.Vt()
+    u = ((x64 * s2[None, :]) @ Vt.T) @ U.T
+    b = ((g64 * s1[None, :]) @ U) @ Vt
+    return b * s2[None, :], np.sum(g64 * u, axis=0), np.sum(x64 * b, axis=0)
+
+
 def rel_err(y: np.ndarray, y_ref: np.ndarray) -> float:
     """Normwise relative error ||y - y_ref||_F / ||y_ref||_F (float64)."""
     y = np.asarray(y, dtype=np.float64)

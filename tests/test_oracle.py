@@ -302,3 +302,88 @@ def test_rel_err():
     a = np.array([3.0, 4.0])
     assert O.rel_err(a, a) == 0.0
     assert O.rel_err(a * 1.001, a) == pytest.approx(1e-3)
+
+
+# --------------------------------------------------------------------------
+# scale-only reconstruction: transposed packing and the gradients of s1, s2, x
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("n_out,n_red", [(1, 1), (5, 31), (33, 70), (64, 32), (40, 100)])
+def test_transpose_bits_brute_force(n_out, n_red):
+    g = np.random.default_rng(n_out * 1000 + n_red)
+    M = np.where(g.random((n_out, n_red)) < 0.5, -1.0, 1.0)
+    words = _py_pack(M.tolist())
+    T_words = O.transpose_bits_ref(words, n_out, n_red)
+    assert T_words.shape == ((n_out + 31) // 32, n_red)
+    # element (e, o) of the transposed matrix is element (o, e) of M, bit by bit
+    for e in range(n_red):
+        for o in range(n_out):
+            bit = (int(T_words[o // 32, e]) >> (o % 32)) & 1
+            assert bit == (1 if M[o, e] < 0 else 0)
+    # padding bits of the transposed words are 0
+    if n_out % 32:
+        assert np.all((T_words[-1].astype(np.uint64) >> np.uint64(n_out % 32)) == 0)
+
+
+def _grads_case(seed, d_out, d_in, r, T):
+    g = np.random.default_rng(seed)
+    U, V = _rand_pm1(g, (d_out, r)), _rand_pm1(g, (d_in, r))
+    s1 = synth.scales_lognormal(f"sg/s1/{seed}", d_out)
+    s2 = synth.scales_halfnormal(f"sg/s2/{seed}", d_in)
+    L = _layer_from_pm1(U, V, s1, s2)
+    x = g.standard_normal((T, d_in)).astype(np.float32)
+    gy = g.standard_normal((T, d_out)).astype(np.float32)
+    return L, U, V, s1, s2, x, gy
+
+
+def _loss(U, V, s1, s2, x, gy):
+    """<g, W x> summed over tokens, by reconstruct-then-multiply."""
+    return float(np.sum(gy.astype(np.float64) * O.linear_ref(_layer_from_pm1(U, V, s1, s2), x)))
+
+
+@pytest.mark.parametrize("d_out,d_in,r,T", [(3, 5, 2, 1), (7, 11, 4, 3), (16, 9, 33, 2)])
+def test_scale_grads_finite_differences(d_out, d_in, r, T):
+    """The loss is linear in s1 and, separately, in s2 and in x: a step of
+    delta in one value changes it by exactly delta times that value's gradient
+    (up to float64 rounding).  The layer holds fp32 values, so each step is the
+    difference of two fp32 numbers."""
+    L, U, V, s1, s2, x, gy = _grads_case(d_out * 31 + d_in, d_out, d_in, r, T)
+    dx, ds1, ds2 = O.scale_grads_ref(L, x, gy)
+    base = _loss(U, V, s1, s2, x, gy)
+
+    def stepped(v, idx):
+        vp = v.copy()
+        vp[idx] = np.float32(v[idx] + np.float32(1.0))
+        return vp, float(vp[idx]) - float(v[idx])
+
+    for i in range(d_out):
+        s1p, delta = stepped(s1, i)
+        d = _loss(U, V, s1p, s2, x, gy) - base
+        assert abs(d - delta * ds1[i]) <= 1e-9 * (1 + abs(delta * ds1[i]) + abs(base))
+    for j in range(d_in):
+        s2p, delta = stepped(s2, j)
+        d = _loss(U, V, s1, s2p, x, gy) - base
+        assert abs(d - delta * ds2[j]) <= 1e-9 * (1 + abs(delta * ds2[j]) + abs(base))
+    for t in range(T):
+        for j in range(d_in):
+            xp, delta = stepped(x, (t, j))
+            d = _loss(U, V, s1, s2, xp, gy) - base
+            assert abs(d - delta * dx[t, j]) <= 1e-9 * (1 + abs(delta * dx[t, j]) + abs(base))
+
+
+def test_scale_grads_adjoint_and_euler_identities():
+    """<g, W x> = <W^T g, x> = <s1, ds1> = <s2, ds2> (the loss is homogeneous of
+    degree one in x, in s1 and in s2)."""
+    L, U, V, s1, s2, x, gy = _grads_case(5, 40, 70, 24, 5)
+    dx, ds1, ds2 = O.scale_grads_ref(L, x, gy)
+    base = _loss(U, V, s1, s2, x, gy)
+    for v in (np.sum(dx * x.astype(np.float64)), np.dot(ds1, s1.astype(np.float64)),
+              np.dot(ds2, s2.astype(np.float64))):
+        assert abs(v - base) <= 1e-10 * (abs(base) + 1)
+
+
+def test_scale_grads_factored_equals_dense():
+    L, U, V, s1, s2, x, gy = _grads_case(9, 48, 80, 40, 4)
+    for a, b in zip(O.scale_grads_factored_ref(L, x, gy), O.scale_grads_ref(L, x, gy)):
+        assert O.rel_err(a, b) <= 1e-12
