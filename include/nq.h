@@ -180,6 +180,46 @@ nq_status nq_seq_run(nq_seq* s, void* workspace, size_t workspace_bytes, void* s
 void nq_seq_destroy(nq_seq* s);
 
 /*
+ * Scale-only reconstruction (section 3 "Phase 3: Scale-Only Model
+ * Reconstruction": with the binary factors frozen only s1 and s2 are tuned).
+ *
+ * nq_transpose_signs -- sign words of the transposed sign matrix.  src holds an
+ *   n_out x n_red sign matrix S in the layout above (row stride ld); dst
+ *   receives S^T, i.e. n_red outputs with a reduction over n_out:
+ *     bit b of dst[w*ldt + e] = bit (e%32) of src[(e/32)*ld + 32w+b]
+ *   for e < n_red, 32w+b < n_out; padding bits are 0; columns n_red..ldt-1 are
+ *   not written.  dst is [ceil(n_out/32)][ldt] words, ldt >= n_red, and must
+ *   not overlap src.  The transposed layer's words are
+ *     ut_bits = nq_transpose_signs(u_bits,  n_out=d_out, n_red=r,    ld=ldu)  [ceil(d_out/32)][ldut >= r]
+ *     v_bits  = nq_transpose_signs(vt_bits, n_out=r,     n_red=d_in, ld=ldv)  [ceil(r/32)][ldvv >= d_in]
+ *   Errors: NQ_ERR_ARG for null pointers, sizes < 1, ld < n_out, ldt < n_red,
+ *   misaligned pointers; NQ_ERR_UNSUPPORTED if a buffer exceeds 2 GiB.
+ *
+ * nq_lrb_scale_grads -- for y = W x (W as in nq_lrb_linear) and the gradient
+ *   g = dL/dy of a loss, the gradients with respect to the input and the scales:
+ *     dx[t][j] = sum_i W[i][j] g[t][i]
+ *     ds1[i]   = sum_t g[t][i] * (U V^T (s2 (.) x_t))_i
+ *     ds2[j]   = sum_t x[t][j] * (V U^T (s1 (.) g_t))_j
+ *   x: [T][d_in] fp32 or bf16 (x_dtype); g: [T][d_out] fp32; dx: [T][d_in]
+ *   fp32; ds1: [d_out] fp32; ds2: [d_in] fp32 (overwritten, not accumulated).
+ *   ut_bits/v_bits: the transposed layer's words from nq_transpose_signs.
+ *   Both products run through the kernels of nq_lrb_linear (decode regime for
+ *   T <= 8, GEMM regime above, with the same arithmetic); the token sums are
+ *   fp32 in token order (deterministic).
+ *   workspace: at least nq_lrb_scale_grads_workspace_bytes(L, T) bytes,
+ *   256-byte aligned.  Errors: as for nq_lrb_linear, for L and for the
+ *   transposed layer's words; NQ_ERR_ARG for a null or misaligned g, ds1 or
+ *   ds2.
+ */
+nq_status nq_transpose_signs(const uint32_t* src, int64_t n_out, int64_t n_red, int64_t ld,
+                             uint32_t* dst, int64_t ldt, void* stream);
+size_t nq_lrb_scale_grads_workspace_bytes(const nq_lrb* L, int64_t T);
+nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t ldut,
+                             const uint32_t* v_bits, int64_t ldvv, const void* x, nq_dtype x_dtype,
+                             const float* g, int64_t T, float* dx, float* ds1, float* ds2,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * nq_fill_random_words -- synthetic sign words for large benchmark matrices:
  *   dst[i] = low 32 bits of SplitMix64(seed, i), i < n, where SplitMix64(seed,
  *   i) is output number i+1 of the SplitMix64 stream started at `seed`

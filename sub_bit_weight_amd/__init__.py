@@ -6,7 +6,8 @@ no fallback: if libnq.so is missing or fails to load, every call raises.
 
 Names follow the C ABI in include/nq.h:
   pack_signs, unpack_signs, lrb_linear, lrb_workspace_bytes, reconstruct,
-  storage_bits, fill_random_words, Seq (nq_seq_*), last_error.
+  storage_bits, fill_random_words, Seq (nq_seq_*), transpose_signs,
+  lrb_scale_grads (nq_lrb_scale_grads*), last_error.
 """
 from __future__ import annotations
 
@@ -26,7 +27,8 @@ STATUS_NAMES = {0: "NQ_OK", 1: "NQ_ERR_ARG", 2: "NQ_ERR_UNSUPPORTED", 3: "NQ_ERR
 EXPORTED = [
     "nq_pack_signs", "nq_unpack_signs", "nq_lrb_workspace_bytes", "nq_lrb_linear", "nq_reconstruct",
     "nq_storage_bits", "nq_seq_create", "nq_seq_workspace_bytes", "nq_seq_run", "nq_seq_destroy",
-    "nq_fill_random_words", "nq_last_error", "nq_version",
+    "nq_fill_random_words", "nq_last_error", "nq_version", "nq_transpose_signs",
+    "nq_lrb_scale_grads_workspace_bytes", "nq_lrb_scale_grads",
 ]
 
 
@@ -81,6 +83,12 @@ def lib() -> ctypes.CDLL:
     L.nq_seq_destroy.restype = None
     L.nq_fill_random_words.argtypes = [vp, i64, u64, vp]
     L.nq_fill_random_words.restype = st
+    L.nq_transpose_signs.argtypes = [vp, i64, i64, i64, vp, i64, vp]
+    L.nq_transpose_signs.restype = st
+    L.nq_lrb_scale_grads_workspace_bytes.argtypes = [P(nq_lrb), i64]
+    L.nq_lrb_scale_grads_workspace_bytes.restype = sz
+    L.nq_lrb_scale_grads.argtypes = [P(nq_lrb), vp, i64, vp, i64, vp, ctypes.c_int, vp, i64, vp, vp, vp, vp, sz, vp]
+    L.nq_lrb_scale_grads.restype = st
     L.nq_last_error.argtypes = []
     L.nq_last_error.restype = ctypes.c_char_p
     L.nq_version.argtypes = []
@@ -229,6 +237,61 @@ def reconstruct(layer: Lrb, out: torch.Tensor | None = None, stream=None) -> tor
 
 def storage_bits(d_out: int, d_in: int, r: int) -> int:
     return int(lib().nq_storage_bits(d_out, d_in, r))
+
+
+# ---------------------------------------------------------------- scale-only reconstruction
+
+
+def transpose_signs(bits: torch.Tensor, n_out: int, n_red: int, ld: int | None = None,
+                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Sign words of the transposed matrix: [ceil(n_out/32)][n_red] (int32 storage)."""
+    _dev(bits, "bits")
+    ld = bits.shape[1] if ld is None else ld
+    if out is None:
+        out = torch.empty((n_words(n_out), n_red), dtype=torch.int32, device=bits.device)
+    _check(lib().nq_transpose_signs(_ptr(bits), n_out, n_red, ld, _ptr(out), out.shape[1], _stream(stream)))
+    return out
+
+
+@dataclass
+class Adjoint:
+    """Sign words of a layer's transposed matrix W^T (from transpose_signs)."""
+    ut_bits: torch.Tensor  # [ceil(d_out/32)][>= r]: U^T, outputs k < r, words along d_out
+    v_bits: torch.Tensor   # [ceil(r/32)][>= d_in]: V, outputs j < d_in, words along r
+
+    @staticmethod
+    def of(layer: Lrb, stream=None) -> "Adjoint":
+        return Adjoint(transpose_signs(layer.u_bits, layer.d_out, layer.r, stream=stream),
+                       transpose_signs(layer.vt_bits, layer.r, layer.d_in, stream=stream))
+
+
+def lrb_scale_grads_workspace_bytes(layer: Lrb, T: int) -> int:
+    s = layer.struct()
+    return int(lib().nq_lrb_scale_grads_workspace_bytes(ctypes.byref(s), T))
+
+
+def lrb_scale_grads(layer: Lrb, adj: Adjoint, x: torch.Tensor, g: torch.Tensor,
+                    workspace: torch.Tensor | None = None, stream=None):
+    """(dx, ds1, ds2) for y = W x and g = dL/dy: dx [T][d_in], ds1 [d_out], ds2 [d_in] (fp32)."""
+    _dev(x, "x")
+    _dev(g, "g")
+    T = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != layer.d_in:
+        raise ValueError(f"x must be [T][{layer.d_in}], got {tuple(x.shape)}")
+    if g.dtype != torch.float32 or tuple(g.shape) != (T, layer.d_out) or not g.is_contiguous():
+        raise ValueError(f"g must be contiguous float32 [{T}][{layer.d_out}]")
+    s = layer.struct()
+    dx = torch.empty((T, layer.d_in), dtype=torch.float32, device=x.device)
+    ds1 = torch.empty(layer.d_out, dtype=torch.float32, device=x.device)
+    ds2 = torch.empty(layer.d_in, dtype=torch.float32, device=x.device)
+    need = int(lib().nq_lrb_scale_grads_workspace_bytes(ctypes.byref(s), T))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().nq_lrb_scale_grads(ctypes.byref(s), _ptr(adj.ut_bits), adj.ut_bits.shape[1], _ptr(adj.v_bits),
+                                    adj.v_bits.shape[1], _ptr(x), _x_dtype(x), _ptr(g), T, _ptr(dx), _ptr(ds1),
+                                    _ptr(ds2), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)))
+    return dx, ds1, ds2
 
 
 class Seq:

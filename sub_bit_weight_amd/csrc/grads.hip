@@ -1,0 +1,100 @@
+// Scale-only reconstruction (research.samsung.com NanoQuant blog, section 3,
+// "Phase 3: Scale-Only Model Reconstruction"): with the binary factors frozen,
+// only s1 and s2 are tuned, and the loss reaches earlier layers through the
+// input gradient.  For y = W x, W = s1 (.) U V^T (.) s2 (section 2, the
+// factorization equation) and an output gradient g, by the chain rule:
+//     u = U (V^T (s2 (.) x)),   b = V (U^T (s1 (.) g)),
+//     dx = s2 (.) b,   ds1 = sum_t g (.) u,   ds2 = sum_t x (.) b.
+// u is the layer's forward product without the row scale; b is the transposed
+// layer's (W^T = s2 (.) V U^T (.) s1 is again a low-rank binary matrix, with
+// the roles of U and V exchanged) without its row scale.  Both run through
+// the forward kernels; the transposed layer's sign words come from
+// transpose_signs_kernel.  This file holds the transposition and the token
+// reductions.
+#include "nq_internal.h"
+
+namespace nq {
+
+namespace {
+
+// Sign words of the transposed sign matrix.  The source holds an n_out x n_red
+// sign matrix as words[w][o] (bit b: element (o, 32w+b)); the result holds its
+// transpose as words_t[w'][e] (bit b': element (e, 32w'+b') of the transpose,
+// i.e. (32w'+b', e) of the source).  A wave transposes two 32 x 32 blocks: lane
+// l holds source word (w, 32*(wt + l/32) + l%32); the ballot of bit b over the
+// wave gives, in its low and high halves, the transposed words of element
+// 32w + b for both blocks, and lane b (resp. 32 + b) keeps them.
+__global__ __launch_bounds__(256) void transpose_signs_kernel(const uint32_t* __restrict__ src, int64_t n_out,
+                                                              int64_t n_red, int64_t ld, uint32_t* __restrict__ dst,
+                                                              int64_t ldt, int64_t nwt_pairs) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nw = (n_red + 31) / 32, nwt = (n_out + 31) / 32;
+  if (wave >= nw * nwt_pairs) return;  // whole waves exit together
+  const int64_t w = wave / nwt_pairs;
+  const int64_t wt = (wave % nwt_pairs) * 2 + (lane >> 5);  // this lane's block of the transpose
+  const int64_t o = wt * 32 + (lane & 31);
+  const uint32_t word = o < n_out ? src[w * ld + o] : 0u;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int b = 0; b < 32; ++b) {
+    const unsigned long long m = __ballot((word >> b) & 1u);
+    if ((lane & 31) == b) mine = lane < 32 ? (uint32_t)m : (uint32_t)(m >> 32);
+  }
+  const int64_t e = w * 32 + (lane & 31);
+  if (wt < nwt && e < n_red) dst[wt * ldt + e] = mine;
+}
+
+// dx[t][j] = s2[j] b[t][j],  ds2[j] = sum_t x[t][j] b[t][j]  (columns j < d_in)
+// ds1[i] = sum_t g[t][i] u[t][i]                            (columns d_in + i)
+// One thread per column, tokens in order: deterministic fp32 sums.
+__global__ __launch_bounds__(256) void scale_grads_finish_kernel(const void* __restrict__ x, int x_bf16,
+                                                                 const float* __restrict__ g,
+                                                                 const float* __restrict__ u,
+                                                                 const float* __restrict__ b,
+                                                                 const float* __restrict__ s2, int64_t T,
+                                                                 int64_t d_in, int64_t d_out, float* __restrict__ dx,
+                                                                 float* __restrict__ ds1, float* __restrict__ ds2) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c < d_in) {
+    const float sc = s2[c];
+    float acc = 0.0f;
+    for (int64_t t = 0; t < T; ++t) {
+      const int64_t i = t * d_in + c;
+      const float bv = b[i];
+      const float xv = x_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(x)[i] << 16)
+                              : static_cast<const float*>(x)[i];
+      dx[i] = sc * bv;
+      acc = fmaf(xv, bv, acc);
+    }
+    ds2[c] = acc;
+  } else if (c < d_in + d_out) {
+    const int64_t k = c - d_in;
+    float acc = 0.0f;
+    for (int64_t t = 0; t < T; ++t) acc = fmaf(g[t * d_out + k], u[t * d_out + k], acc);
+    ds1[k] = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_transpose_signs(const uint32_t* src, int64_t n_out, int64_t n_red, int64_t ld, uint32_t* dst,
+                                  int64_t ldt, hipStream_t s) {
+  const int64_t nw = cdiv(n_red, kWordBits), nwt = cdiv(n_out, kWordBits);
+  const int64_t pairs = cdiv(nwt, 2);
+  const int64_t blocks = cdiv(nw * pairs, 4);
+  hipLaunchKernelGGL(transpose_signs_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, n_out, n_red, ld, dst, ldt,
+                     pairs);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_grads_finish(const void* x, nq_dtype xd, const float* g, const float* u, const float* b,
+                                     const float* s2, int64_t T, int64_t d_in, int64_t d_out, float* dx, float* ds1,
+                                     float* ds2, hipStream_t s) {
+  const int64_t blocks = cdiv(d_in + d_out, 256);
+  hipLaunchKernelGGL(scale_grads_finish_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, (int)(xd == NQ_BF16), g, u,
+                     b, s2, T, d_in, d_out, dx, ds1, ds2);
+  return hipGetLastError();
+}
+
+}  // namespace nq

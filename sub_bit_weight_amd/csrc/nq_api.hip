@@ -100,6 +100,36 @@ hipError_t launch_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T,
   return decode_xor() ? launch_decode(L, x, xd, T, y, ws, s) : launch_dec_linear(L, x, xd, T, y, ws, s);
 }
 
+// The transposed layer W^T = s2 (.) V U^T (.) s1 as an LRB matrix.
+nq_lrb adjoint_layer(const nq_lrb& L, const uint32_t* ut_bits, int64_t ldut, const uint32_t* v_bits, int64_t ldvv) {
+  nq_lrb A;
+  A.d_out = L.d_in;
+  A.d_in = L.d_out;
+  A.r = L.r;
+  A.u_bits = v_bits;  // outputs j < d_in, words along r
+  A.ldu = ldvv;
+  A.vt_bits = ut_bits;  // outputs k < r, words along d_out
+  A.ldv = ldut;
+  A.s1 = L.s2;
+  A.s2 = L.s1;
+  return A;
+}
+
+// Workspace of nq_lrb_scale_grads: [u: T x d_out][b: T x d_in][one linear's
+// workspace, used by the two products in turn].
+struct ScaleGradsLayout {
+  size_t off_u, off_b, off_lin, bytes;
+};
+ScaleGradsLayout scale_grads_layout(const nq_lrb& L, int64_t T) {
+  ScaleGradsLayout g;
+  g.off_u = 0;
+  g.off_b = align_up((size_t)T * L.d_out * sizeof(float));
+  g.off_lin = g.off_b + align_up((size_t)T * L.d_in * sizeof(float));
+  const nq_lrb A = adjoint_layer(L, L.vt_bits, L.r, L.u_bits, L.d_in);  // sizes only
+  g.bytes = g.off_lin + std::max(linear_workspace(L, T), linear_workspace(A, T));
+  return g;
+}
+
 }  // namespace
 }  // namespace nq
 
@@ -291,6 +321,57 @@ nq_status nq_reconstruct(const nq_lrb* L, float* w, void* stream) {
   if (!w) return set_error("nq_reconstruct: null w"), NQ_ERR_ARG;
   if (!aligned(w, 4)) return set_error("nq_reconstruct: w not 4-byte aligned"), NQ_ERR_ARG;
   return hip_status(launch_reconstruct(*L, w, (hipStream_t)stream), "nq_reconstruct launch");
+}
+
+nq_status nq_transpose_signs(const uint32_t* src, int64_t n_out, int64_t n_red, int64_t ld, uint32_t* dst,
+                             int64_t ldt, void* stream) {
+  clear_error();
+  nq_status st = check_words("nq_transpose_signs", src, n_out, n_red, ld);
+  if (st != NQ_OK) return st;
+  if ((st = check_words("nq_transpose_signs", dst, n_red, n_out, ldt)) != NQ_OK) return st;
+  if (cdiv(n_red, kWordBits) * ld >= (int64_t(1) << 29) || cdiv(n_out, kWordBits) * ldt >= (int64_t(1) << 29))
+    return set_error("nq_transpose_signs: a sign-word buffer exceeds 2 GiB"), NQ_ERR_UNSUPPORTED;
+  return hip_status(launch_transpose_signs(src, n_out, n_red, ld, dst, ldt, (hipStream_t)stream),
+                    "nq_transpose_signs launch");
+}
+
+size_t nq_lrb_scale_grads_workspace_bytes(const nq_lrb* L, int64_t T) {
+  if (check_lrb("nq_lrb_scale_grads_workspace_bytes", L) != NQ_OK || T < 1 || T > (int64_t(1) << 24)) return 0;
+  return scale_grads_layout(*L, T).bytes;
+}
+
+nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t ldut, const uint32_t* v_bits,
+                             int64_t ldvv, const void* x, nq_dtype x_dtype, const float* g, int64_t T, float* dx,
+                             float* ds1, float* ds2, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* who = "nq_lrb_scale_grads";
+  nq_status st = check_lrb(who, L);
+  if (st != NQ_OK) return st;
+  // the transposed layer W^T: outputs d_in, reduction d_out; its U is V (words
+  // along r), its V^T is U^T (words along d_out); its scales are s2 and s1
+  nq_lrb A = adjoint_layer(*L, ut_bits, ldut, v_bits, ldvv);
+  if ((st = check_lrb("nq_lrb_scale_grads (transposed sign words)", &A)) != NQ_OK) return st;
+  if ((st = check_io(who, L, x, x_dtype, T, dx)) != NQ_OK) return st;
+  if (!g || !ds1 || !ds2) return set_error("%s: null g, ds1 or ds2", who), NQ_ERR_ARG;
+  if (!aligned(g, 4) || !aligned(ds1, 4) || !aligned(ds2, 4))
+    return set_error("%s: g, ds1 or ds2 not 4-byte aligned", who), NQ_ERR_ARG;
+  const ScaleGradsLayout lay = scale_grads_layout(*L, T);
+  if (!workspace || workspace_bytes < lay.bytes)
+    return set_error("%s: workspace %zu bytes, need %zu", who, workspace ? workspace_bytes : 0, lay.bytes),
+           NQ_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return set_error("%s: workspace not 256-byte aligned", who), NQ_ERR_ARG;
+  char* ws = static_cast<char*>(workspace);
+  float* u = reinterpret_cast<float*>(ws + lay.off_u);
+  float* b = reinterpret_cast<float*>(ws + lay.off_b);
+  hipStream_t s = (hipStream_t)stream;
+  nq_lrb Lu = *L;  // u = U (V^T (s2 (.) x)): the forward product without s1
+  Lu.s1 = nullptr;
+  A.s1 = nullptr;  // b = V (U^T (s1 (.) g)): the transposed product without s2
+  hipError_t e = launch_linear(Lu, x, x_dtype, T, u, ws + lay.off_lin, s);
+  if (e == hipSuccess) e = launch_linear(A, g, NQ_F32, T, b, ws + lay.off_lin, s);
+  if (e == hipSuccess)
+    e = launch_scale_grads_finish(x, x_dtype, g, u, b, L->s2, T, L->d_in, L->d_out, dx, ds1, ds2, s);
+  return hip_status(e, "nq_lrb_scale_grads launch");
 }
 
 nq_status nq_fill_random_words(uint32_t* dst, int64_t n, uint64_t seed, void* stream) {

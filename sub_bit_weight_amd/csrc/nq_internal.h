@@ -90,6 +90,14 @@ int dec_persistent_grid(int64_t T);
 hipError_t launch_dec_persistent(const StageDesc* segs, const int* tile_seg, int ntiles, int* ints, int n_ints,
                                  int64_t T, int grid, hipStream_t s);
 
+// Scale-only reconstruction: transposed sign words and the token reductions
+// of the scale gradients (grads.hip).
+hipError_t launch_transpose_signs(const uint32_t* src, int64_t n_out, int64_t n_red, int64_t ld, uint32_t* dst,
+                                  int64_t ldt, hipStream_t s);
+hipError_t launch_scale_grads_finish(const void* x, nq_dtype xd, const float* g, const float* u, const float* b,
+                                     const float* s2, int64_t T, int64_t d_in, int64_t d_out, float* dx, float* ds1,
+                                     float* ds2, hipStream_t s);
+
 // Matrix-core regime (T > 8).
 // split = false: never split a GEMM's reduction (entries of a sequence run
 // concurrently and fill the chip together).

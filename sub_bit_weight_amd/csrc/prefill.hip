@@ -522,14 +522,15 @@ __global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
     }
 }
 
-// y[m][n] = colscale[n] * sum over splits of part[split][m][n], in split order.
+// y[m][n] = colscale[n] * sum over splits of part[split][m][n], in split order
+// (colscale may be null: no scale).
 __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, int nsplit, int64_t MN,
                                                         int64_t N, const float* __restrict__ colscale,
                                                         float* __restrict__ y) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += (int64_t)gridDim.x * 256) {
     float acc = part[i];
     for (int sp = 1; sp < nsplit; ++sp) acc += part[(int64_t)sp * MN + i];
-    y[i] = colscale[i % N] * acc;
+    y[i] = colscale ? colscale[i % N] * acc : acc;
   }
 }
 

@@ -123,3 +123,45 @@ def test_seq_rejects_bad_entries():
     assert lib.nq_seq_workspace_bytes(h) > 0
     assert lib.nq_seq_run(h, None, 0, None) == nq.NQ_ERR_WORKSPACE
     lib.nq_seq_destroy(h)
+
+
+def test_transpose_signs_rejects_bad_args():
+    lib = nq.lib()
+    assert lib.nq_transpose_signs(None, 4, 4, 4, DUMMY, 4, None) == nq.NQ_ERR_ARG
+    assert lib.nq_transpose_signs(DUMMY, 4, 5, 3, DUMMY, 5, None) == nq.NQ_ERR_ARG    # ld < n_out
+    assert lib.nq_transpose_signs(DUMMY, 4, 5, 4, DUMMY, 4, None) == nq.NQ_ERR_ARG    # ldt < n_red
+    assert lib.nq_transpose_signs(DUMMY, 0, 5, 4, DUMMY, 5, None) == nq.NQ_ERR_ARG
+    assert lib.nq_transpose_signs(DUMMY, 4, 5, 4, None, 5, None) == nq.NQ_ERR_ARG
+    assert lib.nq_transpose_signs(DUMMY, 1 << 20, 1 << 20, 1 << 20, DUMMY, 1 << 20, None) == nq.NQ_ERR_UNSUPPORTED
+
+
+def _grads(layer, ut=DUMMY, ldut=32, v=DUMMY, ldvv=64, x=DUMMY, dtype=nq.NQ_BF16, g=DUMMY, T=1, dx=DUMMY,
+           ds1=DUMMY, ds2=DUMMY, ws=DUMMY, wsb=1 << 40):
+    return nq.lib().nq_lrb_scale_grads(ctypes.byref(layer), ut, ldut, v, ldvv, x, dtype, g, T, dx, ds1, ds2, ws,
+                                       wsb, None)
+
+
+def test_scale_grads_rejects_bad_args():
+    L = _layer()  # d_out = d_in = 64, r = 32: U^T words [2][>= 32], V words [1][>= 64]
+    assert _grads(_layer(d_in=0)) == nq.NQ_ERR_ARG
+    assert _grads(L, ut=None) == nq.NQ_ERR_ARG
+    assert _grads(L, ldut=31) == nq.NQ_ERR_ARG
+    assert _grads(L, ldvv=63) == nq.NQ_ERR_ARG
+    assert _grads(L, v=DUMMY + 2) == nq.NQ_ERR_ARG
+    assert _grads(L, g=None) == nq.NQ_ERR_ARG
+    assert _grads(L, ds1=DUMMY + 1) == nq.NQ_ERR_ARG
+    assert _grads(L, ds2=None) == nq.NQ_ERR_ARG
+    assert _grads(L, dx=None) == nq.NQ_ERR_ARG
+    assert _grads(L, T=0) == nq.NQ_ERR_ARG
+    assert _grads(L, ws=None) == nq.NQ_ERR_WORKSPACE
+    assert _grads(L, wsb=16) == nq.NQ_ERR_WORKSPACE
+    assert _grads(L, ws=DUMMY + 4) == nq.NQ_ERR_ARG
+
+
+def test_scale_grads_workspace_query():
+    L = _layer()
+    lib = nq.lib()
+    need = lib.nq_lrb_scale_grads_workspace_bytes(ctypes.byref(L), 16)
+    assert need >= 16 * (64 + 64) * 4 + lib.nq_lrb_workspace_bytes(ctypes.byref(L), 16)
+    assert lib.nq_lrb_scale_grads_workspace_bytes(ctypes.byref(L), 0) == 0
+    assert lib.nq_lrb_scale_grads_workspace_bytes(ctypes.byref(_layer(r=0)), 4) == 0

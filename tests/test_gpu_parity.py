@@ -362,3 +362,69 @@ def test_decode_non_finite_input(bad, T):
     assert not np.any(np.isfinite(y[T - 1]))
     if T > 1:
         assert O.rel_err(y[: T - 1], y_ref[: T - 1]) <= 1e-5
+
+
+# ---------------------------------------------------------------- scale-only reconstruction
+
+
+@pytest.mark.parametrize("n_out,n_red,ld_pad,ldt_pad", [(1, 1, 0, 0), (33, 70, 3, 1), (64, 32, 0, 0),
+                                                        (100, 257, 5, 7), (512, 96, 0, 0), (31, 1000, 0, 2)])
+def test_transpose_signs_bit_exact(n_out, n_red, ld_pad, ldt_pad):
+    nw = nq.n_words(n_red)
+    ld = n_out + ld_pad
+    words = nq.fill_random_words(nw * ld, 77 + n_out, G.DEV).view(nw, ld)
+    host = synth.random_words(77 + n_out, np.arange(nw * ld, dtype=np.uint64)).reshape(nw, ld)
+    # the source's padding bits (past n_red) must be 0: clear them on both sides
+    if n_red % 32:
+        keep = np.uint32((1 << (n_red % 32)) - 1)
+        host[-1] &= keep
+        words[-1] &= int(np.array(keep).view(np.int32))
+    out = torch.full((nq.n_words(n_out), n_red + ldt_pad), -1, dtype=torch.int32, device=G.DEV)
+    nq.transpose_signs(words, n_out, n_red, ld=ld, out=out)
+    got = G.words_to_host(out)
+    want = O.transpose_bits_ref(host, n_out, n_red)
+    np.testing.assert_array_equal(got[:, :n_red], want)
+    assert np.all(got[:, n_red:] == np.uint32(0xFFFFFFFF))  # columns past n_red are not written
+
+
+GRAD_SHAPES = [(33, 47, 5), (65, 129, 31), (100, 37, 64), (256, 320, 96)]
+
+
+@pytest.mark.parametrize("shape", GRAD_SHAPES)
+@pytest.mark.parametrize("T,x_dtype", [(1, "bf16"), (3, "f32"), (8, "bf16"), (9, "f32"), (64, "bf16"), (130, "f32")])
+def test_scale_grads_parity(shape, T, x_dtype):
+    d_out, d_in, r = shape
+    cfg = G.tiny_config(f"grads/{x_dtype}", x_dtype=x_dtype)
+    dev, ref, _ = G.latent_layer(cfg, synth.LayerShape("grads", d_out, d_in, r))
+    x = synth.activations(f"grads/x/{d_in}/{T}", T, d_in, x_dtype)
+    g = synth.activations(f"grads/g/{d_out}/{T}", T, d_out, "f32")
+    adj = nq.Adjoint.of(dev)
+    dx, ds1, ds2 = nq.lrb_scale_grads(dev, adj, G.to_device_x(x, x_dtype), torch.from_numpy(g).to(G.DEV))
+    rdx, rds1, rds2 = O.scale_grads_factored_ref(ref, x, g)
+    # dx and ds2 come from the transposed product of g (fp32); ds1 from the
+    # forward product of x, whose matrix-core form rounds bf16 activations
+    e = [O.rel_err(dx.cpu().numpy(), rdx), O.rel_err(ds1.cpu().numpy(), rds1), O.rel_err(ds2.cpu().numpy(), rds2)]
+    print(f"grads {shape} T{T} {x_dtype}: dx {e[0]:.2e} ds1 {e[1]:.2e} ds2 {e[2]:.2e}")
+    assert e[0] <= 1e-5 and e[2] <= 1e-5
+    assert e[1] <= G.tol_for(T, x_dtype)
+
+
+def test_scale_grads_padded_words_and_workspace_reuse():
+    """Adjoint words with row padding, a shared workspace over two calls of
+    different T, and the decode and GEMM regimes back to back."""
+    shape = synth.LayerShape("gradspad", 96, 200, 40)
+    cfg = G.tiny_config("gradspad", x_dtype="f32")
+    dev, ref, _ = G.latent_layer(cfg, shape, ld_pad=3)
+    ut = nq.transpose_signs(dev.u_bits, shape.d_out, shape.r,
+                            out=torch.empty((nq.n_words(shape.d_out), shape.r + 5), dtype=torch.int32, device=G.DEV))
+    v = nq.transpose_signs(dev.vt_bits, shape.r, shape.d_in,
+                           out=torch.empty((nq.n_words(shape.r), shape.d_in + 2), dtype=torch.int32, device=G.DEV))
+    adj = nq.Adjoint(ut, v)
+    ws = torch.empty(nq.lrb_scale_grads_workspace_bytes(dev, 40), dtype=torch.uint8, device=G.DEV)
+    for T in (40, 2):
+        x = synth.activations(f"gradspad/x/{T}", T, shape.d_in, "f32")
+        g = synth.activations(f"gradspad/g/{T}", T, shape.d_out, "f32")
+        dx, ds1, ds2 = nq.lrb_scale_grads(dev, adj, G.to_device_x(x, "f32"), torch.from_numpy(g).to(G.DEV),
+                                          workspace=ws)
+        for got, want in zip((dx, ds1, ds2), O.scale_grads_factored_ref(ref, x, g)):
+            assert O.rel_err(got.cpu().numpy(), want) <= 1e-5
