@@ -24,7 +24,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16/bf16 matrix cores, TFLOP/s
-VALU_LANE_OPS = 256 * 64 * 2.4e9  # MI355X vector ALU lane-ops per second (256 CUs, 2.4 GHz)
 DECODE_SRC = os.path.join(ROOT, "sub_bit_weight_amd", "csrc", "decode_mfma.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_persistent_70b_stack_hbm_traffic.md")
 
@@ -180,6 +179,72 @@ def time_prefill(stack, T: int, device: str):
     return t0.elapsed_time(t1), seq, xs, ys
 
 
+def time_scale_grads(stack, T: int, device: str, reps: int = 3) -> dict:
+    """The scale-only reconstruction step (gradients of s1, s2 and x for a given
+    output gradient) over the linears of layer 0 at T tokens: the transposed
+    sign words are made once (timed separately), then `reps` passes."""
+    import numpy as np
+    import torch
+
+    import sub_bit_weight_amd as nq
+    import synth
+    from oracle import nq_oracle as O
+    per = len(stack.cfg.layers)
+    layers, shapes = stack.layers[:per], stack.shapes[:per]
+    gen = torch.Generator(device=device).manual_seed(2048)
+    xs = [torch.randn((T, s.d_in), generator=gen, device=device).to(torch.bfloat16) for s in shapes]
+    gs = [torch.randn((T, s.d_out), generator=gen, device=device).to(torch.bfloat16) for s in shapes]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # transposed sign words: outputs allocated first, so only the kernels are timed
+    outs = [(torch.empty((nq.n_words(L.d_out), L.r), dtype=torch.int32, device=device),
+             torch.empty((nq.n_words(L.r), L.d_in), dtype=torch.int32, device=device)) for L in layers]
+
+    def transpose_all():
+        for L, (ut, v) in zip(layers, outs):
+            nq.transpose_signs(L.u_bits, L.d_out, L.r, out=ut)
+            nq.transpose_signs(L.vt_bits, L.r, L.d_in, out=v)
+    transpose_all()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        transpose_all()
+    e1.record()
+    torch.cuda.synchronize()
+    t_ms = e0.elapsed_time(e1) / reps
+    adjs = [nq.Adjoint(ut, v) for ut, v in outs]
+    t_bytes = sum(2 * (L.u_bits.numel() + L.vt_bits.numel()) * 4 for L in layers)  # read + write
+    ws = torch.empty(max(nq.lrb_scale_grads_workspace_bytes(L, T) for L in layers), dtype=torch.uint8, device=device)
+    for L, a, x, g in zip(layers, adjs, xs, gs):  # warm-up pass
+        nq.lrb_scale_grads(L, a, x, g, workspace=ws)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        for L, a, x, g in zip(layers, adjs, xs, gs):
+            nq.lrb_scale_grads(L, a, x, g, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = sum(2 * 2 * T * s.r * (s.d_in + s.d_out) for s in shapes)  # forward + transposed product
+    # parity on a few tokens of layer 0's k against the float64 oracle
+    k = [s.name for s in shapes].index("k")
+    s = shapes[k]
+    inp = synth.lrb_inputs(stack.cfg, s, 0)
+    nwu, nwv = (s.r + 31) // 32, (s.d_in + 31) // 32
+    ref = O.LRB(synth.random_words(inp["u_seed"], np.arange(nwu * s.d_out, dtype=np.uint64)).reshape(nwu, s.d_out),
+                synth.random_words(inp["v_seed"], np.arange(nwv * s.r, dtype=np.uint64)).reshape(nwv, s.r),
+                inp["s1"], inp["s2"], s.d_out, s.d_in, s.r)
+    xq, gq = xs[k][:4].contiguous(), gs[k][:4].contiguous()
+    got = nq.lrb_scale_grads(layers[k], adjs[k], xq, gq)
+    want = O.scale_grads_factored_ref(ref, xq.float().cpu().numpy(), gq.float().cpu().numpy())
+    err = max(O.rel_err(a.cpu().numpy(), b) for a, b in zip(got, want))
+    return {"T": T, "linears": f"layer 0 ({per} linears)", "ms_per_layer": ms,
+            "tflops": flops / (ms * 1e-3) / 1e12, "frac_of_f16_peak": flops / (ms * 1e-3) / 1e12 / F16_PEAK_TFLOPS,
+            "algorithmic_flop_per_layer": flops,
+            "includes": "forward product without s1, transposed product without s2, token sums; x and g bf16",
+            "transpose_ms_per_layer": t_ms, "transpose_gbs": t_bytes / (t_ms * 1e-3) / 1e9,
+            "parity_rel_err": err, "parity_case": "layer 0 k, 4 tokens, max over dx, ds1, ds2"}
+
+
 def vendor_gemm_reference(shapes, T: int, device: str) -> dict:
     """Context for the matrix-core roofline: torch.matmul (hipBLASLt) on dense
     bf16 operands of the same GEMM shapes as the two LRB stages (M = T,
@@ -259,6 +324,7 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-055", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-grads", action="store_true", help="skip the scale-gradient (calibration) leg")
     ap.add_argument("--prefill-serial", action="store_true",
                     help="also time the prefill pass as serial single-linear calls on one stream")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -323,6 +389,12 @@ def main() -> int:
             log(f"[bench] prefill serial {sms:.1f} ms/pass")
         extra["prefill"]["vendor_dense_bf16_gemm_tflops"] = vendor_gemm_reference(stack.shapes[:len(cfg.layers)],
                                                                                   Tp, device)
+    if not args.no_grads:
+        log("[bench] scale gradients T=2048 (layer 0)")
+        extra["scale_grads"] = time_scale_grads(stack, 2048, device)
+        g = extra["scale_grads"]
+        log(f"[bench] scale gradients {g['ms_per_layer']:.2f} ms/layer, {g['tflops']:.0f} TFLOP/s, "
+            f"parity {g['parity_rel_err']:.2e}")
     del stack
     torch.cuda.empty_cache()
 
@@ -352,10 +424,11 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "dec_persistent_kernel<1> (one launch per step)",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic()},
-        # The decode kernel's own ceiling: 18 VALU lane-ops per 32-weight sign
-        # word (2 shifts, 8 nibble address selects, 8 fp32 adds) against
-        # 256 CUs x 64 lanes x 2.4 GHz of VALU lane-ops.
-        "decode_valu_ceiling_gbs": VALU_LANE_OPS / 18.0 * 4 / 1e9,
+        # The decode kernel's compute ceilings at 2.4 GHz: one 16x16x128
+        # fp4 x fp8 MFMA (32 cycles) per 64 sign words and SIMD; 11 full-rate
+        # VALU ops (2 cycles per wave64 op) per word expansion.
+        "decode_mfma_ceiling_gbs": 256 * 4 * 2.4e9 / 32 * 256 / 1e9,
+        "decode_valu_ceiling_gbs": 256 * 4 * 2.4e9 / (11 * 2) * 256 / 1e9,
         "parity_rel_err": err,
     }
     out.update(extra)

@@ -200,24 +200,25 @@ void nq_seq_destroy(nq_seq* s);
  *     dx[t][j] = sum_i W[i][j] g[t][i]
  *     ds1[i]   = sum_t g[t][i] * (U V^T (s2 (.) x_t))_i
  *     ds2[j]   = sum_t x[t][j] * (V U^T (s1 (.) g_t))_j
- *   x: [T][d_in] fp32 or bf16 (x_dtype); g: [T][d_out] fp32; dx: [T][d_in]
- *   fp32; ds1: [d_out] fp32; ds2: [d_in] fp32 (overwritten, not accumulated).
+ *   x: [T][d_in] fp32 or bf16 (x_dtype); g: [T][d_out] fp32 or bf16
+ *   (g_dtype); dx: [T][d_in] fp32; ds1: [d_out] fp32; ds2: [d_in] fp32
+ *   (overwritten, not accumulated).
  *   ut_bits/v_bits: the transposed layer's words from nq_transpose_signs.
  *   Both products run through the kernels of nq_lrb_linear (decode regime for
  *   T <= 8, GEMM regime above, with the same arithmetic); the token sums are
  *   fp32 in token order (deterministic).
  *   workspace: at least nq_lrb_scale_grads_workspace_bytes(L, T) bytes,
  *   256-byte aligned.  Errors: as for nq_lrb_linear, for L and for the
- *   transposed layer's words; NQ_ERR_ARG for a null or misaligned g, ds1 or
- *   ds2.
+ *   transposed layer's words; NQ_ERR_ARG for an unknown g_dtype or a null or
+ *   misaligned g, ds1 or ds2.
  */
 nq_status nq_transpose_signs(const uint32_t* src, int64_t n_out, int64_t n_red, int64_t ld,
                              uint32_t* dst, int64_t ldt, void* stream);
 size_t nq_lrb_scale_grads_workspace_bytes(const nq_lrb* L, int64_t T);
 nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t ldut,
                              const uint32_t* v_bits, int64_t ldvv, const void* x, nq_dtype x_dtype,
-                             const float* g, int64_t T, float* dx, float* ds1, float* ds2,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             const void* g, nq_dtype g_dtype, int64_t T, float* dx, float* ds1,
+                             float* ds2, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * nq_fill_random_words -- synthetic sign words for large benchmark matrices:

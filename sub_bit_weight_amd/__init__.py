@@ -87,7 +87,8 @@ def lib() -> ctypes.CDLL:
     L.nq_transpose_signs.restype = st
     L.nq_lrb_scale_grads_workspace_bytes.argtypes = [P(nq_lrb), i64]
     L.nq_lrb_scale_grads_workspace_bytes.restype = sz
-    L.nq_lrb_scale_grads.argtypes = [P(nq_lrb), vp, i64, vp, i64, vp, ctypes.c_int, vp, i64, vp, vp, vp, vp, sz, vp]
+    L.nq_lrb_scale_grads.argtypes = [P(nq_lrb), vp, i64, vp, i64, vp, ctypes.c_int, vp, ctypes.c_int, i64, vp, vp, vp,
+                                     vp, sz, vp]
     L.nq_lrb_scale_grads.restype = st
     L.nq_last_error.argtypes = []
     L.nq_last_error.restype = ctypes.c_char_p
@@ -272,14 +273,14 @@ def lrb_scale_grads_workspace_bytes(layer: Lrb, T: int) -> int:
 
 def lrb_scale_grads(layer: Lrb, adj: Adjoint, x: torch.Tensor, g: torch.Tensor,
                     workspace: torch.Tensor | None = None, stream=None):
-    """(dx, ds1, ds2) for y = W x and g = dL/dy: dx [T][d_in], ds1 [d_out], ds2 [d_in] (fp32)."""
+    """(dx, ds1, ds2) for y = W x and g = dL/dy (fp32 or bf16): dx [T][d_in], ds1 [d_out], ds2 [d_in] (fp32)."""
     _dev(x, "x")
     _dev(g, "g")
     T = x.shape[0]
     if x.dim() != 2 or x.shape[1] != layer.d_in:
         raise ValueError(f"x must be [T][{layer.d_in}], got {tuple(x.shape)}")
-    if g.dtype != torch.float32 or tuple(g.shape) != (T, layer.d_out) or not g.is_contiguous():
-        raise ValueError(f"g must be contiguous float32 [{T}][{layer.d_out}]")
+    if tuple(g.shape) != (T, layer.d_out) or not g.is_contiguous():
+        raise ValueError(f"g must be contiguous [{T}][{layer.d_out}]")
     s = layer.struct()
     dx = torch.empty((T, layer.d_in), dtype=torch.float32, device=x.device)
     ds1 = torch.empty(layer.d_out, dtype=torch.float32, device=x.device)
@@ -288,7 +289,7 @@ def lrb_scale_grads(layer: Lrb, adj: Adjoint, x: torch.Tensor, g: torch.Tensor,
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _check(lib().nq_lrb_scale_grads(ctypes.byref(s), _ptr(adj.ut_bits), adj.ut_bits.shape[1], _ptr(adj.v_bits),
-                                    adj.v_bits.shape[1], _ptr(x), _x_dtype(x), _ptr(g), T, _ptr(dx), _ptr(ds1),
+                                    adj.v_bits.shape[1], _ptr(x), _x_dtype(x), _ptr(g), _x_dtype(g), T, _ptr(dx), _ptr(ds1),
                                     _ptr(ds2), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)))
     return dx, ds1, ds2

@@ -45,35 +45,63 @@ __global__ __launch_bounds__(256) void transpose_signs_kernel(const uint32_t* __
   if (wt < nwt && e < n_red) dst[wt * ldt + e] = mine;
 }
 
+__device__ inline float load_act(const void* p, int bf16, int64_t i) {
+  return bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16) : static_cast<const float*>(p)[i];
+}
+
 // dx[t][j] = s2[j] b[t][j],  ds2[j] = sum_t x[t][j] b[t][j]  (columns j < d_in)
 // ds1[i] = sum_t g[t][i] u[t][i]                            (columns d_in + i)
-// One thread per column, tokens in order: deterministic fp32 sums.
-__global__ __launch_bounds__(256) void scale_grads_finish_kernel(const void* __restrict__ x, int x_bf16,
-                                                                 const float* __restrict__ g,
-                                                                 const float* __restrict__ u,
-                                                                 const float* __restrict__ b,
-                                                                 const float* __restrict__ s2, int64_t T,
-                                                                 int64_t d_in, int64_t d_out, float* __restrict__ dx,
-                                                                 float* __restrict__ ds1, float* __restrict__ ds2) {
+// Work item (column tile of 256, token chunk of tc): one thread per
+// column walks the chunk's tokens in order; rows are read as whole 256- or
+// 1024-byte segments per wave.  A single chunk writes ds1 / ds2 itself; else
+// each chunk writes its partial sums, part[chunk][column], and
+// scale_grads_sum_kernel adds them in chunk order.  Both orders are fixed:
+// the sums do not depend on scheduling.
+__global__ __launch_bounds__(256) void scale_grads_partial_kernel(
+    const void* __restrict__ x, int x_bf16, const void* __restrict__ g, int g_bf16, const float* __restrict__ u,
+    const float* __restrict__ b, const float* __restrict__ s2, int64_t T, int64_t tc, int64_t d_in, int64_t d_out,
+    float* __restrict__ dx, float* __restrict__ part, float* __restrict__ ds1, float* __restrict__ ds2) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.y * tc;
+  const int64_t t1 = t0 + tc < T ? t0 + tc : T;
+  const int64_t ncols = d_in + d_out;
+  float acc = 0.0f;
   if (c < d_in) {
     const float sc = s2[c];
-    float acc = 0.0f;
-    for (int64_t t = 0; t < T; ++t) {
+#pragma unroll 8
+    for (int64_t t = t0; t < t1; ++t) {
       const int64_t i = t * d_in + c;
       const float bv = b[i];
-      const float xv = x_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(x)[i] << 16)
-                              : static_cast<const float*>(x)[i];
       dx[i] = sc * bv;
-      acc = fmaf(xv, bv, acc);
+      acc = fmaf(load_act(x, x_bf16, i), bv, acc);
     }
-    ds2[c] = acc;
-  } else if (c < d_in + d_out) {
+  } else if (c < ncols) {
     const int64_t k = c - d_in;
-    float acc = 0.0f;
-    for (int64_t t = 0; t < T; ++t) acc = fmaf(g[t * d_out + k], u[t * d_out + k], acc);
-    ds1[k] = acc;
+#pragma unroll 8
+    for (int64_t t = t0; t < t1; ++t) acc = fmaf(load_act(g, g_bf16, t * d_out + k), u[t * d_out + k], acc);
+  } else {
+    return;
   }
+  if (gridDim.y > 1)
+    part[(int64_t)blockIdx.y * ncols + c] = acc;
+  else if (c < d_in)
+    ds2[c] = acc;
+  else
+    ds1[c - d_in] = acc;
+}
+
+__global__ __launch_bounds__(256) void scale_grads_sum_kernel(const float* __restrict__ part, int nchunks,
+                                                              int64_t d_in, int64_t d_out, float* __restrict__ ds1,
+                                                              float* __restrict__ ds2) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t ncols = d_in + d_out;
+  if (c >= ncols) return;
+  float acc = 0.0f;
+  for (int q = 0; q < nchunks; ++q) acc += part[(int64_t)q * ncols + c];
+  if (c < d_in)
+    ds2[c] = acc;
+  else
+    ds1[c - d_in] = acc;
 }
 
 }  // namespace
@@ -88,12 +116,26 @@ hipError_t launch_transpose_signs(const uint32_t* src, int64_t n_out, int64_t n_
   return hipGetLastError();
 }
 
-hipError_t launch_scale_grads_finish(const void* x, nq_dtype xd, const float* g, const float* u, const float* b,
-                                     const float* s2, int64_t T, int64_t d_in, int64_t d_out, float* dx, float* ds1,
-                                     float* ds2, hipStream_t s) {
-  const int64_t blocks = cdiv(d_in + d_out, 256);
-  hipLaunchKernelGGL(scale_grads_finish_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, (int)(xd == NQ_BF16), g, u,
-                     b, s2, T, d_in, d_out, dx, ds1, ds2);
+namespace {
+// tokens per chunk: kGradTokens, grown so that there are at most kGradChunks
+int64_t grad_chunk_tokens(int64_t T) { return std::max(kGradTokens, cdiv(T, kGradChunks)); }
+}  // namespace
+
+size_t scale_grads_partial_bytes(int64_t T, int64_t d_in, int64_t d_out) {
+  const int64_t nchunks = cdiv(T, grad_chunk_tokens(T));
+  return nchunks > 1 ? (size_t)nchunks * (size_t)(d_in + d_out) * sizeof(float) : 0;
+}
+
+hipError_t launch_scale_grads_finish(const void* x, nq_dtype xd, const void* g, nq_dtype gd, const float* u,
+                                     const float* b, const float* s2, int64_t T, int64_t d_in, int64_t d_out, float* dx,
+                                     float* part, float* ds1, float* ds2, hipStream_t s) {
+  const int64_t col_tiles = cdiv(d_in + d_out, 256);
+  const int64_t tc = grad_chunk_tokens(T), nchunks = cdiv(T, tc);
+  hipLaunchKernelGGL(scale_grads_partial_kernel, dim3((unsigned)col_tiles, (unsigned)nchunks), dim3(256), 0, s, x,
+                     (int)(xd == NQ_BF16), g, (int)(gd == NQ_BF16), u, b, s2, T, tc, d_in, d_out, dx, part, ds1, ds2);
+  if (nchunks > 1)
+    hipLaunchKernelGGL(scale_grads_sum_kernel, dim3((unsigned)col_tiles), dim3(256), 0, s, part, (int)nchunks, d_in,
+                       d_out, ds1, ds2);
   return hipGetLastError();
 }
 

@@ -115,16 +115,17 @@ nq_lrb adjoint_layer(const nq_lrb& L, const uint32_t* ut_bits, int64_t ldut, con
   return A;
 }
 
-// Workspace of nq_lrb_scale_grads: [u: T x d_out][b: T x d_in][one linear's
-// workspace, used by the two products in turn].
+// Workspace of nq_lrb_scale_grads: [u: T x d_out][b: T x d_in][per-chunk
+// partial sums][one linear's workspace, used by the two products in turn].
 struct ScaleGradsLayout {
-  size_t off_u, off_b, off_lin, bytes;
+  size_t off_u, off_b, off_part, off_lin, bytes;
 };
 ScaleGradsLayout scale_grads_layout(const nq_lrb& L, int64_t T) {
   ScaleGradsLayout g;
   g.off_u = 0;
   g.off_b = align_up((size_t)T * L.d_out * sizeof(float));
-  g.off_lin = g.off_b + align_up((size_t)T * L.d_in * sizeof(float));
+  g.off_part = g.off_b + align_up((size_t)T * L.d_in * sizeof(float));
+  g.off_lin = g.off_part + align_up(scale_grads_partial_bytes(T, L.d_in, L.d_out));
   const nq_lrb A = adjoint_layer(L, L.vt_bits, L.r, L.u_bits, L.d_in);  // sizes only
   g.bytes = g.off_lin + std::max(linear_workspace(L, T), linear_workspace(A, T));
   return g;
@@ -341,8 +342,9 @@ size_t nq_lrb_scale_grads_workspace_bytes(const nq_lrb* L, int64_t T) {
 }
 
 nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t ldut, const uint32_t* v_bits,
-                             int64_t ldvv, const void* x, nq_dtype x_dtype, const float* g, int64_t T, float* dx,
-                             float* ds1, float* ds2, void* workspace, size_t workspace_bytes, void* stream) {
+                             int64_t ldvv, const void* x, nq_dtype x_dtype, const void* g, nq_dtype g_dtype,
+                             int64_t T, float* dx, float* ds1, float* ds2, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   clear_error();
   const char* who = "nq_lrb_scale_grads";
   nq_status st = check_lrb(who, L);
@@ -352,9 +354,10 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
   nq_lrb A = adjoint_layer(*L, ut_bits, ldut, v_bits, ldvv);
   if ((st = check_lrb("nq_lrb_scale_grads (transposed sign words)", &A)) != NQ_OK) return st;
   if ((st = check_io(who, L, x, x_dtype, T, dx)) != NQ_OK) return st;
+  if (g_dtype != NQ_F32 && g_dtype != NQ_BF16) return set_error("%s: unknown g dtype %d", who, (int)g_dtype), NQ_ERR_ARG;
   if (!g || !ds1 || !ds2) return set_error("%s: null g, ds1 or ds2", who), NQ_ERR_ARG;
-  if (!aligned(g, 4) || !aligned(ds1, 4) || !aligned(ds2, 4))
-    return set_error("%s: g, ds1 or ds2 not 4-byte aligned", who), NQ_ERR_ARG;
+  if (!aligned(g, g_dtype == NQ_F32 ? 4 : 2) || !aligned(ds1, 4) || !aligned(ds2, 4))
+    return set_error("%s: g, ds1 or ds2 misaligned", who), NQ_ERR_ARG;
   const ScaleGradsLayout lay = scale_grads_layout(*L, T);
   if (!workspace || workspace_bytes < lay.bytes)
     return set_error("%s: workspace %zu bytes, need %zu", who, workspace ? workspace_bytes : 0, lay.bytes),
@@ -368,9 +371,10 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
   Lu.s1 = nullptr;
   A.s1 = nullptr;  // b = V (U^T (s1 (.) g)): the transposed product without s2
   hipError_t e = launch_linear(Lu, x, x_dtype, T, u, ws + lay.off_lin, s);
-  if (e == hipSuccess) e = launch_linear(A, g, NQ_F32, T, b, ws + lay.off_lin, s);
+  if (e == hipSuccess) e = launch_linear(A, g, g_dtype, T, b, ws + lay.off_lin, s);
   if (e == hipSuccess)
-    e = launch_scale_grads_finish(x, x_dtype, g, u, b, L->s2, T, L->d_in, L->d_out, dx, ds1, ds2, s);
+    e = launch_scale_grads_finish(x, x_dtype, g, g_dtype, u, b, L->s2, T, L->d_in, L->d_out, dx,
+                                  reinterpret_cast<float*>(ws + lay.off_part), ds1, ds2, s);
   return hip_status(e, "nq_lrb_scale_grads launch");
 }
 

@@ -94,9 +94,14 @@ hipError_t launch_dec_persistent(const StageDesc* segs, const int* tile_seg, int
 // of the scale gradients (grads.hip).
 hipError_t launch_transpose_signs(const uint32_t* src, int64_t n_out, int64_t n_red, int64_t ld, uint32_t* dst,
                                   int64_t ldt, hipStream_t s);
-hipError_t launch_scale_grads_finish(const void* x, nq_dtype xd, const float* g, const float* u, const float* b,
-                                     const float* s2, int64_t T, int64_t d_in, int64_t d_out, float* dx, float* ds1,
-                                     float* ds2, hipStream_t s);
+// Token chunks of the scale gradients' sums: kGradTokens tokens each, more
+// when T > kGradTokens * kGradChunks.  T > kGradTokens needs
+// scale_grads_partial_bytes of scratch (part) for the per-chunk sums.
+constexpr int64_t kGradTokens = 64, kGradChunks = 1024;
+size_t scale_grads_partial_bytes(int64_t T, int64_t d_in, int64_t d_out);
+hipError_t launch_scale_grads_finish(const void* x, nq_dtype xd, const void* g, nq_dtype gd, const float* u,
+                                     const float* b, const float* s2, int64_t T, int64_t d_in, int64_t d_out, float* dx,
+                                     float* part, float* ds1, float* ds2, hipStream_t s);
 
 // Matrix-core regime (T > 8).
 // split = false: never split a GEMM's reduction (entries of a sequence run

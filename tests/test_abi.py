@@ -135,10 +135,10 @@ def test_transpose_signs_rejects_bad_args():
     assert lib.nq_transpose_signs(DUMMY, 1 << 20, 1 << 20, 1 << 20, DUMMY, 1 << 20, None) == nq.NQ_ERR_UNSUPPORTED
 
 
-def _grads(layer, ut=DUMMY, ldut=32, v=DUMMY, ldvv=64, x=DUMMY, dtype=nq.NQ_BF16, g=DUMMY, T=1, dx=DUMMY,
-           ds1=DUMMY, ds2=DUMMY, ws=DUMMY, wsb=1 << 40):
-    return nq.lib().nq_lrb_scale_grads(ctypes.byref(layer), ut, ldut, v, ldvv, x, dtype, g, T, dx, ds1, ds2, ws,
-                                       wsb, None)
+def _grads(layer, ut=DUMMY, ldut=32, v=DUMMY, ldvv=64, x=DUMMY, dtype=nq.NQ_BF16, g=DUMMY, gdtype=nq.NQ_F32, T=1,
+           dx=DUMMY, ds1=DUMMY, ds2=DUMMY, ws=DUMMY, wsb=1 << 40):
+    return nq.lib().nq_lrb_scale_grads(ctypes.byref(layer), ut, ldut, v, ldvv, x, dtype, g, gdtype, T, dx, ds1, ds2,
+                                       ws, wsb, None)
 
 
 def test_scale_grads_rejects_bad_args():
@@ -149,6 +149,9 @@ def test_scale_grads_rejects_bad_args():
     assert _grads(L, ldvv=63) == nq.NQ_ERR_ARG
     assert _grads(L, v=DUMMY + 2) == nq.NQ_ERR_ARG
     assert _grads(L, g=None) == nq.NQ_ERR_ARG
+    assert _grads(L, gdtype=5) == nq.NQ_ERR_ARG
+    assert _grads(L, g=DUMMY + 2) == nq.NQ_ERR_ARG                  # fp32 g needs 4-byte alignment
+    assert _grads(L, g=DUMMY + 1, gdtype=nq.NQ_BF16) == nq.NQ_ERR_ARG
     assert _grads(L, ds1=DUMMY + 1) == nq.NQ_ERR_ARG
     assert _grads(L, ds2=None) == nq.NQ_ERR_ARG
     assert _grads(L, dx=None) == nq.NQ_ERR_ARG
