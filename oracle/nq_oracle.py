@@ -255,6 +255,32 @@ def scale_grads_factored_ref(L: LRB, x: np.ndarray, g: np.ndarray):
     return b * s2[None, :], np.sum(g64 * u, axis=0), np.sum(x64 * b, axis=0)
 
 
+# --------------------------------------------------------------------------
+# magnitude balancing and scale extraction (section 3, "Magnitude Balancing
+# and Scale Extraction"): after the ADMM step the continuous factors can be
+# rescaled inversely without changing their product; the method fixes that
+# freedom by equalising their Frobenius norms and reads the scale vectors off
+# the balanced factors as per-row mean absolute values.
+# --------------------------------------------------------------------------
+
+
+def balance_ref(U_hat: np.ndarray, V_hat: np.ndarray):
+    """(U, V, s1, s2, eta) in float64 for the latent factors U_hat [d_out][r]
+    and V_hat [d_in][r]:
+        eta = sqrt(||V_hat||_F / ||U_hat||_F),  U = eta U_hat,  V = V_hat / eta,
+        s1[i] = mean_k |U[i, k]|,  s2[j] = mean_k |V[j, k]|.
+    Reading where the section is silent: if either norm is 0 the product is 0
+    and no ratio exists; eta is then 1 (the factors are left as they are)."""
+    U_hat = np.asarray(U_hat, dtype=np.float32).astype(np.float64)
+    V_hat = np.asarray(V_hat, dtype=np.float32).astype(np.float64)
+    nu = np.linalg.norm(U_hat)
+    nv = np.linalg.norm(V_hat)
+    eta = float(np.sqrt(nv / nu)) if nu > 0 and nv > 0 else 1.0
+    U = eta * U_hat
+    V = V_hat / eta
+    return U, V, np.mean(np.abs(U), axis=1), np.mean(np.abs(V), axis=1), eta
+
+
 def rel_err(y: np.ndarray, y_ref: np.ndarray) -> float:
     """Normwise relative error ||y - y_ref||_F / ||y_ref||_F (float64)."""
     y = np.asarray(y, dtype=np.float64)

@@ -387,3 +387,65 @@ def test_scale_grads_factored_equals_dense():
     L, U, V, s1, s2, x, gy = _grads_case(9, 48, 80, 40, 4)
     for a, b in zip(O.scale_grads_factored_ref(L, x, gy), O.scale_grads_ref(L, x, gy)):
         assert O.rel_err(a, b) <= 1e-12
+
+
+# ---- magnitude balancing and scale extraction --------------------------------
+
+def test_balance_hand_examples():
+    """Hand-worked cases (tests/golden/balance_example.json), incl. the zero
+    factor where the ratio of norms does not exist."""
+    for c in _load("balance_example.json")["cases"]:
+        U, V, s1, s2, eta = O.balance_ref(np.array(c["U_hat"], np.float32), np.array(c["V_hat"], np.float32))
+        assert eta == pytest.approx(c["eta"], rel=1e-15)
+        np.testing.assert_allclose(U, c["U"], rtol=1e-15, atol=0)
+        np.testing.assert_allclose(V, c["V"], rtol=1e-15, atol=0)
+        np.testing.assert_allclose(s1, c["s1"], rtol=1e-15, atol=0)
+        np.testing.assert_allclose(s2, c["s2"], rtol=1e-15, atol=0)
+
+
+def _latents(seed, d_out, d_in, r, su=1.0, sv=1.0):
+    g = np.random.default_rng(seed)
+    return ((g.standard_normal((d_out, r)) * su).astype(np.float32),
+            (g.standard_normal((d_in, r)) * sv).astype(np.float32))
+
+
+def test_balance_invariants():
+    """Equal balanced norms; the product U V^T unchanged; signs unchanged;
+    the result does not depend on how the latent scale is split between the
+    factors (c U_hat, V_hat / c give the same U, V, s1, s2)."""
+    Uh, Vh = _latents(1, 37, 53, 11, su=0.01, sv=30.0)
+    U, V, s1, s2, eta = O.balance_ref(Uh, Vh)
+    assert np.linalg.norm(U) == pytest.approx(np.linalg.norm(V), rel=1e-13)
+    np.testing.assert_allclose(U @ V.T, Uh.astype(np.float64) @ Vh.astype(np.float64).T, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(np.signbit(U), np.signbit(Uh)) and np.array_equal(np.signbit(V), np.signbit(Vh))
+    c = np.float32(8.0)  # a power of two keeps the rescaled latents exact in fp32
+    U2, V2, s12, s22, eta2 = O.balance_ref(Uh * c, Vh / c)
+    assert eta2 == pytest.approx(eta / 8.0, rel=1e-14)
+    for a, b in ((U2, U), (V2, V), (s12, s1), (s22, s2)):
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=0)
+
+
+def test_balance_brute_force_exact():
+    """Integer latents: eta^4 equals the exact ratio of squared norms, and the
+    scales equal eta times (or 1/eta times) the exact mean of the row's
+    absolute values (Fractions, plain loops)."""
+    g = np.random.default_rng(3)
+    Uh = g.integers(-9, 10, size=(4, 3)).astype(np.float32)
+    Vh = g.integers(-9, 10, size=(5, 3)).astype(np.float32)
+    U, V, s1, s2, eta = O.balance_ref(Uh, Vh)
+    su = sum(Fraction(int(v)) ** 2 for v in Uh.ravel())
+    sv = sum(Fraction(int(v)) ** 2 for v in Vh.ravel())
+    assert eta ** 4 == pytest.approx(float(sv / su), rel=1e-14)
+    for i in range(4):
+        mean = sum(abs(Fraction(int(v))) for v in Uh[i]) / 3
+        assert s1[i] == pytest.approx(eta * float(mean), rel=1e-15)
+    for j in range(5):
+        mean = sum(abs(Fraction(int(v))) for v in Vh[j]) / 3
+        assert s2[j] == pytest.approx(float(mean) / eta, rel=1e-15)
+
+
+def test_balance_already_balanced_is_identity():
+    Uh, Vh = _latents(4, 16, 16, 8)
+    Vh = (Vh * (np.linalg.norm(Uh.astype(np.float64)) / np.linalg.norm(Vh.astype(np.float64)))).astype(np.float32)
+    U, V, s1, s2, eta = O.balance_ref(Uh, Vh)
+    assert eta == pytest.approx(1.0, abs=1e-7)
