@@ -245,6 +245,59 @@ def time_scale_grads(stack, T: int, device: str, reps: int = 3) -> dict:
             "parity_rel_err": err, "parity_case": "layer 0 k, 4 tokens, max over dx, ds1, ds2"}
 
 
+def time_balance(shapes, device: str, reps: int = 5) -> dict:
+    """Magnitude balancing and scale extraction of the fp32 latent factors of
+    layer 0's linears (U_hat [d_out][r], V_hat [d_in][r]), balanced factors
+    written to separate buffers.  Algorithmic bytes: the latents read twice
+    (row statistics, then scaling) and written once."""
+    import torch
+
+    import sub_bit_weight_amd as nq
+    from oracle import nq_oracle as O
+    gen = torch.Generator(device=device).manual_seed(55)
+    lat = [(torch.randn((s.d_out, s.r), generator=gen, device=device) * 0.05,
+            torch.randn((s.d_in, s.r), generator=gen, device=device) * 2.0) for s in shapes]
+    outs = [(torch.empty_like(u), torch.empty_like(v)) for u, v in lat]
+    sc = [(torch.empty(s.d_out, device=device), torch.empty(s.d_in, device=device), torch.empty(1, device=device))
+          for s in shapes]
+    ws = torch.empty(max(nq.lib().nq_balance_workspace_bytes(s.d_out, s.d_in) for s in shapes), dtype=torch.uint8,
+                     device=device)
+    lib = nq.lib()
+
+    def run(balanced: bool):
+        for s, (u, v), (uo, vo), (s1, s2, eta) in zip(shapes, lat, outs, sc):
+            st = lib.nq_balance_factors(u.data_ptr(), s.d_out, s.r, v.data_ptr(), s.d_in, s.r, s.r,
+                                        uo.data_ptr() if balanced else None, vo.data_ptr() if balanced else None,
+                                        s1.data_ptr(), s2.data_ptr(), eta.data_ptr(), ws.data_ptr(), ws.numel(),
+                                        torch.cuda.current_stream().cuda_stream)
+            assert st == 0, lib.nq_last_error()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    lat_bytes = sum((s.d_out + s.d_in) * s.r * 4 for s in shapes)
+    for balanced, nbytes in ((True, 3 * lat_bytes), (False, lat_bytes)):
+        run(balanced)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            run(balanced)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res["balanced_factors" if balanced else "scales_only"] = {
+            "ms_per_layer": ms, "gbs": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e12 / 8.0,
+            "algorithmic_bytes": nbytes}
+    run(True)
+    # parity on layer 0's first linear: scales and eta against the float64 oracle
+    s0 = shapes[0]
+    U0, V0, rs1, rs2, reta = O.balance_ref(lat[0][0].cpu().numpy(), lat[0][1].cpu().numpy())
+    err = max(O.rel_err(sc[0][0].cpu().numpy(), rs1), O.rel_err(sc[0][1].cpu().numpy(), rs2),
+              O.rel_err(outs[0][0].cpu().numpy(), U0), O.rel_err(outs[0][1].cpu().numpy(), V0),
+              abs(float(sc[0][2].item()) / reta - 1))
+    res.update({"linears": f"layer 0 ({len(shapes)} linears)", "latent_bytes": lat_bytes, "parity_rel_err": err,
+                "parity_case": f"{s0.name}: U, V, s1, s2, eta"})
+    return res
+
+
 def vendor_gemm_reference(shapes, T: int, device: str) -> dict:
     """Context for the matrix-core roofline: torch.matmul (hipBLASLt) on dense
     bf16 operands of the same GEMM shapes as the two LRB stages (M = T,
@@ -325,6 +378,7 @@ def main() -> int:
     ap.add_argument("--no-055", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-grads", action="store_true", help="skip the scale-gradient (calibration) leg")
+    ap.add_argument("--no-balance", action="store_true", help="skip the magnitude-balancing leg")
     ap.add_argument("--prefill-serial", action="store_true",
                     help="also time the prefill pass as serial single-linear calls on one stream")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -395,6 +449,13 @@ def main() -> int:
         g = extra["scale_grads"]
         log(f"[bench] scale gradients {g['ms_per_layer']:.2f} ms/layer, {g['tflops']:.0f} TFLOP/s, "
             f"parity {g['parity_rel_err']:.2e}")
+    if not args.no_balance:
+        log("[bench] magnitude balancing (layer 0 latents)")
+        extra["balance"] = time_balance(stack.shapes[:len(cfg.layers)], device)
+        b = extra["balance"]
+        log(f"[bench] balancing {b['balanced_factors']['ms_per_layer']:.2f} ms/layer "
+            f"({b['balanced_factors']['gbs']:.0f} GB/s), scales only {b['scales_only']['ms_per_layer']:.2f} ms "
+            f"({b['scales_only']['gbs']:.0f} GB/s), parity {b['parity_rel_err']:.2e}")
     del stack
     torch.cuda.empty_cache()
 

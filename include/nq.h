@@ -221,6 +221,35 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
                              float* ds2, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Magnitude balancing and scale extraction (section 3, "Magnitude Balancing
+ * and Scale Extraction"): the step between the ADMM factorization and the
+ * sign packing.  The latent factors can be rescaled inversely without
+ * changing their product; balancing equalises their Frobenius norms and the
+ * scale vectors are the balanced factors' per-row mean absolute values.
+ *
+ * nq_balance_factors --
+ *     eta = sqrt(||V_hat||_F / ||U_hat||_F)      (1 if either norm is 0)
+ *     U = eta * U_hat,   V = V_hat / eta
+ *     s1[i] = mean_k |U[i][k]|,   s2[j] = mean_k |V[j][k]|
+ *   u_hat: [d_out][ldu] fp32, row i's r entries first (the U latent layout of
+ *   nq_pack_signs when ldu = r); v_hat: [d_in][ldv] likewise.  u_out, v_out:
+ *   both null (scales only) or both given, with the inputs' strides; each may
+ *   be its input (in place) but must not otherwise overlap anything.  s1:
+ *   [d_out], s2: [d_in], eta: [1] fp32 device.  Row sums are fp32 in a fixed
+ *   order, the norms fp64 (deterministic).  Signs are unchanged (eta > 0), so
+ *   nq_pack_signs may read either the latents or the balanced factors.
+ *   workspace: at least nq_balance_workspace_bytes(d_out, d_in) bytes,
+ *   256-byte aligned.  Errors: NQ_ERR_ARG for null inputs, scales or eta,
+ *   sizes < 1, ldu or ldv < r, only one of u_out / v_out, pointers not 4-byte
+ *   aligned; NQ_ERR_WORKSPACE for a missing or short workspace.
+ */
+size_t nq_balance_workspace_bytes(int64_t d_out, int64_t d_in);
+nq_status nq_balance_factors(const float* u_hat, int64_t d_out, int64_t ldu, const float* v_hat,
+                             int64_t d_in, int64_t ldv, int64_t r, float* u_out, float* v_out,
+                             float* s1, float* s2, float* eta, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * nq_fill_random_words -- synthetic sign words for large benchmark matrices:
  *   dst[i] = low 32 bits of SplitMix64(seed, i), i < n, where SplitMix64(seed,
  *   i) is output number i+1 of the SplitMix64 stream started at `seed`

@@ -28,7 +28,8 @@ EXPORTED = [
     "nq_pack_signs", "nq_unpack_signs", "nq_lrb_workspace_bytes", "nq_lrb_linear", "nq_reconstruct",
     "nq_storage_bits", "nq_seq_create", "nq_seq_workspace_bytes", "nq_seq_run", "nq_seq_destroy",
     "nq_fill_random_words", "nq_last_error", "nq_version", "nq_transpose_signs",
-    "nq_lrb_scale_grads_workspace_bytes", "nq_lrb_scale_grads",
+    "nq_lrb_scale_grads_workspace_bytes", "nq_lrb_scale_grads", "nq_balance_workspace_bytes",
+    "nq_balance_factors",
 ]
 
 
@@ -90,6 +91,10 @@ def lib() -> ctypes.CDLL:
     L.nq_lrb_scale_grads.argtypes = [P(nq_lrb), vp, i64, vp, i64, vp, ctypes.c_int, vp, ctypes.c_int, i64, vp, vp, vp,
                                      vp, sz, vp]
     L.nq_lrb_scale_grads.restype = st
+    L.nq_balance_workspace_bytes.argtypes = [i64, i64]
+    L.nq_balance_workspace_bytes.restype = sz
+    L.nq_balance_factors.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.nq_balance_factors.restype = st
     L.nq_last_error.argtypes = []
     L.nq_last_error.restype = ctypes.c_char_p
     L.nq_version.argtypes = []
@@ -293,6 +298,38 @@ def lrb_scale_grads(layer: Lrb, adj: Adjoint, x: torch.Tensor, g: torch.Tensor,
                                     _ptr(ds2), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)))
     return dx, ds1, ds2
+
+
+def balance_factors(u_hat: torch.Tensor, v_hat: torch.Tensor, r: int | None = None, balanced: bool = True,
+                    inplace: bool = False, workspace: torch.Tensor | None = None, stream=None):
+    """Magnitude balancing and scale extraction of latent factors u_hat
+    [d_out][>= r] and v_hat [d_in][>= r] (fp32, row stride = shape[1]).
+    Returns (U, V, s1, s2, eta): the balanced factors (None when balanced is
+    False; the inputs themselves when inplace), the scales and eta ([1])."""
+    _dev(u_hat, "u_hat")
+    _dev(v_hat, "v_hat")
+    for t, n in ((u_hat, "u_hat"), (v_hat, "v_hat")):
+        if t.dtype != torch.float32 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{n} must be 2-D float32 with unit column stride")
+    r = u_hat.shape[1] if r is None else r
+    d_out, d_in = u_hat.shape[0], v_hat.shape[0]
+    dev = u_hat.device
+    if balanced:
+        uo = u_hat if inplace else torch.empty_like(u_hat)
+        vo = v_hat if inplace else torch.empty_like(v_hat)
+    else:
+        uo = vo = None
+    s1 = torch.empty(d_out, dtype=torch.float32, device=dev)
+    s2 = torch.empty(d_in, dtype=torch.float32, device=dev)
+    eta = torch.empty(1, dtype=torch.float32, device=dev)
+    need = int(lib().nq_balance_workspace_bytes(d_out, d_in))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().nq_balance_factors(_ptr(u_hat), d_out, u_hat.stride(0), _ptr(v_hat), d_in, v_hat.stride(0), r,
+                                    None if uo is None else _ptr(uo), None if vo is None else _ptr(vo), _ptr(s1),
+                                    _ptr(s2), _ptr(eta), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)))
+    return uo, vo, s1, s2, eta
 
 
 class Seq:

@@ -378,6 +378,38 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
   return hip_status(e, "nq_lrb_scale_grads launch");
 }
 
+size_t nq_balance_workspace_bytes(int64_t d_out, int64_t d_in) {
+  if (d_out < 1 || d_in < 1 || d_out > (int64_t(1) << 30) || d_in > (int64_t(1) << 30)) return 0;
+  return balance_workspace_bytes(d_out, d_in);
+}
+
+nq_status nq_balance_factors(const float* u_hat, int64_t d_out, int64_t ldu, const float* v_hat, int64_t d_in,
+                             int64_t ldv, int64_t r, float* u_out, float* v_out, float* s1, float* s2, float* eta,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* who = "nq_balance_factors";
+  if (!u_hat || !v_hat || !s1 || !s2 || !eta) return set_error("%s: null input, scale or eta", who), NQ_ERR_ARG;
+  if (d_out < 1 || d_in < 1 || r < 1 || d_out > (int64_t(1) << 30) || d_in > (int64_t(1) << 30))
+    return set_error("%s: bad sizes d_out=%lld d_in=%lld r=%lld", who, (long long)d_out, (long long)d_in,
+                     (long long)r),
+           NQ_ERR_ARG;
+  if (ldu < r || ldv < r)
+    return set_error("%s: ldu=%lld / ldv=%lld below r=%lld", who, (long long)ldu, (long long)ldv, (long long)r),
+           NQ_ERR_ARG;
+  if ((u_out == nullptr) != (v_out == nullptr)) return set_error("%s: give both u_out and v_out or neither", who), NQ_ERR_ARG;
+  if (!aligned(u_hat, 4) || !aligned(v_hat, 4) || !aligned(u_out, 4) || !aligned(v_out, 4) || !aligned(s1, 4) ||
+      !aligned(s2, 4) || !aligned(eta, 4))
+    return set_error("%s: a pointer is not 4-byte aligned", who), NQ_ERR_ARG;
+  const size_t need = balance_workspace_bytes(d_out, d_in);
+  if (!workspace || workspace_bytes < need)
+    return set_error("%s: workspace %zu bytes, need %zu", who, workspace ? workspace_bytes : 0, need),
+           NQ_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return set_error("%s: workspace not 256-byte aligned", who), NQ_ERR_ARG;
+  return hip_status(launch_balance(u_hat, ldu, v_hat, ldv, d_out, d_in, r, u_out, v_out, s1, s2, eta, workspace,
+                                   (hipStream_t)stream),
+                    "nq_balance_factors launch");
+}
+
 nq_status nq_fill_random_words(uint32_t* dst, int64_t n, uint64_t seed, void* stream) {
   clear_error();
   if (!dst || n < 0) return set_error("nq_fill_random_words: null dst or n < 0"), NQ_ERR_ARG;

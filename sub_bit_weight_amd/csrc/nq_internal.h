@@ -103,6 +103,13 @@ hipError_t launch_scale_grads_finish(const void* x, nq_dtype xd, const void* g, 
                                      const float* b, const float* s2, int64_t T, int64_t d_in, int64_t d_out, float* dx,
                                      float* part, float* ds1, float* ds2, hipStream_t s);
 
+// Magnitude balancing and scale extraction (balance.hip).  workspace: at
+// least balance_workspace_bytes(d_out, d_in), 256-byte aligned.
+size_t balance_workspace_bytes(int64_t d_out, int64_t d_in);
+hipError_t launch_balance(const float* uh, int64_t ldu, const float* vh, int64_t ldv, int64_t d_out, int64_t d_in,
+                          int64_t r, float* uo, float* vo, float* s1, float* s2, float* eta, void* workspace,
+                          hipStream_t s);
+
 // Matrix-core regime (T > 8).
 // split = false: never split a GEMM's reduction (entries of a sequence run
 // concurrently and fill the chip together).

@@ -168,3 +168,37 @@ def test_scale_grads_workspace_query():
     assert need >= 16 * (64 + 64) * 4 + lib.nq_lrb_workspace_bytes(ctypes.byref(L), 16)
     assert lib.nq_lrb_scale_grads_workspace_bytes(ctypes.byref(L), 0) == 0
     assert lib.nq_lrb_scale_grads_workspace_bytes(ctypes.byref(_layer(r=0)), 4) == 0
+
+
+def _balance(u=DUMMY, d_out=8, ldu=4, v=DUMMY, d_in=5, ldv=4, r=4, uo=None, vo=None, s1=DUMMY, s2=DUMMY, eta=DUMMY,
+             ws=DUMMY, wsb=1 << 20):
+    return nq.lib().nq_balance_factors(u, d_out, ldu, v, d_in, ldv, r, uo, vo, s1, s2, eta, ws, wsb, None)
+
+
+def test_balance_rejects_bad_args():
+    """Every check runs on the host before any HIP call."""
+    assert _balance(u=None) == nq.NQ_ERR_ARG
+    assert _balance(v=None) == nq.NQ_ERR_ARG
+    assert _balance(s1=None) == nq.NQ_ERR_ARG
+    assert _balance(s2=None) == nq.NQ_ERR_ARG
+    assert _balance(eta=None) == nq.NQ_ERR_ARG
+    assert _balance(d_out=0) == nq.NQ_ERR_ARG
+    assert _balance(d_in=0) == nq.NQ_ERR_ARG
+    assert _balance(r=0) == nq.NQ_ERR_ARG
+    assert _balance(ldu=3) == nq.NQ_ERR_ARG
+    assert _balance(ldv=3) == nq.NQ_ERR_ARG
+    assert _balance(uo=DUMMY) == nq.NQ_ERR_ARG          # only one of the outputs
+    assert _balance(vo=DUMMY) == nq.NQ_ERR_ARG
+    assert _balance(u=DUMMY + 2) == nq.NQ_ERR_ARG       # not 4-byte aligned
+    assert _balance(uo=DUMMY + 1, vo=DUMMY) == nq.NQ_ERR_ARG
+    assert _balance(ws=None) == nq.NQ_ERR_WORKSPACE
+    assert _balance(wsb=16) == nq.NQ_ERR_WORKSPACE
+    assert _balance(ws=DUMMY + 4) == nq.NQ_ERR_ARG      # not 256-byte aligned
+    assert "nq_balance_factors" in nq.lib().nq_last_error().decode()
+
+
+def test_balance_workspace_query():
+    lib = nq.lib()
+    assert lib.nq_balance_workspace_bytes(8, 5) >= 2 * 13 * 4
+    assert lib.nq_balance_workspace_bytes(0, 5) == 0
+    assert lib.nq_balance_workspace_bytes(8, 0) == 0

@@ -3,6 +3,8 @@ seeded inputs.  Packing, the pack/unpack round trip, the word layout and the
 dense reconstruction are bit-exact; nq_lrb_linear is within the normwise
 relative-error bar (2e-3 for bf16 activations in the matrix-core regime,
 1e-5 for fp32 arithmetic)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -10,6 +12,7 @@ import torch
 import synth
 from oracle import nq_oracle as O
 from tests import gpu_cases as G
+from tests.conftest import GOLDEN
 
 pytestmark = pytest.mark.gpu
 
@@ -444,3 +447,69 @@ def test_scale_grads_many_token_chunks():
     dx, ds1, ds2 = nq.lrb_scale_grads(dev, nq.Adjoint.of(dev), G.to_device_x(x, "bf16"), G.to_device_x(g, "bf16"))
     for got, want in zip((dx, ds1, ds2), O.scale_grads_factored_ref(ref, x, g)):
         assert O.rel_err(got.cpu().numpy(), want) <= G.prefill_tol("bf16")
+
+
+# ---- magnitude balancing and scale extraction --------------------------------
+
+# (d_out, d_in, r, row padding): the row stride r + pad decides between the
+# float4 path (stride a multiple of 4) and the one-float path
+BAL_CASES = [(1, 1, 1, 0), (2, 3, 2, 0), (37, 53, 11, 0), (64, 96, 64, 0), (300, 129, 257, 0),
+             (33, 65, 100, 3), (40, 24, 61, 4), (130, 7, 1000, 0), (50, 70, 61, 3), (9, 5, 6, 2)]
+
+
+@pytest.mark.parametrize("d_out,d_in,r,pad", BAL_CASES)
+@pytest.mark.parametrize("mode", ["balanced", "scales", "inplace"])
+def test_balance_parity(d_out, d_in, r, pad, mode):
+    uh = np.full((d_out, r + pad), 1e6, np.float32)
+    vh = np.full((d_in, r + pad), -1e6, np.float32)
+    uh[:, :r] = synth.normal_f32(f"bal/u/{d_out}/{r}", (d_out, r)) * np.float32(0.02)
+    vh[:, :r] = synth.normal_f32(f"bal/v/{d_in}/{r}", (d_in, r)) * np.float32(3.0)
+    U0, V0, rs1, rs2, reta = O.balance_ref(uh[:, :r], vh[:, :r])
+    du, dv = torch.from_numpy(uh).to(G.DEV), torch.from_numpy(vh).to(G.DEV)
+    U, V, s1, s2, eta = nq.balance_factors(du, dv, r=r, balanced=mode != "scales", inplace=mode == "inplace")
+    assert abs(float(eta.item()) / reta - 1) <= 1e-6
+    assert O.rel_err(s1.cpu().numpy(), rs1) <= 1e-6 and O.rel_err(s2.cpu().numpy(), rs2) <= 1e-6
+    if mode == "scales":
+        assert U is None and V is None
+        return
+    if mode == "inplace":
+        assert U is du and V is dv
+    Uh, Vh = U.cpu().numpy(), V.cpu().numpy()
+    assert O.rel_err(Uh[:, :r], U0) <= 1e-6 and O.rel_err(Vh[:, :r], V0) <= 1e-6
+    # row padding (1e6 / -1e6) enters no sum (checked above) and is not written
+    if mode == "inplace":
+        assert np.all(Uh[:, r:] == np.float32(1e6)) and np.all(Vh[:, r:] == np.float32(-1e6))
+    # eta > 0: the balanced factors pack to the same sign words
+    a = nq.pack_signs(U, d_out, r, U.stride(0), 1)
+    b = nq.pack_signs(torch.from_numpy(uh).to(G.DEV), d_out, r, r + pad, 1)
+    assert torch.equal(a, b)
+
+
+def test_balance_zero_factor_and_golden():
+    """A zero factor (eta = 1 by the stated reading) and the hand-worked
+    cases of tests/golden/balance_example.json through the library."""
+    import json
+    with open(os.path.join(GOLDEN, "balance_example.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        uh = torch.tensor(c["U_hat"], dtype=torch.float32, device=G.DEV)
+        vh = torch.tensor(c["V_hat"], dtype=torch.float32, device=G.DEV)
+        U, V, s1, s2, eta = nq.balance_factors(uh, vh)
+        assert float(eta.item()) == pytest.approx(c["eta"], rel=1e-6)
+        np.testing.assert_allclose(U.cpu().numpy(), c["U"], rtol=1e-6, atol=0)
+        np.testing.assert_allclose(V.cpu().numpy(), c["V"], rtol=1e-6, atol=0)
+        np.testing.assert_allclose(s1.cpu().numpy(), c["s1"], rtol=1e-6, atol=0)
+        np.testing.assert_allclose(s2.cpu().numpy(), c["s2"], rtol=1e-6, atol=0)
+
+
+def test_balance_llama_shape():
+    """Latents of a 4096 x 11008 MLP projection at rank 2368, against the
+    oracle on every element."""
+    d_out, d_in, r = 11008, 4096, 2368
+    uh = synth.normal_f32("bal/big/u", (d_out, r)) * np.float32(0.05)
+    vh = synth.normal_f32("bal/big/v", (d_in, r)) * np.float32(2.0)
+    U0, V0, rs1, rs2, reta = O.balance_ref(uh, vh)
+    U, V, s1, s2, eta = nq.balance_factors(torch.from_numpy(uh).to(G.DEV), torch.from_numpy(vh).to(G.DEV))
+    assert abs(float(eta.item()) / reta - 1) <= 1e-6
+    for got, want in ((U, U0), (V, V0), (s1, rs1), (s2, rs2)):
+        assert O.rel_err(got.cpu().numpy(), want) <= 1e-6
