@@ -256,6 +256,23 @@ def scale_grads_factored_ref(L: LRB, x: np.ndarray, g: np.ndarray):
 
 
 # --------------------------------------------------------------------------
+# refinement forward (section 3, "Step 3: Factorized Component Refinement"):
+# the binary factors are the signs of real latents that the refinement keeps
+# updating, so the forward pass takes sign() of the latents as it goes.
+# --------------------------------------------------------------------------
+
+
+def linear_latent_ref(U_lat: np.ndarray, V_lat: np.ndarray, s1, s2, x: np.ndarray) -> np.ndarray:
+    """y = s1 (.) sign(U_lat) (sign(V_lat)^T (s2 (.) x)) in float64, for U_lat
+    [d_out][r], V_lat [d_in][r], x [T][d_in]; sign(v) = -1 for v < 0, else +1
+    (+0, -0 and NaN give +1)."""
+    SU = np.where(np.asarray(U_lat, dtype=np.float32) < 0, -1.0, 1.0)
+    SV = np.where(np.asarray(V_lat, dtype=np.float32) < 0, -1.0, 1.0)
+    z = np.asarray(x, dtype=np.float32).astype(np.float64) * np.asarray(s2, dtype=np.float32).astype(np.float64)
+    return ((z @ SV) @ SU.T) * np.asarray(s1, dtype=np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
 # magnitude balancing and scale extraction (section 3, "Magnitude Balancing
 # and Scale Extraction"): after the ADMM step the continuous factors can be
 # rescaled inversely without changing their product; the method fixes that

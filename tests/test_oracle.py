@@ -449,3 +449,35 @@ def test_balance_already_balanced_is_identity():
     Vh = (Vh * (np.linalg.norm(Uh.astype(np.float64)) / np.linalg.norm(Vh.astype(np.float64)))).astype(np.float32)
     U, V, s1, s2, eta = O.balance_ref(Uh, Vh)
     assert eta == pytest.approx(1.0, abs=1e-7)
+
+
+# ---- refinement forward from latents -----------------------------------------
+
+def test_linear_latent_equals_pack_then_linear():
+    """The sign-of-latent forward against the packed route (bit packing, word
+    unpacking and the factored product: no shared arithmetic)."""
+    g = np.random.default_rng(11)
+    d_out, d_in, r, T = 37, 70, 45, 3
+    Ul = g.standard_normal((d_out, r)).astype(np.float32)
+    Vl = g.standard_normal((d_in, r)).astype(np.float32)
+    Ul[0, :5] = [0.0, -0.0, np.nan, -np.inf, np.inf]
+    Vl[3, :3] = [-0.0, np.nan, 0.0]
+    s1 = g.random(d_out).astype(np.float32)
+    s2 = g.random(d_in).astype(np.float32)
+    x = g.standard_normal((T, d_in)).astype(np.float32)
+    L = O.LRB(O.pack_ref(Ul), O.pack_ref(Vl.T), s1, s2, d_out, d_in, r)
+    got = O.linear_latent_ref(Ul, Vl, s1, s2, x)
+    assert O.rel_err(got, O.linear_factored_ref(L, x)) <= 1e-13
+    assert O.rel_err(got, O.linear_ref(L, x)) <= 1e-12
+
+
+def test_linear_latent_hand_case():
+    """d_out=2, d_in=2, r=1: sign(U) = [+1, -1] (the 0 packs as +1),
+    sign(V) = [-1, +1]; W = s1 * [[-1, 1], [1, -1]] * s2."""
+    U = np.array([[0.0], [-2.0]], np.float32)
+    V = np.array([[-0.5], [3.0]], np.float32)
+    s1 = np.array([2.0, 1.0], np.float32)
+    s2 = np.array([1.0, 0.5], np.float32)
+    x = np.array([[4.0, 2.0]], np.float32)
+    # z = s2 x = [4, 1]; t = sign(V)^T z = -4 + 1 = -3; u = sign(U) t = [-3, 3]; y = s1 u
+    np.testing.assert_array_equal(O.linear_latent_ref(U, V, s1, s2, x), [[-6.0, 3.0]])
