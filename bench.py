@@ -298,6 +298,47 @@ def time_balance(shapes, device: str, reps: int = 5) -> dict:
     return res
 
 
+def time_latent(shapes, device: str, reps: int = 5) -> dict:
+    """The refinement forward from fp32 latent factors (signs packed at the
+    call, then the packed layer) over layer 0's linears, at T=1 and T=2048
+    (bf16 x).  At T=1 the latents dominate the bytes: GB/s counts the latent
+    reads, the packed words written and read back, x and y."""
+    import torch
+
+    import sub_bit_weight_amd as nq
+    gen = torch.Generator(device=device).manual_seed(77)
+    lat = [(torch.randn((s.d_out, s.r), generator=gen, device=device),
+            torch.randn((s.d_in, s.r), generator=gen, device=device),
+            torch.rand(s.d_out, generator=gen, device=device), torch.rand(s.d_in, generator=gen, device=device))
+           for s in shapes]
+    res = {"linears": f"layer 0 ({len(shapes)} linears)"}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for T in (1, 2048):
+        xs = [torch.randn((T, s.d_in), generator=gen, device=device).to(torch.bfloat16) for s in shapes]
+        ys = [torch.empty((T, s.d_out), device=device) for s in shapes]
+        ws = torch.empty(max(nq.lib().nq_lrb_latent_workspace_bytes(s.d_out, s.d_in, s.r, T) for s in shapes),
+                         dtype=torch.uint8, device=device)
+
+        def run():
+            for (u, v, s1, s2), x, y in zip(lat, xs, ys):
+                nq.lrb_linear_latent(u, v, s1, s2, x, y=y, workspace=ws)
+        run()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = sum((s.d_out + s.d_in) * s.r * 4 + 2 * (s.d_out + s.d_in) * s.r // 8 + T * (2 * s.d_in + 4 * s.d_out)
+                     for s in shapes)
+        flops = sum(2 * T * s.r * (s.d_in + s.d_out) for s in shapes)
+        res[f"T{T}"] = {"ms_per_layer": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                        "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e12 / 8.0, "tflops": flops / (ms * 1e-3) / 1e12,
+                        "algorithmic_bytes": nbytes}
+    return res
+
+
 def vendor_gemm_reference(shapes, T: int, device: str) -> dict:
     """Context for the matrix-core roofline: torch.matmul (hipBLASLt) on dense
     bf16 operands of the same GEMM shapes as the two LRB stages (M = T,
@@ -379,6 +420,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-grads", action="store_true", help="skip the scale-gradient (calibration) leg")
     ap.add_argument("--no-balance", action="store_true", help="skip the magnitude-balancing leg")
+    ap.add_argument("--no-latent", action="store_true", help="skip the latent-factor forward leg")
     ap.add_argument("--prefill-serial", action="store_true",
                     help="also time the prefill pass as serial single-linear calls on one stream")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -456,6 +498,12 @@ def main() -> int:
         log(f"[bench] balancing {b['balanced_factors']['ms_per_layer']:.2f} ms/layer "
             f"({b['balanced_factors']['gbs']:.0f} GB/s), scales only {b['scales_only']['ms_per_layer']:.2f} ms "
             f"({b['scales_only']['gbs']:.0f} GB/s), parity {b['parity_rel_err']:.2e}")
+    if not args.no_latent:
+        log("[bench] refinement forward from latents (layer 0)")
+        extra["latent_forward"] = time_latent(stack.shapes[:len(cfg.layers)], device)
+        lf = extra["latent_forward"]
+        log(f"[bench] latent forward T=1 {lf['T1']['ms_per_layer']:.2f} ms/layer ({lf['T1']['gbs']:.0f} GB/s), "
+            f"T=2048 {lf['T2048']['ms_per_layer']:.2f} ms/layer ({lf['T2048']['tflops']:.0f} TFLOP/s)")
     del stack
     torch.cuda.empty_cache()
 

@@ -29,7 +29,7 @@ EXPORTED = [
     "nq_storage_bits", "nq_seq_create", "nq_seq_workspace_bytes", "nq_seq_run", "nq_seq_destroy",
     "nq_fill_random_words", "nq_last_error", "nq_version", "nq_transpose_signs",
     "nq_lrb_scale_grads_workspace_bytes", "nq_lrb_scale_grads", "nq_balance_workspace_bytes",
-    "nq_balance_factors",
+    "nq_balance_factors", "nq_lrb_latent_workspace_bytes", "nq_lrb_linear_latent",
 ]
 
 
@@ -91,6 +91,10 @@ def lib() -> ctypes.CDLL:
     L.nq_lrb_scale_grads.argtypes = [P(nq_lrb), vp, i64, vp, i64, vp, ctypes.c_int, vp, ctypes.c_int, i64, vp, vp, vp,
                                      vp, sz, vp]
     L.nq_lrb_scale_grads.restype = st
+    L.nq_lrb_latent_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.nq_lrb_latent_workspace_bytes.restype = sz
+    L.nq_lrb_linear_latent.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp, vp, vp, ctypes.c_int, i64, vp, vp, sz, vp]
+    L.nq_lrb_linear_latent.restype = st
     L.nq_balance_workspace_bytes.argtypes = [i64, i64]
     L.nq_balance_workspace_bytes.restype = sz
     L.nq_balance_factors.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -230,6 +234,32 @@ def lrb_linear(layer: Lrb, x: torch.Tensor, y: torch.Tensor | None = None,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _check(lib().nq_lrb_linear(ctypes.byref(s), _ptr(x), _x_dtype(x), T, _ptr(y), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y
+
+
+def lrb_linear_latent(u_lat: torch.Tensor, v_lat: torch.Tensor, s1: torch.Tensor, s2: torch.Tensor,
+                      x: torch.Tensor, r: int | None = None, y: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = s1 (.) sign(U)(sign(V)^T (s2 (.) x)) from fp32 latents u_lat [d_out][>= r],
+    v_lat [d_in][>= r] (row stride = shape[1]); x [T][d_in] fp32/bf16 -> y fp32."""
+    for t, n in ((u_lat, "u_lat"), (v_lat, "v_lat"), (s1, "s1"), (s2, "s2"), (x, "x")):
+        _dev(t, n)
+    for t, n in ((u_lat, "u_lat"), (v_lat, "v_lat")):
+        if t.dtype != torch.float32 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{n} must be 2-D float32 with unit column stride")
+    r = u_lat.shape[1] if r is None else r
+    d_out, d_in = u_lat.shape[0], v_lat.shape[0]
+    if x.dim() != 2 or x.shape[1] != d_in:
+        raise ValueError(f"x must be [T][{d_in}], got {tuple(x.shape)}")
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, d_out), dtype=torch.float32, device=x.device)
+    need = int(lib().nq_lrb_latent_workspace_bytes(d_out, d_in, r, T))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().nq_lrb_linear_latent(_ptr(u_lat), u_lat.stride(0), _ptr(v_lat), v_lat.stride(0), d_out, d_in, r,
+                                      _ptr(s1), _ptr(s2), _ptr(x), _x_dtype(x), T, _ptr(y), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)))
     return y
 
 

@@ -315,6 +315,67 @@ nq_status nq_lrb_linear(const nq_lrb* L, const void* x, nq_dtype x_dtype, int64_
   return hip_status(launch_linear(*L, x, x_dtype, T, y, workspace, (hipStream_t)stream), "nq_lrb_linear launch");
 }
 
+namespace {
+// Workspace of nq_lrb_linear_latent: [U words][V^T words][the linear's].
+struct LatentLayout {
+  nq_lrb L;  // sign-word pointers relative to the workspace start
+  size_t off_u, off_v, off_lin, bytes;
+};
+LatentLayout latent_layout(int64_t d_out, int64_t d_in, int64_t r, const float* s1, const float* s2, int64_t T) {
+  LatentLayout g;
+  g.L = nq_lrb{d_out, d_in, r, nullptr, d_out, nullptr, r, s1, s2};
+  g.off_u = 0;
+  g.off_v = align_up((size_t)cdiv(r, kWordBits) * d_out * sizeof(uint32_t));
+  g.off_lin = g.off_v + align_up((size_t)cdiv(d_in, kWordBits) * r * sizeof(uint32_t));
+  g.L.u_bits = reinterpret_cast<const uint32_t*>(uintptr_t{1} << 40);  // stand-ins for sizing
+  g.L.vt_bits = g.L.u_bits;
+  g.bytes = g.off_lin + linear_workspace(g.L, T);
+  return g;
+}
+}  // namespace
+
+size_t nq_lrb_latent_workspace_bytes(int64_t d_out, int64_t d_in, int64_t r, int64_t T) {
+  if (d_out < 1 || d_in < 1 || r < 1 || T < 1 || T > (int64_t(1) << 24)) return 0;
+  static const float one = 1.0f;
+  const LatentLayout g = latent_layout(d_out, d_in, r, &one, &one, T);
+  if (check_lrb("nq_lrb_latent_workspace_bytes", &g.L) != NQ_OK) return 0;
+  return g.bytes;
+}
+
+nq_status nq_lrb_linear_latent(const float* u_lat, int64_t ldu_lat, const float* v_lat, int64_t ldv_lat,
+                               int64_t d_out, int64_t d_in, int64_t r, const float* s1, const float* s2, const void* x,
+                               nq_dtype x_dtype, int64_t T, float* y, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  clear_error();
+  const char* who = "nq_lrb_linear_latent";
+  if (!u_lat || !v_lat) return set_error("%s: null latent", who), NQ_ERR_ARG;
+  if (d_out < 1 || d_in < 1 || r < 1) return set_error("%s: sizes must be >= 1", who), NQ_ERR_ARG;
+  if (ldu_lat < r || ldv_lat < r)
+    return set_error("%s: latent row strides %lld / %lld below r=%lld", who, (long long)ldu_lat, (long long)ldv_lat,
+                     (long long)r),
+           NQ_ERR_ARG;
+  if (!aligned(u_lat, 4) || !aligned(v_lat, 4)) return set_error("%s: latent not 4-byte aligned", who), NQ_ERR_ARG;
+  LatentLayout g = latent_layout(d_out, d_in, r, s1, s2, T);
+  nq_status st = check_lrb(who, &g.L);
+  if (st != NQ_OK) return st;
+  if ((st = check_io(who, &g.L, x, x_dtype, T, y)) != NQ_OK) return st;
+  if (!workspace || workspace_bytes < g.bytes)
+    return set_error("%s: workspace %zu bytes, need %zu", who, workspace ? workspace_bytes : 0, g.bytes),
+           NQ_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return set_error("%s: workspace not 256-byte aligned", who), NQ_ERR_ARG;
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* ub = reinterpret_cast<uint32_t*>(ws + g.off_u);
+  uint32_t* vb = reinterpret_cast<uint32_t*>(ws + g.off_v);
+  g.L.u_bits = ub;
+  g.L.vt_bits = vb;
+  hipStream_t s = (hipStream_t)stream;
+  // U latent [d_out][ldu_lat]: outputs d_out, reduction r; V latent [d_in][ldv_lat]: outputs r, reduction d_in
+  hipError_t e = launch_pack(u_lat, d_out, r, ldu_lat, 1, ub, d_out, s);
+  if (e == hipSuccess) e = launch_pack(v_lat, r, d_in, 1, ldv_lat, vb, r, s);
+  if (e == hipSuccess) e = launch_linear(g.L, x, x_dtype, T, y, ws + g.off_lin, s);
+  return hip_status(e, "nq_lrb_linear_latent launch");
+}
+
 nq_status nq_reconstruct(const nq_lrb* L, float* w, void* stream) {
   clear_error();
   nq_status st = check_lrb("nq_reconstruct", L);

@@ -202,3 +202,34 @@ def test_balance_workspace_query():
     assert lib.nq_balance_workspace_bytes(8, 5) >= 2 * 13 * 4
     assert lib.nq_balance_workspace_bytes(0, 5) == 0
     assert lib.nq_balance_workspace_bytes(8, 0) == 0
+
+
+def _latent(u=DUMMY, ldu=8, v=DUMMY, ldv=8, d_out=16, d_in=24, r=8, s1=DUMMY, s2=DUMMY, x=DUMMY,
+            dtype=nq.NQ_F32, T=1, y=DUMMY, ws=DUMMY, wsb=1 << 30):
+    return nq.lib().nq_lrb_linear_latent(u, ldu, v, ldv, d_out, d_in, r, s1, s2, x, dtype, T, y, ws, wsb, None)
+
+
+def test_linear_latent_rejects_bad_args():
+    assert _latent(u=None) == nq.NQ_ERR_ARG
+    assert _latent(v=None) == nq.NQ_ERR_ARG
+    assert _latent(ldu=7) == nq.NQ_ERR_ARG
+    assert _latent(ldv=7) == nq.NQ_ERR_ARG
+    assert _latent(r=0) == nq.NQ_ERR_ARG
+    assert _latent(d_out=0) == nq.NQ_ERR_ARG
+    assert _latent(u=DUMMY + 2) == nq.NQ_ERR_ARG
+    assert _latent(s1=None) == nq.NQ_ERR_ARG
+    assert _latent(x=None) == nq.NQ_ERR_ARG
+    assert _latent(T=0) == nq.NQ_ERR_ARG
+    assert _latent(dtype=7) == nq.NQ_ERR_ARG
+    assert _latent(ws=None) == nq.NQ_ERR_WORKSPACE
+    assert _latent(wsb=64) == nq.NQ_ERR_WORKSPACE
+    assert _latent(ws=DUMMY + 8) == nq.NQ_ERR_ARG
+    assert "nq_lrb_linear_latent" in nq.lib().nq_last_error().decode()
+
+
+def test_linear_latent_workspace_query():
+    lib = nq.lib()
+    need = lib.nq_lrb_latent_workspace_bytes(16, 24, 8, 1)
+    assert need >= 16 * 4 + 8 * 4   # one word row of U and one of V^T at least
+    assert lib.nq_lrb_latent_workspace_bytes(16, 24, 0, 1) == 0
+    assert lib.nq_lrb_latent_workspace_bytes(16, 24, 8, 0) == 0

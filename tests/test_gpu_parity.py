@@ -35,8 +35,10 @@ def test_fill_words_matches_host_splitmix(n, seed):
 # ---------------------------------------------------------------- packing
 
 
-@pytest.mark.parametrize("n_out,n_red,ld_pad", [(1, 1, 0), (5, 31, 3), (64, 64, 0), (33, 100, 1),
-                                                (256, 256, 0), (300, 1000, 5), (4096, 2048, 0)])
+# the last case has more outputs than one launch's grid covers (more than
+# 65535 x 16), so workgroups take a second group of outputs
+@pytest.mark.parametrize("n_out,n_red,ld_pad", [(1, 1, 0), (5, 31, 3), (64, 64, 0), (33, 100, 1), (65, 129, 2),
+                                                (68, 77, 0), (128, 1000, 3), (256, 256, 0), (300, 1000, 5), (4096, 2048, 0), (1_048_600, 3, 1)])
 def test_pack_bit_exact(n_out, n_red, ld_pad):
     M = synth.normal_f32(f"pack/{n_out}/{n_red}", (n_out, n_red))
     ref = O.pack_ref(M)
@@ -513,3 +515,36 @@ def test_balance_llama_shape():
     assert abs(float(eta.item()) / reta - 1) <= 1e-6
     for got, want in ((U, U0), (V, V0), (s1, rs1), (s2, rs2)):
         assert O.rel_err(got.cpu().numpy(), want) <= 1e-6
+
+
+# ---- refinement forward from latent factors -----------------------------------
+
+@pytest.mark.parametrize("shape", [(33, 47, 5), (100, 257, 64), (256, 320, 96)])
+@pytest.mark.parametrize("T,x_dtype", [(1, "f32"), (5, "bf16"), (8, "f32"), (9, "bf16"), (64, "f32"), (130, "bf16")])
+def test_linear_latent_parity(shape, T, x_dtype):
+    """Bit-equal to nq_pack_signs + nq_lrb_linear, and within the layer's bar
+    of the oracle; latents with padded rows and +0, -0, NaN entries."""
+    d_out, d_in, r = shape
+    pad = 3
+    Ul = np.full((d_out, r + pad), -7.0, np.float32)
+    Vl = np.full((d_in, r + pad), -7.0, np.float32)
+    Ul[:, :r] = synth.normal_f32(f"lat/u/{shape}", (d_out, r))
+    Vl[:, :r] = synth.normal_f32(f"lat/v/{shape}", (d_in, r))
+    Ul[0, :3] = [0.0, -0.0, np.nan]
+    Vl[1, :3] = [np.nan, -0.0, 0.0]
+    cfg = G.tiny_config(f"lat/{x_dtype}", x_dtype=x_dtype)
+    s1 = synth.scales(cfg, f"lat/s1/{d_out}", d_out)
+    s2 = synth.scales(cfg, f"lat/s2/{d_in}", d_in)
+    x = synth.activations(f"lat/x/{d_in}/{T}", T, d_in, x_dtype)
+    du, dv = torch.from_numpy(Ul).to(G.DEV), torch.from_numpy(Vl).to(G.DEV)
+    ds1, ds2 = torch.from_numpy(s1).to(G.DEV), torch.from_numpy(s2).to(G.DEV)
+    dx = G.to_device_x(x, x_dtype)
+    y = nq.lrb_linear_latent(du, dv, ds1, ds2, dx, r=r)
+    # the packed route through the separate calls
+    ub = nq.pack_signs(du, d_out, r, r + pad, 1)
+    vb = nq.pack_signs(dv, r, d_in, 1, r + pad)
+    layer = nq.Lrb(d_out, d_in, r, ub, vb, ds1, ds2)
+    y2 = nq.lrb_linear(layer, dx)
+    assert torch.equal(y, y2)
+    want = O.linear_latent_ref(Ul[:, :r], Vl[:, :r], s1, s2, x)
+    assert O.rel_err(y.cpu().numpy(), want) <= G.tol_for(T, x_dtype)
