@@ -421,6 +421,8 @@ def main() -> int:
     ap.add_argument("--no-grads", action="store_true", help="skip the scale-gradient (calibration) leg")
     ap.add_argument("--no-balance", action="store_true", help="skip the magnitude-balancing leg")
     ap.add_argument("--no-latent", action="store_true", help="skip the latent-factor forward leg")
+    ap.add_argument("--no-rank-sweep", action="store_true",
+                    help="skip decode at 0.25x .. 2x the 1-bit ranks (0.25 .. 2 bit/weight)")
     ap.add_argument("--prefill-serial", action="store_true",
                     help="also time the prefill pass as serial single-linear calls on one stream")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -517,6 +519,26 @@ def main() -> int:
                                   "hbm_gbs": b55 / (ms55 * 1e-3) / 1e9, "algorithmic_bytes": b55}
         del seq55, st55
         torch.cuda.empty_cache()
+
+    if not args.no_rank_sweep:
+        import sub_bit_weight_amd as nq
+        # the decode kernels across ranks: 0.25 .. 2.0 bit/weight of sign storage
+        sweep = []
+        for frac in (0.25, 0.5, 0.75, 1.0, 1.5, 2.0):
+            cfgf = synth.Config(f"70b_stack_{frac}", f"Llama-2-70B linear stack, {frac} x the 1-bit rank",
+                                synth.llama2_70b_layer(frac), (1,), "bf16", n_layers=80, words="splitmix")
+            stf = Stack(cfgf, args.layers, device)
+            msf, seqf, _, _ = time_decode(stf, 1, args.steps, args.warmup, device)
+            bf = algorithmic_bytes(stf.shapes, 1)
+            weights = sum(sh.d_out * sh.d_in for sh in stf.shapes)
+            bits = sum(nq.storage_bits(sh.d_out, sh.d_in, sh.r) for sh in stf.shapes) / weights
+            sweep.append({"rank_frac": frac, "bits_per_weight": bits, "ms_per_step": msf,
+                          "tokens_per_s": 1000.0 / msf, "hbm_gbs": bf / (msf * 1e-3) / 1e9,
+                          "frac_of_hbm_peak": bf / (msf * 1e-3) / 1e12 / 8.0})
+            log(f"[bench] rank x{frac}: {bits:.3f} bit/weight, {msf:.3f} ms/step, {sweep[-1]['hbm_gbs']:.0f} GB/s")
+            del seqf, stf
+            torch.cuda.empty_cache()
+        extra["rank_sweep"] = sweep
 
     out = {
         "metric": "decode tokens/s + HBM GB/s (T=1), prefill TFLOP/s (T=2048), 70B-shaped LRB layers",
