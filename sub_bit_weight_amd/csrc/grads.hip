@@ -90,6 +90,66 @@ __global__ __launch_bounds__(256) void scale_grads_partial_kernel(
     ds1[c - d_in] = acc;
 }
 
+// Four adjacent columns per thread (d_in, d_out multiples of 4; x, g, dx
+// aligned for 16-byte fp32 / 8-byte bf16 vectors, checked on the host): the
+// same per-column sums in the same order as scale_grads_partial_kernel, read
+// and written as vectors.
+__device__ inline float4 load_act4(const void* p, int bf16, int64_t i) {
+  if (bf16) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                       __uint_as_float(w.y & 0xffff0000u));
+  }
+  return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+}
+
+__global__ __launch_bounds__(256) void scale_grads_partial4_kernel(
+    const void* __restrict__ x, int x_bf16, const void* __restrict__ g, int g_bf16, const float* __restrict__ u,
+    const float* __restrict__ b, const float* __restrict__ s2, int64_t T, int64_t tc, int64_t d_in, int64_t d_out,
+    float* __restrict__ dx, float* __restrict__ part, float* __restrict__ ds1, float* __restrict__ ds2) {
+  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int64_t t0 = (int64_t)blockIdx.y * tc;
+  const int64_t t1 = t0 + tc < T ? t0 + tc : T;
+  const int64_t ncols = d_in + d_out;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (c < d_in) {
+    const float4 sc = make_float4(s2[c], s2[c + 1], s2[c + 2], s2[c + 3]);
+#pragma unroll 4
+    for (int64_t t = t0; t < t1; ++t) {
+      const int64_t i = t * d_in + c;
+      const float4 bv = *reinterpret_cast<const float4*>(b + i);
+      *reinterpret_cast<float4*>(dx + i) = make_float4(sc.x * bv.x, sc.y * bv.y, sc.z * bv.z, sc.w * bv.w);
+      const float4 xv = load_act4(x, x_bf16, i);
+      acc.x = fmaf(xv.x, bv.x, acc.x);
+      acc.y = fmaf(xv.y, bv.y, acc.y);
+      acc.z = fmaf(xv.z, bv.z, acc.z);
+      acc.w = fmaf(xv.w, bv.w, acc.w);
+    }
+  } else if (c < ncols) {
+    const int64_t k = c - d_in;
+#pragma unroll 4
+    for (int64_t t = t0; t < t1; ++t) {
+      const float4 gv = load_act4(g, g_bf16, t * d_out + k);
+      const float4 uv = *reinterpret_cast<const float4*>(u + t * d_out + k);
+      acc.x = fmaf(gv.x, uv.x, acc.x);
+      acc.y = fmaf(gv.y, uv.y, acc.y);
+      acc.z = fmaf(gv.z, uv.z, acc.z);
+      acc.w = fmaf(gv.w, uv.w, acc.w);
+    }
+  } else {
+    return;
+  }
+  if (gridDim.y > 1) {
+    *reinterpret_cast<float4*>(part + (int64_t)blockIdx.y * ncols + c) = acc;
+  } else {
+    float* d = c < d_in ? ds2 + c : ds1 + (c - d_in);
+    d[0] = acc.x;
+    d[1] = acc.y;
+    d[2] = acc.z;
+    d[3] = acc.w;
+  }
+}
+
 __global__ __launch_bounds__(256) void scale_grads_sum_kernel(const float* __restrict__ part, int nchunks,
                                                               int64_t d_in, int64_t d_out, float* __restrict__ ds1,
                                                               float* __restrict__ ds2) {
@@ -131,8 +191,16 @@ hipError_t launch_scale_grads_finish(const void* x, nq_dtype xd, const void* g, 
                                      float* part, float* ds1, float* ds2, hipStream_t s) {
   const int64_t col_tiles = cdiv(d_in + d_out, 256);
   const int64_t tc = grad_chunk_tokens(T), nchunks = cdiv(T, tc);
-  hipLaunchKernelGGL(scale_grads_partial_kernel, dim3((unsigned)col_tiles, (unsigned)nchunks), dim3(256), 0, s, x,
-                     (int)(xd == NQ_BF16), g, (int)(gd == NQ_BF16), u, b, s2, T, tc, d_in, d_out, dx, part, ds1, ds2);
+  const auto vec_ok = [](const void* p, nq_dtype d) { return (uintptr_t)p % (d == NQ_BF16 ? 8 : 16) == 0; };
+  if (d_in % 4 == 0 && d_out % 4 == 0 && vec_ok(x, xd) && vec_ok(g, gd) && (uintptr_t)dx % 16 == 0 &&
+      (uintptr_t)u % 16 == 0 && (uintptr_t)b % 16 == 0 && (uintptr_t)part % 16 == 0)
+    hipLaunchKernelGGL(scale_grads_partial4_kernel, dim3((unsigned)cdiv((d_in + d_out) / 4, 256), (unsigned)nchunks),
+                       dim3(256), 0, s, x, (int)(xd == NQ_BF16), g, (int)(gd == NQ_BF16), u, b, s2, T, tc, d_in,
+                       d_out, dx, part, ds1, ds2);
+  else
+    hipLaunchKernelGGL(scale_grads_partial_kernel, dim3((unsigned)col_tiles, (unsigned)nchunks), dim3(256), 0, s, x,
+                       (int)(xd == NQ_BF16), g, (int)(gd == NQ_BF16), u, b, s2, T, tc, d_in, d_out, dx, part, ds1,
+                       ds2);
   if (nchunks > 1)
     hipLaunchKernelGGL(scale_grads_sum_kernel, dim3((unsigned)col_tiles), dim3(256), 0, s, part, (int)nchunks, d_in,
                        d_out, ds1, ds2);
