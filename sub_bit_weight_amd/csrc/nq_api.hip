@@ -182,7 +182,7 @@ namespace {
 // stage 2).
 int seq_lag() {
   const char* e = getenv("NQ_SEQ_LAG");
-  const int v = e ? atoi(e) : 128;
+  const int v = e ? atoi(e) : 320;
   return v < 0 ? 0 : v;
 }
 
