@@ -201,7 +201,12 @@ void plan_persistent(nq_seq* s) {
   s->n_ints = ints;
   const int64_t lag = seq_lag();
   // descriptors: pieces of x, stage 1, pieces of t, stage 2
-  const int64_t pre = std::max<int64_t>(lag / 2, 1), lag2 = lag * 3 / 4;
+  // how far ahead of its stage 1 a linear's x pieces are made, and how far
+  // behind it its t pieces (NQ_SEQ_PRE, NQ_SEQ_LAG2: linears; tuning knobs)
+  const char* ep = getenv("NQ_SEQ_PRE");
+  const char* e2 = getenv("NQ_SEQ_LAG2");
+  const int64_t pre = std::max<int64_t>(ep ? atoi(ep) : lag / 2, 1);
+  const int64_t lag2 = std::min<int64_t>(std::max<int64_t>(e2 ? atoi(e2) : lag * 3 / 4, 0), lag);
   for (int64_t i = 0; i < std::min(pre, n); ++i) s->order.push_back({(int)i, 0});
   for (int64_t i = 0; i < n; ++i) {
     if (i + pre < n) s->order.push_back({(int)(i + pre), 0});
