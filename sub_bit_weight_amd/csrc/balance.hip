@@ -77,7 +77,9 @@ __global__ __launch_bounds__(1024) void balance_eta_kernel(const float* __restri
   __shared__ double su[1024], sv[1024];
   const int tid = threadIdx.x;
   double a = 0.0, b = 0.0;
+#pragma unroll 8
   for (int64_t i = tid; i < d_out; i += 1024) a += (double)sq_sum[i];
+#pragma unroll 8
   for (int64_t i = tid; i < d_in; i += 1024) b += (double)sq_sum[d_out + i];
   su[tid] = a;
   sv[tid] = b;
