@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void balance_rows_kernel(const float* __restri
   if (Vec4) {
     const int64_t n4 = r / 4;
     const float4* p4 = reinterpret_cast<const float4*>(p);
+#pragma unroll 4
     for (int64_t i = lane; i < n4; i += 64) {
       const float4 v = p4[i];
       a += fabsf(v.x) + fabsf(v.y) + fabsf(v.z) + fabsf(v.w);
@@ -128,11 +129,13 @@ __global__ __launch_bounds__(256) void balance_apply_kernel(const float* uh, int
     const float4* p4 = reinterpret_cast<const float4*>(p);
     float4* o4 = reinterpret_cast<float4*>(o);
     if (is_u) {
+#pragma unroll 4
       for (int64_t i = lane; i < n4; i += 64) {
         const float4 v = p4[i];
         o4[i] = make_float4(eta * v.x, eta * v.y, eta * v.z, eta * v.w);
       }
     } else {
+#pragma unroll 4
       for (int64_t i = lane; i < n4; i += 64) {
         const float4 v = p4[i];
         o4[i] = make_float4(v.x / eta, v.y / eta, v.z / eta, v.w / eta);
