@@ -281,6 +281,28 @@ nq_status nq_balance_factors(const float* u_hat, int64_t d_out, int64_t ldu, con
  */
 nq_status nq_fill_random_words(uint32_t* dst, int64_t n, uint64_t seed, void* stream);
 
+/*
+ * nq_lrb_linear_noalloc -- nq_lrb_linear without a caller workspace and
+ *   without any device allocation, for callers that cannot allocate device
+ *   memory: code under HIP graph capture, tight serving loops, harnesses that
+ *   forbid hipMalloc.  The caller still passes x and y; the workspace is a
+ *   fixed array of NQ_NOALLOC_SCRATCH_BYTES bytes inside the library, one copy
+ *   per GPU, held from the first use on that GPU until the process ends.
+ *   Arguments, results and regimes are those of nq_lrb_linear (same kernels,
+ *   bit-identical y).  Every call on one GPU uses that GPU's one array, so
+ *   calls on one GPU whose executions overlap (different streams or threads
+ *   without ordering between them) race and give wrong results; order them.
+ *   The decode regime clears the array's counters with a fill kernel at the
+ *   start of each call (no memset).  16 MiB covers the decode regime (T <= 8)
+ *   at every Llama-2-70B linear shape up to 2 bits/weight and small GEMM
+ *   batches.  Errors: as for nq_lrb_linear; NQ_ERR_UNSUPPORTED when the call
+ *   needs more workspace than the array holds (nq_lrb_workspace_bytes(L, T) >
+ *   NQ_NOALLOC_SCRATCH_BYTES), checked before any HIP call.
+ */
+#define NQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+nq_status nq_lrb_linear_noalloc(const nq_lrb* L, const void* x, nq_dtype x_dtype, int64_t T, float* y,
+                                void* stream);
+
 /* Thread-local message for the last non-OK status of this thread ("" if none). */
 const char* nq_last_error(void);
 

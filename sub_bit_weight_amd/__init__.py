@@ -29,8 +29,11 @@ EXPORTED = [
     "nq_storage_bits", "nq_seq_create", "nq_seq_workspace_bytes", "nq_seq_run", "nq_seq_destroy",
     "nq_fill_random_words", "nq_last_error", "nq_version", "nq_transpose_signs",
     "nq_lrb_scale_grads_workspace_bytes", "nq_lrb_scale_grads", "nq_balance_workspace_bytes",
-    "nq_balance_factors", "nq_lrb_latent_workspace_bytes", "nq_lrb_linear_latent",
+    "nq_balance_factors", "nq_lrb_latent_workspace_bytes", "nq_lrb_linear_latent", "nq_lrb_linear_noalloc",
 ]
+
+# Size of the library's fixed per-GPU workspace array (NQ_NOALLOC_SCRATCH_BYTES in nq.h).
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class NqError(RuntimeError):
@@ -70,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.nq_lrb_workspace_bytes.restype = sz
     L.nq_lrb_linear.argtypes = [P(nq_lrb), vp, ctypes.c_int, i64, vp, vp, sz, vp]
     L.nq_lrb_linear.restype = st
+    L.nq_lrb_linear_noalloc.argtypes = [P(nq_lrb), vp, ctypes.c_int, i64, vp, vp]
+    L.nq_lrb_linear_noalloc.restype = st
     L.nq_reconstruct.argtypes = [P(nq_lrb), vp, vp]
     L.nq_reconstruct.restype = st
     L.nq_storage_bits.argtypes = [i64, i64, i64]
@@ -234,6 +239,22 @@ def lrb_linear(layer: Lrb, x: torch.Tensor, y: torch.Tensor | None = None,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _check(lib().nq_lrb_linear(ctypes.byref(s), _ptr(x), _x_dtype(x), T, _ptr(y), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y
+
+
+def lrb_linear_noalloc(layer: Lrb, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """lrb_linear with the library's fixed per-GPU workspace (nq_lrb_linear_noalloc):
+    no device allocation at all, so y must be given.  Calls on one GPU must not
+    overlap (they share the workspace)."""
+    _dev(x, "x")
+    _dev(y, "y")
+    if x.dim() != 2 or x.shape[1] != layer.d_in:
+        raise ValueError(f"x must be [T][{layer.d_in}], got {tuple(x.shape)}")
+    T = x.shape[0]
+    if tuple(y.shape) != (T, layer.d_out) or y.dtype != torch.float32:
+        raise ValueError(f"y must be float32 [{T}][{layer.d_out}]")
+    s = layer.struct()
+    _check(lib().nq_lrb_linear_noalloc(ctypes.byref(s), _ptr(x), _x_dtype(x), T, _ptr(y), _stream(stream)))
     return y
 
 

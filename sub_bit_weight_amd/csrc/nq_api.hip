@@ -45,6 +45,8 @@ nq_status check_words(const char* who, const void* p, int64_t n_out, int64_t n_r
   return NQ_OK;
 }
 
+}  // namespace
+
 nq_status check_lrb(const char* who, const nq_lrb* L) {
   if (!L) return set_error("%s: null layer", who), NQ_ERR_ARG;
   if (L->d_out < 1 || L->d_in < 1 || L->r < 1)
@@ -89,16 +91,18 @@ bool decode_xor() {
 // in_seq: the linear is an entry of a sequence plan, whose entries run
 // concurrently; the matrix-core regime then never splits a reduction (the
 // entries fill the chip together, and a split only adds partial-sum traffic).
-size_t linear_workspace(const nq_lrb& L, int64_t T, bool in_seq = false) {
+size_t linear_workspace(const nq_lrb& L, int64_t T, bool in_seq) {
   if (T > kDecodeMaxT) return prefill_workspace_bytes(L, T, !in_seq);
   return decode_xor() ? decode_workspace_bytes(L, T) : dec_workspace_bytes(L, T);
 }
 
 hipError_t launch_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
-                         hipStream_t s, bool in_seq = false) {
+                         hipStream_t s, bool in_seq) {
   if (T > kDecodeMaxT) return launch_prefill(L, x, xd, T, y, ws, s, !in_seq);
   return decode_xor() ? launch_decode(L, x, xd, T, y, ws, s) : launch_dec_linear(L, x, xd, T, y, ws, s);
 }
+
+namespace {
 
 // The transposed layer W^T = s2 (.) V U^T (.) s1 as an LRB matrix.
 nq_lrb adjoint_layer(const nq_lrb& L, const uint32_t* ut_bits, int64_t ldut, const uint32_t* v_bits, int64_t ldvv) {

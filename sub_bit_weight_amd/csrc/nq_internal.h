@@ -22,6 +22,17 @@ constexpr int64_t kWordBits = 32;
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// ---------------------------------------------------------------- validation and dispatch (nq_api.hip)
+// Host-side argument checks of a packed layer and of a call's x, T, y; each
+// sets the thread-local message and returns a non-OK status on failure.
+nq_status check_lrb(const char* who, const nq_lrb* L);
+nq_status check_io(const char* who, const nq_lrb* L, const void* x, nq_dtype xd, int64_t T, const float* y);
+// Workspace and launch of one linear in the regime T selects (in_seq: an entry
+// of a sequence plan, whose GEMMs never split their reductions).
+size_t linear_workspace(const nq_lrb& L, int64_t T, bool in_seq = false);
+hipError_t launch_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
+                         hipStream_t s, bool in_seq = false);
+
 // ---------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launch (hipGetLastError after the launch).
 hipError_t launch_pack(const float* src, int64_t n_out, int64_t n_red, int64_t so, int64_t sr,

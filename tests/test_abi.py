@@ -233,3 +233,20 @@ def test_linear_latent_workspace_query():
     assert need >= 16 * 4 + 8 * 4   # one word row of U and one of V^T at least
     assert lib.nq_lrb_latent_workspace_bytes(16, 24, 0, 1) == 0
     assert lib.nq_lrb_latent_workspace_bytes(16, 24, 8, 0) == 0
+
+
+def test_noalloc_host_checks():
+    """nq_lrb_linear_noalloc validates like nq_lrb_linear and refuses calls whose
+    workspace exceeds the library's fixed array, all before any HIP call."""
+    lib = nq.lib()
+
+    def call(layer, T=1, dtype=nq.NQ_BF16, x=DUMMY, y=DUMMY):
+        return lib.nq_lrb_linear_noalloc(ctypes.byref(layer), x, dtype, T, y, None)
+    assert call(_layer(d_out=0)) == nq.NQ_ERR_ARG
+    assert call(_layer(), T=0) == nq.NQ_ERR_ARG
+    assert call(_layer(), dtype=5) == nq.NQ_ERR_ARG
+    assert call(_layer(), y=None) == nq.NQ_ERR_ARG
+    big = _layer(d_out=28672, d_in=8192, r=6336, ldu=28672, ldv=6336)
+    assert lib.nq_lrb_workspace_bytes(ctypes.byref(big), 64) > nq.NOALLOC_SCRATCH_BYTES
+    assert call(big, T=64) == nq.NQ_ERR_UNSUPPORTED
+    assert "scratch" in nq.last_error()
