@@ -257,8 +257,9 @@ nq_status nq_lrb_linear_latent(const float* u_lat, int64_t ldu_lat, const float*
  *   nq_pack_signs when ldu = r); v_hat: [d_in][ldv] likewise.  u_out, v_out:
  *   both null (scales only) or both given, with the inputs' strides; each may
  *   be its input (in place) but must not otherwise overlap anything.  s1:
- *   [d_out], s2: [d_in], eta: [1] fp32 device.  Row sums are fp32 in a fixed
- *   order, the norms fp64 (deterministic).  Signs are unchanged (eta > 0), so
+ *   [d_out], s2: [d_in], eta: [1] fp32 device.  Sums of |.| are fp32, sums of
+ *   squares and the norms fp64 (every finite fp32 latent), all in a fixed order
+ *   (deterministic).  Signs are unchanged (eta > 0), so
  *   nq_pack_signs may read either the latents or the balanced factors.
  *   workspace: at least nq_balance_workspace_bytes(d_out, d_in) bytes,
  *   256-byte aligned.  Errors: NQ_ERR_ARG for null inputs, scales or eta,

@@ -11,6 +11,7 @@ Names follow the C ABI in include/nq.h:
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -127,6 +128,14 @@ def _stream(stream=None) -> int:
     return stream.cuda_stream
 
 
+def _on(stream):
+    """Allocation context for a call on `stream`: buffers made for the call
+    (outputs, workspace) belong to that stream in torch's caching allocator, so
+    a workspace freed at return cannot be handed to work on another stream
+    while the call's kernels still use it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
@@ -153,7 +162,8 @@ def pack_signs(src: torch.Tensor, n_out: int, n_red: int, stride_out: int, strid
         raise ValueError("src must be float32")
     ld = n_out if ld is None else ld
     if out is None:
-        out = torch.zeros((n_words(n_red), ld), dtype=torch.int32, device=src.device)
+        with _on(stream):
+            out = torch.zeros((n_words(n_red), ld), dtype=torch.int32, device=src.device)
     _check(lib().nq_pack_signs(_ptr(src), n_out, n_red, stride_out, stride_red, _ptr(out), ld, _stream(stream)))
     return out
 
@@ -174,7 +184,8 @@ def unpack_signs(bits: torch.Tensor, n_out: int, n_red: int, ld: int | None = No
                  stream=None) -> torch.Tensor:
     _dev(bits, "bits")
     ld = bits.shape[1] if ld is None else ld
-    out = torch.empty((n_out, n_red), dtype=torch.float32, device=bits.device)
+    with _on(stream):
+        out = torch.empty((n_out, n_red), dtype=torch.float32, device=bits.device)
     _check(lib().nq_unpack_signs(_ptr(bits), n_out, n_red, ld, _ptr(out), _stream(stream)))
     return out
 
@@ -183,7 +194,8 @@ def fill_random_words(n: int, seed: int, device="cuda", out: torch.Tensor | None
                       stream=None) -> torch.Tensor:
     """Synthetic sign words: low 32 bits of SplitMix64(seed, i) (an input generator)."""
     if out is None:
-        out = torch.empty(n, dtype=torch.int32, device=device)
+        with _on(stream):
+            out = torch.empty(n, dtype=torch.int32, device=device)
     _check(lib().nq_fill_random_words(_ptr(out), n, seed & 0xFFFFFFFFFFFFFFFF, _stream(stream)))
     return out
 
@@ -203,8 +215,23 @@ class Lrb:
     s2: torch.Tensor       # [d_in] float32
 
     def struct(self) -> nq_lrb:
+        """The C struct, after checking what the C ABI cannot see: dtypes,
+        shapes and sizes of the tensors (a short buffer would otherwise be read
+        past its end by the kernels)."""
         for name in ("u_bits", "vt_bits", "s1", "s2"):
             _dev(getattr(self, name), name)
+        if min(self.d_out, self.d_in, self.r) < 1:
+            raise ValueError(f"sizes must be >= 1: {self.d_out}, {self.d_in}, {self.r}")
+        for name, rows, cols in (("u_bits", n_words(self.r), self.d_out), ("vt_bits", n_words(self.d_in), self.r)):
+            t = getattr(self, name)
+            if t.dtype not in (torch.int32, torch.uint32) or t.dim() != 2:
+                raise ValueError(f"{name} must be 2-D 32-bit words, got {t.dtype} {tuple(t.shape)}")
+            if t.shape[0] < rows or t.shape[1] < cols:
+                raise ValueError(f"{name} must be at least [{rows}][{cols}], got {tuple(t.shape)}")
+        for name, n in (("s1", self.d_out), ("s2", self.d_in)):
+            t = getattr(self, name)
+            if t.dtype != torch.float32 or t.numel() < n:
+                raise ValueError(f"{name} must be float32 with >= {n} elements, got {t.dtype} {t.numel()}")
         return nq_lrb(self.d_out, self.d_in, self.r,
                       self.u_bits.data_ptr(), self.u_bits.shape[1],
                       self.vt_bits.data_ptr(), self.vt_bits.shape[1],
@@ -232,11 +259,12 @@ def lrb_linear(layer: Lrb, x: torch.Tensor, y: torch.Tensor | None = None,
         raise ValueError(f"x must be [T][{layer.d_in}], got {tuple(x.shape)}")
     T = x.shape[0]
     s = layer.struct()
-    if y is None:
-        y = torch.empty((T, layer.d_out), dtype=torch.float32, device=x.device)
     need = int(lib().nq_lrb_workspace_bytes(ctypes.byref(s), T))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        if y is None:
+            y = torch.empty((T, layer.d_out), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _check(lib().nq_lrb_linear(ctypes.byref(s), _ptr(x), _x_dtype(x), T, _ptr(y), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)))
     return y
@@ -273,11 +301,12 @@ def lrb_linear_latent(u_lat: torch.Tensor, v_lat: torch.Tensor, s1: torch.Tensor
     if x.dim() != 2 or x.shape[1] != d_in:
         raise ValueError(f"x must be [T][{d_in}], got {tuple(x.shape)}")
     T = x.shape[0]
-    if y is None:
-        y = torch.empty((T, d_out), dtype=torch.float32, device=x.device)
     need = int(lib().nq_lrb_latent_workspace_bytes(d_out, d_in, r, T))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        if y is None:
+            y = torch.empty((T, d_out), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _check(lib().nq_lrb_linear_latent(_ptr(u_lat), u_lat.stride(0), _ptr(v_lat), v_lat.stride(0), d_out, d_in, r,
                                       _ptr(s1), _ptr(s2), _ptr(x), _x_dtype(x), T, _ptr(y), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -287,7 +316,8 @@ def lrb_linear_latent(u_lat: torch.Tensor, v_lat: torch.Tensor, s1: torch.Tensor
 def reconstruct(layer: Lrb, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     s = layer.struct()
     if out is None:
-        out = torch.empty((layer.d_out, layer.d_in), dtype=torch.float32, device=layer.s1.device)
+        with _on(stream):
+            out = torch.empty((layer.d_out, layer.d_in), dtype=torch.float32, device=layer.s1.device)
     _check(lib().nq_reconstruct(ctypes.byref(s), _ptr(out), _stream(stream)))
     return out
 
@@ -305,7 +335,8 @@ def transpose_signs(bits: torch.Tensor, n_out: int, n_red: int, ld: int | None =
     _dev(bits, "bits")
     ld = bits.shape[1] if ld is None else ld
     if out is None:
-        out = torch.empty((n_words(n_out), n_red), dtype=torch.int32, device=bits.device)
+        with _on(stream):
+            out = torch.empty((n_words(n_out), n_red), dtype=torch.int32, device=bits.device)
     _check(lib().nq_transpose_signs(_ptr(bits), n_out, n_red, ld, _ptr(out), out.shape[1], _stream(stream)))
     return out
 
@@ -338,12 +369,13 @@ def lrb_scale_grads(layer: Lrb, adj: Adjoint, x: torch.Tensor, g: torch.Tensor,
     if tuple(g.shape) != (T, layer.d_out) or not g.is_contiguous():
         raise ValueError(f"g must be contiguous [{T}][{layer.d_out}]")
     s = layer.struct()
-    dx = torch.empty((T, layer.d_in), dtype=torch.float32, device=x.device)
-    ds1 = torch.empty(layer.d_out, dtype=torch.float32, device=x.device)
-    ds2 = torch.empty(layer.d_in, dtype=torch.float32, device=x.device)
     need = int(lib().nq_lrb_scale_grads_workspace_bytes(ctypes.byref(s), T))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        dx = torch.empty((T, layer.d_in), dtype=torch.float32, device=x.device)
+        ds1 = torch.empty(layer.d_out, dtype=torch.float32, device=x.device)
+        ds2 = torch.empty(layer.d_in, dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _check(lib().nq_lrb_scale_grads(ctypes.byref(s), _ptr(adj.ut_bits), adj.ut_bits.shape[1], _ptr(adj.v_bits),
                                     adj.v_bits.shape[1], _ptr(x), _x_dtype(x), _ptr(g), _x_dtype(g), T, _ptr(dx), _ptr(ds1),
                                     _ptr(ds2), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -365,17 +397,18 @@ def balance_factors(u_hat: torch.Tensor, v_hat: torch.Tensor, r: int | None = No
     r = u_hat.shape[1] if r is None else r
     d_out, d_in = u_hat.shape[0], v_hat.shape[0]
     dev = u_hat.device
-    if balanced:
-        uo = u_hat if inplace else torch.empty_like(u_hat)
-        vo = v_hat if inplace else torch.empty_like(v_hat)
-    else:
-        uo = vo = None
-    s1 = torch.empty(d_out, dtype=torch.float32, device=dev)
-    s2 = torch.empty(d_in, dtype=torch.float32, device=dev)
-    eta = torch.empty(1, dtype=torch.float32, device=dev)
     need = int(lib().nq_balance_workspace_bytes(d_out, d_in))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with _on(stream):
+        if balanced:
+            uo = u_hat if inplace else torch.empty_like(u_hat)
+            vo = v_hat if inplace else torch.empty_like(v_hat)
+        else:
+            uo = vo = None
+        s1 = torch.empty(d_out, dtype=torch.float32, device=dev)
+        s2 = torch.empty(d_in, dtype=torch.float32, device=dev)
+        eta = torch.empty(1, dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check(lib().nq_balance_factors(_ptr(u_hat), d_out, u_hat.stride(0), _ptr(v_hat), d_in, v_hat.stride(0), r,
                                     None if uo is None else _ptr(uo), None if vo is None else _ptr(vo), _ptr(s1),
                                     _ptr(s2), _ptr(eta), _ptr(workspace), workspace.numel() * workspace.element_size(),

@@ -8,7 +8,10 @@
 //
 // HBM-bound: one read of both latents for the row statistics, then (when the
 // balanced latents are wanted) one read and one write to scale them.
-//   balance_rows_kernel   one wave per row: sum |.| and sum (.)^2, fp32
+//   balance_rows_kernel   one wave per row: sum |.| in fp32, sum (.)^2 in fp64
+//                         (fp32 squares would overflow above |v| ~ 1.8e19 and
+//                         vanish below ~1e-23; squares of fp32 values are
+//                         exact in fp64)
 //   balance_eta_kernel    one workgroup: the squared norms in fp64, eta
 //   balance_apply_kernel  one wave per row: s, and the scaled row
 // Rows 0..d_out-1 are U's, d_out..d_out+d_in-1 are V's.  Every sum has a
@@ -21,7 +24,8 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;  // one wave per row, 256 threads
 
-__device__ inline float wave_sum(float v) {
+template <typename F>
+__device__ inline F wave_sum(F v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
   return v;
@@ -40,12 +44,13 @@ template <bool Vec4>
 __global__ __launch_bounds__(256) void balance_rows_kernel(const float* __restrict__ uh, int64_t ldu,
                                                            const float* __restrict__ vh, int64_t ldv, int64_t d_out,
                                                            int64_t rows, int64_t r, float* __restrict__ abs_sum,
-                                                           float* __restrict__ sq_sum) {
+                                                           double* __restrict__ sq_sum) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole waves
   const float* p = row_ptr(uh, ldu, vh, ldv, d_out, row);
-  float a = 0.0f, q = 0.0f;
+  float a = 0.0f;
+  double q = 0.0;
   int64_t k0 = 0;
   if (Vec4) {
     const int64_t n4 = r / 4;
@@ -54,14 +59,15 @@ __global__ __launch_bounds__(256) void balance_rows_kernel(const float* __restri
     for (int64_t i = lane; i < n4; i += 64) {
       const float4 v = p4[i];
       a += fabsf(v.x) + fabsf(v.y) + fabsf(v.z) + fabsf(v.w);
-      q = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, q))));
+      const double x = v.x, y = v.y, z = v.z, w = v.w;
+      q = fma(x, x, fma(y, y, fma(z, z, fma(w, w, q))));
     }
     k0 = n4 * 4;
   }
   for (int64_t k = k0 + lane; k < r; k += 64) {
     const float v = p[k];
     a += fabsf(v);
-    q = fmaf(v, v, q);
+    q = fma((double)v, (double)v, q);
   }
   a = wave_sum(a);
   q = wave_sum(q);
@@ -73,15 +79,15 @@ __global__ __launch_bounds__(256) void balance_rows_kernel(const float* __restri
 
 // eta from the rows' squared sums; one workgroup of 1024 threads, thread i
 // adds rows i, i + 1024, ... in fp64, then a fixed tree over the threads.
-__global__ __launch_bounds__(1024) void balance_eta_kernel(const float* __restrict__ sq_sum, int64_t d_out,
+__global__ __launch_bounds__(1024) void balance_eta_kernel(const double* __restrict__ sq_sum, int64_t d_out,
                                                            int64_t d_in, float* __restrict__ eta) {
   __shared__ double su[1024], sv[1024];
   const int tid = threadIdx.x;
   double a = 0.0, b = 0.0;
 #pragma unroll 8
-  for (int64_t i = tid; i < d_out; i += 1024) a += (double)sq_sum[i];
+  for (int64_t i = tid; i < d_out; i += 1024) a += sq_sum[i];
 #pragma unroll 8
-  for (int64_t i = tid; i < d_in; i += 1024) b += (double)sq_sum[d_out + i];
+  for (int64_t i = tid; i < d_in; i += 1024) b += sq_sum[d_out + i];
   su[tid] = a;
   sv[tid] = b;
   __syncthreads();
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(256) void balance_apply_kernel(const float* uh, int
 }  // namespace
 
 size_t balance_workspace_bytes(int64_t d_out, int64_t d_in) {
-  return 2 * align_up((size_t)(d_out + d_in) * sizeof(float));
+  return align_up((size_t)(d_out + d_in) * sizeof(float)) + align_up((size_t)(d_out + d_in) * sizeof(double));
 }
 
 hipError_t launch_balance(const float* uh, int64_t ldu, const float* vh, int64_t ldv, int64_t d_out, int64_t d_in,
@@ -161,7 +167,7 @@ hipError_t launch_balance(const float* uh, int64_t ldu, const float* vh, int64_t
                           hipStream_t s) {
   const int64_t rows = d_out + d_in;
   float* abs_sum = static_cast<float*>(workspace);
-  float* sq_sum = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)rows * sizeof(float)));
+  double* sq_sum = reinterpret_cast<double*>(static_cast<char*>(workspace) + align_up((size_t)rows * sizeof(float)));
   const bool vec4 = ((uintptr_t)uh % 16 == 0) && ((uintptr_t)vh % 16 == 0) && ldu % 4 == 0 && ldv % 4 == 0;
   const dim3 grid((unsigned)cdiv(rows, kRowsPerBlock));
   if (vec4)

@@ -210,6 +210,18 @@ CONFIGS = {
 }
 
 
+def stack_config(frac: float) -> Config:
+    """The 80-layer Llama-2-70B-shaped stack with every rank at `frac` times its
+    ~1-bit value (1.0 and 0.55 are the named configs; other fractions are the
+    rank-sweep stacks)."""
+    if frac == 1.0:
+        return CONFIGS["70b_stack"]
+    if frac == 0.55:
+        return CONFIGS["70b_stack_055"]
+    return Config(f"70b_stack_{frac}", f"Llama-2-70B linear stack, {frac} x the 1-bit rank",
+                  llama2_70b_layer(frac), (1,), "bf16", n_layers=80, words="splitmix")
+
+
 def scales(cfg: Config, tag: str, n: int) -> np.ndarray:
     if cfg.scale_kind == "lognormal":
         return scales_lognormal(tag, n)

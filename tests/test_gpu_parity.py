@@ -11,6 +11,7 @@ import torch
 
 import synth
 from oracle import nq_oracle as O
+from tests import checks as C
 from tests import gpu_cases as G
 from tests.conftest import GOLDEN
 
@@ -85,10 +86,13 @@ def test_reconstruct_bit_exact(shape):
 
 
 def _linear_err(dev, ref, x_np, x_dtype, factored=False):
+    """Normwise error of nq_lrb_linear against the oracle; the per-token,
+    elementwise and deterministic bars of tests/checks.py must hold too."""
     y = nq.lrb_linear(dev, G.to_device_x(x_np, x_dtype)).cpu().numpy()
-    y_ref = O.linear_factored_ref(ref, x_np) if factored else O.linear_ref(ref, x_np)
     assert np.all(np.isfinite(y))
-    return O.rel_err(y, y_ref)
+    e = C.full_check(y, ref, x_np, G.tol_for(x_np.shape[0], x_dtype), x_dtype, factored)
+    assert e["pass"], e
+    return e["normwise"]
 
 
 def test_config_single_lrb_fp32():
@@ -239,9 +243,15 @@ def test_sequence_many_linears_parity(T):
 
 
 def _sampled_err(dev, ref, x_np, rows, x_dtype="bf16"):
+    """Normwise error on sampled output rows (all tokens); the per-token,
+    elementwise and deterministic bars must hold too."""
     y = nq.lrb_linear(dev, G.to_device_x(x_np, x_dtype)).cpu().numpy()
     assert np.all(np.isfinite(y))
-    return O.rel_err(y[:, rows], O.sampled_linear_ref(ref, x_np, rows))
+    e = C.sampled_check(y[:, rows], ref, x_np, rows, G.tol_for(x_np.shape[0], x_dtype), x_dtype)
+    print(f"  per-token max {e['per_token_max']:.2e}, elementwise/rms max {e['elem_rms_max']:.2e}, "
+          f"bound ratio {e['bound_ratio_max']:.2e}")
+    assert e["pass"], e
+    return e["normwise"]
 
 
 @pytest.mark.parametrize("name", ["k", "down"])
@@ -548,3 +558,21 @@ def test_linear_latent_parity(shape, T, x_dtype):
     assert torch.equal(y, y2)
     want = O.linear_latent_ref(Ul[:, :r], Vl[:, :r], s1, s2, x)
     assert O.rel_err(y.cpu().numpy(), want) <= G.tol_for(T, x_dtype)
+
+
+@pytest.mark.parametrize("su,sv", [(1e20, 1e-25), (1e-25, 1e20), (3e19, 3e19), (1e-24, 1e-24)])
+def test_balance_extreme_magnitudes(su, sv):
+    """Latents whose squares leave the fp32 range (|v| above ~1.8e19 or below
+    ~1e-23): the squared norms are accumulated in fp64, so eta, the scales and
+    the balanced factors still match the oracle."""
+    d_out, d_in, r = 70, 90, 100
+    uh = (synth.normal_f32(f"balx/u/{su}", (d_out, r)) * np.float32(su)).astype(np.float32)
+    vh = (synth.normal_f32(f"balx/v/{sv}", (d_in, r)) * np.float32(sv)).astype(np.float32)
+    U0, V0, rs1, rs2, reta = O.balance_ref(uh, vh)
+    U, V, s1, s2, eta = nq.balance_factors(torch.from_numpy(uh).to(G.DEV), torch.from_numpy(vh).to(G.DEV))
+    print(f"balance |U|~{su:g} |V|~{sv:g}: eta {float(eta.item()):.4e} (oracle {reta:.4e})")
+    assert abs(float(eta.item()) / reta - 1) <= 1e-6
+    for got, want in ((s1, rs1), (s2, rs2), (U, U0), (V, V0)):
+        g = got.cpu().numpy()
+        assert np.all(np.isfinite(g))
+        assert O.rel_err(g, want) <= 1e-6
