@@ -144,3 +144,12 @@ def full_check(y: np.ndarray, ref: O.LRB, x: np.ndarray, tol: float, x_dtype: st
     y_ref = O.linear_factored_ref(ref, x) if factored else O.linear_ref(ref, x)
     return check(y, y_ref, tol, abs_terms(ref, x), gamma(T, x_dtype, ref.d_in, ref.r),
                  token_bars=token_bars_apply(ref.d_out, ref))
+
+
+def latent_ref(cfg, shape, layer_idx: int = 0) -> O.LRB:
+    """The oracle's copy of a linear whose signs come from the config's fp32
+    latents, packed by the oracle itself."""
+    import synth
+    inp = synth.lrb_inputs(cfg, shape, layer_idx)
+    return O.LRB(O.pack_ref(inp["U_latent"]), O.pack_ref(inp["V_latent"].T), inp["s1"], inp["s2"],
+                 shape.d_out, shape.d_in, shape.r)
