@@ -220,7 +220,9 @@ constexpr int kChunkWords = kChunkSteps * kStepWords;  // 32 word rows
 constexpr int kRingSteps = 8;                         // steps of sign words in flight per lane
 static_assert(kChunkSteps % kRingSteps == 0, "ring slots are compile-time within a chunk");
 constexpr int kStepInts = 64 * 8;                     // B fragments of one step and MFMA (64 lanes x 32 bytes)
-constexpr int kPrepGroups = kMRows / 256;            // chunks per round of an input-piece tile
+constexpr int kPrepGroups = kMRows / 256;            // work items per round of an input-piece tile
+constexpr int kPrepItemsSeq = 8;                      // work items per input-piece tile: sequences
+constexpr int kPrepItemsSingle = kPrepGroups;         // and single calls (one round)
 // B columns are (token t, piece p) -> t*kPieces + p; every 16 of them form
 // one MFMA column group (T*kPieces columns: 1 group up to T = 3, 2 up to 6,
 // 3 up to 8).
@@ -248,9 +250,9 @@ constexpr int mfma_lds() { return sum_off<T>() + T * kMRows; }
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int T>
-struct MfmaIn {
-  uint32_t x[T][4];  // raw bf16 / fp32 bits of this thread's 4 elements
+// One token's inputs for this thread's 4 elements of a chunk.
+struct PieceIn {
+  uint32_t x[4];  // raw bf16 / fp32 bits
   float cs[4];
 };
 
@@ -262,47 +264,36 @@ __device__ inline int task_element(int task, int k) {
   return 32 * wr + 4 * (4 * ih + k) + 3 - j;
 }
 
-// Loads of a chunk's inputs.  Elements at or past cend read element `safe`
-// (any in-bounds index) and are dropped later, so chunks past the span can be
-// loaded too: the loads keep a fixed count and position in the pipeline.
-template <int T>
-__device__ inline void mfma_load_inputs(const StageDesc& S, int task, int64_t c0, int64_t cend, int64_t safe,
-                                        MfmaIn<T>& in) {
+// Loads of token t's inputs in a chunk.  Elements at or past cend read element
+// 0 of the token (always in bounds) and are dropped later, so the loads keep a
+// fixed count and position in the pipeline.
+__device__ inline void piece_load_inputs(const StageDesc& S, int task, int t, int64_t c0, int64_t cend, PieceIn& in) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int64_t e = c0 + task_element(task, k);
-    const int64_t ec = e < cend ? e : safe;
+    const int64_t ec = e < cend ? e : 0;
     in.cs[k] = S.colscale ? gload(S.colscale + ec) : 1.0f;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int64_t idx = (int64_t)t * S.n_red + ec;
-      in.x[t][k] = S.x_bf16 ? (uint32_t)gload(static_cast<const uint16_t*>(S.xin) + idx)
-                            : gload(static_cast<const uint32_t*>(S.xin) + idx);
-    }
+    const int64_t idx = (int64_t)t * S.n_red + ec;
+    in.x[k] = S.x_bf16 ? (uint32_t)gload(static_cast<const uint16_t*>(S.xin) + idx)
+                       : gload(static_cast<const uint32_t*>(S.xin) + idx);
   }
 }
 
-template <int T>
-__device__ inline float mfma_value(const StageDesc& S, const MfmaIn<T>& in, int task, int64_t c0, int64_t cend, int t,
-                                  int k) {
-  const float x = S.x_bf16 ? bf16_bits(in.x[t][k]) : __uint_as_float(in.x[t][k]);
+__device__ inline float piece_value(const StageDesc& S, const PieceIn& in, int task, int64_t c0, int64_t cend, int k) {
+  const float x = S.x_bf16 ? bf16_bits(in.x[k]) : __uint_as_float(in.x[k]);
   return c0 + task_element(task, k) < cend ? x * in.cs[k] : 0.0f;
 }
 
-// Largest |v| of the chunk per token into slot[t] (float bits of a
-// non-negative value order like unsigned integers; NaN orders above inf).
-template <int T>
-__device__ inline void mfma_chunk_max(const StageDesc& S, const MfmaIn<T>& in, int task, int64_t c0, int64_t cend,
-                                      unsigned* slot) {
+// Largest |v| of the chunk into *slot (float bits of a non-negative value
+// order like unsigned integers; NaN orders above inf).
+__device__ inline void piece_chunk_max(const StageDesc& S, const PieceIn& in, int task, int64_t c0, int64_t cend,
+                                       unsigned* slot) {
+  unsigned m = 0;
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    unsigned m = 0;
+  for (int k = 0; k < 4; ++k) m = max(m, __float_as_uint(fabsf(piece_value(S, in, task, c0, cend, k))));
 #pragma unroll
-    for (int k = 0; k < 4; ++k) m = max(m, __float_as_uint(fabsf(mfma_value<T>(S, in, task, c0, cend, t, k))));
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off));
-    if ((threadIdx.x & 63) == 0) atomicMax(slot + t, m);
-  }
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) atomicMax(slot, m);
 }
 
 // Scale exponent s for a chunk maximum (float bits): max * 2^s in [64, 128).
@@ -346,72 +337,81 @@ __device__ inline int max_fp8_exponent(int d) {
 template <int T>
 constexpr int chunk_blocks() { return kChunkSteps * 2 * 4 * T * kPieces; }
 
-// One input-piece tile: chunks [kPrepChunks*tile, ...) of the stage input
-// (fewer tiles, each with its own latency, fences and barriers, cost less
-// than one tile per chunk).  Each group of 256 threads of the workgroup takes
-// a chunk per round; per chunk each thread makes one B dword
-// (4 consecutive reduction positions) per piece and token; the next round's
-// inputs load while the current ones are converted.
-constexpr int kPrepChunks = 8;
-
+// One input-piece tile: work items [S.prep_items * tile, ...) of the stage
+// input, item i being chunk i / T for token i % T.  Each group of 256 threads
+// of the workgroup takes an item per round; per item each thread makes one B
+// dword (4 consecutive reduction positions) per piece; the next round's
+// inputs load while the current ones are converted.  Items per tile trade the
+// tile count (each with its own latency, fences and barriers) against the
+// time the stage waits for its pieces: sequences take eight, single calls two
+// (one round, so the pieces of a token are ready one tile latency after the
+// launch, whatever T).
 template <int T>
 __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* err) {
   constexpr int NC = T * kPieces;
   constexpr int64_t kChunkElems = kChunkWords * kWordBits;
-  unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + slot_off<T>());  // [round&1][group][T]
+  unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + slot_off<T>());  // [round&1][group]
   const int tid = threadIdx.x, half = tid >> 8, task = tid & 255;  // half: this thread's group
-  const int ch0 = tile * kPrepChunks;
-  const int ch1 = min(ch0 + kPrepChunks, (int)cdiv(S.n_red, kChunkElems));
+  const int nitems = (int)cdiv(S.n_red, kChunkElems) * T;
+  const int it0 = tile * S.prep_items;
+  const int it1 = min(it0 + S.prep_items, nitems);
   wait_input(S, err);
   const int wr = task >> 3, j = (task >> 1) & 3, ih = task & 1;
   const int kk = wr >> 2, gw = wr & 3;
   const int gp = 2 * (gw & 1) + (j >> 1);
   const int64_t task_off = (int64_t)(((kk * 2 + (gw >> 1)) * 4 + gp) * NC) * 4 + 2 * (j & 1) + ih;
-  if (tid < 2 * kPrepGroups * T) slots[tid] = 0;
-  MfmaIn<T> in, nxt;
-  mfma_load_inputs<T>(S, task, (ch0 + half) * kChunkElems, S.n_red, 0, in);
+  if (tid < 2 * kPrepGroups) slots[tid] = 0;
+  // the item this group takes in a round (past the tile's last: the last item
+  // again for the loads, nothing stored)
+  auto item_of = [&](int r0) { return min(r0 + half, nitems - 1); };
+  PieceIn in, nxt;
+  {
+    const int it = item_of(it0);
+    piece_load_inputs(S, task, it % T, (int64_t)(it / T) * kChunkElems, S.n_red, in);
+  }
   __syncthreads();
-  for (int r0 = ch0, round = 0; r0 < ch1; r0 += kPrepGroups, ++round) {
-    const int ch = r0 + half;  // this group's chunk (past ch1: loads clamp, nothing is stored)
+  for (int r0 = it0, round = 0; r0 < it1; r0 += kPrepGroups, ++round) {
+    const bool mine = r0 + half < it1;  // wave-uniform: a group is 4 whole waves
+    const int it = item_of(r0);
+    const int ch = it / T, t = it % T;
     const int64_t c0 = ch * kChunkElems;
-    unsigned* slot = slots + ((round & 1) * kPrepGroups + half) * T;
-    mfma_chunk_max<T>(S, in, task, c0, S.n_red, slot);
-    mfma_load_inputs<T>(S, task, c0 + kPrepGroups * kChunkElems, S.n_red, 0, nxt);  // next round (or none)
-    __syncthreads();  // the chunks' maxima are complete
-    if (ch < ch1) {   // wave-uniform: a group is 4 whole waves
+    unsigned* slot = slots + (round & 1) * kPrepGroups + half;
+    piece_chunk_max(S, in, task, c0, S.n_red, slot);
+    {
+      const int itn = item_of(r0 + kPrepGroups);  // next round's item (or the last again)
+      piece_load_inputs(S, task, itn % T, (int64_t)(itn / T) * kChunkElems, S.n_red, nxt);
+    }
+    __syncthreads();  // the items' maxima are complete
+    if (mine) {
       uint32_t* dst = S.bfrag + (int64_t)ch * chunk_blocks<T>() * 4 + task_off;
+      const int shift = chunk_shift(*slot);
+      float r[4];
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int shift = chunk_shift(slot[t]);
-        float r[4];
+      for (int k = 0; k < 4; ++k)
+        r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000) : ldexpf(piece_value(S, in, task, c0, S.n_red, k), shift);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000)
-                                    : ldexpf(mfma_value<T>(S, in, task, c0, S.n_red, t, k), shift);
-#pragma unroll
-        for (int p = 0; p < kPieces; ++p) {
-          int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
-          d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
-          // this dword and the partner thread's (task ^ 1, same wave) form one group of 8
-          int emax = max_fp8_exponent(d);
-          emax = max(emax, __shfl_xor(emax, 1));
-          d = keep_fp8_exponents(d, max(1, emax - 7));
-          store_agent(reinterpret_cast<float*>(dst + (t * kPieces + p) * 4), __int_as_float(d));
-          if (p + 1 < kPieces) {
-            typedef float v2f __attribute__((ext_vector_type(2)));
-            const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
-            const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
-            r[0] = (r[0] - lo.x) * 16.0f;
-            r[1] = (r[1] - lo.y) * 16.0f;
-            r[2] = (r[2] - hi.x) * 16.0f;
-            r[3] = (r[3] - hi.y) * 16.0f;
-          }
+      for (int p = 0; p < kPieces; ++p) {
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+        d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
+        // this dword and the partner thread's (task ^ 1, same wave) form one group of 8
+        int emax = max_fp8_exponent(d);
+        emax = max(emax, __shfl_xor(emax, 1));
+        d = keep_fp8_exponents(d, max(1, emax - 7));
+        store_agent(reinterpret_cast<float*>(dst + (t * kPieces + p) * 4), __int_as_float(d));
+        if (p + 1 < kPieces) {
+          typedef float v2f __attribute__((ext_vector_type(2)));
+          const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
+          const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
+          r[0] = (r[0] - lo.x) * 16.0f;
+          r[1] = (r[1] - lo.y) * 16.0f;
+          r[2] = (r[2] - hi.x) * 16.0f;
+          r[3] = (r[3] - hi.y) * 16.0f;
         }
-        if (task == 0) store_agent(reinterpret_cast<float*>(S.bsig + (int64_t)ch * T + t), __int_as_float(shift));
       }
+      if (task == 0) store_agent(reinterpret_cast<float*>(S.bsig + (int64_t)ch * T + t), __int_as_float(shift));
     }
     __syncthreads();  // every thread has read this round's maxima
-    if (task < T) slot[task] = 0;  // reused two rounds on (its maxima come after the next barrier)
+    if (task == 0) *slot = 0;  // reused two rounds on (its maximum comes after the next barrier)
     in = nxt;
   }
   if (S.signal) {
@@ -680,24 +680,13 @@ __device__ inline void stage_tile(const StageDesc& S, int local, float* lds, int
     mfma_tile<T, false>(S, local, lds, s_flag, err);
 }
 
-template <int T>
-__global__ __launch_bounds__(kMRows) __attribute__((amdgpu_waves_per_eu(min_waves<T>())))
-void dec_stage_kernel(StageDesc S, int* err) {
-  __shared__ __attribute__((aligned(16))) float lds[mfma_lds<T>()];
-  int* s_flag = reinterpret_cast<int*>(lds);
-  mfma_lds_init<T>(reinterpret_cast<int*>(lds));
-  __syncthreads();
-  stage_tile<T>(S, blockIdx.x, lds, s_flag, err);
-}
-
 // ints: [0] error flag (sticky), [1] next tile, [2] workgroups exited,
-// [3 .. n_ints) per-linear counters.  The last workgroup to exit zeroes
+// [3 .. n_ints) per-linear counters.  Workgroups take tiles in schedule order
+// from the counter at [1]; `lookup(tile, S, local)` gives a tile's descriptor
+// and its index within its stage.  The last workgroup to exit zeroes
 // [1 .. n_ints), so consecutive runs need no separate reset launch.
-template <int T>
-__global__ __launch_bounds__(kMRows) __attribute__((amdgpu_waves_per_eu(min_waves<T>())))
-void dec_persistent_kernel(const StageDesc* __restrict__ segs, const int* __restrict__ tile_seg, int ntiles, int* ints,
-                           int n_ints) {
-  __shared__ __attribute__((aligned(16))) float lds[mfma_lds<T>()];
+template <int T, typename Lookup>
+__device__ inline void persistent_tiles(Lookup lookup, int ntiles, int* ints, int n_ints, float* lds) {
   int& s_flag = reinterpret_cast<int*>(lds)[0];  // aliases B fragments (see stage_tile)
   int& s_tile = reinterpret_cast<int*>(lds)[1];
   int* err = ints;
@@ -709,8 +698,10 @@ void dec_persistent_kernel(const StageDesc* __restrict__ segs, const int* __rest
   while (tile < ntiles) {
     int nxt;  // thread 0's (no initial value: a write would wait for loads in flight)
     if (threadIdx.x == 0) nxt = add_relaxed(next_tile, 1);  // prefetch the next tile id
-    const StageDesc S = segs[tile_seg[tile]];  // one lookup (a scan over the segments stalled for microseconds)
-    stage_tile<T>(S, tile - S.tile0, lds, &s_flag, err);
+    StageDesc S;
+    int local;
+    lookup(tile, S, local);
+    stage_tile<T>(S, local, lds, &s_flag, err);
     if (threadIdx.x == 0) s_tile = nxt;
     __syncthreads();
     tile = __builtin_amdgcn_readfirstlane(s_tile);
@@ -726,6 +717,43 @@ void dec_persistent_kernel(const StageDesc* __restrict__ segs, const int* __rest
   __syncthreads();
   if (s_flag)
     for (int i = 1 + threadIdx.x; i < n_ints; i += blockDim.x) ints[i] = 0;
+}
+
+// A sequence plan: descriptors and the per-tile descriptor table in the
+// workspace (uploaded once per plan).
+template <int T>
+__global__ __launch_bounds__(kMRows) __attribute__((amdgpu_waves_per_eu(min_waves<T>())))
+void dec_persistent_kernel(const StageDesc* __restrict__ segs, const int* __restrict__ tile_seg, int ntiles, int* ints,
+                           int n_ints) {
+  __shared__ __attribute__((aligned(16))) float lds[mfma_lds<T>()];
+  persistent_tiles<T>(
+      [&](int tile, StageDesc& S, int& local) {
+        S = segs[tile_seg[tile]];  // one lookup (a scan over the segments stalled for microseconds)
+        local = tile - S.tile0;
+      },
+      ntiles, ints, n_ints, lds);
+}
+
+// One linear (a single call): its descriptors travel in the kernel arguments.
+struct LinearSched {
+  StageDesc d[kMaxLinearDescs];
+  int end[kMaxLinearDescs];  // cumulative tile counts
+};
+
+template <int T>
+__global__ __launch_bounds__(kMRows) __attribute__((amdgpu_waves_per_eu(min_waves<T>())))
+void dec_linear_kernel(LinearSched L, int* ints, int n_ints) {
+  __shared__ __attribute__((aligned(16))) float lds[mfma_lds<T>()];
+  persistent_tiles<T>(
+      [&](int tile, StageDesc& S, int& local) {
+        // the stage is uniform across the workgroup: select a pointer into the
+        // argument segment (scalar loads), not a copy of each descriptor
+        const int k = (tile >= L.end[0]) + (tile >= L.end[1]) + (tile >= L.end[2]);
+        const StageDesc* P = &L.d[k];
+        S = *P;
+        local = tile - P->tile0;
+      },
+      L.end[kMaxLinearDescs - 1], ints, n_ints, lds);
 }
 
 __global__ void zero_ints_kernel(int* p, int64_t n) {
@@ -765,18 +793,6 @@ hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = imin(cdiv(n, 256), 1024);
   hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_dec_stage(const StageDesc& S, int64_t T, int* err, hipStream_t s) {
-  const unsigned grid = (unsigned)(S.nrb * S.nks);
-  switch (T) {
-#define NQ_CASE(TT) \
-  case TT: hipLaunchKernelGGL(dec_stage_kernel<TT>, dim3(grid), dim3(kMRows), 0, s, S, err); break;
-    NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
-#undef NQ_CASE
-    default: return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 
@@ -933,7 +949,8 @@ int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
     pc.kind = 1;
     pc.bfrag = reinterpret_cast<uint32_t*>(buf);
     pc.bsig = reinterpret_cast<int*>(buf + align_up((size_t)nch * 64 * T * kPieces * 16));
-    pc.nrb = (int)cdiv(nch, kPrepChunks);  // tiles
+    pc.prep_items = split ? kPrepItemsSingle : kPrepItemsSeq;
+    pc.nrb = (int)cdiv(nch * T, pc.prep_items);  // tiles
     pc.nks = 1;
     pc.signal = ready;
     return pc;
@@ -955,27 +972,39 @@ int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
   return 4;
 }
 
+// Single calls: [error flag][next tile][exited][the linear's counters] then
+// the linear's buffers; one persistent launch runs the four stages, each tile
+// waiting on the counters of the stage it reads.
 size_t dec_workspace_bytes(const nq_lrb& L, int64_t T) {
-  return align_up((size_t)(1 + dec_linear_counters(L, T, true)) * sizeof(int)) + dec_linear_bytes(L, T, true);
+  return align_up((size_t)(3 + dec_linear_counters(L, T, true)) * sizeof(int)) + dec_linear_bytes(L, T, true);
 }
 
 hipError_t launch_dec_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
                              hipStream_t s) {
   char* base = static_cast<char*>(ws);
-  int* err = reinterpret_cast<int*>(base);
-  int* ctr = err + 1;
-  const int nctr = dec_linear_counters(L, T, true);
-  char* lin = base + align_up((size_t)(1 + nctr) * sizeof(int));
-  StageDesc d[kMaxLinearDescs];
-  const int nd = dec_stage_descs(L, x, xd, T, y, true, lin, ctr, d);
-  hipError_t e;
-  if ((e = launch_zero_ints(err, 1 + nctr, s)) != hipSuccess) return e;
+  int* ints = reinterpret_cast<int*>(base);
+  const int n_ints = 3 + dec_linear_counters(L, T, true);
+  char* lin = base + align_up((size_t)n_ints * sizeof(int));
+  LinearSched sched;
+  const int nd = dec_stage_descs(L, x, xd, T, y, true, lin, ints + 3, sched.d);
+  if (nd != kMaxLinearDescs) return hipErrorInvalidValue;
+  int tiles = 0;
   for (int i = 0; i < nd; ++i) {
-    d[i].signal = nullptr;  // stream order separates the launches
-    d[i].wait_ctr = nullptr;
-    if ((e = launch_dec_stage(d[i], T, err, s)) != hipSuccess) return e;
+    sched.d[i].tile0 = tiles;
+    tiles += sched.d[i].nrb * sched.d[i].nks;
+    sched.end[i] = tiles;
   }
-  return hipSuccess;
+  hipError_t e;
+  if ((e = launch_zero_ints(ints, n_ints, s)) != hipSuccess) return e;
+  const int grid = (int)imin(tiles, dec_persistent_grid(T));
+  switch (T) {
+#define NQ_CASE(TT)                                                                                        \
+  case TT: hipLaunchKernelGGL(dec_linear_kernel<TT>, dim3(grid), dim3(kMRows), 0, s, sched, ints, n_ints); break;
+    NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
+#undef NQ_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace nq

@@ -74,6 +74,7 @@ struct StageDesc {
   int kind;               // 0: stage tiles (nrb x nks); 1: input-piece tiles (nrb = tiles, nks = 1)
   uint32_t* bfrag;        // matrix-core operand pieces of the stage input (written by kind 1, read by kind 0)
   int* bsig;              // per chunk and token: scale exponent of the pieces
+  int prep_items;         // kind 1: (chunk, token) work items per tile
   int tile0;              // first tile of this stage in a persistent schedule
 };
 struct StagePlan {
