@@ -73,6 +73,28 @@ class Stack:
         torch.cuda.synchronize()
 
 
+PREFILL_SRC = os.path.join(ROOT, "sub_bit_weight_amd", "csrc", "prefill.hip")
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_gemm_70b_t2048_counters.md")
+
+
+def summary_field(path: str, src: str, src_key: str, field: str):
+    """A number from a committed counter summary, or None when the kernel
+    source changed since the counters were taken (sha256 recorded there)."""
+    import hashlib
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    fields = {k[2:].strip(): v.strip() for k, v in
+              (line.split(":", 1) for line in text.splitlines() if ":" in line and line.startswith("- "))}
+    if fields.get(src_key) != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    try:
+        return float(fields[field])
+    except (KeyError, ValueError):
+        return None
+
+
 def measured_traffic():
     """HBM bytes per decode launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, calibrated against a copy of known size), or None
@@ -672,6 +694,10 @@ def main() -> int:
                     help="also time the prefill pass as serial single-linear calls on one stream")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
+    ap.add_argument("--prefill-profile", type=int, default=0, metavar="N",
+                    help="only run layer 0's seven T=2048 linears N times each, one after another, each as a "
+                         "one-entry sequence plan (the kernels and tiles of the benchmarked pass, in a fixed "
+                         "order: for profilers)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -696,6 +722,21 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"bytes_read_per_copy": a.numel() * 4,
                                                "bytes_written_per_copy": a.numel() * 4, "copies": 5}}))
+        return 0
+
+    if args.prefill_profile:
+        import sub_bit_weight_amd as nq
+        stack = Stack(synth.CONFIGS["70b_prefill"], 1, device)
+        Tp = 2048
+        for L, s in zip(stack.layers, stack.shapes):
+            x = torch.from_numpy(synth.x_for(stack.cfg, s.d_in, Tp)).to(device).to(torch.bfloat16)
+            y = torch.empty((Tp, s.d_out), dtype=torch.float32, device=device)
+            seq = nq.Seq([L], [x], [y])
+            for _ in range(args.prefill_profile):
+                seq.run()
+            torch.cuda.synchronize()
+            log(f"[bench] profile: {s.name} {s.d_out}x{s.d_in} r{s.r} T{Tp} x{args.prefill_profile}")
+            seq.close()
         return 0
 
     cfg = synth.stack_config(1.0)
@@ -746,7 +787,9 @@ def main() -> int:
                             "tokens_per_s": Tp / (pms * 1e-3), "algorithmic_flop": flops,
                             "roofline": {"bound": "mfma", "kernel": "gemm_kernel (whole pass incl. prep kernels)",
                                          "achieved": tf, "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                         "frac": tf / F16_PEAK_TFLOPS, "traffic": None,
+                                         "frac": tf / F16_PEAK_TFLOPS,
+                                         "traffic": summary_field(PREFILL_COUNTERS, PREFILL_SRC, "prefill.hip sha256",
+                                                                  "hbm bytes per pass"),
                                          "basis": f"median of {len(ptimes)} passes, HIP events on the caller's "
                                                   "stream around each pass"},
                             "operands": "fp16 (per-token power-of-two scaled) x +-1, fp32 accumulate",
