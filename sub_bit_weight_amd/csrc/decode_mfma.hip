@@ -22,6 +22,8 @@
 //    whose input is produced by other tiles first waits for them.  Waits only
 //    target earlier tiles, which are already running, so the queue always
 //    drains; each wait also has a spin limit that records an error and exits.
+#include <stdlib.h>
+
 #include "nq_internal.h"
 
 namespace nq {
@@ -91,6 +93,21 @@ __device__ inline void stores_done_barrier() {
 // block re-reads, out of the L2 (measured: 5.3 -> 5.6 TB/s on the 70B stack).
 constexpr int kStreamLoad = 2;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past every sign-word buffer (< 2 GiB)
+
+// The next tile id of a persistent workgroup is taken from the queue counter
+// by thread 0 once the current tile enters its last chunk (or last round):
+// early enough that the atomic's latency is hidden, late enough that a tile
+// another stage waits for is not held behind a long tile that this workgroup
+// has yet to finish.  (Taking it when the current tile started kept, e.g.,
+// the t pieces of a linear behind a 224-step stage-1 tile while that
+// linear's stage-2 tiles spun.)  Tiles outside a persistent loop pass none.
+struct NextTile {
+  int* counter;         // queue counter (null: no claim)
+  int id = 0x7fffffff;  // thread 0: the claimed id (past every queue until claimed)
+  __device__ inline void claim() {
+    if (counter && threadIdx.x == 0) id = add_relaxed(counter, 1);
+  }
+};
 
 // A tile whose input is made by other tiles of the same launch (a stage by
 // its input-piece tiles, the pieces of t by the stage-1 row blocks) waits
@@ -212,12 +229,13 @@ __device__ void finish_rows(const StageDesc& S, int rb, int ks, int64_t o, bool 
 // row), and component q feeds the MFMAs of set q.
 
 constexpr int kMfmaMaxT = 8;
+constexpr int kMaxGroupT = 3;                          // largest T whose tiles take groups of row blocks
 constexpr int kMRows = 512;                            // rows per tile = threads per workgroup (8 waves)
 constexpr int kPieces = 5;                            // fp8 pieces per token
 constexpr int kStepWords = 4;                         // word rows per MFMA step
 constexpr int kChunkSteps = 8;                        // steps per staged chunk
 constexpr int kChunkWords = kChunkSteps * kStepWords;  // 32 word rows
-constexpr int kRingSteps = 8;                         // steps of sign words in flight per lane
+constexpr int kRingSteps = 4;                         // steps of sign words in flight per lane
 static_assert(kChunkSteps % kRingSteps == 0, "ring slots are compile-time within a chunk");
 constexpr int kStepInts = 64 * 8;                     // B fragments of one step and MFMA (64 lanes x 32 bytes)
 constexpr int kPrepGroups = kMRows / 256;            // work items per round of an input-piece tile
@@ -228,11 +246,12 @@ constexpr int kPrepItemsSingle = kPrepGroups;         // and single calls (one r
 // 3 up to 8).
 template <int T>
 constexpr int col_groups() { return (T * kPieces + 15) / 16; }
-// Steps of sign words in flight per lane: with two column groups the ring is
-// half as deep, so that two workgroups fit a CU (their registers); the CU
-// then keeps as many bytes in flight as one workgroup with the full ring.
+// Steps of sign words in flight per lane: 4 (16 KB per wave).  8 kept twice
+// the bytes in flight and measured 1-4 % slower (same box; 70B stacks and 7B
+// attention sequences): the deeper queues lengthen every other global access
+// of a tile (input counters, pieces, descriptors), which wait behind them.
 template <int T>
-constexpr int ring_steps() { return col_groups<T>() == 2 ? kRingSteps / 2 : kRingSteps; }
+constexpr int ring_steps() { return kRingSteps; }
 // LDS of a workgroup, in 4-byte words: [B fragments, two chunk buffers of
 // kChunkSteps x col_groups x kStepInts] [chunk scale exponents, two buffers of
 // T] [per-chunk maxima of an input-piece tile] [row sums [T][kMRows]]
@@ -245,7 +264,9 @@ constexpr int slot_off() { return sig_off<T>() + 2 * T; }
 template <int T>
 constexpr int sum_off() { return slot_off<T>() + 2 * kPrepGroups * T; }
 template <int T>
-constexpr int mfma_lds() { return sum_off<T>() + T * kMRows; }
+constexpr int flag_off() { return sum_off<T>() + T * kMRows; }  // two shared words: s_flag, s_tile
+template <int T>
+constexpr int mfma_lds() { return flag_off<T>() + 4; }
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -347,7 +368,7 @@ constexpr int chunk_blocks() { return kChunkSteps * 2 * 4 * T * kPieces; }
 // (one round, so the pieces of a token are ready one tile latency after the
 // launch, whatever T).
 template <int T>
-__device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* err) {
+__device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* err, NextTile& next) {
   constexpr int NC = T * kPieces;
   constexpr int64_t kChunkElems = kChunkWords * kWordBits;
   unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + slot_off<T>());  // [round&1][group]
@@ -371,6 +392,7 @@ __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* e
   }
   __syncthreads();
   for (int r0 = it0, round = 0; r0 < it1; r0 += kPrepGroups, ++round) {
+    if (r0 + kPrepGroups >= it1) next.claim();  // the tile's last round
     const bool mine = r0 + half < it1;  // wave-uniform: a group is 4 whole waves
     const int it = item_of(r0);
     const int ch = it / T, t = it % T;
@@ -467,13 +489,21 @@ __device__ inline float row16_sum(float v) {
 // W4: sign words are read 4 rows at a time (16-byte loads); otherwise one
 // word per load (row counts or strides that are not multiples of 4).
 template <int T, bool W4>
-__device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_flag, int* err) {
+__device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_flag, int* err, NextTile& next) {
   static_assert(T <= kMfmaMaxT, "tokens");
   constexpr int G = col_groups<T>();
   int* lds = reinterpret_cast<int*>(ldsf);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, col = lane & 15, grp = lane >> 4;
-  const int rb = local % S.nrb;
-  const int ks = local / S.nrb;
+  // a tile is rb_group consecutive row blocks (rb0 ..) of one reduction span;
+  // for T > 3 always one (the host plans it so): the loop over row blocks
+  // costs those tiles registers they do not have
+  constexpr bool kGroups = T <= kMaxGroupT;
+  const int group = kGroups ? S.rb_group : 1;
+  const int nrbt = (S.nrb + group - 1) / group;
+  const int rbt = local % nrbt;
+  const int ks = local / nrbt;
+  const int rb0 = rbt * group;
+  const int nrbs = kGroups ? min(group, S.nrb - rb0) : 1;
   const int64_t span0 = (int64_t)ks * S.kc;
   const int64_t span1 = imin(span0 + S.kc, S.n_red);
   const int w0 = __builtin_amdgcn_readfirstlane((int)(span0 / kWordBits));
@@ -482,32 +512,35 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   const int nk = (nw + kStepWords - 1) / kStepWords;
   const int nchunks = (nw + kChunkWords - 1) / kChunkWords;
 
-  // byte offset of this lane's q-th word from word row 4k; rows at or past
-  // n_rows (in the last row block) get an offset past any buffer (sign-word
-  // buffers are below 2 GiB), so their loads read 0 without memory traffic
-  // instead of words of the next word row
-  const int row0 = rb * kMRows + wv * 64 + 4 * col;
-  const uint32_t voff = 4u * (uint32_t)row0 + (uint32_t)grp * ld4;
-  uint32_t qoff[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) qoff[q] = row0 + q < S.n_rows ? voff + 4u * q : kOutOfRange;
-  // Step k reads word row 4k + grp of the span through a buffer resource that
-  // starts at word row 4k and ends with row n_rows-1 of the span's last word
-  // row: words past the span (a partial last step, steps past the last) or
-  // past the last row are out of range and read as 0 without touching memory
-  // (with W4, n_rows is a multiple of 4, so a 16-byte load is entirely in or
-  // out of range).  Everything but the lane offset is scalar.
-  auto load_step = [&](int k, u32x4& dst) {
+  // this lane's first row in the tile's first row block (row block i adds
+  // i * kMRows) and its byte offset in a word row
+  const int lrow = rb0 * kMRows + wv * 64 + 4 * col;
+  const uint32_t lane_off = 4u * (uint32_t)lrow + (uint32_t)grp * ld4;
+  // Step k of row block i reads word row 4k + grp of the span through a buffer
+  // resource that starts at word row 4k and ends with row n_rows-1 of the
+  // span's last word row: words past the span (a partial last step, steps past
+  // the last) or past the last row are out of range and read as 0 without
+  // touching memory (with W4, n_rows is a multiple of 4, so a 16-byte load is
+  // entirely in or out of range).  Rows at or past n_rows (in the last row
+  // block) get an offset past any buffer (sign-word buffers are below 2 GiB)
+  // instead of words of the next word row; row blocks past the tile's last
+  // read nothing.  Everything but the lane offset is scalar.
+  auto load_step = [&](int i, int k, u32x4& dst) {
     const int wb = kStepWords * k;  // from the span start
-    const int rows_left = max(nw - wb, 0);
+    const int rows_left = i < nrbs ? max(nw - wb, 0) : 0;
     const uint32_t nrec = rows_left > 0 ? (uint32_t)(rows_left - 1) * ld4 + 4u * (uint32_t)S.n_rows : 0u;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t*>(S.bits) + (int64_t)(w0 + wb) * S.ld, (short)0, (int)nrec, 0x00020000);
+    const int row = lrow + i * kMRows;
+    const uint32_t off = lane_off + 4u * (uint32_t)(i * kMRows);
     if constexpr (W4) {  // n_rows % 4 == 0: the lane's 4 rows are all valid or all past the end
-      dst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)qoff[0], 0, kStreamLoad));
+      const uint32_t o = row < S.n_rows ? off : kOutOfRange;
+      dst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)o, 0, kStreamLoad));
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dst[q] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)qoff[q], 0, kStreamLoad);
+      for (int q = 0; q < 4; ++q)
+        dst[q] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(row + q < S.n_rows ? off + 4u * q : kOutOfRange), 0,
+                                                      kStreamLoad);
     }
   };
 
@@ -557,7 +590,7 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   constexpr int R = ring_steps<T>();
   u32x4 ring[R];
 #pragma unroll
-  for (int k = 0; k < R; ++k) load_step(k, ring[k]);
+  for (int k = 0; k < R; ++k) load_step(0, k, ring[k]);
   wait_input(S, err);  // the stage's pieces are final
   load_chunk(chunk0);
   store_chunk(0);
@@ -571,8 +604,52 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
 #pragma unroll
     for (int cg = 0; cg < G; ++cg) acc[q][cg] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
+  // row block ri is complete: add the pieces of each token across the lanes
+  // of a row (and the column groups); lane col == 0 of every row group writes
+  // its 4 rows of every set; then the rows' results, and a clear start for
+  // the next row block
+  auto finish_rb = [&](int ri) {
+    float* sums = ldsf + sum_off<T>();
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {  // C row 4*grp + r of set q is row 16*grp + 4r + q of the wave
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float u = 0.0f;
+#pragma unroll
+          for (int cg = 0; cg < G; ++cg)
+            if ((16 * cg + 15) / kPieces >= t && (16 * cg) / kPieces <= t)  // the group holds columns of token t
+              u += (16 * cg + col) / kPieces == t ? acc[q][cg][r] : 0.0f;
+          v[q] = row16_sum(u);
+        }
+        if (col == 0)
+          *reinterpret_cast<float4*>(sums + t * kMRows + wv * 64 + grp * 16 + 4 * r) =
+              make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+    __syncthreads();
+    float accr[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) accr[t] = sums[t * kMRows + tid];
+    const int rb = rb0 + ri;
+    const int64_t o = (int64_t)rb * kMRows + tid;
+    finish_rows<T>(S, rb, ks, o, o < S.n_rows, accr, s_flag);  // ends with a barrier: sums are free again
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int cg = 0; cg < G; ++cg) acc[q][cg] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  };
+
+  // the tile's row blocks run back to back: virtual chunk vc is chunk c of row
+  // block ri; the ring's loads R steps ahead cross into the next row block, so
+  // its first sign words are in flight while this one finishes
+  const int nvc = nrbs * nchunks;
+  int ri = 0, c = 0;
+  for (int vc = 0; vc < nvc; ++vc) {
+    if (vc + 1 == nvc) next.claim();  // the tile's last chunk
+    const int buf = vc & 1;
     // E8M0 scale of this lane's column in every group (2^0 for columns past
     // the last piece, whose B entries are 0; a NaN chunk has NaN pieces)
     int bscale[G];
@@ -582,7 +659,7 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
       const int sg = lds[sig_off<T>() + buf * T + min(tc, T - 1)];
       bscale[cg] = tc < T ? 127 - (sg == kShiftNaN ? 0 : sg) - 4 * pc : 127;
     }
-    load_chunk(chunk0 + c + 1);  // next chunk's pieces (or none)
+    load_chunk(chunk0 + (c + 1 < nchunks ? c + 1 : 0));  // next chunk's pieces (the next row block's first)
 
     const u32x4* bfrag = reinterpret_cast<const u32x4*>(lds + buf * b_ints<T>()) + lane;
     // B fragments: with one column group the next step's are read a step ahead;
@@ -624,39 +701,24 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
                 __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[cg], acc[q][cg], 4, 0, 0, 127, 0, bscale[cg]);
         }
       }
-      load_step(k + R, ring[kk % R]);  // past the span: out of range, no memory access
-      if (kk == kChunkSteps / 2) store_chunk(buf ^ 1);    // the other buffer was last read in chunk c-1
+      // the load R steps ahead: this row block's step k + R, or, past its last
+      // chunk, the next row block's step kk + R - 8 (past the tile's last row
+      // block: out of range, no memory access); no branch around the load
+      const bool next_rb = kk + R >= kChunkSteps && c + 1 == nchunks;
+      load_step(next_rb ? ri + 1 : ri, next_rb ? kk + R - kChunkSteps : k + R, ring[kk % R]);
+      if (kk == kChunkSteps / 2) store_chunk(buf ^ 1);    // the other buffer was last read in chunk vc-1
     }
-    __syncthreads();  // chunk c+1's fragments are in LDS; every wave is done with chunk c's
-  }
-
-  // add the pieces of each token across the lanes of a row (and the column
-  // groups); lane col == 0 of every row group writes its 4 rows of every set
-  float* sums = ldsf + sum_off<T>();
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {  // C row 4*grp + r of set q is row 16*grp + 4r + q of the wave
-      float v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float u = 0.0f;
-#pragma unroll
-        for (int cg = 0; cg < G; ++cg)
-          if ((16 * cg + 15) / kPieces >= t && (16 * cg) / kPieces <= t)  // the group holds columns of token t
-            u += (16 * cg + col) / kPieces == t ? acc[q][cg][r] : 0.0f;
-        v[q] = row16_sum(u);
-      }
-      if (col == 0)
-        *reinterpret_cast<float4*>(sums + t * kMRows + wv * 64 + grp * 16 + 4 * r) = make_float4(v[0], v[1], v[2], v[3]);
+    __syncthreads();  // chunk vc+1's fragments are in LDS; every wave is done with chunk vc's
+    if (c + 1 < nchunks) {
+      ++c;
+      continue;
     }
+    if constexpr (!kGroups) break;  // one row block: its finish follows the loop
+    finish_rb(ri);
+    ++ri;
+    c = 0;
   }
-  __syncthreads();
-  float accr[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) accr[t] = sums[t * kMRows + tid];
-  const int64_t o = (int64_t)rb * kMRows + tid;
-  finish_rows<T>(S, rb, ks, o, o < S.n_rows, accr, s_flag);
+  if constexpr (!kGroups) finish_rb(0);
 }
 
 // With one or two column groups: 4 waves per SIMD (at most 128 VGPRs) and 2
@@ -666,18 +728,14 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
 template <int T>
 constexpr int min_waves() { return col_groups<T>() <= 2 ? 4 : 2; }
 
-// The workgroup's two shared flag words live in the first entries of LDS (B
-// fragments of column 0 in chunk buffer 0): every write to them follows the
-// barrier after a tile's last fragment read, and the next tile's first chunk
-// copy follows the barrier after their last read.
 template <int T>
-__device__ inline void stage_tile(const StageDesc& S, int local, float* lds, int* s_flag, int* err) {
+__device__ inline void stage_tile(const StageDesc& S, int local, float* lds, int* s_flag, int* err, NextTile& next) {
   if (S.kind == 1)
-    mfma_prep_tile<T>(S, local, lds, err);
+    mfma_prep_tile<T>(S, local, lds, err, next);
   else if (S.w_vec)
-    mfma_tile<T, true>(S, local, lds, s_flag, err);
+    mfma_tile<T, true>(S, local, lds, s_flag, err, next);
   else
-    mfma_tile<T, false>(S, local, lds, s_flag, err);
+    mfma_tile<T, false>(S, local, lds, s_flag, err, next);
 }
 
 // ints: [0] error flag (sticky), [1] next tile, [2] workgroups exited,
@@ -687,8 +745,8 @@ __device__ inline void stage_tile(const StageDesc& S, int local, float* lds, int
 // [1 .. n_ints), so consecutive runs need no separate reset launch.
 template <int T, typename Lookup>
 __device__ inline void persistent_tiles(Lookup lookup, int ntiles, int* ints, int n_ints, float* lds) {
-  int& s_flag = reinterpret_cast<int*>(lds)[0];  // aliases B fragments (see stage_tile)
-  int& s_tile = reinterpret_cast<int*>(lds)[1];
+  int& s_flag = reinterpret_cast<int*>(lds)[flag_off<T>()];
+  int& s_tile = reinterpret_cast<int*>(lds)[flag_off<T>() + 1];
   int* err = ints;
   int* next_tile = ints + 1;
   mfma_lds_init<T>(reinterpret_cast<int*>(lds));
@@ -696,13 +754,13 @@ __device__ inline void persistent_tiles(Lookup lookup, int ntiles, int* ints, in
   __syncthreads();
   int tile = __builtin_amdgcn_readfirstlane(s_tile);
   while (tile < ntiles) {
-    int nxt;  // thread 0's (no initial value: a write would wait for loads in flight)
-    if (threadIdx.x == 0) nxt = add_relaxed(next_tile, 1);  // prefetch the next tile id
+    NextTile next;  // thread 0 claims the next tile id during the tile's last chunk
+    next.counter = next_tile;
     StageDesc S;
     int local;
     lookup(tile, S, local);
-    stage_tile<T>(S, local, lds, &s_flag, err);
-    if (threadIdx.x == 0) s_tile = nxt;
+    stage_tile<T>(S, local, lds, &s_flag, err, next);
+    if (threadIdx.x == 0) s_tile = next.id;
     __syncthreads();
     tile = __builtin_amdgcn_readfirstlane(s_tile);
     __syncthreads();
@@ -836,11 +894,18 @@ namespace {
 // and one release per row block.  (Capping the span at 8K or 16K elements to
 // shorten the longest tiles measured slower: the extra fixups cost more than
 // the shorter dependency waits they buy.)
-constexpr int64_t kSeqSpan = 0;
+int64_t seq_span() {
+  static const int64_t v = [] {
+    const char* e = getenv("NQ_SEQ_SPAN");
+    const long long x = e ? atoll(e) : 0;
+    return (int64_t)(x < 0 ? 0 : x);
+  }();
+  return v;
+}
 
 void plans(const nq_lrb& L, int64_t T, bool split, StagePlan* p1, StagePlan* p2) {
-  *p1 = dec_stage_plan(L.r, L.d_in, T, split ? dec_single_span(L.r, L.d_in, T) : kSeqSpan);
-  *p2 = dec_stage_plan(L.d_out, L.r, T, split ? dec_single_span(L.d_out, L.r, T) : kSeqSpan);
+  *p1 = dec_stage_plan(L.r, L.d_in, T, split ? dec_single_span(L.r, L.d_in, T) : seq_span());
+  *p2 = dec_stage_plan(L.d_out, L.r, T, split ? dec_single_span(L.d_out, L.r, T) : seq_span());
 }
 
 size_t part_bytes(const StagePlan& p, int64_t T) {
@@ -880,6 +945,25 @@ int dec_linear_counters(const nq_lrb& L, int64_t T, bool split) {
 }
 
 
+// Sequences: row blocks per stage tile (T <= kMaxGroupT only), so that a tile streams about 32
+// MFMA steps (256 KB of sign words) however short the stage's reduction is;
+// the per-tile costs (descriptor lookup, input wait, first pieces, the ring's
+// start) are then paid once per group.  Measured (same box, ms per step or
+// GB/s; 1 = one row block per tile / 32 / 64): 70B 0.55 bit 0.945 / 0.940 /
+// 0.929, 0.25x ranks 0.544 / 0.523 / 0.519, 1 bit flat; 7B attention over 505
+// copies 4231 / 4535 / 4075 GB/s, 7B MLP set 3912 / 4105 / 4194 GB/s
+// (NQ_SEQ_TILE_STEPS: tuning knob).
+int seq_rb_group(const StagePlan& p, int64_t T) {
+  if (T > kMaxGroupT) return 1;
+  static const int steps = [] {
+    const char* e = getenv("NQ_SEQ_TILE_STEPS");
+    const int v = e ? atoi(e) : 32;
+    return v < 1 ? 1 : v;
+  }();
+  const int per_rb = (int)cdiv(p.kc, kChunkWords * kWordBits) * kChunkSteps;  // whole chunks
+  return (int)imax(1, imin(p.nrb, steps / per_rb));
+}
+
 // Sign words of a stage can be read 4 rows at a time (16-byte loads).
 bool words_vec(const uint32_t* bits, int64_t ld, int64_t n_rows) {
   return reinterpret_cast<uintptr_t>(bits) % 16 == 0 && ld % 4 == 0 && n_rows % 4 == 0;
@@ -918,6 +1002,7 @@ int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
   a.kc = p1.kc;
   a.nks = p1.nks;
   a.nrb = p1.nrb;
+  a.rb_group = split ? 1 : seq_rb_group(p1, T);
   a.x_bf16 = xd == NQ_BF16;
   a.w_vec = words_vec(L.vt_bits, L.ldv, L.r);
   a.kind = 0;
@@ -939,6 +1024,7 @@ int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
   b.kc = p2.kc;
   b.nks = p2.nks;
   b.nrb = p2.nrb;
+  b.rb_group = split ? 1 : seq_rb_group(p2, T);
   b.x_bf16 = 0;
   b.w_vec = words_vec(L.u_bits, L.ldu, L.d_out);
   // input-piece tiles before each stage; each stage waits for its pieces,
@@ -951,6 +1037,7 @@ int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
     pc.bsig = reinterpret_cast<int*>(buf + align_up((size_t)nch * 64 * T * kPieces * 16));
     pc.prep_items = split ? kPrepItemsSingle : kPrepItemsSeq;
     pc.nrb = (int)cdiv(nch * T, pc.prep_items);  // tiles
+    pc.rb_group = 1;
     pc.nks = 1;
     pc.signal = ready;
     return pc;
@@ -991,7 +1078,7 @@ hipError_t launch_dec_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_
   int tiles = 0;
   for (int i = 0; i < nd; ++i) {
     sched.d[i].tile0 = tiles;
-    tiles += sched.d[i].nrb * sched.d[i].nks;
+    tiles += stage_tiles(sched.d[i]);
     sched.end[i] = tiles;
   }
   hipError_t e;

@@ -211,15 +211,16 @@ void plan_persistent(nq_seq* s) {
   const char* e2 = getenv("NQ_SEQ_LAG2");
   const int64_t pre = std::max<int64_t>(ep ? atoi(ep) : lag / 2, 1);
   const int64_t lag2 = std::min<int64_t>(std::max<int64_t>(e2 ? atoi(e2) : lag * 3 / 4, 0), lag);
-  for (int64_t i = 0; i < std::min(pre, n); ++i) s->order.push_back({(int)i, 0});
+  auto E = [](int64_t i) { return (int)i; };
+  for (int64_t i = 0; i < std::min(pre, n); ++i) s->order.push_back({E(i), 0});
   for (int64_t i = 0; i < n; ++i) {
-    if (i + pre < n) s->order.push_back({(int)(i + pre), 0});
-    s->order.push_back({(int)i, 1});
-    if (i >= lag2) s->order.push_back({(int)(i - lag2), 2});
-    if (i >= lag) s->order.push_back({(int)(i - lag), 3});
+    if (i + pre < n) s->order.push_back({E(i + pre), 0});
+    s->order.push_back({E(i), 1});
+    if (i >= lag2) s->order.push_back({E(i - lag2), 2});
+    if (i >= lag) s->order.push_back({E(i - lag), 3});
   }
-  for (int64_t i = std::max<int64_t>(0, n - lag2); i < n; ++i) s->order.push_back({(int)i, 2});
-  for (int64_t i = std::max<int64_t>(0, n - lag); i < n; ++i) s->order.push_back({(int)i, 3});
+  for (int64_t i = std::max<int64_t>(0, n - lag2); i < n; ++i) s->order.push_back({E(i), 2});
+  for (int64_t i = std::max<int64_t>(0, n - lag); i < n; ++i) s->order.push_back({E(i), 3});
   // tile counts do not depend on where the buffers are: count them with the
   // descriptors of a stand-in workspace address
   s->ntiles = 0;
@@ -228,7 +229,7 @@ void plan_persistent(nq_seq* s) {
     StageDesc d[kMaxLinearDescs];
     dec_stage_descs(s->layers[o.first], s->xs[o.first], s->xd, s->T, s->ys[o.first], false, stand_in,
                     reinterpret_cast<int*>(stand_in), d);
-    s->ntiles += d[o.second].nrb * d[o.second].nks;
+    s->ntiles += stage_tiles(d[o.second]);
   }
   s->off_sched = align_up((size_t)ints * sizeof(int));
   s->off_tseg = align_up(s->off_sched + s->order.size() * sizeof(StageDesc));
@@ -251,7 +252,7 @@ nq_status build_and_upload(nq_seq* s, void* ws, hipStream_t stream) {
   for (auto& o : s->order) {
     StageDesc d = st[o.first][o.second];
     d.tile0 = (int)s->tile_seg.size();
-    s->tile_seg.insert(s->tile_seg.end(), (size_t)d.nrb * d.nks, (int)s->segs.size());
+    s->tile_seg.insert(s->tile_seg.end(), (size_t)stage_tiles(d), (int)s->segs.size());
     s->segs.push_back(d);
   }
   if ((int64_t)s->tile_seg.size() != s->ntiles) return set_error("nq_seq_run: tile count changed"), NQ_ERR_ARG;

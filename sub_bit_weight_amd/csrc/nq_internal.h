@@ -69,6 +69,7 @@ struct StageDesc {
   int wait_target;
   int n_rows, n_red;
   int kc, nks, nrb;       // reduction span per tile (elements), spans, row blocks
+  int rb_group;           // kind 0: consecutive row blocks per tile (one span); kind 1: 1
   int x_bf16;
   int w_vec;              // bits 16-byte aligned, ld and n_rows multiples of 4: 16-byte word loads
   int kind;               // 0: stage tiles (nrb x nks); 1: input-piece tiles (nrb = tiles, nks = 1)
@@ -77,6 +78,11 @@ struct StageDesc {
   int prep_items;         // kind 1: (chunk, token) work items per tile
   int tile0;              // first tile of this stage in a persistent schedule
 };
+// Tiles of a stage: kind 0, groups of rb_group row blocks per span; kind 1,
+// nrb input-piece tiles (rb_group 1, nks 1).
+__host__ __device__ inline int stage_tiles(const StageDesc& d) {
+  return (d.nrb + d.rb_group - 1) / d.rb_group * d.nks;
+}
 struct StagePlan {
   int64_t n_rows, n_red;
   int kc, nks, nrb;
