@@ -201,11 +201,16 @@ __device__ void finish_rows(const StageDesc& S, int rb, int ks, int64_t o, bool 
 //    v * 2^s = q0 + q1/16 + q2/256 + ... (each q the round-to-nearest fp8 of
 //    the scaled remainder), kPieces per token, each piece a matrix column.
 //    2^s brings the chunk's largest |v| into [64, 128), so no piece saturates;
-//    five pieces carry v to about 2^-20 of that largest value.
+//    four pieces carry v to within 2^-16 of that largest value (the worst
+//    case; round-to-nearest remainders alternate in sign, and a model of the
+//    split measures about 2^-20, a relative error of ~4e-7 per stage).  A
+//    fifth piece (~3e-9) added nothing next to the fp32 sums (~1e-7) but a
+//    column per token: with four, T <= 4 fits one 16-column group and T <= 8
+//    two.
 //  * One v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 A, fp8 B; the B scale of a
 //    column is the 2^-(s+4p) of its piece) then gives, for 16 rows and 128
 //    reduction elements, the signed sums of 16 piece columns (one column
-//    group; up to three groups for T <= 8).  Products of +-1 and fp8 values
+//    group; two for T = 5..8).  Products of +-1 and fp8 values
 //    are exact and accumulate in fp32 across the chunks of the span; the
 //    pieces of a token are added across lanes at the end of the tile.
 // Operand layouts of the 16x16x128 fp4 x fp8 form (measured on the device):
@@ -229,9 +234,9 @@ __device__ void finish_rows(const StageDesc& S, int rb, int ks, int64_t o, bool 
 // row), and component q feeds the MFMAs of set q.
 
 constexpr int kMfmaMaxT = 8;
-constexpr int kMaxGroupT = 3;                          // largest T whose tiles take groups of row blocks
+constexpr int kMaxGroupT = 4;                          // largest T whose tiles take groups of row blocks
 constexpr int kMRows = 512;                            // rows per tile = threads per workgroup (8 waves)
-constexpr int kPieces = 5;                            // fp8 pieces per token
+constexpr int kPieces = 4;                            // fp8 pieces per token
 constexpr int kStepWords = 4;                         // word rows per MFMA step
 constexpr int kChunkSteps = 8;                        // steps per staged chunk
 constexpr int kChunkWords = kChunkSteps * kStepWords;  // 32 word rows
@@ -242,8 +247,7 @@ constexpr int kPrepGroups = kMRows / 256;            // work items per round of 
 constexpr int kPrepItemsSeq = 8;                      // work items per input-piece tile: sequences
 constexpr int kPrepItemsSingle = kPrepGroups;         // and single calls (one round)
 // B columns are (token t, piece p) -> t*kPieces + p; every 16 of them form
-// one MFMA column group (T*kPieces columns: 1 group up to T = 3, 2 up to 6,
-// 3 up to 8).
+// one MFMA column group (T*kPieces columns: 1 group up to T = 4, 2 up to 8).
 template <int T>
 constexpr int col_groups() { return (T * kPieces + 15) / 16; }
 // Steps of sign words in flight per lane: 4 (16 KB per wave).  8 kept twice
@@ -254,17 +258,29 @@ template <int T>
 constexpr int ring_steps() { return kRingSteps; }
 // LDS of a workgroup, in 4-byte words: [B fragments, two chunk buffers of
 // kChunkSteps x col_groups x kStepInts] [chunk scale exponents, two buffers of
-// T] [per-chunk maxima of an input-piece tile] [row sums [T][kMRows]]
+// T] [per-round maxima of an input-piece tile] [row sums [T][kMRows]] [two
+// shared flag words].  Stores that only keep loads out of branches (blocks
+// past a chunk's last, scale exponents of threads past T) go to the row sums,
+// which are unused until a row block's end.
+// T = 8 (kSumsInB) keeps its row sums in the first chunk buffer instead and
+// those stores in a region of their own: two workgroups then fit a CU's
+// 160 KB.  That buffer is free at a tile's end (one row block per tile, the
+// last chunk read before the barrier that ends the loop) and, with all 32
+// columns used, has no zero columns to keep (see mfma_lds_init).
 template <int T>
 constexpr int b_ints() { return kChunkSteps * col_groups<T>() * kStepInts; }
+template <int T>
+constexpr bool sums_in_b() { return T > kMaxGroupT && T * kPieces == 16 * col_groups<T>(); }
 template <int T>
 constexpr int sig_off() { return 2 * b_ints<T>(); }
 template <int T>
 constexpr int slot_off() { return sig_off<T>() + 2 * T; }
 template <int T>
-constexpr int sum_off() { return slot_off<T>() + 2 * kPrepGroups * T; }
+constexpr int sum_off() { return sums_in_b<T>() ? 0 : slot_off<T>() + 2 * kPrepGroups; }
 template <int T>
-constexpr int flag_off() { return sum_off<T>() + T * kMRows; }  // two shared words: s_flag, s_tile
+constexpr int dummy_off() { return sums_in_b<T>() ? slot_off<T>() + 2 * kPrepGroups : sum_off<T>(); }
+template <int T>
+constexpr int flag_off() { return dummy_off<T>() + kMRows * (sums_in_b<T>() ? 1 : T); }  // s_flag, s_tile
 template <int T>
 constexpr int mfma_lds() { return flag_off<T>() + 4; }
 
@@ -318,14 +334,15 @@ __device__ inline void piece_chunk_max(const StageDesc& S, const PieceIn& in, in
 }
 
 // Scale exponent s for a chunk maximum (float bits): max * 2^s in [64, 128).
-// s is capped at 107 so that the MFMA scale of the last piece, 2^-(s+20),
-// stays within the E8M0 range; only chunks whose largest |v| is below 2^-81
-// start below 64 and so keep fewer significant bits.  A non-finite maximum
+// s is capped at 115 so that the MFMA scale of the last piece,
+// 2^-(s+4(kPieces-1)), stays within the E8M0 range; only chunks whose largest
+// |v| is below 2^-89 start below 64 and so keep fewer significant bits.  A non-finite maximum
 // gives kShiftNaN: the chunk's pieces are NaN.
 constexpr int kShiftNaN = 1 << 20;
+constexpr int kMaxShift = 127 - 4 * (kPieces - 1);
 __device__ inline int chunk_shift(unsigned mbits) {
   const int e = (int)((mbits >> 23) & 0xFF);
-  return e == 255 ? kShiftNaN : min(133 - e, 107);
+  return e == 255 ? kShiftNaN : min(133 - e, kMaxShift);
 }
 
 // The 16x16x128 fp4 x fp8 MFMA adds each group of 8 consecutive products
@@ -546,9 +563,8 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
 
   // This thread's compact blocks of a chunk (see mfma_prep_tile) and their
   // LDS places.  Every thread loads NBT blocks (past the chunk's last block:
-  // the last one again, written to the row-sum area, unused until the tile's
-  // end) and the chunk's scale exponents, so no branch surrounds the
-  // loads.  Chunk c+1 is loaded during chunk c and written to the other LDS
+  // the last one again, written to the dummy region of the LDS layout) and
+  // the chunk's scale exponents, so no branch surrounds the loads.  Chunk c+1 is loaded during chunk c and written to the other LDS
   // buffer half-way through it (the loads are then waited for with the sign
   // words issued after them still in flight); one barrier per chunk.  A chunk
   // past the stage's last loads the last one again.
@@ -561,7 +577,7 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
     const int bi = tid + m * kMRows;
     const int n = bi % NC, rest = bi / NC;
     const int g = rest % 4, h = (rest / 4) % 2, kk = rest / 8;
-    lds_at[m] = bi < NB ? (kk * G + n / 16) * kStepInts + h * 256 + (n % 16 + 16 * g) * 4 : sum_off<T>();
+    lds_at[m] = bi < NB ? (kk * G + n / 16) * kStepInts + h * 256 + (n % 16 + 16 * g) * 4 : dummy_off<T>();
     blk_at[m] = min(bi, NB - 1);
   }
   const int chunk0 = (int)(span0 / (kChunkWords * kWordBits));
@@ -578,10 +594,9 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   auto store_chunk = [&](int buf) {
 #pragma unroll
     for (int m = 0; m < NBT; ++m) *reinterpret_cast<u32x4*>(lds + buf * b_ints<T>() + lds_at[m]) = blk[m];
-    // every thread stores (threads past T into the row-sum area, unused until
-    // the tile's end), so the compiler cannot move the load into a branch
-    // behind later sign-word loads
-    lds[tid < T ? sig_off<T>() + buf * T + tid : sum_off<T>() + tid] = sig;
+    // every thread stores (threads past T into the dummy region), so the
+    // compiler cannot move the load into a branch behind later sign-word loads
+    lds[tid < T ? sig_off<T>() + buf * T + tid : dummy_off<T>() + tid] = sig;
   };
   // the first sign words do not depend on the stage input: in flight while
   // the wait and the first chunk's pieces complete (loads complete in issue
@@ -721,12 +736,12 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   if constexpr (!kGroups) finish_rb(0);
 }
 
-// With one or two column groups: 4 waves per SIMD (at most 128 VGPRs) and 2
-// workgroups per CU (two groups: a half-deep ring and B fragments read at
-// their step make room for the second group's accumulators); with three
-// (74-115 KB of LDS) 2 waves per SIMD, one workgroup per CU.
+// 4 waves per SIMD (at most 128 VGPRs) and 2 workgroups per CU for every T
+// (with two column groups B fragments are read at their own step, to make
+// room for the second group's accumulators).
 template <int T>
-constexpr int min_waves() { return col_groups<T>() <= 2 ? 4 : 2; }
+constexpr int min_waves() { return 4; }
+static_assert(col_groups<kMfmaMaxT>() <= 2, "T <= 8 in two column groups");
 
 template <int T>
 __device__ inline void stage_tile(const StageDesc& S, int local, float* lds, int* s_flag, int* err, NextTile& next) {

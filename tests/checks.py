@@ -62,9 +62,9 @@ def gamma(T: int, x_dtype: str, d_in: int, r: int) -> float:
     of at most u_in * sum |v| in total, and each stage's fp32 accumulation
     adds at most n * U32 * sum |terms| (n sequential additions); stage 2 sums
     r terms each bounded by sum_j |z_j|, which gives the factor r inside A.
-      decode (T <= 8): a stage input is carried by fp8 pieces to 2^-20 of its
+      decode (T <= 8): a stage input is carried by fp8 pieces to 2^-16 of its
         1024-element chunk's largest value, so the chunk's errors add to at
-        most 1024 * 2^-20 = 2^-10 of the chunk's sum of |v|; u_in = 2^-10 + U32
+        most 1024 * 2^-16 = 2^-6 of the chunk's sum of |v|; u_in = 2^-6 + U32
         (the s2 * x product); up to two roundings per 128-element step, plus
         the lane and span sums: n = 2 * ceil(n_red / 128) + 16.
       GEMM regime: activations rounded to fp16 after a power-of-two row scale
@@ -79,7 +79,7 @@ def gamma(T: int, x_dtype: str, d_in: int, r: int) -> float:
     def n_mfma(n):
         return 16 * (-(-n // 16) + 64)
     if T <= 8:
-        u_in = 2.0 ** -10 + U32
+        u_in = 2.0 ** -6 + U32
         n = n_dec(d_in) + n_dec(r)
     else:
         u_in = (2.0 ** -11 + 2.0 ** -20) if x_dtype == "bf16" else 2.0 ** -21
