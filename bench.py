@@ -678,7 +678,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=40,
-                    help="untimed steps first; the chip takes ~30 ms of this load to settle its clocks")
+                    help="untimed steps first; launches after an idle gap run up to 40%% slower for ~30 ms")
     ap.add_argument("--layers", type=int, default=80, help="decoder layers in the stack (80 = Llama-2-70B)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-055", action="store_true")
