@@ -747,6 +747,9 @@ def main() -> int:
     log("[bench] decode T=1")
     ms, seq, xs, ys = time_decode(stack, T, args.steps, args.warmup, device)
     bytes_step = algorithmic_bytes(stack.shapes, T)
+    import sub_bit_weight_amd as nq
+    head_bits = (sum(nq.storage_bits(sh.d_out, sh.d_in, sh.r) for sh in stack.shapes)
+                 / sum(sh.d_out * sh.d_in for sh in stack.shapes))
     gbs = bytes_step / (ms * 1e-3) / 1e9
     log(f"[bench] decode {ms:.3f} ms/step, {gbs:.0f} GB/s (one persistent-kernel launch per step)")
     parity = stack_parity(stack, xs, ys, STACK_PICKS)
@@ -857,7 +860,7 @@ def main() -> int:
         sweep = []
         for frac in (0.25, 0.5, 0.75, 1.0, 1.5, 2.0):
             if frac == 1.0:  # the headline stack
-                sweep.append({"rank_frac": 1.0, "bits_per_weight": None, "ms_per_step": ms,
+                sweep.append({"rank_frac": 1.0, "bits_per_weight": head_bits, "ms_per_step": ms,
                               "tokens_per_s": 1000.0 / ms, "hbm_gbs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
                               "algorithmic_bytes": bytes_step, "parity": parity, "note": "the headline run"})
                 continue
