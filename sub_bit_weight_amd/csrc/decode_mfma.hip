@@ -196,7 +196,7 @@ __device__ void finish_rows(const StageDesc& S, int rb, int ks, int64_t o, bool 
 //  * A sign word becomes four dwords of fp4 (e2m1) values: dword j holds, in
 //    nibble i, element 4i+3-j as +1.0 (0x2) or -1.0 (0xA): the word doubled j
 //    times, masked to bit 3 of every nibble, ORed with 0x2 in every nibble.
-//    That is eleven full-rate VALU operations per word.
+//    That is seven full-rate VALU operations per word.
 //  * The inputs v = colscale (.) x are cut into fp8 (e4m3) pieces:
 //    v * 2^s = q0 + q1/16 + q2/256 + ... (each q the round-to-nearest fp8 of
 //    the scaled remainder), kPieces per token, each piece a matrix column.
@@ -483,13 +483,34 @@ __device__ inline uint32_t twice(uint32_t x) {
   return y;
 }
 
-__device__ inline v8i expand_word(uint32_t x) {
+// The two constants of the expansion, held in registers for the whole tile:
+// as literals the mask and the OR cannot share one instruction (a three-operand
+// VALU instruction takes no literal here), and the compiler would issue them
+// as two.  Made by asm so that they are not rematerialised at every use.
+struct ExpandConsts {
+  uint32_t mask;  // SGPR: 0x88888888, the sign bit of every nibble
+  uint32_t one;   // VGPR: 0x22222222, +1.0 in every nibble
+};
+__device__ inline ExpandConsts expand_consts() {
+  ExpandConsts c;
+  asm volatile("s_mov_b32 %0, 0x88888888" : "=s"(c.mask));
+  asm volatile("v_mov_b32 %0, 0x22222222" : "=v"(c.one));
+  return c;
+}
+__device__ inline uint32_t and_or(uint32_t x, const ExpandConsts& c) {
+  uint32_t y;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(y) : "v"(x), "s"(c.mask), "v"(c.one));
+  return y;
+}
+
+// Seven full-rate VALU instructions per word: three doublings, four AND-ORs.
+__device__ inline v8i expand_word(uint32_t x, const ExpandConsts& c) {
   const uint32_t x1 = twice(x), x2 = twice(x1), x3 = twice(x2);
   v8i a;
-  a[0] = (int)((x & 0x88888888u) | 0x22222222u);
-  a[1] = (int)((x1 & 0x88888888u) | 0x22222222u);
-  a[2] = (int)((x2 & 0x88888888u) | 0x22222222u);
-  a[3] = (int)((x3 & 0x88888888u) | 0x22222222u);
+  a[0] = (int)and_or(x, c);
+  a[1] = (int)and_or(x1, c);
+  a[2] = (int)and_or(x2, c);
+  a[3] = (int)and_or(x3, c);
   a[4] = a[5] = a[6] = a[7] = 0;
   return a;
 }
@@ -611,6 +632,7 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   store_chunk(0);
   __syncthreads();  // chunk 0's fragments are in LDS buffer 0
 
+  const ExpandConsts xc = expand_consts();
   // the sums of all chunks accumulate in acc: each chunk's B column (token t,
   // piece p) carries the MFMA scale 2^-(s_t + 4p) of that chunk
   v4f acc[4][G];
@@ -709,7 +731,7 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
       if (k < nk) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const v8i a = expand_word(ring[kk % R][q]);
+          const v8i a = expand_word(ring[kk % R][q], xc);
 #pragma unroll
           for (int cg = 0; cg < G; ++cg)
             acc[q][cg] =
