@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16/bf16 matrix cores, TFLOP/s
+WARM_MS = 100.0               # untimed GPU time before the secondary legs: launches after an idle gap run slower
 DECODE_SRC = os.path.join(ROOT, "sub_bit_weight_amd", "csrc", "decode_mfma.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_persistent_70b_stack_hbm_traffic.md")
 
@@ -115,7 +116,10 @@ def measured_traffic():
         return None
 
 
-def time_decode(stack, T: int, steps: int, warmup: int, device: str):
+def time_decode(stack, T: int, steps: int, warmup: int, device: str, min_warm_ms: float = 0.0):
+    """ms per step of one sequence plan over the stack, after `warmup` untimed
+    steps (more if needed to fill `min_warm_ms`: launches after an idle gap run
+    slower for ~30 ms)."""
     import torch
 
     import sub_bit_weight_amd as nq
@@ -125,7 +129,8 @@ def time_decode(stack, T: int, steps: int, warmup: int, device: str):
     xs = [xs_by_din[s.d_in] for s in stack.shapes]
     ys = [torch.empty((T, s.d_out), dtype=torch.float32, device=device) for s in stack.shapes]
     seq = nq.Seq(stack.layers, xs, ys)
-    for _ in range(warmup):
+    warm = _warm(seq.run, warmup, min_warm_ms)
+    for _ in range(warm):
         seq.run()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -136,6 +141,22 @@ def time_decode(stack, T: int, steps: int, warmup: int, device: str):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     return ms, seq, xs, ys
+
+
+def _warm(fn, n: int, min_ms: float) -> int:
+    """Untimed calls still to make: n, or enough to fill min_ms of GPU time
+    (one synchronized call measures the duration); the measuring call counts."""
+    if min_ms <= 0:
+        return n
+    import time
+
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    ms = max((time.perf_counter() - t0) * 1e3, 1e-3)
+    return max(n - 1, int(min_ms / ms))
 
 
 def _summ(checks: list) -> dict:
@@ -252,7 +273,8 @@ def time_scale_grads(stack, T: int, device: str, reps: int = 3) -> dict:
         for L, (ut, v) in zip(layers, outs):
             nq.transpose_signs(L.u_bits, L.d_out, L.r, out=ut)
             nq.transpose_signs(L.vt_bits, L.r, L.d_in, out=v)
-    transpose_all()
+    for _ in range(_warm(transpose_all, 1, WARM_MS)):
+        transpose_all()
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
@@ -263,13 +285,15 @@ def time_scale_grads(stack, T: int, device: str, reps: int = 3) -> dict:
     adjs = [nq.Adjoint(ut, v) for ut, v in outs]
     t_bytes = sum(2 * (L.u_bits.numel() + L.vt_bits.numel()) * 4 for L in layers)  # read + write
     ws = torch.empty(max(nq.lrb_scale_grads_workspace_bytes(L, T) for L in layers), dtype=torch.uint8, device=device)
-    for L, a, x, g in zip(layers, adjs, xs, gs):  # warm-up pass
-        nq.lrb_scale_grads(L, a, x, g, workspace=ws)
+    def grads_all():
+        for L, a, x, g in zip(layers, adjs, xs, gs):
+            nq.lrb_scale_grads(L, a, x, g, workspace=ws)
+    for _ in range(_warm(grads_all, 1, WARM_MS)):
+        grads_all()
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
-        for L, a, x, g in zip(layers, adjs, xs, gs):
-            nq.lrb_scale_grads(L, a, x, g, workspace=ws)
+        grads_all()
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
@@ -324,7 +348,8 @@ def time_balance(shapes, device: str, reps: int = 5) -> dict:
     res = {}
     lat_bytes = sum((s.d_out + s.d_in) * s.r * 4 for s in shapes)
     for balanced, nbytes in ((True, 3 * lat_bytes), (False, lat_bytes)):
-        run(balanced)
+        for _ in range(_warm(lambda: run(balanced), 1, WARM_MS)):
+            run(balanced)
         torch.cuda.synchronize()
         e0.record()
         for _ in range(reps):
@@ -372,7 +397,8 @@ def time_latent(shapes, device: str, reps: int = 5) -> dict:
         def run():
             for (u, v, s1, s2), x, y in zip(lat, xs, ys):
                 nq.lrb_linear_latent(u, v, s1, s2, x, y=y, workspace=ws)
-        run()
+        for _ in range(_warm(run, 1, WARM_MS)):
+            run()
         torch.cuda.synchronize()
         e0.record()
         for _ in range(reps):
@@ -428,7 +454,8 @@ def time_single_configs(device: str, reps: int = 200) -> dict:
         return torch.cuda.Event(enable_timing=True)
 
     def timed(fn, n):
-        fn()
+        for _ in range(_warm(fn, 1, WARM_MS)):  # past the first ~30 ms after an idle gap
+            fn()
         torch.cuda.synchronize()
         a, b = ev(), ev()
         a.record()
@@ -525,7 +552,7 @@ def time_single_configs(device: str, reps: int = 200) -> dict:
             seq_shapes = [s for _ in sets for s in cfg.layers]
             ys = [torch.empty((T, s.d_out), device=device) for s in seq_shapes]
             seq = nq.Seq(seq_layers, [xd[s.d_in] for s in seq_shapes], ys)
-            seq_ms = timed(seq.run, 10)
+            seq_ms = timed(seq.run, 50)
             assert seq.device_error() == 0
             nl = len(cfg.layers)
             par += [C.full_check(ys[i].cpu().numpy(), C.latent_ref(cfg, s), xs[s.d_in], 1e-5, "bf16", factored=True)
@@ -763,7 +790,7 @@ def main() -> int:
         # (one decoder layer): little overlap across layers
         os.environ["NQ_SEQ_LAG"] = "7"
         try:
-            ms7, seq7, xs7, ys7 = time_decode(stack, T, args.steps, args.warmup, device)
+            ms7, seq7, xs7, ys7 = time_decode(stack, T, args.steps, args.warmup, device, WARM_MS)
         finally:
             del os.environ["NQ_SEQ_LAG"]
         p7 = stack_parity(stack, xs7, ys7, STACK_PICKS[:2])
@@ -837,7 +864,7 @@ def main() -> int:
     def stack_leg(frac, picks):
         cfgf = synth.stack_config(frac)
         stf = Stack(cfgf, args.layers, device)
-        msf, seqf, xsf, ysf = time_decode(stf, 1, args.steps, args.warmup, device)
+        msf, seqf, xsf, ysf = time_decode(stf, 1, args.steps, args.warmup, device, WARM_MS)
         bf = algorithmic_bytes(stf.shapes, 1)
         weights = sum(sh.d_out * sh.d_in for sh in stf.shapes)
         import sub_bit_weight_amd as nq
