@@ -585,10 +585,14 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   // This thread's compact blocks of a chunk (see mfma_prep_tile) and their
   // LDS places.  Every thread loads NBT blocks (past the chunk's last block:
   // the last one again, written to the dummy region of the LDS layout) and
-  // the chunk's scale exponents, so no branch surrounds the loads.  Chunk c+1 is loaded during chunk c and written to the other LDS
-  // buffer half-way through it (the loads are then waited for with the sign
-  // words issued after them still in flight); one barrier per chunk.  A chunk
-  // past the stage's last loads the last one again.
+  // the chunk's scale exponents, so no branch surrounds the loads.  Chunk c+1
+  // is copied into the other LDS buffer during chunk c in two halves of the
+  // blocks: the first loaded at the chunk's start and written at step 2, the
+  // second loaded then and written at step 6 (the loads are waited for with
+  // the sign words issued after them still in flight); one barrier per chunk.
+  // Half the blocks in registers at a time leaves T >= 7 fewer spills (measured
+  // +2 % at T = 7, 8; one half at the chunk's middle measured the same for
+  // T <= 6).  A chunk past the stage's last loads the last one again.
   constexpr int NB = chunk_blocks<T>();
   constexpr int NBT = (NB + kMRows - 1) / kMRows;  // blocks per thread
   constexpr int NC = T * kPieces;
@@ -604,17 +608,21 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   const int chunk0 = (int)(span0 / (kChunkWords * kWordBits));
   const int last_chunk = (int)((S.n_red - 1) / (kChunkWords * kWordBits));
   const u32x4* bsrc = reinterpret_cast<const u32x4*>(S.bfrag);
-  u32x4 blk[NBT];
+  constexpr int NH = (NBT + 1) / 2;  // blocks per thread and half
+  u32x4 blk[NH];
   int sig;
-  auto load_chunk = [&](int ch) {
+  auto load_half = [&](int ch, int hh) {
     ch = min(ch, last_chunk);
 #pragma unroll
-    for (int m = 0; m < NBT; ++m) blk[m] = gload(bsrc + (int64_t)ch * NB + blk_at[m]);
-    sig = gload(S.bsig + (int64_t)ch * T + min(tid, T - 1));
+    for (int m = 0; m < NH; ++m)
+      if (hh * NH + m < NBT) blk[m] = gload(bsrc + (int64_t)ch * NB + blk_at[hh * NH + m]);
+    if (hh == 0) sig = gload(S.bsig + (int64_t)ch * T + min(tid, T - 1));
   };
-  auto store_chunk = [&](int buf) {
+  auto store_half = [&](int buf, int hh) {
 #pragma unroll
-    for (int m = 0; m < NBT; ++m) *reinterpret_cast<u32x4*>(lds + buf * b_ints<T>() + lds_at[m]) = blk[m];
+    for (int m = 0; m < NH; ++m)
+      if (hh * NH + m < NBT) *reinterpret_cast<u32x4*>(lds + buf * b_ints<T>() + lds_at[hh * NH + m]) = blk[m];
+    if (hh != 0) return;
     // every thread stores (threads past T into the dummy region), so the
     // compiler cannot move the load into a branch behind later sign-word loads
     lds[tid < T ? sig_off<T>() + buf * T + tid : dummy_off<T>() + tid] = sig;
@@ -628,8 +636,10 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
 #pragma unroll
   for (int k = 0; k < R; ++k) load_step(0, k, ring[k]);
   wait_input(S, err);  // the stage's pieces are final
-  load_chunk(chunk0);
-  store_chunk(0);
+  load_half(chunk0, 0);
+  store_half(0, 0);
+  load_half(chunk0, 1);
+  store_half(0, 1);
   __syncthreads();  // chunk 0's fragments are in LDS buffer 0
 
   const ExpandConsts xc = expand_consts();
@@ -696,7 +706,8 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
       const int sg = lds[sig_off<T>() + buf * T + min(tc, T - 1)];
       bscale[cg] = tc < T ? 127 - (sg == kShiftNaN ? 0 : sg) - 4 * pc : 127;
     }
-    load_chunk(chunk0 + (c + 1 < nchunks ? c + 1 : 0));  // next chunk's pieces (the next row block's first)
+    const int nxt_chunk = chunk0 + (c + 1 < nchunks ? c + 1 : 0);
+    load_half(nxt_chunk, 0);  // next chunk's pieces (the next row block's first)
 
     const u32x4* bfrag = reinterpret_cast<const u32x4*>(lds + buf * b_ints<T>()) + lane;
     // B fragments: with one column group the next step's are read a step ahead;
@@ -743,7 +754,11 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
       // block: out of range, no memory access); no branch around the load
       const bool next_rb = kk + R >= kChunkSteps && c + 1 == nchunks;
       load_step(next_rb ? ri + 1 : ri, next_rb ? kk + R - kChunkSteps : k + R, ring[kk % R]);
-      if (kk == kChunkSteps / 2) store_chunk(buf ^ 1);    // the other buffer was last read in chunk vc-1
+      if (kk == 2) {  // the other buffer was last read in chunk vc-1
+        store_half(buf ^ 1, 0);
+        load_half(nxt_chunk, 1);
+      }
+      if (kk == 6) store_half(buf ^ 1, 1);
     }
     __syncthreads();  // chunk vc+1's fragments are in LDS; every wave is done with chunk vc's
     if (c + 1 < nchunks) {
