@@ -243,9 +243,7 @@ constexpr int kChunkWords = kChunkSteps * kStepWords;  // 32 word rows
 constexpr int kRingSteps = 4;                         // steps of sign words in flight per lane
 static_assert(kChunkSteps % kRingSteps == 0, "ring slots are compile-time within a chunk");
 constexpr int kStepInts = 64 * 8;                     // B fragments of one step and MFMA (64 lanes x 32 bytes)
-constexpr int kPrepGroups = kMRows / 256;            // work items per round of an input-piece tile
-constexpr int kPrepItemsSeq = 8;                      // work items per input-piece tile: sequences
-constexpr int kPrepItemsSingle = kPrepGroups;         // and single calls (one round)
+constexpr int kPrepGroups = kMRows / 256;            // chunks per round of an input-piece tile
 // B columns are (token t, piece p) -> t*kPieces + p; every 16 of them form
 // one MFMA column group (T*kPieces columns: 1 group up to T = 4, 2 up to 8).
 template <int T>
@@ -258,8 +256,8 @@ template <int T>
 constexpr int ring_steps() { return kRingSteps; }
 // LDS of a workgroup, in 4-byte words: [B fragments, two chunk buffers of
 // kChunkSteps x col_groups x kStepInts] [chunk scale exponents, two buffers of
-// T] [per-round maxima of an input-piece tile] [row sums [T][kMRows]] [two
-// shared flag words].  Stores that only keep loads out of branches (blocks
+// T] [per-round maxima of an input-piece tile, [2][kPrepGroups][T]] [row sums
+// [T][kMRows], 16-byte aligned] [two shared flag words].  Stores that only keep loads out of branches (blocks
 // past a chunk's last, scale exponents of threads past T) go to the row sums,
 // which are unused until a row block's end.
 // T = 8 (kSumsInB) keeps its row sums in the first chunk buffer instead and
@@ -275,10 +273,11 @@ template <int T>
 constexpr int sig_off() { return 2 * b_ints<T>(); }
 template <int T>
 constexpr int slot_off() { return sig_off<T>() + 2 * T; }
+constexpr int align4(int x) { return (x + 3) & ~3; }
 template <int T>
-constexpr int sum_off() { return sums_in_b<T>() ? 0 : slot_off<T>() + 2 * kPrepGroups; }
+constexpr int sum_off() { return sums_in_b<T>() ? 0 : align4(slot_off<T>() + 2 * kPrepGroups * T); }
 template <int T>
-constexpr int dummy_off() { return sums_in_b<T>() ? slot_off<T>() + 2 * kPrepGroups : sum_off<T>(); }
+constexpr int dummy_off() { return sums_in_b<T>() ? align4(slot_off<T>() + 2 * kPrepGroups * T) : sum_off<T>(); }
 template <int T>
 constexpr int flag_off() { return dummy_off<T>() + kMRows * (sums_in_b<T>() ? 1 : T); }  // s_flag, s_tile
 template <int T>
@@ -287,9 +286,10 @@ constexpr int mfma_lds() { return flag_off<T>() + 4; }
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// One token's inputs for this thread's 4 elements of a chunk.
+// Every token's inputs for this thread's 4 elements of a chunk.
+template <int T>
 struct PieceIn {
-  uint32_t x[4];  // raw bf16 / fp32 bits
+  uint32_t x[T][4];  // raw bf16 / fp32 bits
   float cs[4];
 };
 
@@ -301,36 +301,46 @@ __device__ inline int task_element(int task, int k) {
   return 32 * wr + 4 * (4 * ih + k) + 3 - j;
 }
 
-// Loads of token t's inputs in a chunk.  Elements at or past cend read element
-// 0 of the token (always in bounds) and are dropped later, so the loads keep a
-// fixed count and position in the pipeline.
-__device__ inline void piece_load_inputs(const StageDesc& S, int task, int t, int64_t c0, int64_t cend, PieceIn& in) {
+// Loads of every token's inputs in a chunk (the column scales once).  Elements
+// at or past cend read element 0 of the token (always in bounds) and are
+// dropped later, so the loads keep a fixed count and position in the pipeline.
+template <int T>
+__device__ inline void piece_load_inputs(const StageDesc& S, int task, int64_t c0, int64_t cend, PieceIn<T>& in) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int64_t e = c0 + task_element(task, k);
     const int64_t ec = e < cend ? e : 0;
     in.cs[k] = S.colscale ? gload(S.colscale + ec) : 1.0f;
-    const int64_t idx = (int64_t)t * S.n_red + ec;
-    in.x[k] = S.x_bf16 ? (uint32_t)gload(static_cast<const uint16_t*>(S.xin) + idx)
-                       : gload(static_cast<const uint32_t*>(S.xin) + idx);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int64_t idx = (int64_t)t * S.n_red + ec;
+      in.x[t][k] = S.x_bf16 ? (uint32_t)gload(static_cast<const uint16_t*>(S.xin) + idx)
+                            : gload(static_cast<const uint32_t*>(S.xin) + idx);
+    }
   }
 }
 
-__device__ inline float piece_value(const StageDesc& S, const PieceIn& in, int task, int64_t c0, int64_t cend, int k) {
-  const float x = S.x_bf16 ? bf16_bits(in.x[k]) : __uint_as_float(in.x[k]);
+template <int T>
+__device__ inline float piece_value(const StageDesc& S, const PieceIn<T>& in, int t, int task, int64_t c0,
+                                    int64_t cend, int k) {
+  const float x = S.x_bf16 ? bf16_bits(in.x[t][k]) : __uint_as_float(in.x[t][k]);
   return c0 + task_element(task, k) < cend ? x * in.cs[k] : 0.0f;
 }
 
-// Largest |v| of the chunk into *slot (float bits of a non-negative value
-// order like unsigned integers; NaN orders above inf).
-__device__ inline void piece_chunk_max(const StageDesc& S, const PieceIn& in, int task, int64_t c0, int64_t cend,
+// Largest |v| of the chunk for every token into slot[t] (float bits of a
+// non-negative value order like unsigned integers; NaN orders above inf).
+template <int T>
+__device__ inline void piece_chunk_max(const StageDesc& S, const PieceIn<T>& in, int task, int64_t c0, int64_t cend,
                                        unsigned* slot) {
-  unsigned m = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) m = max(m, __float_as_uint(fabsf(piece_value(S, in, task, c0, cend, k))));
+  for (int t = 0; t < T; ++t) {
+    unsigned m = 0;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off));
-  if ((threadIdx.x & 63) == 0) atomicMax(slot, m);
+    for (int k = 0; k < 4; ++k) m = max(m, __float_as_uint(fabsf(piece_value(S, in, t, task, c0, cend, k))));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off));
+    if ((threadIdx.x & 63) == 0) atomicMax(slot + t, m);
+  }
 }
 
 // Scale exponent s for a chunk maximum (float bits): max * 2^s in [64, 128).
@@ -375,83 +385,85 @@ __device__ inline int max_fp8_exponent(int d) {
 template <int T>
 constexpr int chunk_blocks() { return kChunkSteps * 2 * 4 * T * kPieces; }
 
-// One input-piece tile: work items [S.prep_items * tile, ...) of the stage
-// input, item i being chunk i / T for token i % T.  Each group of 256 threads
-// of the workgroup takes an item per round; per item each thread makes one B
-// dword (4 consecutive reduction positions) per piece; the next round's
-// inputs load while the current ones are converted.  Items per tile trade the
-// tile count (each with its own latency, fences and barriers) against the
-// time the stage waits for its pieces: sequences take eight, single calls two
-// (one round, so the pieces of a token are ready one tile latency after the
-// launch, whatever T).
+// Chunks per input-piece tile: two per round (one per group of 256 threads),
+// every token of a chunk in the same round (the column scales are loaded once
+// and all of its loads are in flight together).  Sequences take up to four
+// rounds at T = 1 (eight chunks; fewer tiles) and one from T = 4 on; single
+// calls one round, so the pieces are ready one tile latency after the launch.
+__host__ __device__ inline int prep_chunks(int64_t T, bool single) {
+  return single || T >= 4 ? kPrepGroups : (int)(8 / T);
+}
+
+// One input-piece tile: chunks [S.prep_chunks * tile, ...) of the stage input,
+// every token.  Each group of 256 threads takes a chunk per round; per chunk
+// and token each thread makes one B dword (4 consecutive reduction positions)
+// per piece; the next round's inputs load while the current ones are converted.
 template <int T>
 __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* err, NextTile& next) {
   constexpr int NC = T * kPieces;
   constexpr int64_t kChunkElems = kChunkWords * kWordBits;
-  unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + slot_off<T>());  // [round&1][group]
+  unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + slot_off<T>());  // [round&1][group][T]
   const int tid = threadIdx.x, half = tid >> 8, task = tid & 255;  // half: this thread's group
-  const int nitems = (int)cdiv(S.n_red, kChunkElems) * T;
-  const int it0 = tile * S.prep_items;
-  const int it1 = min(it0 + S.prep_items, nitems);
+  const int nch = (int)cdiv(S.n_red, kChunkElems);
+  const int ch0 = tile * S.prep_chunks;
+  const int ch1 = min(ch0 + S.prep_chunks, nch);
   wait_input(S, err);
   const int wr = task >> 3, j = (task >> 1) & 3, ih = task & 1;
   const int kk = wr >> 2, gw = wr & 3;
   const int gp = 2 * (gw & 1) + (j >> 1);
   const int64_t task_off = (int64_t)(((kk * 2 + (gw >> 1)) * 4 + gp) * NC) * 4 + 2 * (j & 1) + ih;
-  if (tid < 2 * kPrepGroups) slots[tid] = 0;
-  // the item this group takes in a round (past the tile's last: the last item
-  // again for the loads, nothing stored)
-  auto item_of = [&](int r0) { return min(r0 + half, nitems - 1); };
-  PieceIn in, nxt;
-  {
-    const int it = item_of(it0);
-    piece_load_inputs(S, task, it % T, (int64_t)(it / T) * kChunkElems, S.n_red, in);
-  }
+  if (tid < 2 * kPrepGroups * T) slots[tid] = 0;
+  // the chunk this group takes in a round (past the tile's last: the last
+  // chunk again for the loads, nothing stored)
+  auto chunk_of = [&](int r0) { return min(r0 + half, nch - 1); };
+  PieceIn<T> in, nxt;
+  piece_load_inputs<T>(S, task, (int64_t)chunk_of(ch0) * kChunkElems, S.n_red, in);
   __syncthreads();
-  for (int r0 = it0, round = 0; r0 < it1; r0 += kPrepGroups, ++round) {
-    if (r0 + kPrepGroups >= it1) next.claim();  // the tile's last round
-    const bool mine = r0 + half < it1;  // wave-uniform: a group is 4 whole waves
-    const int it = item_of(r0);
-    const int ch = it / T, t = it % T;
+  for (int r0 = ch0, round = 0; r0 < ch1; r0 += kPrepGroups, ++round) {
+    const bool last = r0 + kPrepGroups >= ch1;
+    if (last) next.claim();  // the tile's last round
+    const bool mine = r0 + half < ch1;  // wave-uniform: a group is 4 whole waves
+    const int ch = chunk_of(r0);
     const int64_t c0 = ch * kChunkElems;
-    unsigned* slot = slots + (round & 1) * kPrepGroups + half;
-    piece_chunk_max(S, in, task, c0, S.n_red, slot);
-    {
-      const int itn = item_of(r0 + kPrepGroups);  // next round's item (or the last again)
-      piece_load_inputs(S, task, itn % T, (int64_t)(itn / T) * kChunkElems, S.n_red, nxt);
-    }
-    __syncthreads();  // the items' maxima are complete
+    unsigned* slot = slots + ((round & 1) * kPrepGroups + half) * T;
+    piece_chunk_max<T>(S, in, task, c0, S.n_red, slot);
+    if (!last) piece_load_inputs<T>(S, task, (int64_t)chunk_of(r0 + kPrepGroups) * kChunkElems, S.n_red, nxt);
+    __syncthreads();  // the chunks' maxima are complete
     if (mine) {
       uint32_t* dst = S.bfrag + (int64_t)ch * chunk_blocks<T>() * 4 + task_off;
-      const int shift = chunk_shift(*slot);
-      float r[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000) : ldexpf(piece_value(S, in, task, c0, S.n_red, k), shift);
+      for (int t = 0; t < T; ++t) {
+        const int shift = chunk_shift(slot[t]);
+        float r[4];
 #pragma unroll
-      for (int p = 0; p < kPieces; ++p) {
-        int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
-        d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
-        // this dword and the partner thread's (task ^ 1, same wave) form one group of 8
-        int emax = max_fp8_exponent(d);
-        emax = max(emax, __shfl_xor(emax, 1));
-        d = keep_fp8_exponents(d, max(1, emax - 7));
-        store_agent(reinterpret_cast<float*>(dst + (t * kPieces + p) * 4), __int_as_float(d));
-        if (p + 1 < kPieces) {
-          typedef float v2f __attribute__((ext_vector_type(2)));
-          const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
-          const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
-          r[0] = (r[0] - lo.x) * 16.0f;
-          r[1] = (r[1] - lo.y) * 16.0f;
-          r[2] = (r[2] - hi.x) * 16.0f;
-          r[3] = (r[3] - hi.y) * 16.0f;
+        for (int k = 0; k < 4; ++k)
+          r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000)
+                                    : ldexpf(piece_value(S, in, t, task, c0, S.n_red, k), shift);
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) {
+          int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+          d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
+          // this dword and the partner thread's (task ^ 1, same wave) form one group of 8
+          int emax = max_fp8_exponent(d);
+          emax = max(emax, __shfl_xor(emax, 1));
+          d = keep_fp8_exponents(d, max(1, emax - 7));
+          store_agent(reinterpret_cast<float*>(dst + (t * kPieces + p) * 4), __int_as_float(d));
+          if (p + 1 < kPieces) {
+            typedef float v2f __attribute__((ext_vector_type(2)));
+            const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
+            const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
+            r[0] = (r[0] - lo.x) * 16.0f;
+            r[1] = (r[1] - lo.y) * 16.0f;
+            r[2] = (r[2] - hi.x) * 16.0f;
+            r[3] = (r[3] - hi.y) * 16.0f;
+          }
         }
+        if (task == 0) store_agent(reinterpret_cast<float*>(S.bsig + (int64_t)ch * T + t), __int_as_float(shift));
       }
-      if (task == 0) store_agent(reinterpret_cast<float*>(S.bsig + (int64_t)ch * T + t), __int_as_float(shift));
     }
     __syncthreads();  // every thread has read this round's maxima
-    if (task == 0) *slot = 0;  // reused two rounds on (its maximum comes after the next barrier)
-    in = nxt;
+    if (task < T) slot[task] = 0;  // reused two rounds on (its maxima come after the next barrier)
+    if (!last) in = nxt;
   }
   if (S.signal) {
     stores_done_barrier();  // the tile's pieces are at the coherence point
@@ -515,12 +527,10 @@ __device__ inline v8i expand_word(uint32_t x, const ExpandConsts& c) {
   return a;
 }
 
-// Sum over the 16 lanes of a row of the wavefront (DPP rotations).
-__device__ inline float row16_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));  // row_ror:2
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));  // row_ror:1
+// Sum over the 4 lanes of a quad (DPP quad permutations), in every lane of it.
+__device__ inline float quad_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
   return v;
 }
 
@@ -651,29 +661,24 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
 #pragma unroll
     for (int cg = 0; cg < G; ++cg) acc[q][cg] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // row block ri is complete: add the pieces of each token across the lanes
-  // of a row (and the column groups); lane col == 0 of every row group writes
-  // its 4 rows of every set; then the rows' results, and a clear start for
-  // the next row block
+  // row block ri is complete: add the pieces of each token across the quad
+  // of lanes that holds its columns (lane col = 4 t' + p holds piece p of
+  // token 4 cg + t'), then lane 4 t' of every row group writes its 4 rows of
+  // every set; then the rows' results, and a clear start for the next row
+  // block
   auto finish_rb = [&](int ri) {
     float* sums = ldsf + sum_off<T>();
+    static_assert(kPieces == 4, "a token's pieces are one quad of lanes");
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
+    for (int cg = 0; cg < G; ++cg) {
+      const int t = 4 * cg + col / 4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {  // C row 4*grp + r of set q is row 16*grp + 4r + q of the wave
         float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float u = 0.0f;
-#pragma unroll
-          for (int cg = 0; cg < G; ++cg)
-            if ((16 * cg + 15) / kPieces >= t && (16 * cg) / kPieces <= t)  // the group holds columns of token t
-              u += (16 * cg + col) / kPieces == t ? acc[q][cg][r] : 0.0f;
-          v[q] = row16_sum(u);
-        }
-        if (col == 0)
-          *reinterpret_cast<float4*>(sums + t * kMRows + wv * 64 + grp * 16 + 4 * r) =
-              make_float4(v[0], v[1], v[2], v[3]);
+        for (int q = 0; q < 4; ++q) v[q] = quad_sum(acc[q][cg][r]);
+        if ((col & 3) == 0 && t < T)
+          *reinterpret_cast<float4*>(sums + t * kMRows + wv * 64 + grp * 16 + 4 * r) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
     __syncthreads();
@@ -1087,8 +1092,8 @@ int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
     pc.kind = 1;
     pc.bfrag = reinterpret_cast<uint32_t*>(buf);
     pc.bsig = reinterpret_cast<int*>(buf + align_up((size_t)nch * 64 * T * kPieces * 16));
-    pc.prep_items = split ? kPrepItemsSingle : kPrepItemsSeq;
-    pc.nrb = (int)cdiv(nch * T, pc.prep_items);  // tiles
+    pc.prep_chunks = prep_chunks(T, split);
+    pc.nrb = (int)cdiv(nch, pc.prep_chunks);  // tiles
     pc.rb_group = 1;
     pc.nks = 1;
     pc.signal = ready;
