@@ -913,10 +913,11 @@ def main() -> int:
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic()},
         # The decode kernel's compute ceilings at 2.4 GHz: one 16x16x128
-        # fp4 x fp8 MFMA (32 cycles) per 64 sign words and SIMD; 11 full-rate
-        # VALU ops (2 cycles per wave64 op) per word expansion.
+        # fp4 x fp8 MFMA (32 cycles) per 64 sign words and SIMD; 7 full-rate
+        # VALU ops (2 cycles per wave64 op) per word expansion (the whole
+        # kernel issues 9.7 VALU instructions per 64 words, MFMAs included).
         "decode_mfma_ceiling_gbs": 256 * 4 * 2.4e9 / 32 * 256 / 1e9,
-        "decode_valu_ceiling_gbs": 256 * 4 * 2.4e9 / (11 * 2) * 256 / 1e9,
+        "decode_valu_ceiling_gbs": 256 * 4 * 2.4e9 / (7 * 2) * 256 / 1e9,
         "parity": parity,
     }
     out.update(extra)
