@@ -57,7 +57,11 @@ typedef enum {
   NQ_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed           */
 } nq_status;
 
-typedef enum { NQ_F32 = 0, NQ_BF16 = 1 } nq_dtype;
+/* Element type of an activation buffer: NQ_F32 or NQ_BF16.  A plain 32-bit
+   integer rather than an enum type, so that any value a caller passes is
+   well defined in the library (anything else is rejected with NQ_ERR_ARG). */
+typedef int32_t nq_dtype;
+enum { NQ_F32 = 0, NQ_BF16 = 1 };
 
 /* One packed LRB matrix.  A host struct, read only during a call. */
 typedef struct {

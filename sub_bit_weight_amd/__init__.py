@@ -19,7 +19,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libnq.so")
+# NQ_LIBRARY selects another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("NQ_LIBRARY") or os.path.join(_HERE, "libnq.so")
 
 NQ_OK, NQ_ERR_ARG, NQ_ERR_UNSUPPORTED, NQ_ERR_WORKSPACE, NQ_ERR_HIP = range(5)
 NQ_F32, NQ_BF16 = 0, 1

@@ -250,3 +250,53 @@ def test_noalloc_host_checks():
     assert lib.nq_lrb_workspace_bytes(ctypes.byref(big), 64) > nq.NOALLOC_SCRATCH_BYTES
     assert call(big, T=64) == nq.NQ_ERR_UNSUPPORTED
     assert "scratch" in nq.last_error()
+
+
+# Shapes for the host planners: odd and tiny sizes, the 7B and 70B layer
+# shapes, and the rank-sweep extremes.
+PLAN_SHAPES = [(1, 1, 1), (33, 70, 3), (256, 256, 64), (320, 4096, 1088), (4096, 4096, 2048),
+               (11008, 4096, 2368), (4096, 11008, 2368), (1024, 8192, 896), (28672, 8192, 6336),
+               (8192, 28672, 6336), (8192, 8192, 12672)]
+PLAN_T = [1, 2, 3, 4, 5, 7, 8, 9, 16, 63, 64, 65, 2048, 66000]
+
+
+def _packed(d_out, d_in, r):
+    return _layer(d_out=d_out, d_in=d_in, r=r, ldu=d_out, ldv=r)
+
+
+def test_workspace_queries_over_shapes():
+    """Every workspace query and sequence plan over a grid of shapes and token
+    counts: no failure, sizes that grow with T, and a plan per T (the queries
+    walk the tile and split planners, which run on the host alone)."""
+    lib = nq.lib()
+    for d_out, d_in, r in PLAN_SHAPES:
+        L = _packed(d_out, d_in, r)
+        prev = 0
+        for T in PLAN_T:
+            w = lib.nq_lrb_workspace_bytes(ctypes.byref(L), T)
+            g = lib.nq_lrb_scale_grads_workspace_bytes(ctypes.byref(L), T)
+            lat = lib.nq_lrb_latent_workspace_bytes(d_out, d_in, r, T)
+            assert w > 0 and g >= w and lat > 0, (d_out, d_in, r, T)
+            assert w < (1 << 40) and g < (1 << 40) and lat < (1 << 40)
+            if T > 8:  # the matrix-core regime keeps per-token buffers
+                assert w >= prev, (d_out, d_in, r, T)
+                prev = w
+        assert lib.nq_balance_workspace_bytes(d_out, d_in) > 0
+    for T in PLAN_T:
+        layers = (nq.nq_lrb * len(PLAN_SHAPES))(*[_packed(*s) for s in PLAN_SHAPES])
+        xs = (ctypes.c_void_p * len(PLAN_SHAPES))(*([DUMMY] * len(PLAN_SHAPES)))
+        ys = (ctypes.c_void_p * len(PLAN_SHAPES))(*([DUMMY] * len(PLAN_SHAPES)))
+        h = ctypes.c_void_p()
+        assert lib.nq_seq_create(layers, xs, ys, len(PLAN_SHAPES), nq.NQ_BF16, T, ctypes.byref(h)) == nq.NQ_OK, \
+            (T, nq.last_error())
+        assert 0 < lib.nq_seq_workspace_bytes(h) < (1 << 42)
+        lib.nq_seq_destroy(h)
+
+
+@pytest.mark.parametrize("dtype", [-1, 2, 7, 1 << 30, -(1 << 31)])
+def test_every_dtype_value_is_checked(dtype):
+    """Any 32-bit value in a dtype argument is either accepted or rejected on
+    the host (the type is a plain int32, so out-of-range values are defined)."""
+    lib = nq.lib()
+    assert _linear(_layer(), dtype=dtype) == nq.NQ_ERR_ARG
+    assert lib.nq_lrb_linear_noalloc(ctypes.byref(_layer()), DUMMY, dtype, 1, DUMMY, None) == nq.NQ_ERR_ARG
