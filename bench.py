@@ -374,10 +374,10 @@ def time_balance(shapes, device: str, reps: int = 5) -> dict:
 
 
 def time_latent(shapes, device: str, reps: int = 5) -> dict:
-    """The refinement forward from fp32 latent factors (signs packed at the
-    call, then the packed layer) over layer 0's linears, at T=1 and T=2048
-    (bf16 x).  At T=1 the latents dominate the bytes: GB/s counts the latent
-    reads, the packed words written and read back, x and y."""
+    """The refinement forward from fp32 latent factors over layer 0's linears,
+    at T=1 (signs applied as the latents load: GB/s counts the latent reads,
+    the scales, x and y) and T=2048 (signs packed at the call, then the packed
+    layer: the bytes add the packed words written and read back)."""
     import torch
 
     import sub_bit_weight_amd as nq
@@ -406,8 +406,9 @@ def time_latent(shapes, device: str, reps: int = 5) -> dict:
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
-        nbytes = sum((s.d_out + s.d_in) * s.r * 4 + 2 * (s.d_out + s.d_in) * s.r // 8 + T * (2 * s.d_in + 4 * s.d_out)
-                     for s in shapes)
+        # T > 8: the packed words are written and read back
+        nbytes = sum((s.d_out + s.d_in) * s.r * 4 + (0 if T <= 8 else 2 * (s.d_out + s.d_in) * s.r // 8)
+                     + 4 * (s.d_out + s.d_in) + T * (2 * s.d_in + 4 * s.d_out) for s in shapes)
         flops = sum(2 * T * s.r * (s.d_in + s.d_out) for s in shapes)
         # parity of the timed calls' outputs: the k linear (every output)
         from oracle import nq_oracle as O

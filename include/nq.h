@@ -231,14 +231,18 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
  *   pass of the factorized component refinement (section 3 "Step 3:
  *   Factorized Component Refinement", where the binary factors are sign(U) and
  *   sign(V) of latents that the refinement keeps updating).  sign() as in
- *   nq_pack_signs (-1 only for values < 0).  The latents are packed into the
- *   workspace, then the packed layer runs as in nq_lrb_linear: y equals
- *   nq_pack_signs followed by nq_lrb_linear bit for bit.
+ *   nq_pack_signs (-1 only for values < 0).  T <= 8: the two stages read the
+ *   fp32 latents once and apply sign() as they load (no packed words), fp32
+ *   sums in a fixed order.  T > 8: the latents are packed into the workspace,
+ *   then the packed layer runs as in nq_lrb_linear: y equals nq_pack_signs
+ *   followed by nq_lrb_linear bit for bit.
  *   u_lat: [d_out][ldu_lat] fp32 (row i's r entries first), v_lat:
  *   [d_in][ldv_lat] fp32; s1, s2, x, x_dtype, T, y as for nq_lrb_linear.
  *   workspace: at least nq_lrb_latent_workspace_bytes(d_out, d_in, r, T)
  *   bytes, 256-byte aligned.  Errors: NQ_ERR_ARG for null or misaligned
- *   latents, sizes < 1, ldu_lat or ldv_lat < r; otherwise as nq_lrb_linear.
+ *   latents, sizes < 1, ldu_lat or ldv_lat < r; NQ_ERR_UNSUPPORTED at T <= 8
+ *   for shapes whose launch grid would exceed 65535 reduction spans;
+ *   otherwise as nq_lrb_linear.
  */
 size_t nq_lrb_latent_workspace_bytes(int64_t d_out, int64_t d_in, int64_t r, int64_t T);
 nq_status nq_lrb_linear_latent(const float* u_lat, int64_t ldu_lat, const float* v_lat,

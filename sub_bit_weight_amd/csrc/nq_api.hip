@@ -349,6 +349,7 @@ size_t nq_lrb_latent_workspace_bytes(int64_t d_out, int64_t d_in, int64_t r, int
   static const float one = 1.0f;
   const LatentLayout g = latent_layout(d_out, d_in, r, &one, &one, T);
   if (check_lrb("nq_lrb_latent_workspace_bytes", &g.L) != NQ_OK) return 0;
+  if (T <= kLatMaxT) return lat_forward_fits(d_out, d_in, r, T) ? lat_forward_bytes(d_out, d_in, r, T) : 0;
   return g.bytes;
 }
 
@@ -369,6 +370,19 @@ nq_status nq_lrb_linear_latent(const float* u_lat, int64_t ldu_lat, const float*
   nq_status st = check_lrb(who, &g.L);
   if (st != NQ_OK) return st;
   if ((st = check_io(who, &g.L, x, x_dtype, T, y)) != NQ_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (T <= kLatMaxT) {  // decode sizes: the signs are taken as the latents load
+    if (!lat_forward_fits(d_out, d_in, r, T))
+      return set_error("%s: shape exceeds the launch grid", who), NQ_ERR_UNSUPPORTED;
+    const size_t need = lat_forward_bytes(d_out, d_in, r, T);
+    if (!workspace || workspace_bytes < need)
+      return set_error("%s: workspace %zu bytes, need %zu", who, workspace ? workspace_bytes : 0, need),
+             NQ_ERR_WORKSPACE;
+    if (!aligned(workspace, kAlign)) return set_error("%s: workspace not 256-byte aligned", who), NQ_ERR_ARG;
+    return hip_status(launch_lat_forward(u_lat, ldu_lat, v_lat, ldv_lat, d_out, d_in, r, s1, s2, x,
+                                         x_dtype == NQ_BF16, T, y, workspace, s),
+                      "nq_lrb_linear_latent launch");
+  }
   if (!workspace || workspace_bytes < g.bytes)
     return set_error("%s: workspace %zu bytes, need %zu", who, workspace ? workspace_bytes : 0, g.bytes),
            NQ_ERR_WORKSPACE;
@@ -378,7 +392,6 @@ nq_status nq_lrb_linear_latent(const float* u_lat, int64_t ldu_lat, const float*
   uint32_t* vb = reinterpret_cast<uint32_t*>(ws + g.off_v);
   g.L.u_bits = ub;
   g.L.vt_bits = vb;
-  hipStream_t s = (hipStream_t)stream;
   // U latent [d_out][ldu_lat]: outputs d_out, reduction r; V latent [d_in][ldv_lat]: outputs r, reduction d_in
   hipError_t e = launch_pack(u_lat, d_out, r, ldu_lat, 1, ub, d_out, s);
   if (e == hipSuccess) e = launch_pack(v_lat, r, d_in, 1, ldv_lat, vb, r, s);

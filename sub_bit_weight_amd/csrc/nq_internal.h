@@ -123,6 +123,16 @@ hipError_t launch_scale_grads_finish(const void* x, nq_dtype xd, const void* g, 
 
 // Magnitude balancing and scale extraction (balance.hip).  workspace: at
 // least balance_workspace_bytes(d_out, d_in), 256-byte aligned.
+// Refinement forward with the signs taken from the fp32 latents as they load
+// (latent.hip), for T <= kLatMaxT: workspace bytes, whether the launch grid
+// fits, and the launch (zeroes its counters, then the two stages).
+constexpr int kLatMaxT = 8;
+size_t lat_forward_bytes(int64_t d_out, int64_t d_in, int64_t r, int64_t T);
+bool lat_forward_fits(int64_t d_out, int64_t d_in, int64_t r, int64_t T);
+hipError_t launch_lat_forward(const float* u_lat, int64_t ldu, const float* v_lat, int64_t ldv, int64_t d_out,
+                              int64_t d_in, int64_t r, const float* s1, const float* s2, const void* x, bool x_bf16,
+                              int64_t T, float* y, void* ws, hipStream_t s);
+
 size_t balance_workspace_bytes(int64_t d_out, int64_t d_in);
 hipError_t launch_balance(const float* uh, int64_t ldu, const float* vh, int64_t ldv, int64_t d_out, int64_t d_in,
                           int64_t r, float* uo, float* vo, float* s1, float* s2, float* eta, void* workspace,

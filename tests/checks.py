@@ -87,6 +87,25 @@ def gamma(T: int, x_dtype: str, d_in: int, r: int) -> float:
     return 2.0 * u_in + (n + 4) * U32
 
 
+def latent_abs_terms(s1, s2, x, r: int) -> np.ndarray:
+    """A[t, i] = |s1_i| * r * sum_j |s2_j x_tj| (float64) for a layer whose
+    signs come from latents (the same form as abs_terms)."""
+    z = np.abs(np.asarray(x, np.float32).astype(np.float64)) @ np.abs(np.asarray(s2, np.float64))
+    return r * z[:, None] * np.abs(np.asarray(s1, np.float64))[None, :]
+
+
+def gamma_latent(d_in: int, r: int) -> float:
+    """Coefficient of |y - y*| <= gamma * A for the refinement forward at T <= 8
+    (signs applied as the fp32 latents load): the s2 * x product (one rounding),
+    then fp32 sums only.  Sequential additions per output: stage 1 at most 512
+    rows of a span plus one per span (spans of at least 64 rows); stage 2 four
+    per 256-element step of a 2048-element span, six across the wave's lanes
+    and one per span."""
+    n1 = 512 + -(-d_in // 64)
+    n2 = 4 * (2048 // 256) + 6 + -(-r // 2048)
+    return 2.0 * U32 + (n1 + n2 + 4) * U32
+
+
 def check(y, y_ref, tol: float, A=None, gam: float | None = None, k_elem: float = 8.0,
           token_bars: bool = True) -> dict:
     """All bars at once.  Returns the measured errors with a 'pass' flag and the

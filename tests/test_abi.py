@@ -230,7 +230,9 @@ def test_linear_latent_rejects_bad_args():
 def test_linear_latent_workspace_query():
     lib = nq.lib()
     need = lib.nq_lrb_latent_workspace_bytes(16, 24, 8, 1)
-    assert need >= 16 * 4 + 8 * 4   # one word row of U and one of V^T at least
+    assert need >= 8 * 4   # t at least (T <= 8: signs taken as the latents load)
+    need9 = lib.nq_lrb_latent_workspace_bytes(16, 24, 8, 9)
+    assert need9 >= 16 * 4 + 8 * 4   # T > 8: one word row of U and one of V^T at least
     assert lib.nq_lrb_latent_workspace_bytes(16, 24, 0, 1) == 0
     assert lib.nq_lrb_latent_workspace_bytes(16, 24, 8, 0) == 0
 
