@@ -301,19 +301,21 @@ __device__ inline int task_element(int task, int k) {
   return 32 * wr + 4 * (4 * ih + k) + 3 - j;
 }
 
-// Loads of every token's inputs in a chunk (the column scales once).  Elements
-// at or past cend read element 0 of the token (always in bounds) and are
-// dropped later, so the loads keep a fixed count and position in the pipeline.
-template <int T>
-__device__ inline void piece_load_inputs(const StageDesc& S, int task, int64_t c0, int64_t cend, PieceIn<T>& in) {
+// Loads of tokens tok0 .. tok0+NT-1 of a chunk's inputs (the column scales
+// once).  Elements at or past cend read element 0 of the token (always in
+// bounds) and are dropped later, so the loads keep a fixed count and position
+// in the pipeline.
+template <int NT>
+__device__ inline void piece_load_inputs(const StageDesc& S, int task, int tok0, int64_t c0, int64_t cend,
+                                         PieceIn<NT>& in) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int64_t e = c0 + task_element(task, k);
     const int64_t ec = e < cend ? e : 0;
     in.cs[k] = S.colscale ? gload(S.colscale + ec) : 1.0f;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int64_t idx = (int64_t)t * S.n_red + ec;
+    for (int t = 0; t < NT; ++t) {
+      const int64_t idx = (int64_t)(tok0 + t) * S.n_red + ec;
       in.x[t][k] = S.x_bf16 ? (uint32_t)gload(static_cast<const uint16_t*>(S.xin) + idx)
                             : gload(static_cast<const uint32_t*>(S.xin) + idx);
     }
@@ -385,60 +387,73 @@ __device__ inline int max_fp8_exponent(int d) {
 template <int T>
 constexpr int chunk_blocks() { return kChunkSteps * 2 * 4 * T * kPieces; }
 
-// Chunks per input-piece tile: two per round (one per group of 256 threads),
-// every token of a chunk in the same round (the column scales are loaded once
-// and all of its loads are in flight together).  Sequences take up to four
-// rounds at T = 1 (eight chunks; fewer tiles) and one from T = 4 on; single
-// calls one round, so the pieces are ready one tile latency after the launch.
-__host__ __device__ inline int prep_chunks(int64_t T, bool single) {
-  return single || T >= 4 ? kPrepGroups : (int)(8 / T);
+// Input-piece work items: (chunk, group of TG tokens), two per round (one per
+// group of 256 threads).  Sequences take every token of a chunk in one item
+// (TG = T: the column scales load once, all of the chunk's loads are in flight
+// together, fewer items) and up to four rounds per tile at T = 1 (eight
+// chunks), one from T = 3 on.  Single calls take one token per item (TG = 1)
+// and one round per tile: the pieces are ready one item's latency after the
+// launch, on as many workgroups as there are (chunk, token) pairs.
+__host__ __device__ inline int prep_items(int64_t T, bool single) {
+  return single || T >= 3 ? kPrepGroups : (int)(8 / T);
 }
 
-// One input-piece tile: chunks [S.prep_chunks * tile, ...) of the stage input,
-// every token.  Each group of 256 threads takes a chunk per round; per chunk
-// and token each thread makes one B dword (4 consecutive reduction positions)
-// per piece; the next round's inputs load while the current ones are converted.
-template <int T>
+// One input-piece tile: items [S.prep_items * tile, ...) of the stage input,
+// item i being chunk i / (T / TG) with tokens TG * (i % (T / TG)) ...  Each
+// group of 256 threads takes an item per round; per chunk and token each
+// thread makes one B dword (4 consecutive reduction positions) per piece; the
+// next round's inputs load while the current ones are converted.
+template <int T, int TG>
 __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* err, NextTile& next) {
+  static_assert(T % TG == 0, "whole token groups");
+  constexpr int NTG = T / TG;  // token groups per chunk
   constexpr int NC = T * kPieces;
   constexpr int64_t kChunkElems = kChunkWords * kWordBits;
   unsigned* slots = reinterpret_cast<unsigned*>(reinterpret_cast<int*>(ldsf) + slot_off<T>());  // [round&1][group][T]
   const int tid = threadIdx.x, half = tid >> 8, task = tid & 255;  // half: this thread's group
-  const int nch = (int)cdiv(S.n_red, kChunkElems);
-  const int ch0 = tile * S.prep_chunks;
-  const int ch1 = min(ch0 + S.prep_chunks, nch);
+  const int nit = (int)cdiv(S.n_red, kChunkElems) * NTG;
+  const int it0 = tile * S.prep_items;
+  const int it1 = min(it0 + S.prep_items, nit);
   wait_input(S, err);
   const int wr = task >> 3, j = (task >> 1) & 3, ih = task & 1;
   const int kk = wr >> 2, gw = wr & 3;
   const int gp = 2 * (gw & 1) + (j >> 1);
   const int64_t task_off = (int64_t)(((kk * 2 + (gw >> 1)) * 4 + gp) * NC) * 4 + 2 * (j & 1) + ih;
-  if (tid < 2 * kPrepGroups * T) slots[tid] = 0;
-  // the chunk this group takes in a round (past the tile's last: the last
-  // chunk again for the loads, nothing stored)
-  auto chunk_of = [&](int r0) { return min(r0 + half, nch - 1); };
-  PieceIn<T> in, nxt;
-  piece_load_inputs<T>(S, task, (int64_t)chunk_of(ch0) * kChunkElems, S.n_red, in);
+  if (tid < 2 * kPrepGroups * TG) slots[tid] = 0;
+  // the item this group takes in a round (past the tile's last: the last item
+  // again for the loads, nothing stored)
+  auto item_of = [&](int r0) { return min(r0 + half, nit - 1); };
+  PieceIn<TG> in, nxt;
+  {
+    const int it = item_of(it0);
+    piece_load_inputs<TG>(S, task, TG * (it % NTG), (int64_t)(it / NTG) * kChunkElems, S.n_red, in);
+  }
   __syncthreads();
-  for (int r0 = ch0, round = 0; r0 < ch1; r0 += kPrepGroups, ++round) {
-    const bool last = r0 + kPrepGroups >= ch1;
+  for (int r0 = it0, round = 0; r0 < it1; r0 += kPrepGroups, ++round) {
+    const bool last = r0 + kPrepGroups >= it1;
     if (last) next.claim();  // the tile's last round
-    const bool mine = r0 + half < ch1;  // wave-uniform: a group is 4 whole waves
-    const int ch = chunk_of(r0);
+    const bool mine = r0 + half < it1;  // wave-uniform: a group is 4 whole waves
+    const int it = item_of(r0);
+    const int ch = it / NTG, tok0 = TG * (it % NTG);
     const int64_t c0 = ch * kChunkElems;
-    unsigned* slot = slots + ((round & 1) * kPrepGroups + half) * T;
-    piece_chunk_max<T>(S, in, task, c0, S.n_red, slot);
-    if (!last) piece_load_inputs<T>(S, task, (int64_t)chunk_of(r0 + kPrepGroups) * kChunkElems, S.n_red, nxt);
-    __syncthreads();  // the chunks' maxima are complete
+    unsigned* slot = slots + ((round & 1) * kPrepGroups + half) * TG;
+    piece_chunk_max<TG>(S, in, task, c0, S.n_red, slot);
+    if (!last) {
+      const int itn = item_of(r0 + kPrepGroups);
+      piece_load_inputs<TG>(S, task, TG * (itn % NTG), (int64_t)(itn / NTG) * kChunkElems, S.n_red, nxt);
+    }
+    __syncthreads();  // the items' maxima are complete
     if (mine) {
       uint32_t* dst = S.bfrag + (int64_t)ch * chunk_blocks<T>() * 4 + task_off;
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int shift = chunk_shift(slot[t]);
+      for (int tg = 0; tg < TG; ++tg) {
+        const int t = tok0 + tg;
+        const int shift = chunk_shift(slot[tg]);
         float r[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000)
-                                    : ldexpf(piece_value(S, in, t, task, c0, S.n_red, k), shift);
+                                    : ldexpf(piece_value(S, in, tg, task, c0, S.n_red, k), shift);
 #pragma unroll
         for (int p = 0; p < kPieces; ++p) {
           int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
@@ -462,7 +477,7 @@ __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* e
       }
     }
     __syncthreads();  // every thread has read this round's maxima
-    if (task < T) slot[task] = 0;  // reused two rounds on (its maxima come after the next barrier)
+    if (task < TG) slot[task] = 0;  // reused two rounds on (its maxima come after the next barrier)
     if (!last) in = nxt;
   }
   if (S.signal) {
@@ -787,8 +802,10 @@ static_assert(col_groups<kMfmaMaxT>() <= 2, "T <= 8 in two column groups");
 
 template <int T>
 __device__ inline void stage_tile(const StageDesc& S, int local, float* lds, int* s_flag, int* err, NextTile& next) {
-  if (S.kind == 1)
-    mfma_prep_tile<T>(S, local, lds, err, next);
+  if (S.kind == 1 && S.prep_tg == 1)
+    mfma_prep_tile<T, 1>(S, local, lds, err, next);
+  else if (S.kind == 1)
+    mfma_prep_tile<T, T>(S, local, lds, err, next);
   else if (S.w_vec)
     mfma_tile<T, true>(S, local, lds, s_flag, err, next);
   else
@@ -1092,8 +1109,9 @@ int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
     pc.kind = 1;
     pc.bfrag = reinterpret_cast<uint32_t*>(buf);
     pc.bsig = reinterpret_cast<int*>(buf + align_up((size_t)nch * 64 * T * kPieces * 16));
-    pc.prep_chunks = prep_chunks(T, split);
-    pc.nrb = (int)cdiv(nch, pc.prep_chunks);  // tiles
+    pc.prep_tg = split ? 1 : (int)T;
+    pc.prep_items = prep_items(T, split);
+    pc.nrb = (int)cdiv(nch * (T / pc.prep_tg), pc.prep_items);  // tiles
     pc.rb_group = 1;
     pc.nks = 1;
     pc.signal = ready;

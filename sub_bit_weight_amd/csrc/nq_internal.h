@@ -75,7 +75,8 @@ struct StageDesc {
   int kind;               // 0: stage tiles (nrb x nks); 1: input-piece tiles (nrb = tiles, nks = 1)
   uint32_t* bfrag;        // matrix-core operand pieces of the stage input (written by kind 1, read by kind 0)
   int* bsig;              // per chunk and token: scale exponent of the pieces
-  int prep_chunks;        // kind 1: input chunks per tile (every token)
+  int prep_items;         // kind 1: (chunk, token group) work items per tile
+  int prep_tg;            // kind 1: tokens per work item (1 or T)
   int tile0;              // first tile of this stage in a persistent schedule
 };
 // Tiles of a stage: kind 0, groups of rb_group row blocks per span; kind 1,
