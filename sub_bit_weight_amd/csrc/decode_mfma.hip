@@ -35,6 +35,23 @@ constexpr unsigned kSpinLimit = 1u << 21;  // ~1 s of polling, then give up and 
 
 __device__ inline float bf16_bits(uint32_t h) { return __uint_as_float(h << 16); }
 
+// Cross-lane moves within a row of 16 lanes (DPP: no LDS round trip, unlike
+// __shfl_xor, which becomes ds_bpermute).  Every lane of the wave must be active.
+__device__ inline unsigned lane_xor1(unsigned v) {  // quad_perm [1,0,3,2]
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+// Largest of v over the 64 lanes, in every lane: quad, half-row and row steps
+// by DPP, then the four row maxima through scalar registers.
+__device__ inline unsigned wave_max_u32(unsigned v) {
+  v = max(v, lane_xor1(v));
+  v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  const unsigned r0 = (unsigned)__builtin_amdgcn_readlane((int)v, 0), r1 = (unsigned)__builtin_amdgcn_readlane((int)v, 16);
+  const unsigned r2 = (unsigned)__builtin_amdgcn_readlane((int)v, 32), r3 = (unsigned)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -339,8 +356,7 @@ __device__ inline void piece_chunk_max(const StageDesc& S, const PieceIn<T>& in,
     unsigned m = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) m = max(m, __float_as_uint(fabsf(piece_value(S, in, t, task, c0, cend, k))));
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off));
+    m = wave_max_u32(m);
     if ((threadIdx.x & 63) == 0) atomicMax(slot + t, m);
   }
 }
@@ -460,7 +476,7 @@ __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* e
           d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
           // this dword and the partner thread's (task ^ 1, same wave) form one group of 8
           int emax = max_fp8_exponent(d);
-          emax = max(emax, __shfl_xor(emax, 1));
+          emax = max(emax, (int)lane_xor1((unsigned)emax));
           d = keep_fp8_exponents(d, max(1, emax - 7));
           store_agent(reinterpret_cast<float*>(dst + (t * kPieces + p) * 4), __int_as_float(d));
           if (p + 1 < kPieces) {
