@@ -211,7 +211,11 @@ void nq_seq_destroy(nq_seq* s);
  *   ut_bits/v_bits: the transposed layer's words from nq_transpose_signs.
  *   Both products run through the kernels of nq_lrb_linear (decode regime for
  *   T <= 8, GEMM regime above, with the same arithmetic); the token sums are
- *   fp32 in token order (deterministic).
+ *   fp32 in token order (deterministic).  The two products run concurrently:
+ *   the transposed one on a second stream that the library makes on a
+ *   device's first call and keeps, forked from and joined back to `stream`
+ *   (all of the call's work is ordered after what `stream` holds at the call,
+ *   and what is queued on `stream` afterwards is ordered after all of it).
  *   workspace: at least nq_lrb_scale_grads_workspace_bytes(L, T) bytes,
  *   256-byte aligned.  Errors: as for nq_lrb_linear, for L and for the
  *   transposed layer's words; NQ_ERR_ARG for an unknown g_dtype or a null or

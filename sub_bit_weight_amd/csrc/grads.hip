@@ -56,12 +56,15 @@ __device__ inline float load_act(const void* p, int bf16, int64_t i) {
 // 1024-byte segments per wave.  A single chunk writes ds1 / ds2 itself; else
 // each chunk writes its partial sums, part[chunk][column], and
 // scale_grads_sum_kernel adds them in chunk order.  Both orders are fixed:
-// the sums do not depend on scheduling.
+// the sums do not depend on scheduling.  A launch covers columns
+// [c_begin, c_end), so the two halves (from b, from u) can run apart.
 __global__ __launch_bounds__(256) void scale_grads_partial_kernel(
     const void* __restrict__ x, int x_bf16, const void* __restrict__ g, int g_bf16, const float* __restrict__ u,
     const float* __restrict__ b, const float* __restrict__ s2, int64_t T, int64_t tc, int64_t d_in, int64_t d_out,
-    float* __restrict__ dx, float* __restrict__ part, float* __restrict__ ds1, float* __restrict__ ds2) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    float* __restrict__ dx, float* __restrict__ part, float* __restrict__ ds1, float* __restrict__ ds2,
+    int64_t c_begin, int64_t c_end) {
+  const int64_t c = c_begin + (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= c_end) return;
   const int64_t t0 = (int64_t)blockIdx.y * tc;
   const int64_t t1 = t0 + tc < T ? t0 + tc : T;
   const int64_t ncols = d_in + d_out;
@@ -106,8 +109,10 @@ __device__ inline float4 load_act4(const void* p, int bf16, int64_t i) {
 __global__ __launch_bounds__(256) void scale_grads_partial4_kernel(
     const void* __restrict__ x, int x_bf16, const void* __restrict__ g, int g_bf16, const float* __restrict__ u,
     const float* __restrict__ b, const float* __restrict__ s2, int64_t T, int64_t tc, int64_t d_in, int64_t d_out,
-    float* __restrict__ dx, float* __restrict__ part, float* __restrict__ ds1, float* __restrict__ ds2) {
-  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    float* __restrict__ dx, float* __restrict__ part, float* __restrict__ ds1, float* __restrict__ ds2,
+    int64_t c_begin, int64_t c_end) {
+  const int64_t c = c_begin + ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= c_end) return;
   const int64_t t0 = (int64_t)blockIdx.y * tc;
   const int64_t t1 = t0 + tc < T ? t0 + tc : T;
   const int64_t ncols = d_in + d_out;
@@ -152,10 +157,11 @@ __global__ __launch_bounds__(256) void scale_grads_partial4_kernel(
 
 __global__ __launch_bounds__(256) void scale_grads_sum_kernel(const float* __restrict__ part, int nchunks,
                                                               int64_t d_in, int64_t d_out, float* __restrict__ ds1,
-                                                              float* __restrict__ ds2) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+                                                              float* __restrict__ ds2, int64_t c_begin,
+                                                              int64_t c_end) {
+  const int64_t c = c_begin + (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t ncols = d_in + d_out;
-  if (c >= ncols) return;
+  if (c >= c_end) return;
   float acc = 0.0f;
   for (int q = 0; q < nchunks; ++q) acc += part[(int64_t)q * ncols + c];
   if (c < d_in)
@@ -188,22 +194,24 @@ size_t scale_grads_partial_bytes(int64_t T, int64_t d_in, int64_t d_out) {
 
 hipError_t launch_scale_grads_finish(const void* x, nq_dtype xd, const void* g, nq_dtype gd, const float* u,
                                      const float* b, const float* s2, int64_t T, int64_t d_in, int64_t d_out, float* dx,
-                                     float* part, float* ds1, float* ds2, hipStream_t s) {
-  const int64_t col_tiles = cdiv(d_in + d_out, 256);
+                                     float* part, float* ds1, float* ds2, int64_t c_begin, int64_t c_end,
+                                     hipStream_t s) {
+  if (c_end <= c_begin) return hipSuccess;
+  const int64_t col_tiles = cdiv(c_end - c_begin, 256);
   const int64_t tc = grad_chunk_tokens(T), nchunks = cdiv(T, tc);
   const auto vec_ok = [](const void* p, nq_dtype d) { return (uintptr_t)p % (d == NQ_BF16 ? 8 : 16) == 0; };
   if (d_in % 4 == 0 && d_out % 4 == 0 && vec_ok(x, xd) && vec_ok(g, gd) && (uintptr_t)dx % 16 == 0 &&
       (uintptr_t)u % 16 == 0 && (uintptr_t)b % 16 == 0 && (uintptr_t)part % 16 == 0)
-    hipLaunchKernelGGL(scale_grads_partial4_kernel, dim3((unsigned)cdiv((d_in + d_out) / 4, 256), (unsigned)nchunks),
+    hipLaunchKernelGGL(scale_grads_partial4_kernel, dim3((unsigned)cdiv((c_end - c_begin) / 4, 256), (unsigned)nchunks),
                        dim3(256), 0, s, x, (int)(xd == NQ_BF16), g, (int)(gd == NQ_BF16), u, b, s2, T, tc, d_in,
-                       d_out, dx, part, ds1, ds2);
+                       d_out, dx, part, ds1, ds2, c_begin, c_end);
   else
     hipLaunchKernelGGL(scale_grads_partial_kernel, dim3((unsigned)col_tiles, (unsigned)nchunks), dim3(256), 0, s, x,
                        (int)(xd == NQ_BF16), g, (int)(gd == NQ_BF16), u, b, s2, T, tc, d_in, d_out, dx, part, ds1,
-                       ds2);
+                       ds2, c_begin, c_end);
   if (nchunks > 1)
     hipLaunchKernelGGL(scale_grads_sum_kernel, dim3((unsigned)col_tiles), dim3(256), 0, s, part, (int)nchunks, d_in,
-                       d_out, ds1, ds2);
+                       d_out, ds1, ds2, c_begin, c_end);
   return hipGetLastError();
 }
 

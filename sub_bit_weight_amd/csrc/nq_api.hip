@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <array>
 #include <vector>
@@ -120,9 +121,10 @@ nq_lrb adjoint_layer(const nq_lrb& L, const uint32_t* ut_bits, int64_t ldut, con
 }
 
 // Workspace of nq_lrb_scale_grads: [u: T x d_out][b: T x d_in][per-chunk
-// partial sums][one linear's workspace, used by the two products in turn].
+// partial sums][the forward product's linear workspace][the transposed
+// product's] (the two products run concurrently).
 struct ScaleGradsLayout {
-  size_t off_u, off_b, off_part, off_lin, bytes;
+  size_t off_u, off_b, off_part, off_lin, off_lin_t, bytes;
 };
 ScaleGradsLayout scale_grads_layout(const nq_lrb& L, int64_t T) {
   ScaleGradsLayout g;
@@ -131,8 +133,39 @@ ScaleGradsLayout scale_grads_layout(const nq_lrb& L, int64_t T) {
   g.off_part = g.off_b + align_up((size_t)T * L.d_in * sizeof(float));
   g.off_lin = g.off_part + align_up(scale_grads_partial_bytes(T, L.d_in, L.d_out));
   const nq_lrb A = adjoint_layer(L, L.vt_bits, L.r, L.u_bits, L.d_in);  // sizes only
-  g.bytes = g.off_lin + std::max(linear_workspace(L, T), linear_workspace(A, T));
+  g.off_lin_t = g.off_lin + align_up(linear_workspace(L, T));
+  g.bytes = g.off_lin_t + linear_workspace(A, T);
   return g;
+}
+
+// A second stream per device for calls made of two independent products,
+// with the events that fork it from and join it back to the caller's stream.
+// Made on a device's first such call and kept until the process ends; the
+// mutex keeps one call's fork, launches and join together.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::vector<SideStream> g_side;
+
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if ((int)g_side.size() <= dev) g_side.resize(dev + 1);
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);  // default priority
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    ss.s = s, ss.fork = f, ss.join = j;
+  }
+  *out = &ss;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -454,11 +487,29 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
   nq_lrb Lu = *L;  // u = U (V^T (s2 (.) x)): the forward product without s1
   Lu.s1 = nullptr;
   A.s1 = nullptr;  // b = V (U^T (s1 (.) g)): the transposed product without s2
-  hipError_t e = launch_linear(Lu, x, x_dtype, T, u, ws + lay.off_lin, s);
-  if (e == hipSuccess) e = launch_linear(A, g, g_dtype, T, b, ws + lay.off_lin, s);
-  if (e == hipSuccess)
-    e = launch_scale_grads_finish(x, x_dtype, g, g_dtype, u, b, L->s2, T, L->d_in, L->d_out, dx,
-                                  reinterpret_cast<float*>(ws + lay.off_part), ds1, ds2, s);
+  // the two products on two streams: one's prep kernels and last, partly
+  // filled wave of tiles run beside the other's GEMMs
+  hipError_t e;
+  {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* side = nullptr;
+    e = side_stream(&side);
+    if (e == hipSuccess) e = hipEventRecord(side->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    // each stream then takes the token sums of its own product: columns
+    // [0, d_in) (dx and ds2, from b) and [d_in, d_in + d_out) (ds1, from u)
+    float* part = reinterpret_cast<float*>(ws + lay.off_part);
+    if (e == hipSuccess) e = launch_linear(A, g, g_dtype, T, b, ws + lay.off_lin_t, side->s);
+    if (e == hipSuccess)
+      e = launch_scale_grads_finish(x, x_dtype, g, g_dtype, u, b, L->s2, T, L->d_in, L->d_out, dx, part, ds1, ds2,
+                                    0, L->d_in, side->s);
+    if (e == hipSuccess) e = launch_linear(Lu, x, x_dtype, T, u, ws + lay.off_lin, s);
+    if (e == hipSuccess)
+      e = launch_scale_grads_finish(x, x_dtype, g, g_dtype, u, b, L->s2, T, L->d_in, L->d_out, dx, part, ds1, ds2,
+                                    L->d_in, L->d_in + L->d_out, s);
+    if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+  }
   return hip_status(e, "nq_lrb_scale_grads launch");
 }
 

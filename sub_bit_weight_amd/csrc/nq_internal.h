@@ -120,7 +120,8 @@ constexpr int64_t kGradTokens = 64, kGradChunks = 1024;
 size_t scale_grads_partial_bytes(int64_t T, int64_t d_in, int64_t d_out);
 hipError_t launch_scale_grads_finish(const void* x, nq_dtype xd, const void* g, nq_dtype gd, const float* u,
                                      const float* b, const float* s2, int64_t T, int64_t d_in, int64_t d_out, float* dx,
-                                     float* part, float* ds1, float* ds2, hipStream_t s);
+                                     float* part, float* ds1, float* ds2, int64_t c_begin, int64_t c_end,
+                                     hipStream_t s);
 
 // Magnitude balancing and scale extraction (balance.hip).  workspace: at
 // least balance_workspace_bytes(d_out, d_in), 256-byte aligned.
