@@ -35,7 +35,9 @@ constexpr int kS1MinSpan = 64;
 constexpr int kS1Target = 512;            // stage-1 workgroups to aim for (two per CU)
 constexpr int kS2RowsPerWave = 4;
 constexpr int kS2Rows = kS2RowsPerWave * (kLatThreads / 64);  // 16 rows per workgroup
-constexpr int kS2Span = 2048;             // stage-2 reduction elements per workgroup
+constexpr int kS2Span = 2048;             // stage-2 reduction elements per workgroup, at most
+constexpr int kS2MinSpan = 256;
+constexpr int kS2Target = 2048;           // stage-2 workgroups to aim for at T = 1 (divided by T)
 
 __device__ inline float signed_by(float lat, float v) { return lat < 0.0f ? -v : v; }
 
@@ -170,17 +172,17 @@ __global__ __launch_bounds__(kLatThreads) void lat_stage2_kernel(const float* __
                                                                  int64_t d_out, int64_t r, const float* __restrict__ t,
                                                                  const float* __restrict__ s1,
                                                                  float* __restrict__ part, int* __restrict__ ctr,
-                                                                 float* __restrict__ y) {
+                                                                 float* __restrict__ y, int span) {
   __shared__ __attribute__((aligned(16))) float ts[T][kS2Span];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nsp = (int)gridDim.y, sp = (int)blockIdx.y;
-  const int64_t k0 = (int64_t)sp * kS2Span;
-  const int n = (int)imin(kS2Span, r - k0);
-  for (int i = tid; i < T * kS2Span; i += kLatThreads) {
-    const int tt = i / kS2Span, kk = i % kS2Span;
-    ts[tt][kk] = kk < n ? t[(int64_t)tt * r + k0 + kk] : 0.0f;
-  }
+  const int64_t k0 = (int64_t)sp * span;
+  const int n = (int)imin(span, r - k0);
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt)
+    for (int kk = tid; kk < span; kk += kLatThreads)  // span: a multiple of 256, at most kS2Span
+      ts[tt][kk] = kk < n ? t[(int64_t)tt * r + k0 + kk] : 0.0f;
   __syncthreads();
   const int64_t i0 = (int64_t)blockIdx.x * kS2Rows + wv * kS2RowsPerWave;
   float acc[kS2RowsPerWave][T];
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(kLatThreads) void lat_stage2_kernel(const float* __
 #pragma unroll
     for (int tt = 0; tt < T; ++tt) acc[rr][tt] = 0.0f;
   for (int kb = 0; kb < n; kb += 256) {  // (unrolled twice: slower)
-    const int kk = kb + 4 * lane;  // < kS2Span; t is zero past n
+    const int kk = kb + 4 * lane;  // < span; t is zero past n
     float tv[T][4];
 #pragma unroll
     for (int tt = 0; tt < T; ++tt) {
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(kLatThreads) void lat_stage2_kernel(const float* __
 
 struct LatPlan {
   int ncol, nsp1, span1;  // stage 1: column tiles, row spans, rows per span
-  int nrb, nsp2;          // stage 2: row blocks, reduction spans
+  int nrb, nsp2, span2;   // stage 2: row blocks, reduction spans, elements per span
   size_t off_t, off_p1, off_p2, off_c, bytes;
 };
 
@@ -260,7 +262,12 @@ LatPlan lat_plan(int64_t d_out, int64_t d_in, int64_t r, int64_t T) {
   p.span1 = (int)imin(kS1MaxSpan, round_up(cdiv(d_in, nsp), 4));
   p.nsp1 = (int)cdiv(d_in, p.span1);
   p.nrb = (int)cdiv(d_out, kS2Rows);
-  p.nsp2 = (int)cdiv(r, kS2Span);
+  // reduction spans: enough workgroups for the chip, each span a whole number
+  // of the waves' 256-element steps; a workgroup's work per loaded element
+  // grows with T, so fewer are needed (more spans at T = 8 measured 5 % slower)
+  const int64_t want2 = imax(1, cdiv(kS2Target / T, p.nrb));
+  p.span2 = (int)imin(kS2Span, imax(kS2MinSpan, round_up(cdiv(r, want2), kS2MinSpan)));
+  p.nsp2 = (int)cdiv(r, p.span2);
   size_t off = 0;
   p.off_t = off;
   off = align_up(off + (size_t)T * r * sizeof(float));
@@ -294,10 +301,10 @@ hipError_t launch_lat_t(const float* u_lat, int64_t ldu, const float* v_lat, int
                        x_bf16 ? 1 : 0, s2, p.span1, p1, ctr, t);
   if (ldu % 4 == 0 && reinterpret_cast<uintptr_t>(u_lat) % 16 == 0)
     hipLaunchKernelGGL((lat_stage2_kernel<T, true>), g2, dim3(kLatThreads), 0, s, u_lat, ldu, d_out, r, t, s1, p2,
-                       ctr + p.ncol, y);
+                       ctr + p.ncol, y, p.span2);
   else
     hipLaunchKernelGGL((lat_stage2_kernel<T, false>), g2, dim3(kLatThreads), 0, s, u_lat, ldu, d_out, r, t, s1, p2,
-                       ctr + p.ncol, y);
+                       ctr + p.ncol, y, p.span2);
   return hipGetLastError();
 }
 

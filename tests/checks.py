@@ -99,10 +99,10 @@ def gamma_latent(d_in: int, r: int) -> float:
     (signs applied as the fp32 latents load): the s2 * x product (one rounding),
     then fp32 sums only.  Sequential additions per output: stage 1 at most 512
     rows of a span plus one per span (spans of at least 64 rows); stage 2 four
-    per 256-element step of a 2048-element span, six across the wave's lanes
-    and one per span."""
+    per 256-element step of a span of at most 2048 elements, six across the
+    wave's lanes and one per span (spans of at least 256 elements)."""
     n1 = 512 + -(-d_in // 64)
-    n2 = 4 * (2048 // 256) + 6 + -(-r // 2048)
+    n2 = 4 * (2048 // 256) + 6 + -(-r // 256)
     return 2.0 * U32 + (n1 + n2 + 4) * U32
 
 
