@@ -123,6 +123,12 @@ size_t nq_lrb_workspace_bytes(const nq_lrb* L, int64_t T);
  * is scaled by an exact power of two and rounded to fp16 (two fp16 terms for
  * fp32 x), multiplied by the exact +-1 signs with fp32 accumulation, and
  * scaled back.
+ * Small layers at T <= 8 (T*d_in <= 2048 and T*r <= 512 with both rounded up
+ * to whole words, d_out <= 1024) run in one workgroup instead: z, t and y as
+ * fp32 sums in index order with the exact signs (set NQ_DECODE_TINY=0 in the
+ * environment to keep them on the decode kernels above; sequence plans always
+ * use those, so a sequence entry and a single call of such a layer may differ
+ * in the last bits).
  * y is fully overwritten.  Summation order is fixed: results are run-to-run
  * deterministic, but not bitwise equal across regimes.
  * Errors: NQ_ERR_ARG for null pointers, dims < 1, ldu < d_out, ldv < r, T < 1,

@@ -89,6 +89,13 @@ bool decode_xor() {
   return e && strcmp(e, "xor") == 0;
 }
 
+// NQ_DECODE_TINY=0 keeps small layers on the multi-workgroup decode kernels
+// (read at each call, like NQ_DECODE_VARIANT: tests compare the two paths).
+bool tiny_enabled() {
+  const char* e = getenv("NQ_DECODE_TINY");
+  return !(e && strcmp(e, "0") == 0);
+}
+
 // in_seq: the linear is an entry of a sequence plan, whose entries run
 // concurrently; the matrix-core regime then never splits a reduction (the
 // entries fill the chip together, and a split only adds partial-sum traffic).
@@ -100,7 +107,10 @@ size_t linear_workspace(const nq_lrb& L, int64_t T, bool in_seq) {
 hipError_t launch_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
                          hipStream_t s, bool in_seq) {
   if (T > kDecodeMaxT) return launch_prefill(L, x, xd, T, y, ws, s, !in_seq);
-  return decode_xor() ? launch_decode(L, x, xd, T, y, ws, s) : launch_dec_linear(L, x, xd, T, y, ws, s);
+  if (decode_xor()) return launch_decode(L, x, xd, T, y, ws, s);
+  if (tiny_enabled() && tiny_fits(L, T)) return launch_tiny_linear(L, x, xd, T, y, s);  // one workgroup
+
+  return launch_dec_linear(L, x, xd, T, y, ws, s);
 }
 
 namespace {

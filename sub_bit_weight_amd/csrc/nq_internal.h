@@ -35,6 +35,11 @@ hipError_t launch_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T,
 
 // ---------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launch (hipGetLastError after the launch).
+
+// Decode of a small layer (T <= 8) in one workgroup, no workspace (tiny.hip);
+// tiny_fits says which layers take it.
+bool tiny_fits(const nq_lrb& L, int64_t T);
+hipError_t launch_tiny_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, hipStream_t s);
 hipError_t launch_pack(const float* src, int64_t n_out, int64_t n_red, int64_t so, int64_t sr,
                        uint32_t* dst, int64_t ld, hipStream_t s);
 hipError_t launch_unpack(const uint32_t* bits, int64_t n_out, int64_t n_red, int64_t ld, float* dst,

@@ -157,6 +157,35 @@ def test_linear_deterministic():
         assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
+TINY_PATH = [(256, 256, 64), (70, 100, 40), (1024, 2048, 512), (33, 1, 1), (1, 64, 33), (257, 96, 31)]
+
+
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", TINY_PATH)
+def test_tiny_path(shape, x_dtype, monkeypatch):
+    """Small layers at T <= 8 run in one workgroup (z, t, y as fp32 sums in
+    index order): against the oracle at every T the path takes, with padded
+    words, and against the multi-workgroup decode kernels on the same inputs."""
+    d_out, d_in, r = shape
+    cfg = G.tiny_config(f"tinypath/{shape}/{x_dtype}", x_dtype=x_dtype)
+    dev, ref, _ = G.latent_layer(cfg, synth.LayerShape("tp", d_out, d_in, r), ld_pad=3)
+    ran = 0
+    for T in range(1, 9):
+        w32 = lambda n: -(-n // 32) * 32
+        if not (T * w32(d_in) <= 2048 and T * w32(r) <= 512 and d_out <= 1024):
+            continue
+        x = synth.activations(f"tinypath/x/{shape}/{T}/{x_dtype}", T, d_in, x_dtype)
+        err = _linear_err(dev, ref, x, x_dtype)
+        assert err <= 1e-5, (T, err)
+        y_tiny = nq.lrb_linear(dev, G.to_device_x(x, x_dtype)).cpu().numpy()
+        monkeypatch.setenv("NQ_DECODE_TINY", "0")
+        y_dec = nq.lrb_linear(dev, G.to_device_x(x, x_dtype)).cpu().numpy()
+        monkeypatch.delenv("NQ_DECODE_TINY")
+        assert C.errors(y_tiny, y_dec)["normwise"] <= 2e-5, T
+        ran += 1
+    assert ran >= 1
+
+
 @pytest.mark.parametrize("T", [1, 2, 5, 8])
 def test_decode_xor_variant(T, monkeypatch):
     """The per-weight sign-XOR decode kernels (kept for comparison) also match the oracle."""
@@ -167,7 +196,11 @@ def test_decode_xor_variant(T, monkeypatch):
     assert _linear_err(dev, ref, x, "bf16") <= 1e-5
 
 
-def test_sequence_matches_single_calls():
+def test_sequence_matches_single_calls(monkeypatch):
+    # single calls of these small layers would take the one-workgroup path;
+    # the sequence runs the decode kernels, which single calls then match bit
+    # for bit
+    monkeypatch.setenv("NQ_DECODE_TINY", "0")
     cfg = G.tiny_config("seq")
     shapes = [synth.LayerShape("a", 300, 200, 64), synth.LayerShape("b", 96, 300, 40),
               synth.LayerShape("c", 200, 96, 33)]
