@@ -187,6 +187,14 @@ namespace {
 int64_t grad_chunk_tokens(int64_t T) { return std::max(kGradTokens, cdiv(T, kGradChunks)); }
 }  // namespace
 
+hipError_t launch_scale_grads_sums(const float* part, int64_t nchunks, int64_t d_in, int64_t d_out, float* ds1,
+                                   float* ds2, int64_t c_begin, int64_t c_end, hipStream_t s) {
+  if (c_end <= c_begin) return hipSuccess;
+  hipLaunchKernelGGL(scale_grads_sum_kernel, dim3((unsigned)cdiv(c_end - c_begin, 256)), dim3(256), 0, s, part,
+                     (int)nchunks, d_in, d_out, ds1, ds2, c_begin, c_end);
+  return hipGetLastError();
+}
+
 size_t scale_grads_partial_bytes(int64_t T, int64_t d_in, int64_t d_out) {
   const int64_t nchunks = cdiv(T, grad_chunk_tokens(T));
   return nchunks > 1 ? (size_t)nchunks * (size_t)(d_in + d_out) * sizeof(float) : 0;

@@ -132,7 +132,9 @@ nq_lrb adjoint_layer(const nq_lrb& L, const uint32_t* ut_bits, int64_t ldut, con
 
 // Workspace of nq_lrb_scale_grads: [u: T x d_out][b: T x d_in][per-chunk
 // partial sums][the forward product's linear workspace][the transposed
-// product's] (the two products run concurrently).
+// product's] (the two products run concurrently).  In the matrix-core regime
+// the partial sums are per 128-row block of the GEMM outputs and u, b are
+// not stored.
 struct ScaleGradsLayout {
   size_t off_u, off_b, off_part, off_lin, off_lin_t, bytes;
 };
@@ -141,7 +143,10 @@ ScaleGradsLayout scale_grads_layout(const nq_lrb& L, int64_t T) {
   g.off_u = 0;
   g.off_b = align_up((size_t)T * L.d_out * sizeof(float));
   g.off_part = g.off_b + align_up((size_t)T * L.d_in * sizeof(float));
-  g.off_lin = g.off_part + align_up(scale_grads_partial_bytes(T, L.d_in, L.d_out));
+  const size_t part = std::max(scale_grads_partial_bytes(T, L.d_in, L.d_out),
+                               T > kDecodeMaxT ? (size_t)prefill_row_blocks(T) * (L.d_in + L.d_out) * sizeof(float)
+                                               : (size_t)0);
+  g.off_lin = g.off_part + align_up(part);
   const nq_lrb A = adjoint_layer(L, L.vt_bits, L.r, L.u_bits, L.d_in);  // sizes only
   g.off_lin_t = g.off_lin + align_up(linear_workspace(L, T));
   g.bytes = g.off_lin_t + linear_workspace(A, T);
@@ -496,6 +501,32 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
   hipStream_t s = (hipStream_t)stream;
   nq_lrb Lu = *L;  // u = U (V^T (s2 (.) x)): the forward product without s1
   Lu.s1 = nullptr;
+  float* part = reinterpret_cast<float*>(ws + lay.off_part);
+  if (T > kDecodeMaxT) {
+    // matrix-core regime: the GEMMs' epilogues take the token sums per 128-row
+    // block (ds1 from g (.) u with u never stored; ds2 from x (.) b while the
+    // transposed product, its row scale s2 kept, writes dx), and each stream
+    // adds its blocks in order
+    const int64_t nb = prefill_row_blocks(T), ldp = L->d_in + L->d_out;
+    const ProdEpilogue pu{g, g_dtype == NQ_BF16, part + L->d_in, ldp};
+    const ProdEpilogue pb{x, x_dtype == NQ_BF16, part, ldp};
+    hipError_t e;
+    {
+      std::lock_guard<std::mutex> lock(g_side_mu);
+      SideStream* side = nullptr;
+      e = side_stream(&side);
+      if (e == hipSuccess) e = hipEventRecord(side->fork, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+      if (e == hipSuccess) e = launch_prefill(A, g, g_dtype, T, dx, ws + lay.off_lin_t, side->s, true, &pb);
+      if (e == hipSuccess) e = launch_scale_grads_sums(part, nb, L->d_in, L->d_out, ds1, ds2, 0, L->d_in, side->s);
+      if (e == hipSuccess) e = launch_prefill(Lu, x, x_dtype, T, nullptr, ws + lay.off_lin, s, true, &pu);
+      if (e == hipSuccess)
+        e = launch_scale_grads_sums(part, nb, L->d_in, L->d_out, ds1, ds2, L->d_in, L->d_in + L->d_out, s);
+      if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+    }
+    return hip_status(e, "nq_lrb_scale_grads launch");
+  }
   A.s1 = nullptr;  // b = V (U^T (s1 (.) g)): the transposed product without s2
   // the two products on two streams: one's prep kernels and last, partly
   // filled wave of tiles run beside the other's GEMMs
@@ -508,7 +539,6 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
     if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
     // each stream then takes the token sums of its own product: columns
     // [0, d_in) (dx and ds2, from b) and [d_in, d_in + d_out) (ds1, from u)
-    float* part = reinterpret_cast<float*>(ws + lay.off_part);
     if (e == hipSuccess) e = launch_linear(A, g, g_dtype, T, b, ws + lay.off_lin_t, side->s);
     if (e == hipSuccess)
       e = launch_scale_grads_finish(x, x_dtype, g, g_dtype, u, b, L->s2, T, L->d_in, L->d_out, dx, part, ds1, ds2,

@@ -123,6 +123,10 @@ hipError_t launch_transpose_signs(const uint32_t* src, int64_t n_out, int64_t n_
 // scale_grads_partial_bytes of scratch (part) for the per-chunk sums.
 constexpr int64_t kGradTokens = 64, kGradChunks = 1024;
 size_t scale_grads_partial_bytes(int64_t T, int64_t d_in, int64_t d_out);
+// ds2[j] (columns j < d_in) and ds1[i] (columns d_in + i) of columns
+// [c_begin, c_end): the sum of part[q][column] over q < nchunks in order.
+hipError_t launch_scale_grads_sums(const float* part, int64_t nchunks, int64_t d_in, int64_t d_out, float* ds1,
+                                   float* ds2, int64_t c_begin, int64_t c_end, hipStream_t s);
 hipError_t launch_scale_grads_finish(const void* x, nq_dtype xd, const void* g, nq_dtype gd, const float* u,
                                      const float* b, const float* s2, int64_t T, int64_t d_in, int64_t d_out, float* dx,
                                      float* part, float* ds1, float* ds2, int64_t c_begin, int64_t c_end,
@@ -149,7 +153,18 @@ hipError_t launch_balance(const float* uh, int64_t ldu, const float* vh, int64_t
 // split = false: never split a GEMM's reduction (entries of a sequence run
 // concurrently and fill the chip together).
 size_t prefill_workspace_bytes(const nq_lrb& L, int64_t T, bool split = true);
+// A product with the stage-2 output: for every 128-row block q of the output
+// (tokens 128q ..) and column n, psum[q * ldp + n] = sum over the block's rows
+// m of pm[m][n] * v[m][n], v the output before the row scale s1 (pm: [T][d_out],
+// fp32 or bf16).  The output itself is written only when y is not null.
+struct ProdEpilogue {
+  const void* pm;
+  bool pm_bf16;
+  float* psum;
+  int64_t ldp;
+};
+int64_t prefill_row_blocks(int64_t T);  // the 128-row blocks of a T-token output
 hipError_t launch_prefill(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y,
-                          void* ws, hipStream_t s, bool split = true);
+                          void* ws, hipStream_t s, bool split = true, const ProdEpilogue* pe = nullptr);
 
 }  // namespace nq

@@ -304,6 +304,12 @@ __device__ inline void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// An element of the product operand of the stage-2 epilogue (fp32 or bf16).
+__device__ inline float load_prod(const void* p, int bf16, int64_t i) {
+  return bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16) : static_cast<const float*>(p)[i];
+}
+constexpr int kTileRowsFixed = 128;  // output rows per workgroup tile (64 * kTileMB), per product block
+
 // s_waitcnt that waits until at most n vector-memory operations of this wave
 // are outstanding (lgkmcnt and expcnt left alone).
 template <int N>
@@ -333,12 +339,15 @@ struct Pipe {
 // consecutive rows read at the same logical chunk hit 16 distinct 16-byte bank
 // groups, so the 32-row fragment reads below are conflict-free.  The stage's
 // sign words follow: word row q (of the tile's two) at [q][kBN columns].
-template <int NT, int MB>
+// PROD: the epilogue also takes the column products of ProdEpilogue (a kernel
+// of its own, so that the plain GEMM keeps its registers and LDS).
+template <int NT, int MB, bool PROD>
 __global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
     const _Float16* __restrict__ A, const int* __restrict__ erow, const float* __restrict__ crow,
     const uint32_t* __restrict__ bits, int64_t ldb,
     int64_t M, int64_t N, int64_t K, int64_t Kpad, int tiles_m, int tiles_n, int nsplit, int kts,
-    uint32_t sign_mask, uint32_t one, const float* __restrict__ colscale, float* __restrict__ out) {
+    uint32_t sign_mask, uint32_t one, const float* __restrict__ colscale, float* __restrict__ out,
+    const void* __restrict__ pm, int pm_bf16, float* __restrict__ psum, int64_t ldp) {
   using P = Pipe<NT, MB>;
   constexpr bool ROT = NT == 1;  // rotated operand encoding (see rot_element)
   extern __shared__ __attribute__((aligned(16))) char lds[];  // [S][A tiles | sign words]
@@ -500,9 +509,13 @@ __global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
   // applied by whoever adds the partials).
   // Exponents (and, in the rotated encoding, the correction sums) are per
   // reduction piece and row.
-  float* dst = out + (int64_t)split * M * N;
+  // With psum (only without a split), each column's products pm * v over the
+  // tile's rows are summed: per lane over its 16 rows of each 32-row block in
+  // order, then the two lane halves, then the two wave rows through LDS.
+  float* dst = (!PROD || out) ? out + (int64_t)split * M * N : nullptr;
   const int* ep = erow + (int64_t)split * M;
   const float* cp = crow + (int64_t)split * M;
+  float colsum[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -515,11 +528,53 @@ __global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
         for (int c = 0; c < 4; ++c) {
           const int64_t m = m0 + wm * 32 * MB + mb * 32 + 8 * a + 4 * h + c;
           if (m < M && n < N) {
-            const float v = ROT ? acc[mb][nb][4 * a + c] - cp[m] : acc[mb][nb][4 * a + c];
-            dst[m * N + n] = sc * ldexpf(v, -ep[m]);
+            const float v = ldexpf(ROT ? acc[mb][nb][4 * a + c] - cp[m] : acc[mb][nb][4 * a + c], -ep[m]);
+            if (!PROD || dst) dst[m * N + n] = sc * v;
+            if constexpr (PROD) colsum[nb] = fmaf(load_prod(pm, pm_bf16, m * N + n), v, colsum[nb]);
           }
         }
     }
+  if constexpr (PROD) {
+    __shared__ float s_col[2][kBN];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      colsum[nb] += __shfl_xor(colsum[nb], 32);  // lanes l and l+32 hold rows of one column
+      if (h == 0) s_col[wm][wn * 64 + nb * 32 + l32] = colsum[nb];
+    }
+    __syncthreads();
+    if (wm == 0 && h == 0) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int c = wn * 64 + nb * 32 + l32;
+        if (n0 + c < N) psum[(int64_t)(tt / tiles_n) * ldp + n0 + c] = s_col[0][c] + s_col[1][c];
+      }
+    }
+  }
+}
+
+// The same outputs and column products when the reduction was split:
+// v[m][n] = sum over splits of part[split][m][n] in split order, y[m][n] =
+// colscale[n] * v (y may be null), psum[q * ldp + n] = sum over the rows of
+// 128-row block q, in order, of pm[m][n] * v.  Grid: (column tiles of 256,
+// row blocks).
+__global__ __launch_bounds__(256) void split_sum_prod_kernel(const float* __restrict__ part, int nsplit, int64_t M,
+                                                             int64_t N, const float* __restrict__ colscale,
+                                                             float* __restrict__ y, const void* __restrict__ pm,
+                                                             int pm_bf16, float* __restrict__ psum, int64_t ldp) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const int64_t MN = M * N;
+  const int64_t m0 = (int64_t)blockIdx.y * kTileRowsFixed, m1 = imin(m0 + kTileRowsFixed, M);
+  const float sc = colscale ? colscale[n] : 1.0f;
+  float acc = 0.0f;
+  for (int64_t m = m0; m < m1; ++m) {
+    const int64_t i = m * N + n;
+    float v = part[i];
+    for (int sp = 1; sp < nsplit; ++sp) v += part[(int64_t)sp * MN + i];
+    if (y) y[i] = sc * v;
+    acc = fmaf(load_prod(pm, pm_bf16, i), v, acc);
+  }
+  psum[(int64_t)blockIdx.y * ldp + n] = acc;
 }
 
 // y[m][n] = colscale[n] * sum over splits of part[split][m][n], in split order
@@ -580,6 +635,7 @@ hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int
 // shapes: two waves per SIMD hide too little LDS and barrier latency.
 constexpr int kTileMB = 2;
 constexpr int kTileRows = 64 * kTileMB;
+static_assert(kTileRows == kTileRowsFixed, "product blocks are the GEMM's row tiles");
 constexpr int kWgSlots = kTileMB == 2 ? 512 : 256;  // resident workgroups on 256 CUs
 
 // Reduction split of one GEMM: a GEMM with fewer output tiles than resident
@@ -602,10 +658,10 @@ Split split_plan(int64_t M, int64_t N, int64_t Kpad, bool allow) {
   return {(int)cdiv(nk, kts), kts};
 }
 
-template <int NT, int MB>
-hipError_t launch_gemm_t(decltype(&gemm_kernel<NT, MB>) kernel, const _Float16* A, const int* e, const float* c,
+template <int NT, int MB, bool PROD>
+hipError_t launch_gemm_t(decltype(&gemm_kernel<NT, MB, PROD>) kernel, const _Float16* A, const int* e, const float* c,
                          const uint32_t* bits, int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t Kpad, Split sp,
-                         const float* colscale, float* out, hipStream_t s) {
+                         const float* colscale, float* out, const ProdEpilogue* pe, hipStream_t s) {
   using P = Pipe<NT, MB>;
   static bool configured = false;
   if (!configured) {
@@ -617,17 +673,24 @@ hipError_t launch_gemm_t(decltype(&gemm_kernel<NT, MB>) kernel, const _Float16* 
   const int tiles_m = (int)cdiv(M, P::BM), tiles_n = (int)cdiv(N, kBN);
   const unsigned grid = (unsigned)(8 * ((tiles_m * tiles_n * sp.n + 7) / 8));
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), P::LDS, s, A, e, c, bits, ldb, M, N, K, Kpad, tiles_m,
-                     tiles_n, sp.n, sp.kts, kSignMask, kOnePair, colscale, out);
+                     tiles_n, sp.n, sp.kts, kSignMask, kOnePair, colscale, out, pe ? pe->pm : nullptr,
+                     pe ? (int)pe->pm_bf16 : 0, pe ? pe->psum : nullptr, pe ? pe->ldp : (int64_t)0);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(int nt, const _Float16* A, const int* e, const float* c, const uint32_t* bits, int64_t ldb,
                        int64_t M, int64_t N, int64_t K, int64_t Kpad, Split sp, const float* colscale, float* out,
-                       hipStream_t s) {
+                       hipStream_t s, const ProdEpilogue* pe = nullptr) {
   constexpr int MB = kTileMB;
-  return nt == 1
-             ? launch_gemm_t<1, MB>(gemm_kernel<1, MB>, A, e, c, bits, ldb, M, N, K, Kpad, sp, colscale, out, s)
-             : launch_gemm_t<2, MB>(gemm_kernel<2, MB>, A, e, c, bits, ldb, M, N, K, Kpad, sp, colscale, out, s);
+  if (pe)
+    return nt == 1 ? launch_gemm_t<1, MB, true>(gemm_kernel<1, MB, true>, A, e, c, bits, ldb, M, N, K, Kpad, sp,
+                                                colscale, out, pe, s)
+                   : launch_gemm_t<2, MB, true>(gemm_kernel<2, MB, true>, A, e, c, bits, ldb, M, N, K, Kpad, sp,
+                                                colscale, out, pe, s);
+  return nt == 1 ? launch_gemm_t<1, MB, false>(gemm_kernel<1, MB, false>, A, e, c, bits, ldb, M, N, K, Kpad, sp,
+                                               colscale, out, nullptr, s)
+                 : launch_gemm_t<2, MB, false>(gemm_kernel<2, MB, false>, A, e, c, bits, ldb, M, N, K, Kpad, sp,
+                                               colscale, out, nullptr, s);
 }
 
 struct PrefillLayout {
@@ -676,8 +739,10 @@ size_t prefill_workspace_bytes(const nq_lrb& L, int64_t T, bool split) {
   return prefill_layout(L, T, NQ_F32, split).total;
 }
 
+int64_t prefill_row_blocks(int64_t T) { return cdiv(T, kTileRows); }
+
 hipError_t launch_prefill(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
-                          hipStream_t s, bool split) {
+                          hipStream_t s, bool split, const ProdEpilogue* pe) {
   const PrefillLayout d = prefill_layout(L, T, xd, split);
   char* base = static_cast<char*>(ws);
   _Float16* z = reinterpret_cast<_Float16*>(base + d.off_z);
@@ -703,10 +768,16 @@ hipError_t launch_prefill(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T
       hipSuccess)
     return e;
   if (d.sp2.n == 1)
-    return launch_gemm(d.nt, t16, e2, c2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, L.s1, y, s);
+    return launch_gemm(d.nt, t16, e2, c2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, L.s1, y, s, pe);
   if ((e = launch_gemm(d.nt, t16, e2, c2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, nullptr, y2, s)) !=
       hipSuccess)
     return e;
+  if (pe) {
+    const dim3 grid((unsigned)cdiv(L.d_out, 256), (unsigned)cdiv(T, kTileRows));
+    hipLaunchKernelGGL(split_sum_prod_kernel, grid, dim3(256), 0, s, y2, d.sp2.n, T, L.d_out, L.s1, y, pe->pm,
+                       (int)pe->pm_bf16, pe->psum, pe->ldp);
+    return hipGetLastError();
+  }
   const int64_t MN = T * L.d_out;
   const unsigned grid = (unsigned)imin(cdiv(MN, 256), (int64_t)4096);
   hipLaunchKernelGGL(split_sum_kernel, dim3(grid), dim3(256), 0, s, y2, d.sp2.n, MN, L.d_out, L.s1, y);
