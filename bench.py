@@ -288,15 +288,23 @@ def time_scale_grads(stack, T: int, device: str, reps: int = 3) -> dict:
     def grads_all():
         for L, a, x, g in zip(layers, adjs, xs, gs):
             nq.lrb_scale_grads(L, a, x, g, workspace=ws)
-    for _ in range(_warm(grads_all, 1, WARM_MS)):
-        grads_all()
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        grads_all()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    wsb = torch.empty(nq.lrb_scale_grads_batch_workspace_bytes(layers, T), dtype=torch.uint8, device=device)
+
+    def grads_batch():
+        return nq.lrb_scale_grads_batch(layers, adjs, xs, gs, workspace=wsb)
+
+    def timed(fn):
+        for _ in range(_warm(fn, 1, WARM_MS)):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    ms_single = timed(grads_all)
+    ms = timed(grads_batch)
     flops = sum(2 * 2 * T * s.r * (s.d_in + s.d_out) for s in shapes)  # forward + transposed product
     # parity of the timed call itself: layer 0's k at T tokens, every element
     # of dx, ds1 and ds2 against the factored float64 oracle
@@ -304,13 +312,17 @@ def time_scale_grads(stack, T: int, device: str, reps: int = 3) -> dict:
     from tests import checks as C
     k = [s.name for s in shapes].index("k")
     ref = C.splitmix_ref(stack.cfg, shapes[k], 0)
-    got = nq.lrb_scale_grads(layers[k], adjs[k], xs[k], gs[k])
+    got = grads_batch()[k]
+    single = nq.lrb_scale_grads(layers[k], adjs[k], xs[k], gs[k])
     want = O.scale_grads_factored_ref(ref, xs[k].float().cpu().numpy(), gs[k].float().cpu().numpy())
     checks = [C.check(got[0].cpu().numpy(), want[0], 2e-3)]
     checks += [C.check(g.cpu().numpy()[None, :], w[None, :], 2e-3) for g, w in zip(got[1:], want[1:])]
     par = _summ(checks)
-    par["checked"] = f"layer 0 k, T={T}: every element of dx, ds1, ds2"
-    return {"T": T, "linears": f"layer 0 ({per} linears)", "ms_per_layer": ms,
+    par["checked"] = f"layer 0 k, T={T}: every element of dx, ds1, ds2 of the batched call"
+    par["batch_equals_single_calls"] = all(torch.equal(a.view(torch.int32), b.view(torch.int32))
+                                           for a, b in zip(got, single))
+    return {"T": T, "linears": f"layer 0 ({per} linears) in one batched call", "ms_per_layer": ms,
+            "ms_per_layer_single_calls": ms_single,
             "tflops": flops / (ms * 1e-3) / 1e12, "frac_of_f16_peak": flops / (ms * 1e-3) / 1e12 / F16_PEAK_TFLOPS,
             "algorithmic_flop_per_layer": flops,
             "includes": "forward product without s1, transposed product without s2, token sums; x and g bf16",

@@ -236,6 +236,30 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
                              float* ds2, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nq_lrb_scale_grads_batch -- nq_lrb_scale_grads for n independent linears in
+ * one call (the linears of a decoder layer, say: section 3 "Phase 3: Scale-Only
+ * Model Reconstruction" tunes every layer's scales against the model's
+ * outputs).  Linear i takes L[i], ut_bits[i]/ldut[i], v_bits[i]/ldvv[i], x[i],
+ * g[i] and writes dx[i], ds1[i], ds2[i], each as in nq_lrb_scale_grads; all
+ * share T, x_dtype and g_dtype.  The results equal n calls of
+ * nq_lrb_scale_grads bit for bit.  With T > 8 the 2n products (forward and
+ * transposed of each linear) run round-robin on three streams that the library
+ * makes on a device's first such call and keeps, forked from and joined back
+ * to `stream`, so that one product's prep kernels and partly filled GEMM waves
+ * run beside another's GEMMs; with T <= 8 the linears run one after another.
+ *   workspace: at least nq_lrb_scale_grads_batch_workspace_bytes(n, L, T)
+ *   bytes, 256-byte aligned; the query returns 0 for invalid arguments.
+ * Errors: as for nq_lrb_scale_grads, for each linear (the message names it);
+ * NQ_ERR_ARG for n < 1 or a null array.
+ */
+size_t nq_lrb_scale_grads_batch_workspace_bytes(int64_t n, const nq_lrb* L, int64_t T);
+nq_status nq_lrb_scale_grads_batch(int64_t n, const nq_lrb* L, const uint32_t* const* ut_bits,
+                                   const int64_t* ldut, const uint32_t* const* v_bits, const int64_t* ldvv,
+                                   const void* const* x, nq_dtype x_dtype, const void* const* g,
+                                   nq_dtype g_dtype, int64_t T, float* const* dx, float* const* ds1,
+                                   float* const* ds2, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * nq_lrb_linear_latent -- the layer with the signs taken from real latent
  *   factors at the call: y = s1 (.) sign(U)(sign(V)^T (s2 (.) x)), the forward
  *   pass of the factorized component refinement (section 3 "Step 3:

@@ -7,7 +7,8 @@ no fallback: if libnq.so is missing or fails to load, every call raises.
 Names follow the C ABI in include/nq.h:
   pack_signs, unpack_signs, lrb_linear, lrb_workspace_bytes, reconstruct,
   storage_bits, fill_random_words, Seq (nq_seq_*), transpose_signs,
-  lrb_scale_grads (nq_lrb_scale_grads*), last_error.
+  lrb_scale_grads (nq_lrb_scale_grads*), lrb_scale_grads_batch
+  (nq_lrb_scale_grads_batch*), last_error.
 """
 from __future__ import annotations
 
@@ -30,7 +31,8 @@ EXPORTED = [
     "nq_pack_signs", "nq_unpack_signs", "nq_lrb_workspace_bytes", "nq_lrb_linear", "nq_reconstruct",
     "nq_storage_bits", "nq_seq_create", "nq_seq_workspace_bytes", "nq_seq_run", "nq_seq_destroy",
     "nq_fill_random_words", "nq_last_error", "nq_version", "nq_transpose_signs",
-    "nq_lrb_scale_grads_workspace_bytes", "nq_lrb_scale_grads", "nq_balance_workspace_bytes",
+    "nq_lrb_scale_grads_workspace_bytes", "nq_lrb_scale_grads", "nq_lrb_scale_grads_batch_workspace_bytes",
+    "nq_lrb_scale_grads_batch", "nq_balance_workspace_bytes",
     "nq_balance_factors", "nq_lrb_latent_workspace_bytes", "nq_lrb_linear_latent", "nq_lrb_linear_noalloc",
 ]
 
@@ -98,6 +100,11 @@ def lib() -> ctypes.CDLL:
     L.nq_lrb_scale_grads.argtypes = [P(nq_lrb), vp, i64, vp, i64, vp, ctypes.c_int, vp, ctypes.c_int, i64, vp, vp, vp,
                                      vp, sz, vp]
     L.nq_lrb_scale_grads.restype = st
+    L.nq_lrb_scale_grads_batch_workspace_bytes.argtypes = [i64, P(nq_lrb), i64]
+    L.nq_lrb_scale_grads_batch_workspace_bytes.restype = sz
+    L.nq_lrb_scale_grads_batch.argtypes = [i64, P(nq_lrb), P(vp), P(i64), P(vp), P(i64), P(vp), ctypes.c_int, P(vp),
+                                           ctypes.c_int, i64, P(vp), P(vp), P(vp), vp, sz, vp]
+    L.nq_lrb_scale_grads_batch.restype = st
     L.nq_lrb_latent_workspace_bytes.argtypes = [i64, i64, i64, i64]
     L.nq_lrb_latent_workspace_bytes.restype = sz
     L.nq_lrb_linear_latent.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp, vp, vp, ctypes.c_int, i64, vp, vp, sz, vp]
@@ -382,6 +389,49 @@ def lrb_scale_grads(layer: Lrb, adj: Adjoint, x: torch.Tensor, g: torch.Tensor,
                                     _ptr(ds2), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)))
     return dx, ds1, ds2
+
+
+def lrb_scale_grads_batch_workspace_bytes(layers, T: int) -> int:
+    arr = (nq_lrb * len(layers))(*[L.struct() for L in layers])
+    return int(lib().nq_lrb_scale_grads_batch_workspace_bytes(len(layers), arr, T))
+
+
+def lrb_scale_grads_batch(layers, adjs, xs, gs, workspace: torch.Tensor | None = None, stream=None):
+    """lrb_scale_grads for several independent linears in one call (same T and
+    dtypes): a list of (dx, ds1, ds2), equal bit for bit to separate calls."""
+    n = len(layers)
+    if not (n == len(adjs) == len(xs) == len(gs)) or n < 1:
+        raise ValueError("layers, adjs, xs and gs must be non-empty lists of one length")
+    T = xs[0].shape[0]
+    xd, gd = _x_dtype(xs[0]), _x_dtype(gs[0])
+    for L, x, g in zip(layers, xs, gs):
+        _dev(x, "x")
+        _dev(g, "g")
+        if x.dim() != 2 or tuple(x.shape) != (T, L.d_in) or _x_dtype(x) != xd:
+            raise ValueError(f"every x must be [{T}][d_in] of one dtype, got {tuple(x.shape)}")
+        if tuple(g.shape) != (T, L.d_out) or not g.is_contiguous() or _x_dtype(g) != gd:
+            raise ValueError(f"every g must be contiguous [{T}][d_out] of one dtype, got {tuple(g.shape)}")
+    arr = (nq_lrb * n)(*[L.struct() for L in layers])
+    need = int(lib().nq_lrb_scale_grads_batch_workspace_bytes(n, arr, T))
+    dev = xs[0].device
+    with _on(stream):
+        outs = [(torch.empty((T, L.d_in), dtype=torch.float32, device=dev),
+                 torch.empty(L.d_out, dtype=torch.float32, device=dev),
+                 torch.empty(L.d_in, dtype=torch.float32, device=dev)) for L in layers]
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def ptrs(ts):
+        return (ctypes.c_void_p * n)(*[_ptr(t) for t in ts])
+
+    def lds(ts):
+        return (ctypes.c_int64 * n)(*[t.shape[1] for t in ts])
+    _check(lib().nq_lrb_scale_grads_batch(
+        n, arr, ptrs([a.ut_bits for a in adjs]), lds([a.ut_bits for a in adjs]), ptrs([a.v_bits for a in adjs]),
+        lds([a.v_bits for a in adjs]), ptrs(xs), xd, ptrs(gs), gd, T, ptrs([o[0] for o in outs]),
+        ptrs([o[1] for o in outs]), ptrs([o[2] for o in outs]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return outs
 
 
 def balance_factors(u_hat: torch.Tensor, v_hat: torch.Tensor, r: int | None = None, balanced: bool = True,

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <mutex>
 #include <new>
+#include <string>
 #include <array>
 #include <vector>
 
@@ -182,6 +183,96 @@ hipError_t side_stream(SideStream** out) {
   *out = &ss;
   return hipSuccess;
 }
+
+// Streams per device for batched calls (entries round-robin on them), with a
+// fork event and one join event per stream; made on first use and kept, under
+// the same mutex as the side stream.
+constexpr int kBatchLanes = 3;
+struct LaneSet {
+  hipStream_t s[kBatchLanes] = {};
+  hipEvent_t fork = nullptr, join[kBatchLanes] = {};
+};
+std::vector<LaneSet> g_lanes;
+
+hipError_t lane_set(LaneSet** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if ((int)g_lanes.size() <= dev) g_lanes.resize(dev + 1);
+  LaneSet& ls = g_lanes[dev];
+  if (!ls.fork) {
+    LaneSet n;
+    for (int l = 0; l < kBatchLanes && e == hipSuccess; ++l) {
+      e = hipStreamCreateWithFlags(&n.s[l], hipStreamNonBlocking);  // default priority
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join[l], hipEventDisableTiming);
+    }
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    ls = n;
+  }
+  *out = &ls;
+  return hipSuccess;
+}
+
+// Workspace of nq_lrb_scale_grads_batch in the matrix-core regime: per stream
+// [block partial sums][one linear workspace], each sized for the largest of
+// the batch's linears.
+struct BatchGradsLayout {
+  size_t off_part, off_lin, lane, bytes;
+};
+BatchGradsLayout batch_grads_layout(const nq_lrb* L, int64_t n, int64_t T) {
+  size_t part = 0, lin = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    part = std::max(part, (size_t)prefill_row_blocks(T) * (L[i].d_in + L[i].d_out) * sizeof(float));
+    const nq_lrb A = adjoint_layer(L[i], L[i].vt_bits, L[i].r, L[i].u_bits, L[i].d_in);  // sizes only
+    lin = std::max(lin, std::max(linear_workspace(L[i], T), linear_workspace(A, T)));
+  }
+  BatchGradsLayout b;
+  b.off_part = 0;
+  b.off_lin = align_up(part);
+  b.lane = align_up(b.off_lin + lin);
+  b.bytes = kBatchLanes * b.lane;
+  return b;
+}
+
+// Checks of one linear's scale-gradient arguments; the transposed layer into A.
+nq_status check_grads(const char* who, const nq_lrb* L, const uint32_t* ut_bits, int64_t ldut, const uint32_t* v_bits,
+                      int64_t ldvv, const void* x, nq_dtype x_dtype, const void* g, nq_dtype g_dtype, int64_t T,
+                      const float* dx, const float* ds1, const float* ds2, nq_lrb* A) {
+  nq_status st = check_lrb(who, L);
+  if (st != NQ_OK) return st;
+  // the transposed layer W^T: outputs d_in, reduction d_out; its U is V (words
+  // along r), its V^T is U^T (words along d_out); its scales are s2 and s1
+  *A = adjoint_layer(*L, ut_bits, ldut, v_bits, ldvv);
+  if ((st = check_lrb("nq_lrb_scale_grads (transposed sign words)", A)) != NQ_OK) return st;
+  if ((st = check_io(who, L, x, x_dtype, T, dx)) != NQ_OK) return st;
+  if (g_dtype != NQ_F32 && g_dtype != NQ_BF16) return set_error("%s: unknown g dtype %d", who, (int)g_dtype), NQ_ERR_ARG;
+  if (!g || !ds1 || !ds2) return set_error("%s: null g, ds1 or ds2", who), NQ_ERR_ARG;
+  if (!aligned(g, g_dtype == NQ_F32 ? 4 : 2) || !aligned(ds1, 4) || !aligned(ds2, 4))
+    return set_error("%s: g, ds1 or ds2 misaligned", who), NQ_ERR_ARG;
+  return NQ_OK;
+}
+
+// One product chain of the matrix-core regime on stream s: the forward product
+// (transposed = false: u only summed against g into ds1) or the transposed one
+// (dx written, x (.) b summed into ds2), then its blocks added in order.
+hipError_t enqueue_grads_chain(const nq_lrb& L, const nq_lrb& A, bool transposed, const void* x, nq_dtype x_dtype,
+                               const void* g, nq_dtype g_dtype, int64_t T, float* dx, float* ds1, float* ds2,
+                               float* part, char* lin, hipStream_t s) {
+  const int64_t nb = prefill_row_blocks(T), ldp = L.d_in + L.d_out;
+  if (transposed) {
+    const ProdEpilogue pb{x, x_dtype == NQ_BF16, part, ldp};
+    hipError_t e = launch_prefill(A, g, g_dtype, T, dx, lin, s, true, &pb);
+    return e == hipSuccess ? launch_scale_grads_sums(part, nb, L.d_in, L.d_out, ds1, ds2, 0, L.d_in, s) : e;
+  }
+  nq_lrb Lu = L;  // u = U (V^T (s2 (.) x)): the forward product without s1
+  Lu.s1 = nullptr;
+  const ProdEpilogue pu{g, g_dtype == NQ_BF16, part + L.d_in, ldp};
+  hipError_t e = launch_prefill(Lu, x, x_dtype, T, nullptr, lin, s, true, &pu);
+  return e == hipSuccess ? launch_scale_grads_sums(part, nb, L.d_in, L.d_out, ds1, ds2, L.d_in, L.d_in + L.d_out, s)
+                         : e;
+}
+
 
 }  // namespace
 }  // namespace nq
@@ -479,17 +570,9 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
                              void* stream) {
   clear_error();
   const char* who = "nq_lrb_scale_grads";
-  nq_status st = check_lrb(who, L);
+  nq_lrb A;
+  nq_status st = check_grads(who, L, ut_bits, ldut, v_bits, ldvv, x, x_dtype, g, g_dtype, T, dx, ds1, ds2, &A);
   if (st != NQ_OK) return st;
-  // the transposed layer W^T: outputs d_in, reduction d_out; its U is V (words
-  // along r), its V^T is U^T (words along d_out); its scales are s2 and s1
-  nq_lrb A = adjoint_layer(*L, ut_bits, ldut, v_bits, ldvv);
-  if ((st = check_lrb("nq_lrb_scale_grads (transposed sign words)", &A)) != NQ_OK) return st;
-  if ((st = check_io(who, L, x, x_dtype, T, dx)) != NQ_OK) return st;
-  if (g_dtype != NQ_F32 && g_dtype != NQ_BF16) return set_error("%s: unknown g dtype %d", who, (int)g_dtype), NQ_ERR_ARG;
-  if (!g || !ds1 || !ds2) return set_error("%s: null g, ds1 or ds2", who), NQ_ERR_ARG;
-  if (!aligned(g, g_dtype == NQ_F32 ? 4 : 2) || !aligned(ds1, 4) || !aligned(ds2, 4))
-    return set_error("%s: g, ds1 or ds2 misaligned", who), NQ_ERR_ARG;
   const ScaleGradsLayout lay = scale_grads_layout(*L, T);
   if (!workspace || workspace_bytes < lay.bytes)
     return set_error("%s: workspace %zu bytes, need %zu", who, workspace ? workspace_bytes : 0, lay.bytes),
@@ -507,9 +590,6 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
     // block (ds1 from g (.) u with u never stored; ds2 from x (.) b while the
     // transposed product, its row scale s2 kept, writes dx), and each stream
     // adds its blocks in order
-    const int64_t nb = prefill_row_blocks(T), ldp = L->d_in + L->d_out;
-    const ProdEpilogue pu{g, g_dtype == NQ_BF16, part + L->d_in, ldp};
-    const ProdEpilogue pb{x, x_dtype == NQ_BF16, part, ldp};
     hipError_t e;
     {
       std::lock_guard<std::mutex> lock(g_side_mu);
@@ -517,11 +597,11 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
       e = side_stream(&side);
       if (e == hipSuccess) e = hipEventRecord(side->fork, s);
       if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
-      if (e == hipSuccess) e = launch_prefill(A, g, g_dtype, T, dx, ws + lay.off_lin_t, side->s, true, &pb);
-      if (e == hipSuccess) e = launch_scale_grads_sums(part, nb, L->d_in, L->d_out, ds1, ds2, 0, L->d_in, side->s);
-      if (e == hipSuccess) e = launch_prefill(Lu, x, x_dtype, T, nullptr, ws + lay.off_lin, s, true, &pu);
       if (e == hipSuccess)
-        e = launch_scale_grads_sums(part, nb, L->d_in, L->d_out, ds1, ds2, L->d_in, L->d_in + L->d_out, s);
+        e = enqueue_grads_chain(*L, A, true, x, x_dtype, g, g_dtype, T, dx, ds1, ds2, part, ws + lay.off_lin_t,
+                                side->s);
+      if (e == hipSuccess)
+        e = enqueue_grads_chain(*L, A, false, x, x_dtype, g, g_dtype, T, dx, ds1, ds2, part, ws + lay.off_lin, s);
       if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
       if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
     }
@@ -551,6 +631,76 @@ nq_status nq_lrb_scale_grads(const nq_lrb* L, const uint32_t* ut_bits, int64_t l
     if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
   }
   return hip_status(e, "nq_lrb_scale_grads launch");
+}
+
+size_t nq_lrb_scale_grads_batch_workspace_bytes(int64_t n, const nq_lrb* L, int64_t T) {
+  if (n < 1 || n > (int64_t(1) << 20) || !L || T < 1 || T > (int64_t(1) << 24)) return 0;
+  size_t single = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    if (check_lrb("nq_lrb_scale_grads_batch_workspace_bytes", &L[i]) != NQ_OK) return 0;
+    single = std::max(single, scale_grads_layout(L[i], T).bytes);
+  }
+  return T > kDecodeMaxT ? batch_grads_layout(L, n, T).bytes : single;
+}
+
+nq_status nq_lrb_scale_grads_batch(int64_t n, const nq_lrb* L, const uint32_t* const* ut_bits, const int64_t* ldut,
+                                   const uint32_t* const* v_bits, const int64_t* ldvv, const void* const* x,
+                                   nq_dtype x_dtype, const void* const* g, nq_dtype g_dtype, int64_t T,
+                                   float* const* dx, float* const* ds1, float* const* ds2, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* who = "nq_lrb_scale_grads_batch";
+  if (n < 1 || n > (int64_t(1) << 20)) return set_error("%s: n = %lld", who, (long long)n), NQ_ERR_ARG;
+  if (!L || !ut_bits || !ldut || !v_bits || !ldvv || !x || !g || !dx || !ds1 || !ds2)
+    return set_error("%s: null array", who), NQ_ERR_ARG;
+  std::vector<nq_lrb> A((size_t)n);
+  for (int64_t i = 0; i < n; ++i) {
+    nq_status st = check_grads(who, &L[i], ut_bits[i], ldut[i], v_bits[i], ldvv[i], x[i], x_dtype, g[i], g_dtype, T,
+                               dx[i], ds1[i], ds2[i], &A[(size_t)i]);
+    if (st != NQ_OK) {
+      const std::string why = nq_last_error();  // the message buffer is rewritten below
+      return set_error("%s: linear %lld: %s", who, (long long)i, why.c_str()), st;
+    }
+  }
+  const size_t need = nq_lrb_scale_grads_batch_workspace_bytes(n, L, T);
+  if (!workspace || workspace_bytes < need)
+    return set_error("%s: workspace %zu bytes, need %zu", who, workspace ? workspace_bytes : 0, need),
+           NQ_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return set_error("%s: workspace not 256-byte aligned", who), NQ_ERR_ARG;
+  if (T <= kDecodeMaxT) {  // the decode regime: the linears one after another
+    for (int64_t i = 0; i < n; ++i) {
+      nq_status st = nq_lrb_scale_grads(&L[i], ut_bits[i], ldut[i], v_bits[i], ldvv[i], x[i], x_dtype, g[i], g_dtype,
+                                        T, dx[i], ds1[i], ds2[i], workspace, workspace_bytes, stream);
+      if (st != NQ_OK) return st;
+    }
+    return NQ_OK;
+  }
+  // matrix-core regime: the 2n product chains (transposed and forward of each
+  // linear) round-robin on the library's streams, each with its own slice of
+  // the workspace; forked from and joined back to the caller's stream
+  const BatchGradsLayout lay = batch_grads_layout(L, n, T);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    LaneSet* ls = nullptr;
+    e = lane_set(&ls);
+    if (e == hipSuccess) e = hipEventRecord(ls->fork, s);
+    for (int l = 0; l < kBatchLanes && e == hipSuccess; ++l) e = hipStreamWaitEvent(ls->s[l], ls->fork, 0);
+    for (int64_t c = 0; c < 2 * n && e == hipSuccess; ++c) {
+      const int64_t i = c / 2;
+      const int l = (int)(c % kBatchLanes);
+      char* lane = ws + (size_t)l * lay.lane;
+      e = enqueue_grads_chain(L[i], A[(size_t)i], c % 2 == 0, x[i], x_dtype, g[i], g_dtype, T, dx[i], ds1[i], ds2[i],
+                              reinterpret_cast<float*>(lane + lay.off_part), lane + lay.off_lin, ls->s[l]);
+    }
+    for (int l = 0; l < kBatchLanes && e == hipSuccess; ++l) {
+      e = hipEventRecord(ls->join[l], ls->s[l]);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, ls->join[l], 0);
+    }
+  }
+  return hip_status(e, "nq_lrb_scale_grads_batch launch");
 }
 
 size_t nq_balance_workspace_bytes(int64_t d_out, int64_t d_in) {

@@ -170,6 +170,51 @@ def test_scale_grads_workspace_query():
     assert lib.nq_lrb_scale_grads_workspace_bytes(ctypes.byref(_layer(r=0)), 4) == 0
 
 
+def _grads_batch(layers, n=None, ut=DUMMY, ldut=32, v=DUMMY, ldvv=64, x=DUMMY, dtype=nq.NQ_BF16, g=DUMMY,
+                 gdtype=nq.NQ_F32, T=1, dx=DUMMY, ds1=DUMMY, ds2=DUMMY, ws=DUMMY, wsb=1 << 40):
+    k = len(layers)
+    arr = (nq.nq_lrb * k)(*layers)
+
+    def ptrs(p):
+        return (ctypes.c_void_p * k)(*([p] * k))
+
+    def ints(i):
+        return (ctypes.c_int64 * k)(*([i] * k))
+    return nq.lib().nq_lrb_scale_grads_batch(k if n is None else n, arr, ptrs(ut), ints(ldut), ptrs(v), ints(ldvv),
+                                             ptrs(x), dtype, ptrs(g), gdtype, T, ptrs(dx), ptrs(ds1), ptrs(ds2), ws,
+                                             wsb, None)
+
+
+def test_scale_grads_batch_rejects_bad_args():
+    L = _layer()
+    assert _grads_batch([L, L], n=0) == nq.NQ_ERR_ARG
+    assert nq.lib().nq_lrb_scale_grads_batch(1, None, None, None, None, None, None, nq.NQ_BF16, None, nq.NQ_F32, 1,
+                                             None, None, None, DUMMY, 1 << 40, None) == nq.NQ_ERR_ARG
+    assert _grads_batch([L, L], ldut=31) == nq.NQ_ERR_ARG
+    assert "linear 0" in nq.last_error()
+    assert _grads_batch([L, _layer(d_in=0)]) == nq.NQ_ERR_ARG
+    assert "linear 1" in nq.last_error()
+    assert _grads_batch([L, L], gdtype=5) == nq.NQ_ERR_ARG
+    assert _grads_batch([L, L], T=0) == nq.NQ_ERR_ARG
+    assert _grads_batch([L, L], ws=None) == nq.NQ_ERR_WORKSPACE
+    assert _grads_batch([L, L], wsb=16, T=64) == nq.NQ_ERR_WORKSPACE
+    assert _grads_batch([L, L], ws=DUMMY + 4) == nq.NQ_ERR_ARG
+
+
+def test_scale_grads_batch_workspace_query():
+    L = _layer()
+    lib = nq.lib()
+    arr = (nq.nq_lrb * 2)(L, L)
+    for T in (4, 64):
+        single = lib.nq_lrb_scale_grads_workspace_bytes(ctypes.byref(L), T)
+        assert lib.nq_lrb_scale_grads_batch_workspace_bytes(2, arr, T) >= single > 0
+    # matrix-core regime: three streams, each with a linear workspace
+    assert lib.nq_lrb_scale_grads_batch_workspace_bytes(2, arr, 64) >= 3 * lib.nq_lrb_workspace_bytes(ctypes.byref(L), 64)
+    assert lib.nq_lrb_scale_grads_batch_workspace_bytes(0, arr, 64) == 0
+    assert lib.nq_lrb_scale_grads_batch_workspace_bytes(2, arr, 0) == 0
+    assert lib.nq_lrb_scale_grads_batch_workspace_bytes(2, (nq.nq_lrb * 2)(L, _layer(r=0)), 4) == 0
+
+
 def _balance(u=DUMMY, d_out=8, ldu=4, v=DUMMY, d_in=5, ldv=4, r=4, uo=None, vo=None, s1=DUMMY, s2=DUMMY, eta=DUMMY,
              ws=DUMMY, wsb=1 << 20):
     return nq.lib().nq_balance_factors(u, d_out, ldu, v, d_in, ldv, r, uo, vo, s1, s2, eta, ws, wsb, None)

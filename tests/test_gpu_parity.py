@@ -494,6 +494,32 @@ def test_scale_grads_many_token_chunks():
         assert O.rel_err(got.cpu().numpy(), want) <= G.prefill_tol("bf16")
 
 
+@pytest.mark.parametrize("T", [4, 200])
+def test_scale_grads_batch_matches_single_calls(T):
+    """nq_lrb_scale_grads_batch equals one nq_lrb_scale_grads call per linear bit
+    for bit (decode regime: the calls in order; matrix-core regime: the product
+    chains on the library's streams, with split reductions among them), and the
+    factored oracle."""
+    cfg = G.tiny_config(f"gbatch/{T}")
+    shapes = [synth.LayerShape("a", 300, 200, 64), synth.LayerShape("b", 96, 300, 40),
+              synth.LayerShape("c", 640, 512, 96), synth.LayerShape("d", 200, 96, 33)]
+    built = [G.latent_layer(cfg, s, i) for i, s in enumerate(shapes)]
+    layers = [b[0] for b in built]
+    adjs = [nq.Adjoint.of(L) for L in layers]
+    x_np = [synth.activations(f"gbatch/x/{T}/{i}", T, s.d_in, "bf16") for i, s in enumerate(shapes)]
+    g_np = [synth.activations(f"gbatch/g/{T}/{i}", T, s.d_out, "bf16") for i, s in enumerate(shapes)]
+    xs = [G.to_device_x(x, "bf16") for x in x_np]
+    gs = [G.to_device_x(g, "bf16") for g in g_np]
+    outs = nq.lrb_scale_grads_batch(layers, adjs, xs, gs)
+    for i, (L, a, x, g) in enumerate(zip(layers, adjs, xs, gs)):
+        want = nq.lrb_scale_grads(L, a, x, g)
+        for nm, got, w in zip(("dx", "ds1", "ds2"), outs[i], want):
+            assert torch.equal(got.view(torch.int32), w.view(torch.int32)), (i, nm)
+    for i in range(len(shapes)):
+        for got, want in zip(outs[i], O.scale_grads_factored_ref(built[i][1], x_np[i], g_np[i])):
+            assert O.rel_err(got.cpu().numpy(), want) <= G.tol_for(T, "bf16"), i
+
+
 # ---- magnitude balancing and scale extraction --------------------------------
 
 # (d_out, d_in, r, row padding): the row stride r + pad decides between the
