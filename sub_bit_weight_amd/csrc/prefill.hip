@@ -150,6 +150,11 @@ __device__ constexpr int rot_element(int j) {
 //   out[term][m][slot] = fp16 terms of a[m][k]*2^e in the block's slot order
 //   (zero past K); fp32 activations get two terms (hi + lo).
 //   c[sp][m] = sum over the piece of (f - 1) * (fp16 of a*2^e)  (rotated order).
+//   e_next[m] (when not null; one piece, rotated order) = 14 + e - exponent(sum
+//   over the row of |fp16 of a*2^e|): the sum bounds every output of the GEMM
+//   that takes this operand (one row of t), so 2^e_next puts all of that row
+//   below 2^14, the exponent of the next stage's operand written by the GEMM
+//   itself (see gemm_kernel, FUSE).
 // A thread handles whole 32-element blocks: 16-byte loads when `vec` (rows and
 // scales 16-byte aligned), 16 output dwords.  Pieces of up to 256 blocks stay
 // in registers between the two passes; longer ones are read twice.
@@ -158,7 +163,7 @@ __device__ constexpr int rot_element(int j) {
 // the correction sum (rotated order).
 template <bool ROT>
 __device__ inline float convert_block(const float (&v)[32], int e, int64_t M, int64_t Kpad, int nt, int64_t m,
-                                      int64_t blk, _Float16* __restrict__ out) {
+                                      int64_t blk, _Float16* __restrict__ out, float& l1) {
   float csum = 0.0f;
   uint32_t hi[16], lo[16];
 #pragma unroll
@@ -173,6 +178,7 @@ __device__ inline float convert_block(const float (&v)[32], int e, int64_t M, in
         h2[half] = (_Float16)(kPre[p % 4] * (float)hx);
         l2[half] = (_Float16)0.0f;
         csum += (float)(kPre[p % 4] - 1) * (float)hx;
+        l1 += fabsf((float)hx);
       } else {
         h2[half] = hx;
         l2[half] = (_Float16)(x - (float)hx);
@@ -214,7 +220,7 @@ template <int SRC, bool ROT, int NTH, int BPT>
 __global__ __launch_bounds__(NTH) void prep_kernel(const void* __restrict__ a, const float* __restrict__ cs,
                                                    int64_t M, int64_t K, int64_t Kpad, int nt, int nsum, int vec,
                                                    int bps, _Float16* __restrict__ out, int* __restrict__ e_out,
-                                                   float* __restrict__ c_out) {
+                                                   float* __restrict__ c_out, int* __restrict__ e_next) {
   constexpr int NW = NTH / 64;
   __shared__ float red[NW];
   const int64_t m = blockIdx.x;
@@ -247,20 +253,30 @@ __global__ __launch_bounds__(NTH) void prep_kernel(const void* __restrict__ a, c
     e = (ROT ? 11 : 14) - ex;
   }
   if (tid == 0) e_out[(int64_t)sp * M + m] = e;
-  float csum = 0.0f;
+  float csum = 0.0f, l1 = 0.0f;
   for (int64_t base = b0 + tid; base < b1; base += (int64_t)NTH * BPT) {
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
       const int64_t blk = base + (int64_t)i * NTH;
       if (blk < b1) {
         if (!in_regs) load_block<SRC>(a, cs, M, K, nsum, vec != 0, m, blk, v[i]);
-        csum += convert_block<ROT>(v[i], e, M, Kpad, nt, m, blk, out);
+        csum += convert_block<ROT>(v[i], e, M, Kpad, nt, m, blk, out, l1);
       }
     }
   }
   if (ROT) {
     csum = wg_reduce<NW, false>(csum, red);
     if (tid == 0) c_out[(int64_t)sp * M + m] = csum;
+    if (e_next) {
+      l1 = wg_reduce<NW, false>(l1, red);
+      int en = 0;
+      if (l1 > 0.0f && isfinite(l1)) {
+        int ex;
+        frexpf(l1, &ex);  // l1 = f * 2^ex, f in [0.5, 1): the row's outputs stay below 2^(ex - e)
+        en = 14 + e - ex;
+      }
+      if (tid == 0) e_next[m] = en;
+    }
   }
 }
 
@@ -341,15 +357,23 @@ struct Pipe {
 // sign words follow: word row q (of the tile's two) at [q][kBN columns].
 // PROD: the epilogue also takes the column products of ProdEpilogue (a kernel
 // of its own, so that the plain GEMM keeps its registers and LDS).
-template <int NT, int MB, bool PROD>
+// ROT: A in the rotated encoding (one fp16 term only); otherwise pair order.
+// FUSE (stage 1, no split, no column scale): the output is written as the next
+// GEMM's A operand instead of fp32: row m times 2^en[m], one fp16 term in pair
+// order, row stride kpad_next, zero in columns [N, kpad_next).  en comes from
+// the prep kernel's bound, so no value reaches 2^14 and fp16 keeps 2^-11
+// relative accuracy for every value above 2^-14 (2^-28 of the bound).
+template <int NT, int MB, bool PROD, bool ROT, bool FUSE>
 __global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
     const _Float16* __restrict__ A, const int* __restrict__ erow, const float* __restrict__ crow,
     const uint32_t* __restrict__ bits, int64_t ldb,
     int64_t M, int64_t N, int64_t K, int64_t Kpad, int tiles_m, int tiles_n, int nsplit, int kts,
     uint32_t sign_mask, uint32_t one, const float* __restrict__ colscale, float* __restrict__ out,
-    const void* __restrict__ pm, int pm_bf16, float* __restrict__ psum, int64_t ldp) {
+    const void* __restrict__ pm, int pm_bf16, float* __restrict__ psum, int64_t ldp,
+    _Float16* __restrict__ out16, const int* __restrict__ en, int64_t kpad_next) {
   using P = Pipe<NT, MB>;
-  constexpr bool ROT = NT == 1;  // rotated operand encoding (see rot_element)
+  static_assert(!ROT || NT == 1, "the rotated encoding takes one fp16 term");
+  static_assert(!(FUSE && PROD), "a fused stage-1 output has no column products");
   extern __shared__ __attribute__((aligned(16))) char lds[];  // [S][A tiles | sign words]
   const int lane = threadIdx.x % 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -512,9 +536,33 @@ __global__ __launch_bounds__(kThreads, MB == 2 ? 4 : 2) void gemm_kernel(
   // With psum (only without a split), each column's products pm * v over the
   // tile's rows are summed: per lane over its 16 rows of each 32-row block in
   // order, then the two lane halves, then the two wave rows through LDS.
-  float* dst = (!PROD || out) ? out + (int64_t)split * M * N : nullptr;
   const int* ep = erow + (int64_t)split * M;
   const float* cp = crow + (int64_t)split * M;
+  if constexpr (FUSE) {
+    // column n is element l32 of its 32-element block, pair-order slot
+    // 2*(l32 % 16) + l32/16; lanes l32 = 0..31 of a row write one 64-byte run
+    const int slot = 2 * (l32 % 16) + l32 / 16;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int64_t n = n0 + wn * 64 + nb * 32 + l32;
+        if (n >= kpad_next) continue;
+        const int64_t col = n - l32 + slot;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int64_t m = m0 + wm * 32 * MB + mb * 32 + 8 * a + 4 * h + c;
+            if (m < M) {
+              const float v = ROT ? acc[mb][nb][4 * a + c] - cp[m] : acc[mb][nb][4 * a + c];
+              out16[m * kpad_next + col] = n < N ? (_Float16)ldexpf(v, en[m] - ep[m]) : (_Float16)0.0f;
+            }
+          }
+      }
+    return;
+  }
+  float* dst = (!PROD || out) ? out + (int64_t)split * M * N : nullptr;
   float colsum[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -593,7 +641,7 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
 // per piece.  nt == 1 uses the rotated encoding (with correction sums in c).
 template <int SRC>
 hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int64_t Kpad, int nt, int nsum,
-                       int npieces, int bps, _Float16* out, int* e, float* c, hipStream_t s) {
+                       int npieces, int bps, _Float16* out, int* e, float* c, hipStream_t s, int* e_next = nullptr) {
   const int esize = SRC == kABF16Scaled ? 2 : 4;
   const int vec = (reinterpret_cast<uintptr_t>(a) % 16 == 0) && (reinterpret_cast<uintptr_t>(cs) % 16 == 0) &&
                   ((K * esize) % 16 == 0);
@@ -602,7 +650,7 @@ hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int
   const int64_t pblk = imin((int64_t)bps, Kpad / 32);
 #define NQ_PREP(ROT, NTH, BPT)                                                                                    \
   hipLaunchKernelGGL((prep_kernel<SRC, ROT, NTH, BPT>), grid, dim3(NTH), 0, s, a, cs, M, K, Kpad, nt, nsum, vec, bps, \
-                     out, e, c)
+                     out, e, c, e_next)
   // bf16 sources: two blocks per thread in registers; fp32 sources (whose
   // loads need more registers): one
   constexpr int BPT = SRC == kABF16Scaled ? 2 : 1;
@@ -658,11 +706,20 @@ Split split_plan(int64_t M, int64_t N, int64_t Kpad, bool allow) {
   return {(int)cdiv(nk, kts), kts};
 }
 
-template <int NT, int MB, bool PROD>
-hipError_t launch_gemm_t(decltype(&gemm_kernel<NT, MB, PROD>) kernel, const _Float16* A, const int* e, const float* c,
-                         const uint32_t* bits, int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t Kpad, Split sp,
-                         const float* colscale, float* out, const ProdEpilogue* pe, hipStream_t s) {
+// A fused stage-1 output (gemm_kernel, FUSE): the next GEMM's operand, its
+// row exponents and its row stride.
+struct FuseOut {
+  _Float16* out16;
+  const int* en;
+  int64_t kpad;
+};
+
+template <int NT, int MB, bool PROD, bool ROT, bool FUSE>
+hipError_t launch_gemm_t(const _Float16* A, const int* e, const float* c, const uint32_t* bits, int64_t ldb, int64_t M,
+                         int64_t N, int64_t K, int64_t Kpad, Split sp, const float* colscale, float* out,
+                         const ProdEpilogue* pe, const FuseOut* fo, hipStream_t s) {
   using P = Pipe<NT, MB>;
+  const auto kernel = gemm_kernel<NT, MB, PROD, ROT, FUSE>;
   static bool configured = false;
   if (!configured) {
     const hipError_t err =
@@ -674,23 +731,24 @@ hipError_t launch_gemm_t(decltype(&gemm_kernel<NT, MB, PROD>) kernel, const _Flo
   const unsigned grid = (unsigned)(8 * ((tiles_m * tiles_n * sp.n + 7) / 8));
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), P::LDS, s, A, e, c, bits, ldb, M, N, K, Kpad, tiles_m,
                      tiles_n, sp.n, sp.kts, kSignMask, kOnePair, colscale, out, pe ? pe->pm : nullptr,
-                     pe ? (int)pe->pm_bf16 : 0, pe ? pe->psum : nullptr, pe ? pe->ldp : (int64_t)0);
+                     pe ? (int)pe->pm_bf16 : 0, pe ? pe->psum : nullptr, pe ? pe->ldp : (int64_t)0,
+                     fo ? fo->out16 : nullptr, fo ? fo->en : nullptr, fo ? fo->kpad : (int64_t)0);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int nt, const _Float16* A, const int* e, const float* c, const uint32_t* bits, int64_t ldb,
-                       int64_t M, int64_t N, int64_t K, int64_t Kpad, Split sp, const float* colscale, float* out,
-                       hipStream_t s, const ProdEpilogue* pe = nullptr) {
+// nt fp16 terms of A (2: pair order); with nt == 1, rot selects the rotated
+// encoding (A from a prep kernel) or pair order (A from a fused stage 1).
+hipError_t launch_gemm(int nt, bool rot, const _Float16* A, const int* e, const float* c, const uint32_t* bits,
+                       int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t Kpad, Split sp, const float* colscale,
+                       float* out, hipStream_t s, const ProdEpilogue* pe = nullptr, const FuseOut* fo = nullptr) {
   constexpr int MB = kTileMB;
-  if (pe)
-    return nt == 1 ? launch_gemm_t<1, MB, true>(gemm_kernel<1, MB, true>, A, e, c, bits, ldb, M, N, K, Kpad, sp,
-                                                colscale, out, pe, s)
-                   : launch_gemm_t<2, MB, true>(gemm_kernel<2, MB, true>, A, e, c, bits, ldb, M, N, K, Kpad, sp,
-                                                colscale, out, pe, s);
-  return nt == 1 ? launch_gemm_t<1, MB, false>(gemm_kernel<1, MB, false>, A, e, c, bits, ldb, M, N, K, Kpad, sp,
-                                               colscale, out, nullptr, s)
-                 : launch_gemm_t<2, MB, false>(gemm_kernel<2, MB, false>, A, e, c, bits, ldb, M, N, K, Kpad, sp,
-                                               colscale, out, nullptr, s);
+#define NQ_GEMM(NT, PROD, ROT, FUSE) \
+  launch_gemm_t<NT, MB, PROD, ROT, FUSE>(A, e, c, bits, ldb, M, N, K, Kpad, sp, colscale, out, pe, fo, s)
+  if (fo) return rot ? NQ_GEMM(1, false, true, true) : hipErrorInvalidValue;  // stage 1 of bf16 activations
+  if (nt == 2) return pe ? NQ_GEMM(2, true, false, false) : NQ_GEMM(2, false, false, false);
+  if (rot) return pe ? NQ_GEMM(1, true, true, false) : NQ_GEMM(1, false, true, false);
+  return pe ? NQ_GEMM(1, true, false, false) : NQ_GEMM(1, false, false, false);
+#undef NQ_GEMM
 }
 
 struct PrefillLayout {
@@ -755,12 +813,25 @@ hipError_t launch_prefill(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T
   float* y2 = reinterpret_cast<float*>(base + d.off_y2);
   const int bps1 = 2 * d.sp1.kts, bps2 = 2 * d.sp2.kts;  // 32-element blocks per reduction piece
   hipError_t e;
+  // bf16 activations with neither reduction split: stage 1 writes stage 2's
+  // fp16 operand itself (row exponents from the stage-1 prep's bound), so t
+  // makes no fp32 round trip and has no prep kernel; stage 2 takes pair order
+  const bool fuse = xd == NQ_BF16 && d.sp1.n == 1 && d.sp2.n == 1;
   if (xd == NQ_BF16)
-    e = launch_prep<kABF16Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, 1, d.sp1.n, bps1, z, e1, c1, s);
+    e = launch_prep<kABF16Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, 1, d.sp1.n, bps1, z, e1, c1, s,
+                                  fuse ? e2 : nullptr);
   else
     e = launch_prep<kAF32Scaled>(x, L.s2, T, L.d_in, d.kpad1, d.nt, 1, d.sp1.n, bps1, z, e1, c1, s);
   if (e != hipSuccess) return e;
-  if ((e = launch_gemm(d.nt, z, e1, c1, L.vt_bits, L.ldv, T, L.r, L.d_in, d.kpad1, d.sp1, nullptr, t, s)) !=
+  if (fuse) {
+    const FuseOut fo{t16, e2, d.kpad2};
+    if ((e = launch_gemm(1, true, z, e1, c1, L.vt_bits, L.ldv, T, L.r, L.d_in, d.kpad1, d.sp1, nullptr, nullptr, s,
+                         nullptr, &fo)) != hipSuccess)
+      return e;
+    return launch_gemm(1, false, t16, e2, c2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, L.s1, y, s, pe);
+  }
+  const bool rot = d.nt == 1;
+  if ((e = launch_gemm(d.nt, rot, z, e1, c1, L.vt_bits, L.ldv, T, L.r, L.d_in, d.kpad1, d.sp1, nullptr, t, s)) !=
       hipSuccess)
     return e;
   // the stage-2 prep adds stage 1's partial sums while it reads t
@@ -768,8 +839,8 @@ hipError_t launch_prefill(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T
       hipSuccess)
     return e;
   if (d.sp2.n == 1)
-    return launch_gemm(d.nt, t16, e2, c2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, L.s1, y, s, pe);
-  if ((e = launch_gemm(d.nt, t16, e2, c2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, nullptr, y2, s)) !=
+    return launch_gemm(d.nt, rot, t16, e2, c2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, L.s1, y, s, pe);
+  if ((e = launch_gemm(d.nt, rot, t16, e2, c2, L.u_bits, L.ldu, T, L.d_out, L.r, d.kpad2, d.sp2, nullptr, y2, s)) !=
       hipSuccess)
     return e;
   if (pe) {
