@@ -131,6 +131,12 @@ size_t nq_lrb_workspace_bytes(const nq_lrb* L, int64_t T);
  * in the last bits).
  * y is fully overwritten.  Summation order is fixed: results are run-to-run
  * deterministic, but not bitwise equal across regimes.
+ * The decode kernels of a single call keep their dependency counters in a
+ * small array of the library, one slot per stream (up to 64 streams per
+ * device; each launch leaves its slot cleared, so calls need no clearing
+ * launch): calls on different streams may overlap, and a call captured into a
+ * graph keeps the slot of the stream it was captured on, so its replays must
+ * not overlap other calls made on that stream.
  * Errors: NQ_ERR_ARG for null pointers, dims < 1, ldu < d_out, ldv < r, T < 1,
  * an unknown dtype or a misaligned pointer (x, y: 4 bytes; bits, scales: 4
  * bytes); NQ_ERR_UNSUPPORTED when r > 2^24, d_out or d_in > 2^31, or a

@@ -130,8 +130,15 @@ def _check(status: int) -> None:
         raise NqError(status, last_error())
 
 
-def _stream(stream=None) -> int:
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream=None, device: int | None = None) -> int:
+    """The HIP stream handle: `stream`'s, else torch's current stream on
+    `device` (default: the current device)."""
     if stream is None:
+        if _raw_stream is not None and device is not None:
+            return _raw_stream(device)  # no Stream object per call
         stream = torch.cuda.current_stream()
     return stream.cuda_stream
 
@@ -222,10 +229,19 @@ class Lrb:
     s1: torch.Tensor       # [d_out] float32
     s2: torch.Tensor       # [d_in] float32
 
+    def __setattr__(self, name, value):
+        object.__setattr__(self, name, value)
+        object.__setattr__(self, "_struct", None)  # any field change re-validates
+
     def struct(self) -> nq_lrb:
         """The C struct, after checking what the C ABI cannot see: dtypes,
         shapes and sizes of the tensors (a short buffer would otherwise be read
-        past its end by the kernels)."""
+        past its end by the kernels).  Built once and kept until a field is
+        assigned again; tensors must not be resized in place (resize_, set_)
+        while the layer is in use."""
+        cached = self.__dict__.get("_struct")
+        if cached is not None:
+            return cached
         for name in ("u_bits", "vt_bits", "s1", "s2"):
             _dev(getattr(self, name), name)
         if min(self.d_out, self.d_in, self.r) < 1:
@@ -240,10 +256,12 @@ class Lrb:
             t = getattr(self, name)
             if t.dtype != torch.float32 or t.numel() < n:
                 raise ValueError(f"{name} must be float32 with >= {n} elements, got {t.dtype} {t.numel()}")
-        return nq_lrb(self.d_out, self.d_in, self.r,
-                      self.u_bits.data_ptr(), self.u_bits.shape[1],
-                      self.vt_bits.data_ptr(), self.vt_bits.shape[1],
-                      self.s1.data_ptr(), self.s2.data_ptr())
+        st = nq_lrb(self.d_out, self.d_in, self.r,
+                    self.u_bits.data_ptr(), self.u_bits.shape[1],
+                    self.vt_bits.data_ptr(), self.vt_bits.shape[1],
+                    self.s1.data_ptr(), self.s2.data_ptr())
+        object.__setattr__(self, "_struct", st)
+        return st
 
 
 def _x_dtype(x: torch.Tensor) -> int:
@@ -267,14 +285,15 @@ def lrb_linear(layer: Lrb, x: torch.Tensor, y: torch.Tensor | None = None,
         raise ValueError(f"x must be [T][{layer.d_in}], got {tuple(x.shape)}")
     T = x.shape[0]
     s = layer.struct()
-    need = int(lib().nq_lrb_workspace_bytes(ctypes.byref(s), T))
-    with _on(stream):
-        if y is None:
-            y = torch.empty((T, layer.d_out), dtype=torch.float32, device=x.device)
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if y is None or workspace is None:
+        with _on(stream):
+            if y is None:
+                y = torch.empty((T, layer.d_out), dtype=torch.float32, device=x.device)
+            if workspace is None:
+                need = int(lib().nq_lrb_workspace_bytes(ctypes.byref(s), T))
+                workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _check(lib().nq_lrb_linear(ctypes.byref(s), _ptr(x), _x_dtype(x), T, _ptr(y), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(stream)))
+                               workspace.numel() * workspace.element_size(), _stream(stream, x.get_device())))
     return y
 
 
@@ -290,7 +309,8 @@ def lrb_linear_noalloc(layer: Lrb, x: torch.Tensor, y: torch.Tensor, stream=None
     if tuple(y.shape) != (T, layer.d_out) or y.dtype != torch.float32:
         raise ValueError(f"y must be float32 [{T}][{layer.d_out}]")
     s = layer.struct()
-    _check(lib().nq_lrb_linear_noalloc(ctypes.byref(s), _ptr(x), _x_dtype(x), T, _ptr(y), _stream(stream)))
+    _check(lib().nq_lrb_linear_noalloc(ctypes.byref(s), _ptr(x), _x_dtype(x), T, _ptr(y),
+                                       _stream(stream, x.get_device())))
     return y
 
 

@@ -24,6 +24,9 @@
 //    drains; each wait also has a spin limit that records an error and exits.
 #include <stdlib.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "nq_internal.h"
 
 namespace nq {
@@ -183,15 +186,32 @@ __device__ void finish_rows(const StageDesc& S, int rb, int ks, int64_t o, bool 
     }
     if (valid) {
       const float sc = S.rowscale ? gload(S.rowscale + o) : 1.0f;
+      // the spans' sums in span order, loaded kBatch spans at a time (a load
+      // per add would wait out one memory latency per span)
+      constexpr int kBatch = 4;
+      float sum[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) sum[t] = 0.0f;
+      for (int c0 = 0; c0 < S.nks; c0 += kBatch) {
+        float v[kBatch][T];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+            v[i][t] = c0 + i < S.nks ? gload(S.part + ((int64_t)(c0 + i) * T + t) * S.n_rows + o) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (c0 + i < S.nks)
+#pragma unroll
+            for (int t = 0; t < T; ++t) sum[t] += v[i][t];
+      }
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        float sum = 0.0f;
-        for (int c = 0; c < S.nks; ++c) sum += gload(S.part + ((int64_t)c * T + t) * S.n_rows + o);
         float* dst = S.out + (int64_t)t * S.n_rows + o;
         if (S.signal)
-          store_agent(dst, sc * sum);
+          store_agent(dst, sc * sum[t]);
         else
-          gstore(dst, sc * sum);
+          gstore(dst, sc * sum[t]);
       }
     }
     if (tid == 0) gstore(S.rb_count + rb, 0);  // all arrivals happened: ready for the next run
@@ -503,6 +523,88 @@ __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* e
   __syncthreads();  // the slots are reused by the next tile
 }
 
+// Single calls: a stage tile spans one chunk and makes that chunk's input
+// pieces itself, straight into LDS buffer 0 (no input-piece tiles and no hand
+// over through the workspace: for one linear the chain of dependent steps,
+// not the bytes, sets the time).  Thread task = tid & 255 makes the B dword of
+// each piece for 4 reduction positions, as an input-piece tile does, for
+// tokens (tid >> 8) + 2i; the dword goes where the chunk copy of a sequence
+// tile would put it.  Ends with the chunk's fragments and scale exponents in
+// LDS (after a barrier).
+template <int T>
+__device__ inline void tile_pieces(const StageDesc& S, int64_t c0, int* lds) {
+  constexpr int TH = (T + 1) / 2;  // tokens per half of the workgroup
+  constexpr int G = col_groups<T>();
+  const int tid = threadIdx.x, task = tid & 255;
+  const int half = __builtin_amdgcn_readfirstlane(tid >> 8);  // uniform over a wave
+  unsigned* slot = reinterpret_cast<unsigned*>(lds + slot_off<T>());  // [T] chunk maxima
+  const int64_t cend = S.n_red;
+  PieceIn<TH> in;
+  uint32_t eo[4];  // element offsets in a token row (past the end: element 0, dropped later)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t e = c0 + task_element(task, k);
+    eo[k] = e < cend ? (uint32_t)e : 0u;
+    in.cs[k] = S.colscale ? gload(S.colscale + eo[k]) : 1.0f;
+  }
+  // token half + 2i (past T: token T-1 again, dropped below)
+  auto idx = [&](int i, int k) { return (int64_t)min(half + 2 * i, T - 1) * S.n_red + eo[k]; };
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int i = 0; i < TH; ++i)
+      in.x[i][k] = S.x_bf16 ? (uint32_t)gload(static_cast<const uint16_t*>(S.xin) + idx(i, k))
+                            : gload(static_cast<const uint32_t*>(S.xin) + idx(i, k));
+  if (tid < T) slot[tid] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TH; ++i) {
+    unsigned m = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, __float_as_uint(fabsf(piece_value(S, in, i, task, c0, cend, k))));
+    m = wave_max_u32(m);
+    if ((tid & 63) == 0 && half + 2 * i < T) atomicMax(slot + half + 2 * i, m);
+  }
+  __syncthreads();  // the chunk's maxima are complete
+  const int wr = task >> 3, j = (task >> 1) & 3, ih = task & 1;
+  const int kk = wr >> 2, gw = wr & 3;
+  const int gp = 2 * (gw & 1) + (j >> 1);
+  // LDS place of column n's dword: block (kk, group gp, half gw >> 1) of
+  // column n in column group n / 16, dword 2 * (j & 1) + ih
+  const int base = kk * G * kStepInts + (gw >> 1) * 256 + 16 * gp * 4 + 2 * (j & 1) + ih;
+#pragma unroll
+  for (int i = 0; i < TH; ++i) {
+    const int t = half + 2 * i;  // uniform over a wave
+    if (t >= T) continue;
+    const int shift = chunk_shift(slot[t]);
+    float r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000) : ldexpf(piece_value(S, in, i, task, c0, cend, k), shift);
+#pragma unroll
+    for (int p = 0; p < kPieces; ++p) {
+      int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+      d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
+      int emax = max_fp8_exponent(d);  // with the partner thread (task ^ 1): one group of 8
+      emax = max(emax, (int)lane_xor1((unsigned)emax));
+      d = keep_fp8_exponents(d, max(1, emax - 7));
+      const int n = t * kPieces + p;
+      lds[base + (n / 16) * kStepInts + (n % 16) * 4] = d;
+      if (p + 1 < kPieces) {
+        typedef float v2f __attribute__((ext_vector_type(2)));
+        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
+        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
+        r[0] = (r[0] - lo.x) * 16.0f;
+        r[1] = (r[1] - lo.y) * 16.0f;
+        r[2] = (r[2] - hi.x) * 16.0f;
+        r[3] = (r[3] - hi.y) * 16.0f;
+      }
+    }
+    if (task == 0) lds[sig_off<T>() + t] = shift;
+  }
+  __syncthreads();  // the chunk's fragments are in LDS buffer 0
+}
+
 // B columns past the last piece of the last token stay zero for the life of
 // the kernel (the chunk copies never write them): clear them once.
 template <int T>
@@ -567,7 +669,10 @@ __device__ inline float quad_sum(float v) {
 
 // W4: sign words are read 4 rows at a time (16-byte loads); otherwise one
 // word per load (row counts or strides that are not multiples of 4).
-template <int T, bool W4>
+// FUSE (single calls): the span is one chunk whose pieces the tile makes
+// itself (tile_pieces); otherwise they are copied from the stage's
+// input-piece blocks chunk by chunk.
+template <int T, bool W4, bool FUSE>
 __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_flag, int* err, NextTile& next) {
   static_assert(T <= kMfmaMaxT, "tokens");
   constexpr int G = col_groups<T>();
@@ -676,12 +781,16 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
   u32x4 ring[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) load_step(0, k, ring[k]);
-  wait_input(S, err);  // the stage's pieces are final
-  load_half(chunk0, 0);
-  store_half(0, 0);
-  load_half(chunk0, 1);
-  store_half(0, 1);
-  __syncthreads();  // chunk 0's fragments are in LDS buffer 0
+  wait_input(S, err);  // the stage's input (or its pieces) is final
+  if constexpr (FUSE) {
+    tile_pieces<T>(S, span0, lds);
+  } else {
+    load_half(chunk0, 0);
+    store_half(0, 0);
+    load_half(chunk0, 1);
+    store_half(0, 1);
+    __syncthreads();  // chunk 0's fragments are in LDS buffer 0
+  }
 
   const ExpandConsts xc = expand_consts();
   // the sums of all chunks accumulate in acc: each chunk's B column (token t,
@@ -743,7 +852,7 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
       bscale[cg] = tc < T ? 127 - (sg == kShiftNaN ? 0 : sg) - 4 * pc : 127;
     }
     const int nxt_chunk = chunk0 + (c + 1 < nchunks ? c + 1 : 0);
-    load_half(nxt_chunk, 0);  // next chunk's pieces (the next row block's first)
+    if constexpr (!FUSE) load_half(nxt_chunk, 0);  // next chunk's pieces (the next row block's first)
 
     const u32x4* bfrag = reinterpret_cast<const u32x4*>(lds + buf * b_ints<T>()) + lane;
     // B fragments: with one column group the next step's are read a step ahead;
@@ -790,11 +899,13 @@ __device__ void mfma_tile(const StageDesc& S, int local, float* ldsf, int* s_fla
       // block: out of range, no memory access); no branch around the load
       const bool next_rb = kk + R >= kChunkSteps && c + 1 == nchunks;
       load_step(next_rb ? ri + 1 : ri, next_rb ? kk + R - kChunkSteps : k + R, ring[kk % R]);
-      if (kk == 2) {  // the other buffer was last read in chunk vc-1
-        store_half(buf ^ 1, 0);
-        load_half(nxt_chunk, 1);
+      if constexpr (!FUSE) {
+        if (kk == 2) {  // the other buffer was last read in chunk vc-1
+          store_half(buf ^ 1, 0);
+          load_half(nxt_chunk, 1);
+        }
+        if (kk == 6) store_half(buf ^ 1, 1);
       }
-      if (kk == 6) store_half(buf ^ 1, 1);
     }
     __syncthreads();  // chunk vc+1's fragments are in LDS; every wave is done with chunk vc's
     if (c + 1 < nchunks) {
@@ -816,16 +927,26 @@ template <int T>
 constexpr int min_waves() { return 4; }
 static_assert(col_groups<kMfmaMaxT>() <= 2, "T <= 8 in two column groups");
 
-template <int T>
+// SINGLE: a single call's tiles (kind 2 only); otherwise a sequence's (kinds
+// 0 and 1).  Kept apart so that neither kernel carries the other's code and
+// registers.
+template <int T, bool SINGLE>
 __device__ inline void stage_tile(const StageDesc& S, int local, float* lds, int* s_flag, int* err, NextTile& next) {
-  if (S.kind == 1 && S.prep_tg == 1)
-    mfma_prep_tile<T, 1>(S, local, lds, err, next);
-  else if (S.kind == 1)
-    mfma_prep_tile<T, T>(S, local, lds, err, next);
-  else if (S.w_vec)
-    mfma_tile<T, true>(S, local, lds, s_flag, err, next);
-  else
-    mfma_tile<T, false>(S, local, lds, s_flag, err, next);
+  if constexpr (SINGLE) {
+    if (S.w_vec)
+      mfma_tile<T, true, true>(S, local, lds, s_flag, err, next);
+    else
+      mfma_tile<T, false, true>(S, local, lds, s_flag, err, next);
+  } else {
+    if (S.kind == 1 && S.prep_tg == 1)
+      mfma_prep_tile<T, 1>(S, local, lds, err, next);
+    else if (S.kind == 1)
+      mfma_prep_tile<T, T>(S, local, lds, err, next);
+    else if (S.w_vec)
+      mfma_tile<T, true, false>(S, local, lds, s_flag, err, next);
+    else
+      mfma_tile<T, false, false>(S, local, lds, s_flag, err, next);
+  }
 }
 
 // ints: [0] error flag (sticky), [1] next tile, [2] workgroups exited,
@@ -833,7 +954,7 @@ __device__ inline void stage_tile(const StageDesc& S, int local, float* lds, int
 // from the counter at [1]; `lookup(tile, S, local)` gives a tile's descriptor
 // and its index within its stage.  The last workgroup to exit zeroes
 // [1 .. n_ints), so consecutive runs need no separate reset launch.
-template <int T, typename Lookup>
+template <int T, bool SINGLE, typename Lookup>
 __device__ inline void persistent_tiles(Lookup lookup, int ntiles, int* ints, int n_ints, float* lds) {
   int& s_flag = reinterpret_cast<int*>(lds)[flag_off<T>()];
   int& s_tile = reinterpret_cast<int*>(lds)[flag_off<T>() + 1];
@@ -849,7 +970,7 @@ __device__ inline void persistent_tiles(Lookup lookup, int ntiles, int* ints, in
     StageDesc S;
     int local;
     lookup(tile, S, local);
-    stage_tile<T>(S, local, lds, &s_flag, err, next);
+    stage_tile<T, SINGLE>(S, local, lds, &s_flag, err, next);
     if (threadIdx.x == 0) s_tile = next.id;
     __syncthreads();
     tile = __builtin_amdgcn_readfirstlane(s_tile);
@@ -874,7 +995,7 @@ __global__ __launch_bounds__(kMRows) __attribute__((amdgpu_waves_per_eu(min_wave
 void dec_persistent_kernel(const StageDesc* __restrict__ segs, const int* __restrict__ tile_seg, int ntiles, int* ints,
                            int n_ints) {
   __shared__ __attribute__((aligned(16))) float lds[mfma_lds<T>()];
-  persistent_tiles<T>(
+  persistent_tiles<T, false>(
       [&](int tile, StageDesc& S, int& local) {
         S = segs[tile_seg[tile]];  // one lookup (a scan over the segments stalled for microseconds)
         local = tile - S.tile0;
@@ -892,7 +1013,7 @@ template <int T>
 __global__ __launch_bounds__(kMRows) __attribute__((amdgpu_waves_per_eu(min_waves<T>())))
 void dec_linear_kernel(LinearSched L, int* ints, int n_ints) {
   __shared__ __attribute__((aligned(16))) float lds[mfma_lds<T>()];
-  persistent_tiles<T>(
+  persistent_tiles<T, true>(
       [&](int tile, StageDesc& S, int& local) {
         // the stage is uniform across the workgroup: select a pointer into the
         // argument segment (scalar loads), not a copy of each descriptor
@@ -928,14 +1049,10 @@ StagePlan dec_stage_plan(int64_t n_rows, int64_t n_red, int64_t T, int64_t kspan
   return p;
 }
 
-// Single calls split the reduction until the two stages have enough tiles to
-// fill the GPU; sequences keep whole reductions (no partial sums).
-int64_t dec_single_span(int64_t n_rows, int64_t n_red, int64_t T) {
-  const int64_t nrb = cdiv(n_rows, dec_tile_rows(T));
-  const int64_t want = cdiv(512, nrb);
-  const int64_t span = round_up(cdiv(n_red, want), 1024);
-  return span;
-}
+// Single calls split the reduction into spans of one chunk, whose input
+// pieces each tile makes itself (tile_pieces); sequences keep whole
+// reductions (no partial sums).
+int64_t dec_single_span(int64_t, int64_t, int64_t) { return kChunkWords * kWordBits; }
 
 hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
@@ -944,7 +1061,8 @@ hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-int dec_persistent_grid(int64_t T) {
+namespace {
+int persistent_grid_query(int64_t T) {
   int dev = 0, cus = 256, per = 1;
   if (hipGetDevice(&dev) == hipSuccess) {
     hipDeviceProp_t prop;
@@ -959,6 +1077,24 @@ int dec_persistent_grid(int64_t T) {
   }
   if (e != hipSuccess || per < 1) per = 1;
   return cus * per;
+}
+}  // namespace
+
+// Resident workgroups of the persistent kernel, per device and T: queried once
+// (the property and occupancy queries cost microseconds of host time, which a
+// single call would otherwise pay every time).
+int dec_persistent_grid(int64_t T) {
+  constexpr int kDevs = 64;
+  static std::atomic<int> cache[kDevs][kMfmaMaxT + 1];
+  int dev = 0;
+  if (T < 1 || T > kMfmaMaxT || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs)
+    return persistent_grid_query(T);
+  int g = cache[dev][T].load(std::memory_order_relaxed);
+  if (g == 0) {
+    g = persistent_grid_query(T);
+    cache[dev][T].store(g, std::memory_order_relaxed);
+  }
+  return g;
 }
 
 hipError_t launch_dec_persistent(const StageDesc* segs, const int* tile_seg, int ntiles, int* ints, int n_ints,
@@ -1016,14 +1152,15 @@ size_t piece_bytes(int64_t n_red, int64_t T) {
 
 }  // namespace
 
-// Per-linear device buffers: [part1][t][part2][pieces of x][pieces of t].
+// Per-linear device buffers: [part1][t][part2], then for sequences [pieces of
+// x][pieces of t] (single calls make their pieces in LDS).
 size_t dec_linear_bytes(const nq_lrb& L, int64_t T, bool split) {
   StagePlan p1, p2;
   plans(L, T, split, &p1, &p2);
   size_t off = align_up(part_bytes(p1, T));
   off = align_up(off + (size_t)T * L.r * sizeof(float));
   off = align_up(off + part_bytes(p2, T));
-  return off + piece_bytes(L.d_in, T) + piece_bytes(L.r, T);
+  return split ? off : off + piece_bytes(L.d_in, T) + piece_bytes(L.r, T);
 }
 
 // Per-linear counters: [stage-1 row blocks][stage-2 row blocks][t ready]
@@ -1095,7 +1232,7 @@ int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
   a.rb_group = split ? 1 : seq_rb_group(p1, T);
   a.x_bf16 = xd == NQ_BF16;
   a.w_vec = words_vec(L.vt_bits, L.ldv, L.r);
-  a.kind = 0;
+  a.kind = split ? 2 : 0;
   a.tile0 = 0;
   StageDesc b = a;
   b.bits = L.u_bits;
@@ -1117,6 +1254,11 @@ int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
   b.rb_group = split ? 1 : seq_rb_group(p2, T);
   b.x_bf16 = 0;
   b.w_vec = words_vec(L.u_bits, L.ldu, L.d_out);
+  if (split) {  // single call: each tile makes its chunk's pieces; stage 2 waits for t
+    d[0] = a;
+    d[1] = b;
+    return 2;
+  }
   // input-piece tiles before each stage; each stage waits for its pieces,
   // the pieces of t wait for stage 1
   auto pieces = [&](const StageDesc& st, char* buf, int* ready) {
@@ -1150,30 +1292,77 @@ int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, floa
   return 4;
 }
 
-// Single calls: [error flag][next tile][exited][the linear's counters] then
-// the linear's buffers; one persistent launch runs the four stages, each tile
-// waiting on the counters of the stage it reads.
+// Single calls: [error flag][next tile][exited][the linear's counters] (used
+// only when the stream has no counter slot) then the linear's buffers; one
+// persistent launch runs the two stages, each tile making its chunk's input
+// pieces, the stage-2 tiles waiting for t.
 size_t dec_workspace_bytes(const nq_lrb& L, int64_t T) {
   return align_up((size_t)(3 + dec_linear_counters(L, T, true)) * sizeof(int)) + dec_linear_bytes(L, T, true);
 }
 
+namespace {
+
+// Counters of single calls, one slot per (device, stream).  Every launch
+// leaves its counters at zero when it ends (the last workgroup out clears
+// them), and the launches on one stream run one after another, so a stream's
+// slot is zero whenever its next call starts: no clearing launch per call.
+// The array is zero when the code object loads; each GPU has its own copy,
+// whose address is looked up once per device.  A stream is given a slot on
+// its first call and keeps it; past kSlots streams on a device, or for a layer
+// with more counters than a slot holds, the counters live in the workspace and
+// are cleared by a launch before the call.
+constexpr int kSlots = 64, kSlotInts = 1024, kSlotDevices = 64;
+static __device__ __align__(256) int g_slots[kSlots][kSlotInts];
+
+struct SlotTable {
+  int* base = nullptr;  // this device's copy of g_slots
+  hipStream_t stream[kSlots] = {};
+  int used = 0;
+};
+std::mutex g_slot_mu;
+SlotTable g_slot_tab[kSlotDevices];
+
+int* stream_slot(hipStream_t s) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSlotDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_slot_mu);
+  SlotTable& tab = g_slot_tab[dev];
+  if (!tab.base) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_slots)) != hipSuccess || !p) return nullptr;
+    tab.base = static_cast<int*>(p);
+  }
+  for (int i = 0; i < tab.used; ++i)
+    if (tab.stream[i] == s) return tab.base + (size_t)i * kSlotInts;
+  if (tab.used == kSlots) return nullptr;
+  tab.stream[tab.used] = s;
+  return tab.base + (size_t)(tab.used++) * kSlotInts;
+}
+
+}  // namespace
+
 hipError_t launch_dec_linear(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, void* ws,
                              hipStream_t s) {
   char* base = static_cast<char*>(ws);
-  int* ints = reinterpret_cast<int*>(base);
   const int n_ints = 3 + dec_linear_counters(L, T, true);
+  int* slot = n_ints <= kSlotInts ? stream_slot(s) : nullptr;
+  int* ints = slot ? slot : reinterpret_cast<int*>(base);
   char* lin = base + align_up((size_t)n_ints * sizeof(int));
   LinearSched sched;
   const int nd = dec_stage_descs(L, x, xd, T, y, true, lin, ints + 3, sched.d);
-  if (nd != kMaxLinearDescs) return hipErrorInvalidValue;
+  if (nd != 2) return hipErrorInvalidValue;
   int tiles = 0;
-  for (int i = 0; i < nd; ++i) {
-    sched.d[i].tile0 = tiles;
-    tiles += stage_tiles(sched.d[i]);
+  for (int i = 0; i < kMaxLinearDescs; ++i) {  // entries past nd: empty (end = the last end)
+    if (i < nd) {
+      sched.d[i].tile0 = tiles;
+      tiles += stage_tiles(sched.d[i]);
+    } else {
+      sched.d[i] = sched.d[nd - 1];
+    }
     sched.end[i] = tiles;
   }
   hipError_t e;
-  if ((e = launch_zero_ints(ints, n_ints, s)) != hipSuccess) return e;
+  if (!slot && (e = launch_zero_ints(ints, n_ints, s)) != hipSuccess) return e;
   const int grid = (int)imin(tiles, dec_persistent_grid(T));
   switch (T) {
 #define NQ_CASE(TT)                                                                                        \

@@ -65,7 +65,8 @@ extern "C" nq_status nq_lrb_linear_noalloc(const nq_lrb* L, const void* x, nq_dt
   }
   void* ws = nullptr;
   if ((st = scratch_for_current_device(&ws)) != NQ_OK) return st;
-  // the decode regime clears its counters with a fill kernel before its
-  // stages; the GEMM regime writes every workspace value before reading it
+  // the decode regime keeps its counters in the stream's counter slot (or
+  // clears them in the array with a fill kernel); the GEMM regime writes every
+  // workspace value before reading it
   return hip_status(launch_linear(*L, x, x_dtype, T, y, ws, (hipStream_t)stream), "nq_lrb_linear_noalloc launch");
 }

@@ -77,7 +77,8 @@ struct StageDesc {
   int rb_group;           // kind 0: consecutive row blocks per tile (one span); kind 1: 1
   int x_bf16;
   int w_vec;              // bits 16-byte aligned, ld and n_rows multiples of 4: 16-byte word loads
-  int kind;               // 0: stage tiles (nrb x nks); 1: input-piece tiles (nrb = tiles, nks = 1)
+  int kind;               // 0: stage tiles (nrb x nks); 1: input-piece tiles (nrb = tiles, nks = 1);
+                          // 2: stage tiles of one chunk that make their own pieces (single calls)
   uint32_t* bfrag;        // matrix-core operand pieces of the stage input (written by kind 1, read by kind 0)
   int* bsig;              // per chunk and token: scale exponent of the pieces
   int prep_items;         // kind 1: (chunk, token group) work items per tile
@@ -100,7 +101,8 @@ size_t dec_workspace_bytes(const nq_lrb& L, int64_t T);
 size_t dec_linear_bytes(const nq_lrb& L, int64_t T, bool split);
 int dec_linear_counters(const nq_lrb& L, int64_t T, bool split);
 // Descriptors of one linear in dependency order (each waits only on earlier
-// ones): pieces of x, stage 1, pieces of t, stage 2.  Returns their number.
+// ones): sequences (split = false) pieces of x, stage 1, pieces of t, stage 2;
+// single calls (split = true) stage 1, stage 2.  Returns their number.
 constexpr int kMaxLinearDescs = 4;
 int dec_stage_descs(const nq_lrb& L, const void* x, nq_dtype xd, int64_t T, float* y, bool split,
                     char* ws_linear, int* ctr_base, StageDesc* d);

@@ -157,6 +157,43 @@ def test_linear_deterministic():
         assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
+def test_single_calls_on_two_streams_and_counter_fallback():
+    """Single decode calls keep their dependency counters in a library slot per
+    stream.  Calls on two streams at once, and layers with different counter
+    counts one after another on each stream, give what the same calls give one
+    at a time (bit for bit); a layer with more counters than a slot holds (1025
+    stage-2 row blocks) keeps them in its workspace; all match the oracle."""
+    cfg = G.tiny_config("slots")
+    shapes = [synth.LayerShape("a", 1100, 2100, 300), synth.LayerShape("b", 4096, 1024, 1500)]
+    layers = [G.latent_layer(cfg, s) for s in shapes]
+    Ts = (1, 5)
+    xs = {(T, i): synth.activations(f"slots/x/{s.name}/{T}", T, s.d_in, "bf16")
+          for T in Ts for i, s in enumerate(shapes)}
+    xd = {k: G.to_device_x(v, "bf16") for k, v in xs.items()}
+    one_at_a_time = {}
+    for (T, i), x in xd.items():
+        one_at_a_time[T, i] = nq.lrb_linear(layers[i][0], x).cpu()
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    outs = []
+    for _ in range(20):
+        for T, st in zip(Ts, streams):
+            for i in range(len(shapes)):
+                outs.append(((T, i), nq.lrb_linear(layers[i][0], xd[T, i], stream=st)))
+    torch.cuda.synchronize()
+    for key, y in outs:
+        assert torch.equal(y.cpu().view(torch.int32), one_at_a_time[key].view(torch.int32)), key
+    for (T, i), y in one_at_a_time.items():
+        e = C.full_check(y.numpy(), layers[i][1], xs[T, i], G.decode_tol("bf16"), "bf16")
+        assert e["pass"], ((T, i), e)
+    big = synth.LayerShape("big", 524_800, 40, 33)
+    dev, ref = G.splitmix_layer(synth.Config("slots/big", "slots/big", [], (1,), "bf16", words="splitmix"), big)
+    for T in (2, 1):
+        x = synth.activations(f"slots/big/x/{T}", T, big.d_in, "bf16")
+        err = _linear_err(dev, ref, x, "bf16")
+        assert err <= G.decode_tol("bf16"), err
+
+
 TINY_PATH = [(256, 256, 64), (70, 100, 40), (1024, 2048, 512), (33, 1, 1), (1, 64, 33), (257, 96, 31)]
 
 
