@@ -194,6 +194,39 @@ def test_single_calls_on_two_streams_and_counter_fallback():
         assert err <= G.decode_tol("bf16"), err
 
 
+def test_single_call_graph_replays():
+    """A decode-regime single call captured into a graph (one kernel: its
+    counters live in the capture stream's slot, no clearing launch) gives, on
+    every replay, what an eager call gives on the same input, with eager calls
+    on the default stream between the replays."""
+    shape = synth.LayerShape("graph", 1100, 2100, 300)
+    dev, ref, _ = G.latent_layer(G.tiny_config("graph"), shape)
+    T = 3
+    xs = [synth.activations(f"graph/x/{i}", T, shape.d_in, "bf16") for i in range(5)]
+    x = G.to_device_x(xs[0], "bf16")
+    y = torch.empty((T, shape.d_out), device=G.DEV)
+    ws = torch.empty(nq.lrb_workspace_bytes(dev, T), dtype=torch.uint8, device=G.DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        nq.lrb_linear(dev, x, y, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nq.lrb_linear(dev, x, y, ws)
+    for i, x_np in enumerate(xs):
+        x.copy_(G.to_device_x(x_np, "bf16"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        eager = nq.lrb_linear(dev, G.to_device_x(x_np, "bf16"))
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int32), eager.view(torch.int32)), i
+        e = C.full_check(got.cpu().numpy(), ref, x_np, G.decode_tol("bf16"), "bf16")
+        assert e["pass"], (i, e)
+
+
 TINY_PATH = [(256, 256, 64), (70, 100, 40), (1024, 2048, 512), (33, 1, 1), (1, 64, 33), (257, 96, 31)]
 
 
