@@ -448,7 +448,8 @@ def time_single_configs(device: str, reps: int = 200) -> dict:
     >= 1 GiB of distinct copies (copies 1.. drawn with SplitMix64 words, a
     sampled-row oracle check on the last one):
       single_call      -- nq_lrb_linear calls back to back, each on the next copy
-                          (one call per linear; a call is 5 kernel launches);
+                          (one call per linear; a decode-regime call is one
+                          kernel launch);
       sequence         -- the same copies as one sequence plan (one persistent
                           launch for all of them): the HBM rate;
       cache_hot        -- calls back to back on copy 0 only (cache-resident);

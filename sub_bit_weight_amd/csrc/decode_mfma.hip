@@ -257,12 +257,14 @@ __device__ void finish_rows(const StageDesc& S, int rb, int ks, int64_t o, bool 
 // column l%16, rows 4*(l/16) + [0, 4).  The expansion above permutes the
 // elements within each lane's 32, and the B pieces follow the same order.
 //
-// The pieces of a stage's input are made once per stage, by input-piece
-// tiles (eight chunks of 1024 elements each), and stored in the workspace in
-// a compact form (only the 16-byte fragment blocks of the T*kPieces used
-// columns); every row-block tile of the stage copies them into LDS chunk by
-// chunk.  (Making them in every row-block tile took about a fifth of the
-// stream rate: the loads of x and s2, the chunk maxima and the conversions.)
+// In sequences the pieces of a stage's input are made once per stage, by
+// input-piece tiles (eight chunks of 1024 elements each), and stored in the
+// workspace in a compact form (only the 16-byte fragment blocks of the
+// T*kPieces used columns); every row-block tile of the stage copies them into
+// LDS chunk by chunk.  (Making them in every row-block tile took about a fifth
+// of the stream rate: the loads of x and s2, the chunk maxima and the
+// conversions.)  A single call, bound by its chain of dependent steps rather
+// than by bytes, has each tile make its one chunk's pieces (tile_pieces).
 //
 // A workgroup covers 512 rows: each of 8 waves 64 rows as four sets of 16, set q
 // holding rows 4m + q (m = 0..15) of the wave's 64.  For MFMA step k (128
@@ -415,6 +417,31 @@ __device__ inline int max_fp8_exponent(int d) {
   return (int)(max(max(u & 0xFFu, (u >> 8) & 0xFFu), max((u >> 16) & 0xFFu, u >> 24)) >> 3);
 }
 
+// The kPieces fp8 pieces of four consecutive reduction positions r (already
+// times 2^shift), one packed dword per piece: emit(p, dword).  The partner
+// thread (lane ^ 1, the other half of the group of 8) must run it too.
+template <typename Emit>
+__device__ inline void cut_pieces(float (&r)[4], Emit emit) {
+#pragma unroll
+  for (int p = 0; p < kPieces; ++p) {
+    int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+    d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
+    int emax = max_fp8_exponent(d);  // with the partner thread: one group of 8
+    emax = max(emax, (int)lane_xor1((unsigned)emax));
+    d = keep_fp8_exponents(d, max(1, emax - 7));
+    emit(p, d);
+    if (p + 1 < kPieces) {
+      typedef float v2f __attribute__((ext_vector_type(2)));
+      const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
+      const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
+      r[0] = (r[0] - lo.x) * 16.0f;
+      r[1] = (r[1] - lo.y) * 16.0f;
+      r[2] = (r[2] - hi.x) * 16.0f;
+      r[3] = (r[3] - hi.y) * 16.0f;
+    }
+  }
+}
+
 // Compact piece layout of one chunk: 16-byte blocks, block
 // ((step*2 + half)*4 + group)*NC + column holds half `half` of the B fragment
 // of lane (column % 16) + 16*group in column group column / 16, MFMA step
@@ -490,25 +517,10 @@ __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* e
         for (int k = 0; k < 4; ++k)
           r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000)
                                     : ldexpf(piece_value(S, in, tg, task, c0, S.n_red, k), shift);
-#pragma unroll
-        for (int p = 0; p < kPieces; ++p) {
-          int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
-          d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
-          // this dword and the partner thread's (task ^ 1, same wave) form one group of 8
-          int emax = max_fp8_exponent(d);
-          emax = max(emax, (int)lane_xor1((unsigned)emax));
-          d = keep_fp8_exponents(d, max(1, emax - 7));
+        // this dword and the partner thread's (task ^ 1, same wave) form one group of 8
+        cut_pieces(r, [&](int p, int d) {
           store_agent(reinterpret_cast<float*>(dst + (t * kPieces + p) * 4), __int_as_float(d));
-          if (p + 1 < kPieces) {
-            typedef float v2f __attribute__((ext_vector_type(2)));
-            const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
-            const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
-            r[0] = (r[0] - lo.x) * 16.0f;
-            r[1] = (r[1] - lo.y) * 16.0f;
-            r[2] = (r[2] - hi.x) * 16.0f;
-            r[3] = (r[3] - hi.y) * 16.0f;
-          }
-        }
+        });
         if (task == 0) store_agent(reinterpret_cast<float*>(S.bsig + (int64_t)ch * T + t), __int_as_float(shift));
       }
     }
@@ -581,25 +593,10 @@ __device__ inline void tile_pieces(const StageDesc& S, int64_t c0, int* lds) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000) : ldexpf(piece_value(S, in, i, task, c0, cend, k), shift);
-#pragma unroll
-    for (int p = 0; p < kPieces; ++p) {
-      int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
-      d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
-      int emax = max_fp8_exponent(d);  // with the partner thread (task ^ 1): one group of 8
-      emax = max(emax, (int)lane_xor1((unsigned)emax));
-      d = keep_fp8_exponents(d, max(1, emax - 7));
+    cut_pieces(r, [&](int p, int d) {  // the partner thread is task ^ 1, same wave
       const int n = t * kPieces + p;
       lds[base + (n / 16) * kStepInts + (n % 16) * 4] = d;
-      if (p + 1 < kPieces) {
-        typedef float v2f __attribute__((ext_vector_type(2)));
-        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
-        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
-        r[0] = (r[0] - lo.x) * 16.0f;
-        r[1] = (r[1] - lo.y) * 16.0f;
-        r[2] = (r[2] - hi.x) * 16.0f;
-        r[3] = (r[3] - hi.y) * 16.0f;
-      }
-    }
+    });
     if (task == 0) lds[sig_off<T>() + t] = shift;
   }
   __syncthreads();  // the chunk's fragments are in LDS buffer 0
