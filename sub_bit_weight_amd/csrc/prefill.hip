@@ -280,6 +280,103 @@ __global__ __launch_bounds__(NTH) void prep_kernel(const void* __restrict__ a, c
   }
 }
 
+// prep_kernel for bf16 activations in the rotated encoding with the row in one
+// reduction piece (every entry of a sequence), with coalesced memory access:
+// thread tid takes the 8-element chunks tid + i*NTH (i < CPT) of the row, so a
+// wave's loads of x and s2 and its stores cover contiguous bytes (the general
+// kernel's thread takes whole 32-element blocks, and its 16-byte accesses at a
+// 64- or 128-byte lane stride cost the address unit four times the cache-line
+// visits).  A block's four chunks sit in four neighbouring threads of one round;
+// the values go through LDS in element order and each thread reads back its
+// chunk's slots in the rotated order.  Values, exponents, correction sums and
+// the next stage's exponent are those of prep_kernel (the sums over the row
+// are taken in another order).
+template <int NTH, int CPT>
+__global__ __launch_bounds__(NTH) void prep_rot_bf16_kernel(const uint16_t* __restrict__ x, const float* __restrict__ cs,
+                                                            int64_t M, int64_t K, int64_t Kpad,
+                                                            _Float16* __restrict__ out, int* __restrict__ e_out,
+                                                            float* __restrict__ c_out, int* __restrict__ e_next) {
+  constexpr int NW = NTH / 64;
+  __shared__ float red[NW];
+  __shared__ uint16_t stage[NTH * 8];  // one round's fp16 values, element order
+  const int64_t m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t nch = Kpad / 8;
+  float v[CPT][8];
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int64_t c = tid + (int64_t)i * NTH;
+    if (c * 8 < K) {  // K % 8 == 0: a chunk is wholly inside or past the row
+      const uint4 w = *reinterpret_cast<const uint4*>(x + m * K + c * 8);
+      const float4 s0 = *reinterpret_cast<const float4*>(cs + c * 8);
+      const float4 s1 = *reinterpret_cast<const float4*>(cs + c * 8 + 4);
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+      const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[i][2 * k] = __uint_as_float(u[k] << 16) * sc[2 * k];
+        v[i][2 * k + 1] = __uint_as_float(u[k] & 0xFFFF0000u) * sc[2 * k + 1];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[i][k] = 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(v[i][k]));
+  }
+  mx = wg_reduce<NW, true>(mx, red);
+  int e = 0;
+  if (mx > 0.0f && isfinite(mx)) {
+    int ex;
+    frexpf(mx, &ex);
+    e = 11 - ex;  // room for the x8 prescale of the rotated order
+  }
+  if (tid == 0) e_out[m] = e;
+  float csum = 0.0f, l1 = 0.0f;
+  const int q = tid % 4;              // this chunk's place in its 32-element block
+  const int bt = (tid - q) * 8;       // the block's first element in `stage`
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int64_t c = tid + (int64_t)i * NTH;
+    if (i > 0) __syncthreads();  // the previous round's reads are done
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      stage[tid * 8 + k] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v[i][k], e));
+    __syncthreads();
+    if (c < nch) {
+      uint32_t o[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        _Float16 h2[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          // slot j = 8q + 2d + half of the block; its pair index j/2 = 4q + d
+          const int j = 8 * q + 2 * d + half;
+          const float hx = (float)__builtin_bit_cast(_Float16, stage[bt + rot_element(j)]);
+          h2[half] = (_Float16)(kPre[d] * hx);
+          csum += (float)(kPre[d] - 1) * hx;
+          l1 += fabsf(hx);
+        }
+        o[d] = (uint32_t)__builtin_bit_cast(uint16_t, h2[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, h2[1]) << 16);
+      }
+      *reinterpret_cast<uint4*>(out + m * Kpad + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  csum = wg_reduce<NW, false>(csum, red);
+  if (tid == 0) c_out[m] = csum;
+  if (e_next) {
+    l1 = wg_reduce<NW, false>(l1, red);
+    int en = 0;
+    if (l1 > 0.0f && isfinite(l1)) {
+      int ex;
+      frexpf(l1, &ex);
+      en = 14 + e - ex;
+    }
+    if (tid == 0) e_next[m] = en;
+  }
+}
+
 // +-1 fp16 operand of a 32x32x16 MFMA lane: 8 signs of one column, the pairs
 // (b+d, b+d+16) for d = 0..3 of sign word w; fp16 1.0 = 0x3C00, sign bit 15.
 // `mask` (0x80008000) and `one` (0x3C003C00) arrive as kernel arguments: held
@@ -646,6 +743,24 @@ hipError_t launch_prep(const void* a, const float* cs, int64_t M, int64_t K, int
   const int vec = (reinterpret_cast<uintptr_t>(a) % 16 == 0) && (reinterpret_cast<uintptr_t>(cs) % 16 == 0) &&
                   ((K * esize) % 16 == 0);
   const dim3 grid((unsigned)M, (unsigned)npieces);
+  if (SRC == kABF16Scaled && nt == 1 && npieces == 1 && vec) {  // coalesced variant, rows up to 32768
+    const int64_t nch = Kpad / 8;
+#define NQ_PREP_ROT(NTH, CPT)                                                                                 \
+  hipLaunchKernelGGL((prep_rot_bf16_kernel<NTH, CPT>), dim3((unsigned)M), dim3(NTH), 0, s,                    \
+                     static_cast<const uint16_t*>(a), cs, M, K, Kpad, out, e, c, e_next)
+    if (nch <= 256)
+      NQ_PREP_ROT(256, 1);
+    else if (nch <= 512)
+      NQ_PREP_ROT(256, 2);
+    else if (nch <= 1024)
+      NQ_PREP_ROT(256, 4);
+    else if (nch <= 2048)
+      NQ_PREP_ROT(256, 8);
+    else if (nch <= 4096)
+      NQ_PREP_ROT(512, 8);
+#undef NQ_PREP_ROT
+    if (nch <= 4096) return hipGetLastError();
+  }
   // 1 to 8 waves per (row, piece), the fewest that hold the piece in registers
   const int64_t pblk = imin((int64_t)bps, Kpad / 32);
 #define NQ_PREP(ROT, NTH, BPT)                                                                                    \
