@@ -417,27 +417,41 @@ __device__ inline int max_fp8_exponent(int d) {
   return (int)(max(max(u & 0xFFu, (u >> 8) & 0xFFu), max((u >> 16) & 0xFFu, u >> 24)) >> 3);
 }
 
-// The kPieces fp8 pieces of four consecutive reduction positions r (already
-// times 2^shift), one packed dword per piece: emit(p, dword).  The partner
-// thread (lane ^ 1, the other half of the group of 8) must run it too.
-template <typename Emit>
-__device__ inline void cut_pieces(float (&r)[4], Emit emit) {
+// The kPieces fp8 pieces of four consecutive reduction positions, for NT
+// tokens at once: r[i] holds token i's four values (already times 2^shift);
+// emit(i, p, dword) receives piece p of token i as one packed dword.  The
+// pieces of a token depend on one another (each is cut from the remainder of
+// the last), so the tokens' chains are interleaved piece by piece.  The
+// partner thread (lane ^ 1, the other half of each group of 8) must run it
+// too.
+template <int NT, typename Emit>
+__device__ inline void cut_pieces(float (&r)[NT][4], Emit emit) {
 #pragma unroll
   for (int p = 0; p < kPieces; ++p) {
-    int d = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
-    d = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], d, true);
-    int emax = max_fp8_exponent(d);  // with the partner thread: one group of 8
-    emax = max(emax, (int)lane_xor1((unsigned)emax));
-    d = keep_fp8_exponents(d, max(1, emax - 7));
-    emit(p, d);
+    int d[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      d[i] = __builtin_amdgcn_cvt_pk_fp8_f32(r[i][0], r[i][1], 0, false);
+      d[i] = __builtin_amdgcn_cvt_pk_fp8_f32(r[i][2], r[i][3], d[i], true);
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      int emax = max_fp8_exponent(d[i]);  // with the partner thread: one group of 8
+      emax = max(emax, (int)lane_xor1((unsigned)emax));
+      d[i] = keep_fp8_exponents(d[i], max(1, emax - 7));
+      emit(i, p, d[i]);
+    }
     if (p + 1 < kPieces) {
-      typedef float v2f __attribute__((ext_vector_type(2)));
-      const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
-      const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
-      r[0] = (r[0] - lo.x) * 16.0f;
-      r[1] = (r[1] - lo.y) * 16.0f;
-      r[2] = (r[2] - hi.x) * 16.0f;
-      r[3] = (r[3] - hi.y) * 16.0f;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        typedef float v2f __attribute__((ext_vector_type(2)));
+        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(d[i], false);
+        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(d[i], true);
+        r[i][0] = (r[i][0] - lo.x) * 16.0f;
+        r[i][1] = (r[i][1] - lo.y) * 16.0f;
+        r[i][2] = (r[i][2] - hi.x) * 16.0f;
+        r[i][3] = (r[i][3] - hi.y) * 16.0f;
+      }
     }
   }
 }
@@ -508,20 +522,27 @@ __device__ void mfma_prep_tile(const StageDesc& S, int tile, float* ldsf, int* e
     __syncthreads();  // the items' maxima are complete
     if (mine) {
       uint32_t* dst = S.bfrag + (int64_t)ch * chunk_blocks<T>() * 4 + task_off;
+      // tokens in pairs (all TG at once costs the sequence kernel registers)
+      constexpr int NP = TG > 1 ? 2 : 1;
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg) {
-        const int t = tok0 + tg;
-        const int shift = chunk_shift(slot[tg]);
-        float r[4];
+      for (int tg0 = 0; tg0 < TG; tg0 += NP) {
+        float r[NP][4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000)
-                                    : ldexpf(piece_value(S, in, tg, task, c0, S.n_red, k), shift);
-        // this dword and the partner thread's (task ^ 1, same wave) form one group of 8
-        cut_pieces(r, [&](int p, int d) {
-          store_agent(reinterpret_cast<float*>(dst + (t * kPieces + p) * 4), __int_as_float(d));
+        for (int i = 0; i < NP; ++i) {
+          const int tg = min(tg0 + i, TG - 1);
+          const int shift = chunk_shift(slot[tg]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            r[i][k] = shift == kShiftNaN ? __int_as_float(0x7FC00000)
+                                         : ldexpf(piece_value(S, in, tg, task, c0, S.n_red, k), shift);
+          if (task == 0 && tg0 + i < TG)
+            store_agent(reinterpret_cast<float*>(S.bsig + (int64_t)ch * T + tok0 + tg), __int_as_float(shift));
+        }
+        // each dword and the partner thread's (task ^ 1, same wave) form one group of 8
+        cut_pieces<NP>(r, [&](int i, int p, int d) {
+          if (tg0 + i < TG)
+            store_agent(reinterpret_cast<float*>(dst + ((tok0 + tg0 + i) * kPieces + p) * 4), __int_as_float(d));
         });
-        if (task == 0) store_agent(reinterpret_cast<float*>(S.bsig + (int64_t)ch * T + t), __int_as_float(shift));
       }
     }
     __syncthreads();  // every thread has read this round's maxima
@@ -584,21 +605,23 @@ __device__ inline void tile_pieces(const StageDesc& S, int64_t c0, int* lds) {
   // LDS place of column n's dword: block (kk, group gp, half gw >> 1) of
   // column n in column group n / 16, dword 2 * (j & 1) + ih
   const int base = kk * G * kStepInts + (gw >> 1) * 256 + 16 * gp * 4 + 2 * (j & 1) + ih;
+  float r[TH][4];
 #pragma unroll
   for (int i = 0; i < TH; ++i) {
-    const int t = half + 2 * i;  // uniform over a wave
-    if (t >= T) continue;
+    const int t = min(half + 2 * i, T - 1);  // past T: a copy of token T-1, not stored
     const int shift = chunk_shift(slot[t]);
-    float r[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      r[k] = shift == kShiftNaN ? __int_as_float(0x7FC00000) : ldexpf(piece_value(S, in, i, task, c0, cend, k), shift);
-    cut_pieces(r, [&](int p, int d) {  // the partner thread is task ^ 1, same wave
+      r[i][k] = shift == kShiftNaN ? __int_as_float(0x7FC00000) : ldexpf(piece_value(S, in, i, task, c0, cend, k), shift);
+    if (task == 0 && half + 2 * i < T) lds[sig_off<T>() + t] = shift;
+  }
+  cut_pieces<TH>(r, [&](int i, int p, int d) {  // the partner thread is task ^ 1, same wave
+    const int t = half + 2 * i;  // uniform over a wave
+    if (t < T) {
       const int n = t * kPieces + p;
       lds[base + (n / 16) * kStepInts + (n % 16) * 4] = d;
-    });
-    if (task == 0) lds[sig_off<T>() + t] = shift;
-  }
+    }
+  });
   __syncthreads();  // the chunk's fragments are in LDS buffer 0
 }
 
