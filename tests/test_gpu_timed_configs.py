@@ -239,3 +239,13 @@ def test_layer_struct_validation():
             L.struct()
         with pytest.raises(ValueError):
             nq.lrb_linear(L, torch.zeros((1, shape.d_in), dtype=torch.bfloat16, device=G.DEV))
+    # the checked struct is kept between calls; assigning a field checks again
+    x = torch.zeros((1, shape.d_in), dtype=torch.bfloat16, device=G.DEV)
+    nq.lrb_linear(good, x)
+    s1 = good.s1
+    good.s1 = s1[:99]
+    with pytest.raises(ValueError):
+        nq.lrb_linear(good, x)
+    good.s1 = s1
+    nq.lrb_linear(good, x)
+    torch.cuda.synchronize()
