@@ -249,7 +249,7 @@ def time_prefill(stack, T: int, device: str, passes: int = 7):
     return times, seq, xs, ys
 
 
-def time_scale_grads(stack, T: int, device: str, reps: int = 3) -> dict:
+def time_scale_grads(stack, T: int, device: str, reps: int = 3, profile_passes: int = 0) -> dict:
     """The scale-only reconstruction step (gradients of s1, s2 and x for a given
     output gradient) over the linears of layer 0 at T tokens: the transposed
     sign words are made once (timed separately), then `reps` passes."""
@@ -289,6 +289,11 @@ def time_scale_grads(stack, T: int, device: str, reps: int = 3) -> dict:
         for L, a, x, g in zip(layers, adjs, xs, gs):
             nq.lrb_scale_grads(L, a, x, g, workspace=ws)
     wsb = torch.empty(nq.lrb_scale_grads_batch_workspace_bytes(layers, T), dtype=torch.uint8, device=device)
+    if profile_passes:  # for a kernel trace: batched passes with an idle gap between them
+        for _ in range(profile_passes):
+            nq.lrb_scale_grads_batch(layers, adjs, xs, gs, workspace=wsb)
+            torch.cuda.synchronize()
+        return {}
 
     def grads_batch():
         return nq.lrb_scale_grads_batch(layers, adjs, xs, gs, workspace=wsb)
@@ -736,6 +741,9 @@ def main() -> int:
                     help="also time the prefill pass as serial single-linear calls on one stream")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
+    ap.add_argument("--grads-profile", type=int, default=0, metavar="N",
+                    help="run layer 0's batched scale gradients at T=2048 N times, synchronising between "
+                         "passes (for a kernel trace), and exit")
     ap.add_argument("--prefill-profile", type=int, default=0, metavar="N",
                     help="only run layer 0's seven T=2048 linears N times each, one after another, each as a "
                          "one-entry sequence plan (the kernels and tiles of the benchmarked pass, in a fixed "
@@ -764,6 +772,12 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"bytes_read_per_copy": a.numel() * 4,
                                                "bytes_written_per_copy": a.numel() * 4, "copies": 5}}))
+        return 0
+
+    if args.grads_profile:
+        stack = Stack(synth.stack_config(1.0), 1, device)
+        time_scale_grads(stack, 2048, device, profile_passes=args.grads_profile)
+        log(f"[bench] profile: scale gradients, layer 0, T=2048 x{args.grads_profile}")
         return 0
 
     if args.prefill_profile:
